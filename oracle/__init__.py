@@ -1,0 +1,131 @@
+"""Python view of the CPU oracle (test infrastructure only).
+
+Only the tests, the smoke check and the benchmark's CPU-baseline leg import
+this package. The GPU library never does, and this package never imports the
+GPU library.
+
+Arrays cross as numpy arrays holding the raw storage of the dtype:
+float32 for "f32", uint16 bit patterns for "bf16" and "f16".
+"""
+import ctypes
+import os
+
+import numpy as np
+
+from .build import LIB, build as _build
+
+DTYPES = {"f32": 0, "bf16": 1, "f16": 2}
+OPS = {"fwd": 0, "dx": 1, "dw": 2}
+STORAGE = {"f32": np.float32, "bf16": np.uint16, "f16": np.uint16}
+
+
+class Oracle:
+    """Handle on one build of the oracle's shared object."""
+
+    def __init__(self, path=LIB):
+        L = ctypes.CDLL(path)
+        L.oracle_gemm.restype = ctypes.c_int
+        L.oracle_gemm.argtypes = [
+            ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+            ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_void_p, ctypes.c_int64,
+            ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+        ]
+        L.oracle_round.restype = ctypes.c_int
+        L.oracle_round.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_void_p]
+        L.oracle_env_ok.restype = ctypes.c_int
+        L.oracle_version.restype = ctypes.c_int
+        if L.oracle_env_ok() != 1:
+            raise RuntimeError("oracle: floating-point environment is not IEEE RNE without FTZ/DAZ")
+        self.L = L
+        self.path = path
+
+    def gemm(self, op, dt, A, B, m, k, n, bias=None, rows=None, want_r=False, want_S=False):
+        """Evaluate output rows of op in {"fwd","dx","dw"}; shapes are always (m,k,n) of the forward.
+
+        fwd: A = X[m,k], B = W[k,n] -> Y[m,n] (+ bias[n]);  dx: A = dY[m,n], B = W[k,n] -> dX[m,k];
+        dw : A = X[m,k], B = dY[m,n] -> dW[k,n].  Returns (y, r, S); r and S are float64 or None.
+        """
+        o = OPS[op]
+        a_shape = (m, k) if op in ("fwd", "dw") else (m, n)
+        b_shape = (k, n) if op in ("fwd", "dx") else (m, n)
+        _check(A, dt, a_shape, "A")
+        _check(B, dt, b_shape, "B")
+        if bias is not None:
+            _check(bias, dt, (n,), "bias")
+        out_rows = k if op == "dw" else m
+        cols = k if op == "dx" else n
+        if rows is not None:
+            rows = np.ascontiguousarray(rows, dtype=np.int64)
+            nrows = rows.shape[0]
+        else:
+            nrows = out_rows
+        y = np.zeros((nrows, cols), dtype=STORAGE[dt])
+        r = np.zeros((nrows, cols), dtype=np.float64) if want_r else None
+        S = np.zeros((nrows, cols), dtype=np.float64) if want_S else None
+        rc = self.L.oracle_gemm(o, DTYPES[dt], _ptr(A), _ptr(B), _ptr(bias), m, k, n,
+                                _ptr(rows), nrows, _ptr(y), _ptr(r), _ptr(S))
+        if rc != 0:
+            raise ValueError("oracle_gemm rejected its arguments")
+        return y, r, S
+
+    def fwd(self, dt, x, w, bias=None, rows=None, **kw):
+        m, k = x.shape
+        return self.gemm("fwd", dt, x, w, m, k, w.shape[1], bias=bias, rows=rows, **kw)
+
+    def dx(self, dt, dy, w, rows=None, **kw):
+        m, n = dy.shape
+        return self.gemm("dx", dt, dy, w, m, w.shape[0], n, rows=rows, **kw)
+
+    def dw(self, dt, x, dy, rows=None, **kw):
+        m, k = x.shape
+        return self.gemm("dw", dt, x, dy, m, k, dy.shape[1], rows=rows, **kw)
+
+    def round_to(self, dt, r):
+        """Single RNE rounding of float64 values to dt (raw storage out)."""
+        r = np.ascontiguousarray(r, dtype=np.float64)
+        out = np.zeros(r.shape, dtype=STORAGE[dt])
+        if self.L.oracle_round(_ptr(r), r.size, DTYPES[dt], _ptr(out)) != 0:
+            raise ValueError("oracle_round rejected its arguments")
+        return out
+
+
+def _ptr(a):
+    return None if a is None else a.ctypes.data
+
+
+def _check(a, dt, shape, name):
+    if a.dtype != STORAGE[dt] or tuple(a.shape) != tuple(shape) or not a.flags.c_contiguous:
+        raise ValueError(f"oracle: {name} must be a C-contiguous {STORAGE[dt].__name__} array of shape {shape}")
+
+
+_default = None
+
+
+def default():
+    """The oracle built from oracle.cpp in this directory (built on first use if absent)."""
+    global _default
+    if _default is None:
+        if not os.path.exists(LIB):
+            _build()
+        _default = Oracle(LIB)
+    return _default
+
+
+def gemm(*a, **kw):
+    return default().gemm(*a, **kw)
+
+
+def fwd(*a, **kw):
+    return default().fwd(*a, **kw)
+
+
+def dx(*a, **kw):
+    return default().dx(*a, **kw)
+
+
+def dw(*a, **kw):
+    return default().dw(*a, **kw)
+
+
+def round_to(*a, **kw):
+    return default().round_to(*a, **kw)

@@ -1,0 +1,269 @@
+// Plain CPU oracle for the deterministic, batch-invariant GEMM.
+//
+// TEST INFRASTRUCTURE ONLY. Nothing in the GPU library links, includes or
+// calls this file; only the test suite, the smoke check and the CPU-baseline
+// leg of the benchmark load the shared object built from it. It shares no
+// code, header, table or helper with the GPU kernels.
+//
+// It is deliberately slow and single-threaded: every output element is one
+// call of kbn_dot(), written straight from the definition below.
+//
+// What is computed
+// ----------------
+// Carbon README (alia-carbon 0.2.0), "How It Works": a matmul is split into
+// tiles, the operands are upcast to float64, and the tile results are
+// accumulated with Kahan-Babushka-Neumaier (KBN) compensation in a fixed order.
+// The page leaves the tile geometry and the within-tile order open; the
+// readings taken here (each one listed in DESIGN.md, "Readings of the pages"):
+//   * the reduction index is cut into tiles of KT = 32 consecutive indices,
+//     anchored at index 0; the last tile may be short;
+//   * inside tile t the partial is p_t = +0.0 followed by p_t = fma(a_k, b_k, p_t)
+//     for k ascending (every product of two upcast f32/bf16/f16 values is exact
+//     in float64, so each step rounds once);
+//   * across tiles, Neumaier's variant of compensated summation, in ascending
+//     tile order, from (s, c) = (+0.0, +0.0); the result is r = s + c;
+//   * the forward bias is added after the compensated sum, r = r + b_j, in
+//     float64;
+//   * the output is a single round-to-nearest-even from float64 to the output
+//     dtype (sgemm-bi 0.1.2 PyPI page, "Determinism contracts", names an RNE
+//     downcast; here it is applied once, from float64).
+//
+// The three operations (sgemm-bi page, "Use": forward, dW and dX of a linear
+// layer whose weight is stored [in, out]):
+//   fwd: Y[i,j]  = sum_k X[i,k]  * W[k,j]   (+ b[j])   reduction over k < K
+//   dx : dX[i,q] = sum_n dY[i,n] * W[q,n]              reduction over n < N
+//   dw : dW[q,j] = sum_i X[i,q]  * dY[i,j]             reduction over i < M
+//
+// Alongside each output the oracle can return r (the float64 value before the
+// downcast) and S = sum |a_k * b_k| + |b_j|, which bound the fast tier's error.
+
+#include <cfenv>
+#include <cmath>
+#include <cstdint>
+#include <cstring>
+#include <vector>
+#include <algorithm>
+#include <xmmintrin.h>
+
+namespace {
+
+enum Dtype { DT_F32 = 0, DT_BF16 = 1, DT_F16 = 2 };
+enum Op { OP_FWD = 0, OP_DX = 1, OP_DW = 2 };
+constexpr int64_t KT = 32;  // tile width along the reduction index
+
+// ---- exact decode of one stored element into float64 ------------------------
+
+double decode_f16(uint16_t h) {
+  const int sign = h >> 15;
+  const int e = (h >> 10) & 0x1f;
+  const int m = h & 0x3ff;
+  double v;
+  if (e == 0) {
+    v = std::ldexp(static_cast<double>(m), -24);              // zero or subnormal
+  } else if (e == 0x1f) {
+    v = m ? std::nan("") : HUGE_VAL;                          // NaN or infinity
+  } else {
+    v = std::ldexp(static_cast<double>(1024 + m), e - 25);    // normal
+  }
+  return sign ? -v : v;
+}
+
+double decode_bf16(uint16_t h) {
+  const uint32_t u = static_cast<uint32_t>(h) << 16;  // bf16 is the top half of an f32
+  float f;
+  std::memcpy(&f, &u, 4);
+  return static_cast<double>(f);
+}
+
+double decode(const void* base, int64_t idx, int dt) {
+  if (dt == DT_F32) {
+    float f;
+    std::memcpy(&f, static_cast<const char*>(base) + 4 * idx, 4);
+    return static_cast<double>(f);
+  }
+  uint16_t h;
+  std::memcpy(&h, static_cast<const char*>(base) + 2 * idx, 2);
+  return dt == DT_BF16 ? decode_bf16(h) : decode_f16(h);
+}
+
+// ---- single round-to-nearest-even from float64 to the output dtype ----------
+//
+// For the 16-bit formats the rounding is a search in an exhaustive table of
+// every finite non-negative encoding (codes 0 .. max_finite, whose values
+// increase with the code). Ties go to the code with an even last bit. Values
+// at or beyond max_finite + half an ulp go to infinity, as IEEE RNE does.
+
+struct Table16 {
+  std::vector<double> val;   // val[code] for code = 0 .. max_finite
+  uint16_t max_finite;
+  uint16_t inf_code;
+  uint16_t nan_code;
+  double beyond;             // the value the next code would have (2^(emax+1))
+};
+
+Table16 make_table(int dt) {
+  Table16 t;
+  if (dt == DT_BF16) {
+    t.max_finite = 0x7f7f; t.inf_code = 0x7f80; t.nan_code = 0x7fc0; t.beyond = std::ldexp(1.0, 128);
+  } else {
+    t.max_finite = 0x7bff; t.inf_code = 0x7c00; t.nan_code = 0x7e00; t.beyond = std::ldexp(1.0, 16);
+  }
+  for (uint32_t code = 0; code <= t.max_finite; ++code) {
+    const uint16_t h = static_cast<uint16_t>(code);
+    t.val.push_back(dt == DT_BF16 ? decode_bf16(h) : decode_f16(h));
+  }
+  return t;
+}
+
+const Table16& table(int dt) {
+  static const Table16 bf = make_table(DT_BF16);
+  static const Table16 hf = make_table(DT_F16);
+  return dt == DT_BF16 ? bf : hf;
+}
+
+uint16_t round_to_16(double r, int dt) {
+  const Table16& t = table(dt);
+  if (std::isnan(r)) return t.nan_code;
+  const uint16_t sign = std::signbit(r) ? 0x8000 : 0;
+  const double a = std::fabs(r);
+  // lo = largest code whose value is <= a
+  const auto it = std::upper_bound(t.val.begin(), t.val.end(), a);
+  const uint16_t lo = static_cast<uint16_t>((it - t.val.begin()) - 1);
+  if (t.val[lo] == a) return static_cast<uint16_t>(lo | sign);
+  const bool lo_is_max = (lo == t.max_finite);
+  const uint16_t hi = lo_is_max ? t.inf_code : static_cast<uint16_t>(lo + 1);
+  const double v_hi = lo_is_max ? t.beyond : t.val[hi];
+  // Both sums below are exact in float64 (the table holds 8- or 11-bit values).
+  const double twice = 2.0 * a;
+  const double mid2 = t.val[lo] + v_hi;
+  uint16_t code;
+  if (twice < mid2) code = lo;
+  else if (twice > mid2) code = hi;
+  else code = (lo % 2 == 0) ? lo : hi;
+  return static_cast<uint16_t>(code | sign);
+}
+
+void store(void* out, int64_t idx, double r, int dt) {
+  if (dt == DT_F32) {
+    const float f = static_cast<float>(r);  // RNE under the default environment
+    std::memcpy(static_cast<char*>(out) + 4 * idx, &f, 4);
+  } else {
+    const uint16_t h = round_to_16(r, dt);
+    std::memcpy(static_cast<char*>(out) + 2 * idx, &h, 2);
+  }
+}
+
+// ---- the compensated tiled dot product (the whole method for one output) ----
+//
+// a[0..L) and b[0..L) are the two operand sequences along the reduction index,
+// already upcast to float64. Returns r = s + c; *S receives sum |a_k * b_k|.
+
+double kbn_dot(const double* a, const double* b, int64_t L, double* S) {
+  double s = +0.0;
+  double c = +0.0;
+  double abs_sum = 0.0;
+  for (int64_t t0 = 0; t0 < L; t0 += KT) {
+    const int64_t t1 = std::min(t0 + KT, L);
+    double p = +0.0;                        // tile partial p_t
+    for (int64_t k = t0; k < t1; ++k) {
+      p = std::fma(a[k], b[k], p);
+      abs_sum = abs_sum + std::fabs(a[k] * b[k]);
+    }
+    // Neumaier's update of (s, c) with the next tile partial
+    const double tt = s + p;
+    if (std::fabs(s) >= std::fabs(p)) {
+      c = c + ((s - tt) + p);
+    } else {
+      c = c + ((p - tt) + s);
+    }
+    s = tt;
+  }
+  *S = abs_sum;
+  return s + c;
+}
+
+}  // namespace
+
+extern "C" {
+
+int oracle_version(void) { return 1; }
+
+// 1 when the floating-point environment is the IEEE default this oracle needs:
+// round-to-nearest-even, no flush-to-zero, no denormals-are-zero.
+int oracle_env_ok(void) {
+  const unsigned csr = _mm_getcsr();
+  const bool ftz = (csr & 0x8000u) != 0;
+  const bool daz = (csr & 0x0040u) != 0;
+  return (std::fegetround() == FE_TONEAREST && !ftz && !daz) ? 1 : 0;
+}
+
+// Round cnt float64 values to dtype dt (raw bits out: f32 as 4 bytes, bf16/f16 as 2).
+int oracle_round(const double* r, int64_t cnt, int dt, void* out) {
+  if (dt < DT_F32 || dt > DT_F16 || cnt < 0 || (cnt > 0 && (!r || !out))) return -1;
+  for (int64_t i = 0; i < cnt; ++i) store(out, i, r[i], dt);
+  return 0;
+}
+
+// Evaluate rows of one GEMM output.
+//   op   : 0 fwd (A = X[m,k], B = W[k,n], out Y[m,n], bias[n] nullable)
+//          1 dx  (A = dY[m,n], B = W[k,n], out dX[m,k])
+//          2 dw  (A = X[m,k], B = dY[m,n], out dW[k,n])
+//   rows : output row indices to evaluate (NULL: all output rows, in order)
+//   y    : nrows x cols output, raw bits of dtype dt
+//   r, S : nullable nrows x cols float64 (value before rounding; abs-sum bound)
+// Returns 0, or -1 on invalid arguments.
+int oracle_gemm(int op, int dt, const void* A, const void* B, const void* bias,
+                int64_t m, int64_t k, int64_t n, const int64_t* rows, int64_t nrows,
+                void* y, double* r, double* S) {
+  if (op < OP_FWD || op > OP_DW || dt < DT_F32 || dt > DT_F16) return -1;
+  if (m < 1 || k < 1 || n < 1 || !A || !B || !y) return -1;
+  if (op != OP_FWD && bias) return -1;
+  const int64_t out_rows = (op == OP_DW) ? k : m;
+  const int64_t cols = (op == OP_DX) ? k : n;
+  const int64_t L = (op == OP_FWD) ? k : (op == OP_DX ? n : m);  // reduction length
+  if (!rows) nrows = out_rows;
+  for (int64_t ii = 0; ii < nrows; ++ii) {
+    const int64_t row = rows ? rows[ii] : ii;
+    if (row < 0 || row >= out_rows) return -1;
+  }
+
+  // Operand sequences along the reduction index, upcast to float64:
+  //   lhs(row)[l] and rhs(col)[l], l = 0 .. L-1.
+  std::vector<double> rhs(static_cast<size_t>(cols * L));
+  for (int64_t col = 0; col < cols; ++col) {
+    for (int64_t l = 0; l < L; ++l) {
+      int64_t idx;
+      if (op == OP_FWD) idx = l * n + col;        // W[l, col]
+      else if (op == OP_DX) idx = col * n + l;    // W[col, l]
+      else idx = l * n + col;                     // dY[l, col]
+      rhs[col * L + l] = decode(B, idx, dt);
+    }
+  }
+  std::vector<double> lhs(static_cast<size_t>(L));
+  for (int64_t ii = 0; ii < nrows; ++ii) {
+    const int64_t row = rows ? rows[ii] : ii;
+    for (int64_t l = 0; l < L; ++l) {
+      int64_t idx;
+      if (op == OP_FWD) idx = row * k + l;        // X[row, l]
+      else if (op == OP_DX) idx = row * n + l;    // dY[row, l]
+      else idx = l * k + row;                     // X[l, row]
+      lhs[l] = decode(A, idx, dt);
+    }
+    for (int64_t col = 0; col < cols; ++col) {
+      double abs_sum;
+      double v = kbn_dot(lhs.data(), &rhs[col * L], L, &abs_sum);
+      if (bias) {
+        const double bj = decode(bias, col, dt);
+        v = v + bj;
+        abs_sum = abs_sum + std::fabs(bj);
+      }
+      const int64_t o = ii * cols + col;
+      store(y, o, v, dt);
+      if (r) r[o] = v;
+      if (S) S[o] = abs_sum;
+    }
+  }
+  return 0;
+}
+
+}  // extern "C"
