@@ -1,0 +1,260 @@
+"""Python binding of libdetgemm.so: argument marshalling only.
+
+The C entry points (include/det_gemm.h) are exposed under the same names and
+take raw device pointers (ints) or torch tensors, plus an explicit stream, as
+the sgemm-bi 0.1.2 PyPI page's low-level engine does ("Use": raw pointers,
+explicit stream). On top of them sit a functional form, an autograd function
+and a drop-in layer with the weight stored [in, out] (same page, "Use"). Every
+GEMM runs in the library's HIP kernels; there is no fallback path, and a
+missing library raises at first use.
+"""
+import ctypes
+import os
+
+__all__ = [
+    "det_gemm_fwd", "det_gemm_dx", "det_gemm_dw", "det_gemm_strerror", "det_gemm_last_error",
+    "det_gemm_version", "det_gemm_debug_force_family", "DetGemmError", "LIB_PATH",
+    "fwd", "dx", "dw", "deterministic_linear", "Linear", "DTYPES", "TIERS",
+]
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libdetgemm.so")
+
+DTYPES = {"f32": 0, "bf16": 1, "f16": 2}
+TIERS = {"exact": 0, "fast": 1}
+STATUS = {0: "DET_OK", -1: "DET_EINVAL", -2: "DET_EDTYPE", -3: "DET_ETIER", -4: "DET_EDEVICE", -5: "DET_ELAUNCH"}
+
+
+class DetGemmError(RuntimeError):
+    def __init__(self, status, message):
+        super().__init__(f"{STATUS.get(status, status)}: {message}")
+        self.status = status
+
+
+_lib = None
+
+
+def lib():
+    """The loaded libdetgemm.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"{LIB_PATH} is missing: build it with __graft_entry__.build() "
+                              "(hipcc, gfx950); there is no fallback implementation")
+        L = ctypes.CDLL(LIB_PATH)
+        vp, i64, ci = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
+        L.det_gemm_fwd.argtypes = [vp, vp, vp, vp, i64, i64, i64, ci, ci, vp]
+        L.det_gemm_dx.argtypes = [vp, vp, vp, i64, i64, i64, ci, ci, vp]
+        L.det_gemm_dw.argtypes = [vp, vp, vp, i64, i64, i64, ci, ci, vp]
+        for f in (L.det_gemm_fwd, L.det_gemm_dx, L.det_gemm_dw):
+            f.restype = ci
+        L.det_gemm_strerror.argtypes = [ci]
+        L.det_gemm_strerror.restype = ctypes.c_char_p
+        L.det_gemm_last_error.argtypes = []
+        L.det_gemm_last_error.restype = ctypes.c_char_p
+        L.det_gemm_version.restype = ci
+        L.det_gemm_debug_force_family.argtypes = [ci]
+        L.det_gemm_debug_force_family.restype = ci
+        _lib = L
+    return _lib
+
+
+def _p(v):
+    """Pointer value of a torch tensor, an int or None."""
+    if v is None:
+        return None
+    if isinstance(v, int):
+        return v
+    return v.data_ptr()
+
+
+def _code(table, v, what):
+    if isinstance(v, int):
+        return v
+    try:
+        return table[v]
+    except KeyError:
+        raise ValueError(f"unknown {what} {v!r}") from None
+
+
+def _check(status):
+    if status != 0:
+        raise DetGemmError(status, lib().det_gemm_last_error().decode())
+
+
+def det_gemm_fwd(y, x, w, bias, m, k, n, dtype, tier, stream=0):
+    _check(lib().det_gemm_fwd(_p(y), _p(x), _p(w), _p(bias), m, k, n,
+                              _code(DTYPES, dtype, "dtype"), _code(TIERS, tier, "tier"), _p(stream)))
+
+
+def det_gemm_dx(dx_, dy, w, m, k, n, dtype, tier, stream=0):
+    _check(lib().det_gemm_dx(_p(dx_), _p(dy), _p(w), m, k, n,
+                             _code(DTYPES, dtype, "dtype"), _code(TIERS, tier, "tier"), _p(stream)))
+
+
+def det_gemm_dw(dw_, x, dy, m, k, n, dtype, tier, stream=0):
+    _check(lib().det_gemm_dw(_p(dw_), _p(x), _p(dy), m, k, n,
+                             _code(DTYPES, dtype, "dtype"), _code(TIERS, tier, "tier"), _p(stream)))
+
+
+def det_gemm_strerror(status):
+    return lib().det_gemm_strerror(status).decode()
+
+
+def det_gemm_last_error():
+    return lib().det_gemm_last_error().decode()
+
+
+def det_gemm_version():
+    return lib().det_gemm_version()
+
+
+def det_gemm_debug_force_family(family):
+    _check(lib().det_gemm_debug_force_family(family))
+
+
+# ---------------------------------------------------------------- torch layer
+
+def _torch_dtype_name(t):
+    import torch
+    names = {torch.float32: "f32", torch.bfloat16: "bf16", torch.float16: "f16"}
+    if t.dtype not in names:
+        raise TypeError(f"unsupported dtype {t.dtype}; use float32, bfloat16 or float16")
+    return names[t.dtype]
+
+
+def _prep(*ts):
+    import torch
+    out = []
+    dev = None
+    for t in ts:
+        if t is None:
+            out.append(None)
+            continue
+        if not t.is_cuda:
+            raise ValueError("det_gemm operates on device tensors")
+        if dev is None:
+            dev = t.device
+        elif t.device != dev:
+            raise ValueError("all tensors must be on one device")
+        out.append(t.contiguous())
+    if len({t.dtype for t in out if t is not None}) != 1:
+        raise TypeError("all tensors must share one dtype")
+    return out, torch.cuda.current_stream(dev).cuda_stream
+
+
+def fwd(x, w, bias=None, tier="exact", out=None):
+    """y[m,n] = x[m,k] @ w[k,n] (+ bias[n]) on the current stream."""
+    import torch
+    (x, w, bias), stream = _prep(x, w, bias)
+    m, k = x.shape
+    k2, n = w.shape
+    if k2 != k or (bias is not None and tuple(bias.shape) != (n,)):
+        raise ValueError("shape mismatch")
+    y = out if out is not None else torch.empty((m, n), dtype=x.dtype, device=x.device)
+    det_gemm_fwd(y, x, w, bias, m, k, n, _torch_dtype_name(x), tier, stream)
+    return y
+
+
+def dx(dy, w, tier="exact", out=None):
+    """dx[m,k] = dy[m,n] @ w[k,n]^T on the current stream."""
+    import torch
+    (dy, w), stream = _prep(dy, w)
+    m, n = dy.shape
+    k, n2 = w.shape
+    if n2 != n:
+        raise ValueError("shape mismatch")
+    g = out if out is not None else torch.empty((m, k), dtype=dy.dtype, device=dy.device)
+    det_gemm_dx(g, dy, w, m, k, n, _torch_dtype_name(dy), tier, stream)
+    return g
+
+
+def dw(x, dy, tier="exact", out=None):
+    """dw[k,n] = x[m,k]^T @ dy[m,n] on the current stream."""
+    import torch
+    (x, dy), stream = _prep(x, dy)
+    m, k = x.shape
+    m2, n = dy.shape
+    if m2 != m:
+        raise ValueError("shape mismatch")
+    g = out if out is not None else torch.empty((k, n), dtype=x.dtype, device=x.device)
+    det_gemm_dw(g, x, dy, m, k, n, _torch_dtype_name(x), tier, stream)
+    return g
+
+
+def _autograd_fn():
+    import torch
+
+    class DeterministicLinearFn(torch.autograd.Function):
+        @staticmethod
+        def forward(ctx, x, weight, bias, tier):
+            ctx.save_for_backward(x, weight)
+            ctx.tier = tier
+            ctx.has_bias = bias is not None
+            return fwd(x, weight, bias, tier)
+
+        @staticmethod
+        def backward(ctx, gy):
+            x, weight = ctx.saved_tensors
+            gy = gy.contiguous()
+            gx = dx(gy, weight, ctx.tier) if ctx.needs_input_grad[0] else None
+            gw = dw(x, gy, ctx.tier) if ctx.needs_input_grad[1] else None
+            gb = None
+            if ctx.has_bias and ctx.needs_input_grad[2]:
+                ones = torch.ones((x.shape[0], 1), dtype=x.dtype, device=x.device)
+                gb = dw(ones, gy, ctx.tier).reshape(-1)   # column sum in the tier's fixed order
+            return gx, gw, gb, None
+
+    return DeterministicLinearFn
+
+
+_FN = None
+
+
+def deterministic_linear(x, weight, bias=None, tier="exact"):
+    """y = x @ weight (+ bias) with weight stored [in, out]; leading dims of x are flattened."""
+    global _FN
+    if _FN is None:
+        _FN = _autograd_fn()
+    lead = x.shape[:-1]
+    y = _FN.apply(x.reshape(-1, x.shape[-1]), weight, bias, tier)
+    return y.reshape(*lead, weight.shape[1])
+
+
+def _make_linear():
+    import torch
+
+    class Linear(torch.nn.Module):
+        """Drop-in linear layer with the weight stored [in_features, out_features]."""
+
+        def __init__(self, in_features, out_features, bias=True, device=None, dtype=None, tier="exact"):
+            super().__init__()
+            self.in_features, self.out_features, self.tier = in_features, out_features, tier
+            self.weight = torch.nn.Parameter(torch.empty((in_features, out_features), device=device, dtype=dtype))
+            self.bias = torch.nn.Parameter(torch.zeros(out_features, device=device, dtype=dtype)) if bias else None
+            bound = 1.0 / (in_features ** 0.5)
+            with torch.no_grad():
+                self.weight.uniform_(-bound, bound)
+
+        @classmethod
+        def from_torch(cls, layer, tier="exact"):
+            m = cls(layer.in_features, layer.out_features, layer.bias is not None,
+                    layer.weight.device, layer.weight.dtype, tier)
+            with torch.no_grad():
+                m.weight.copy_(layer.weight.t())
+                if layer.bias is not None:
+                    m.bias.copy_(layer.bias)
+            return m
+
+        def forward(self, x):
+            return deterministic_linear(x, self.weight, self.bias, self.tier)
+
+    return Linear
+
+
+def __getattr__(name):
+    if name == "Linear":
+        cls = _make_linear()
+        globals()["Linear"] = cls
+        return cls
+    raise AttributeError(name)

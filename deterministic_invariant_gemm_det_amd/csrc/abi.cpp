@@ -1,0 +1,135 @@
+// C-ABI entry points: argument checks, device check, shape-only dispatch and
+// launch on the caller's stream. The operations and their contracts are stated
+// in include/det_gemm.h.
+
+#include "../../include/det_gemm.h"
+
+#include <atomic>
+#include <cstdio>
+#include <cstring>
+
+#include "common.hpp"
+
+namespace {
+
+thread_local char g_last_error[256] = "";
+std::atomic<int> g_force_family{-1};
+
+constexpr int kMaxDevices = 64;
+// 0 unknown, 1 gfx950, 2 not supported
+std::atomic<int> g_device_ok[kMaxDevices];
+
+det_status_t fail(det_status_t st, const char* fmt, const char* detail = "") {
+  std::snprintf(g_last_error, sizeof(g_last_error), fmt, detail);
+  return st;
+}
+
+det_status_t check_device() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) {
+    (void)hipGetLastError();
+    return fail(DET_EDEVICE, "det_gemm: no current HIP device%s");
+  }
+  if (dev >= kMaxDevices) return fail(DET_EDEVICE, "det_gemm: device index out of range%s");
+  int state = g_device_ok[dev].load(std::memory_order_acquire);
+  if (state == 0) {
+    hipDeviceProp_t prop;
+    if (hipGetDeviceProperties(&prop, dev) != hipSuccess) {
+      (void)hipGetLastError();
+      return fail(DET_EDEVICE, "det_gemm: cannot query the current device%s");
+    }
+    state = (std::strncmp(prop.gcnArchName, "gfx950", 6) == 0) ? 1 : 2;
+    g_device_ok[dev].store(state, std::memory_order_release);
+    if (state == 2) return fail(DET_EDEVICE, "det_gemm: device architecture %s is not gfx950 (MI355X); refusing to run", prop.gcnArchName);
+  }
+  if (state == 2) return fail(DET_EDEVICE, "det_gemm: the current device is not gfx950 (MI355X); refusing to run%s");
+  return DET_OK;
+}
+
+bool mul_ok(int64_t a, int64_t b, int64_t elem) {
+  int64_t p;
+  if (__builtin_mul_overflow(a, b, &p)) return false;
+  return !__builtin_mul_overflow(p, elem, &p);
+}
+
+det_status_t run(detgemm::Op op, void* out, const void* A, const void* B, const void* bias,
+                 int64_t m, int64_t k, int64_t n, det_dtype_t dt, det_tier_t tier, hipStream_t stream) {
+  g_last_error[0] = '\0';
+  if (dt != DET_F32 && dt != DET_BF16 && dt != DET_F16) return fail(DET_EDTYPE, "det_gemm: unknown dtype%s");
+  if (tier != DET_TIER_EXACT && tier != DET_TIER_FAST) return fail(DET_ETIER, "det_gemm: unknown tier%s");
+  if (!out || !A || !B) return fail(DET_EINVAL, "det_gemm: null %s pointer", !out ? "output" : "input");
+  if (m < 1 || k < 1 || n < 1) return fail(DET_EINVAL, "det_gemm: m, k and n must all be >= 1%s");
+  const int64_t esz = dt == DET_F32 ? 4 : 2;
+  if (!mul_ok(m, k, esz) || !mul_ok(k, n, esz) || !mul_ok(m, n, esz))
+    return fail(DET_EINVAL, "det_gemm: tensor size overflows int64%s");
+  const det_status_t dev = check_device();
+  if (dev != DET_OK) return dev;
+
+  detgemm::GemmArgs a;
+  a.A = A;
+  a.B = B;
+  a.bias = bias;
+  a.out = out;
+  switch (op) {
+    case detgemm::OP_FWD: a.rows = m; a.cols = n; a.red = k; a.lda = k; a.ldb = n; break;
+    case detgemm::OP_DX:  a.rows = m; a.cols = k; a.red = n; a.lda = n; a.ldb = n; break;
+    case detgemm::OP_DW:  a.rows = k; a.cols = n; a.red = m; a.lda = k; a.ldb = n; break;
+  }
+  const detgemm::Dt d = static_cast<detgemm::Dt>(dt);
+  hipError_t err;
+  if (tier == DET_TIER_EXACT) {
+    err = detgemm::launch_exact(op, d, a, stream);
+  } else {
+    int fam = g_force_family.load(std::memory_order_relaxed);
+    if (fam < 0) fam = detgemm::fast_auto_family(op, d, a.cols, a.red);
+    err = detgemm::launch_fast(op, d, a, fam, stream);
+  }
+  if (err != hipSuccess) return fail(DET_ELAUNCH, "det_gemm: kernel launch failed: %s", hipGetErrorString(err));
+  return DET_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+det_status_t det_gemm_fwd(void* y, const void* x, const void* w, const void* bias,
+                          int64_t m, int64_t k, int64_t n,
+                          det_dtype_t dt, det_tier_t tier, hipStream_t stream) {
+  return run(detgemm::OP_FWD, y, x, w, bias, m, k, n, dt, tier, stream);
+}
+
+det_status_t det_gemm_dx(void* dx, const void* dy, const void* w,
+                         int64_t m, int64_t k, int64_t n,
+                         det_dtype_t dt, det_tier_t tier, hipStream_t stream) {
+  return run(detgemm::OP_DX, dx, dy, w, nullptr, m, k, n, dt, tier, stream);
+}
+
+det_status_t det_gemm_dw(void* dw, const void* x, const void* dy,
+                         int64_t m, int64_t k, int64_t n,
+                         det_dtype_t dt, det_tier_t tier, hipStream_t stream) {
+  return run(detgemm::OP_DW, dw, x, dy, nullptr, m, k, n, dt, tier, stream);
+}
+
+const char* det_gemm_strerror(det_status_t status) {
+  switch (status) {
+    case DET_OK: return "success";
+    case DET_EINVAL: return "invalid argument (null pointer, size < 1 or size overflow)";
+    case DET_EDTYPE: return "unknown dtype";
+    case DET_ETIER: return "unknown tier";
+    case DET_EDEVICE: return "unsupported or missing device (gfx950 / MI355X required)";
+    case DET_ELAUNCH: return "kernel launch failed";
+  }
+  return "unknown status";
+}
+
+const char* det_gemm_last_error(void) { return g_last_error; }
+
+int det_gemm_version(void) { return 100; }
+
+det_status_t det_gemm_debug_force_family(int family) {
+  if (family < -1 || family > 1) return fail(DET_EINVAL, "det_gemm: family must be -1, 0 or 1%s");
+  g_force_family.store(family, std::memory_order_relaxed);
+  return DET_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,85 @@
+// Internal definitions shared by the library's HIP sources (not part of the ABI).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace detgemm {
+
+enum Op { OP_FWD = 0, OP_DX = 1, OP_DW = 2 };
+
+// One GEMM launch, already mapped onto "output rows x output cols, reduction red":
+//   out[r][c] = sum_l A(r, l) * B(l, c)  (+ bias[c])
+// with A(r, l) = A[r * lda + l] when a_red_contig, else A[l * lda + r];
+//      B(l, c) = B[c * ldb + l] when b_red_contig, else B[l * ldb + c].
+struct GemmArgs {
+  const void* A;
+  const void* B;
+  const void* bias;  // nullable, [cols]
+  void* out;         // [rows][cols], leading dimension cols
+  int64_t lda, ldb;
+  int64_t rows, cols, red;
+};
+
+enum Dt { DT_F32 = 0, DT_BF16 = 1, DT_F16 = 2 };
+
+// ---- element types: exact upcast and the final single rounding -------------
+
+struct F32 {
+  using T = float;
+  __device__ static inline double up(T v) { return static_cast<double>(v); }
+  __device__ static inline float to_f32(T v) { return v; }
+};
+struct BF16 {
+  using T = uint16_t;  // raw bfloat16 bits
+  __device__ static inline double up(T v) { return static_cast<double>(__uint_as_float(static_cast<uint32_t>(v) << 16)); }
+  __device__ static inline float to_f32(T v) { return __uint_as_float(static_cast<uint32_t>(v) << 16); }
+};
+struct F16 {
+  using T = _Float16;
+  __device__ static inline double up(T v) { return static_cast<double>(static_cast<float>(v)); }
+  __device__ static inline float to_f32(T v) { return static_cast<float>(v); }
+};
+
+// float64 -> float32 rounded to odd: the truncation toward zero, with its last
+// bit set when the conversion was inexact (Boldo and Melquiond, "Emulation of
+// FMA and correctly rounded sums: proved algorithms using rounding to odd",
+// IEEE TC 2008). A second rounding from the result to any format with at least
+// two fewer significand bits equals a single rounding from float64.
+__device__ inline float f64_to_f32_odd(double r) {
+  const float f = static_cast<float>(r);  // round to nearest even
+  uint32_t u = __float_as_uint(f);
+  const double back = static_cast<double>(f);
+  if (back != r) {                        // inexact (NaN keeps its NaN-ness)
+    if (__builtin_fabs(back) > __builtin_fabs(r)) u -= 1u;  // step to the neighbour toward zero
+    u |= 1u;
+  }
+  return __uint_as_float(u);
+}
+
+// float32 -> bfloat16 bits, round to nearest even.
+__device__ inline uint16_t f32_to_bf16_rne(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return static_cast<uint16_t>((u >> 16) | 0x40u);  // quiet NaN
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return static_cast<uint16_t>(u >> 16);
+}
+
+// Single round-to-nearest-even of a float64 value to the output type.
+template <typename E> __device__ inline typename E::T round_from_f64(double r);
+template <> __device__ inline float round_from_f64<F32>(double r) { return static_cast<float>(r); }
+template <> __device__ inline uint16_t round_from_f64<BF16>(double r) { return f32_to_bf16_rne(f64_to_f32_odd(r)); }
+template <> __device__ inline _Float16 round_from_f64<F16>(double r) { return static_cast<_Float16>(f64_to_f32_odd(r)); }
+
+// Round-to-nearest-even of an f32 accumulator to the output type.
+template <typename E> __device__ inline typename E::T round_from_f32(float r);
+template <> __device__ inline float round_from_f32<F32>(float r) { return r; }
+template <> __device__ inline uint16_t round_from_f32<BF16>(float r) { return f32_to_bf16_rne(r); }
+template <> __device__ inline _Float16 round_from_f32<F16>(float r) { return static_cast<_Float16>(r); }
+
+// Host-side launchers (one per tier), defined next to their kernels.
+hipError_t launch_exact(Op op, Dt dt, const GemmArgs& a, hipStream_t stream);
+hipError_t launch_fast(Op op, Dt dt, const GemmArgs& a, int family, hipStream_t stream);
+int fast_auto_family(Op op, Dt dt, int64_t cols, int64_t red);
+
+}  // namespace detgemm

@@ -1,0 +1,190 @@
+// Fast tier: matrix-core GEMM with f32 accumulation over a fixed walk of the
+// reduction (sgemm-bi 0.1.2 PyPI page, "Determinism contracts": tensor-core
+// tier with f32 accumulate, bit-identical across runs, forward batch-invariant
+// across all M, two tile families with identical bits, shape-only dispatch).
+//
+// Determinism and batch invariance
+//   * Every output element is produced by the same matrix-core instruction
+//     (V_MFMA_F32_32X32X16_BF16 / _F16 for 16-bit inputs, V_MFMA_F32_16X16X4_F32
+//     for f32 inputs), stepping through the reduction from index 0 upward in
+//     steps of the instruction's depth, starting from a zero accumulator. No
+//     split of the reduction, no atomics. The bias is then added in f32 and the
+//     sum rounded once to the output type.
+//   * An output element's arithmetic therefore involves only its own row of A,
+//     its own column of B and the reduction length: not the row count, the tile
+//     family or the position of its tile. Padding rows and reduction indices
+//     are zeros, which add nothing.
+//   * The two families (large: 128x128 outputs per workgroup, small: 64x64)
+//     differ only in how outputs are grouped into workgroups.
+
+#include "common.hpp"
+
+namespace detgemm {
+namespace {
+
+constexpr int THREADS = 256;  // 4 waves, 2x2
+constexpr int KS = 32;        // reduction depth staged in LDS per step
+
+typedef float v4f __attribute__((ext_vector_type(4)));
+typedef float v16f __attribute__((ext_vector_type(16)));
+typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
+typedef _Float16 v8h __attribute__((ext_vector_type(8)));
+typedef uint16_t v8u16 __attribute__((ext_vector_type(8)));
+
+template <typename E> struct Mfma;
+
+// 32x32 outputs per instruction, depth 16; lane l holds A[l%32][8*(l/32)+j],
+// B[8*(l/32)+j][l%32]; accumulator i of lane l is D[8*(i/4)+4*(l/32)+i%4][l%32].
+template <> struct Mfma<BF16> {
+  static constexpr int BLK = 32, DEPTH = 16, PER = 8, ACC = 16;
+  using Acc = v16f;
+  __device__ static inline Acc step(const uint16_t* a, const uint16_t* b, Acc c) {
+    const v8u16 av = *reinterpret_cast<const v8u16*>(a);
+    const v8u16 bv = *reinterpret_cast<const v8u16*>(b);
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(v8bf, av), __builtin_bit_cast(v8bf, bv), c, 0, 0, 0);
+  }
+  __device__ static inline int row(int lane, int i) { return 8 * (i / 4) + 4 * (lane / 32) + (i % 4); }
+};
+template <> struct Mfma<F16> {
+  static constexpr int BLK = 32, DEPTH = 16, PER = 8, ACC = 16;
+  using Acc = v16f;
+  __device__ static inline Acc step(const _Float16* a, const _Float16* b, Acc c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(*reinterpret_cast<const v8h*>(a), *reinterpret_cast<const v8h*>(b), c, 0, 0, 0);
+  }
+  __device__ static inline int row(int lane, int i) { return 8 * (i / 4) + 4 * (lane / 32) + (i % 4); }
+};
+// 16x16 outputs per instruction, depth 4; lane l holds A[l%16][l/16],
+// B[l/16][l%16]; accumulator i of lane l is D[4*(l/16)+i][l%16].
+template <> struct Mfma<F32> {
+  static constexpr int BLK = 16, DEPTH = 4, PER = 1, ACC = 4;
+  using Acc = v4f;
+  __device__ static inline Acc step(const float* a, const float* b, Acc c) {
+    return __builtin_amdgcn_mfma_f32_16x16x4f32(*a, *b, c, 0, 0, 0);
+  }
+  __device__ static inline int row(int lane, int i) { return 4 * (lane / 16) + i; }
+};
+
+// Stage a KS-deep slice of an operand into LDS, layout dst[x][l] (reduction
+// contiguous, row stride LD) for x < X (row of A or column of B), l < KS.
+//   red_contig: element (x, l) is src[(x0 + x) * ld + l0 + l]
+//   otherwise : element (x, l) is src[(l0 + l) * ld + x0 + x]
+// Out-of-range elements are zeros. Global reads follow the contiguous index.
+template <typename T, int X, int LD, bool RED_CONTIG>
+__device__ inline void stage(T* __restrict__ dst, const T* __restrict__ src, int64_t ld,
+                             int64_t x0, int64_t xlen, int64_t l0, int64_t llen) {
+  for (int idx = threadIdx.x; idx < X * KS; idx += THREADS) {
+    int x, l;
+    if (RED_CONTIG) { x = idx / KS; l = idx % KS; }
+    else            { l = idx / X;  x = idx % X; }
+    const int64_t gx = x0 + x, gl = l0 + l;
+    T v = T(0);
+    if (gx < xlen && gl < llen) v = RED_CONTIG ? src[gx * ld + gl] : src[gl * ld + gx];
+    dst[x * LD + l] = v;
+  }
+}
+
+template <typename E, int BM, int BN, bool A_RED_CONTIG, bool B_RED_CONTIG>
+__global__ void __launch_bounds__(THREADS) fast_kernel(GemmArgs args) {
+  using T = typename E::T;
+  using M = Mfma<E>;
+  constexpr int LD = KS + 16 / (int)sizeof(T) * 2;   // padded row stride (keeps 16-byte alignment)
+  constexpr int WM = BM / 2, WN = BN / 2;            // per-wave outputs
+  constexpr int NI = WM / M::BLK, NJ = WN / M::BLK;  // blocks per wave
+  __shared__ __attribute__((aligned(16))) T As[BM * LD];
+  __shared__ __attribute__((aligned(16))) T Bs[BN * LD];
+
+  const T* __restrict__ A = static_cast<const T*>(args.A);
+  const T* __restrict__ B = static_cast<const T*>(args.B);
+  const int64_t tiles_n = (args.cols + BN - 1) / BN;
+  const int64_t row0 = (static_cast<int64_t>(blockIdx.x) / tiles_n) * BM;
+  const int64_t col0 = (static_cast<int64_t>(blockIdx.x) % tiles_n) * BN;
+  const int wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int wm = (wave >> 1) * WM;
+  const int wn = (wave & 1) * WN;
+  const int lx = lane % M::BLK;                 // row of A / column of B in a block
+  const int lk = (lane / M::BLK) * M::PER;      // first reduction index of the lane
+
+  typename M::Acc acc[NI][NJ];
+#pragma unroll
+  for (int i = 0; i < NI; ++i)
+#pragma unroll
+    for (int j = 0; j < NJ; ++j)
+#pragma unroll
+      for (int e = 0; e < M::ACC; ++e) acc[i][j][e] = 0.0f;
+
+  for (int64_t l0 = 0; l0 < args.red; l0 += KS) {
+    stage<T, BM, LD, A_RED_CONTIG>(As, A, args.lda, row0, args.rows, l0, args.red);
+    stage<T, BN, LD, B_RED_CONTIG>(Bs, B, args.ldb, col0, args.cols, l0, args.red);
+    __syncthreads();
+#pragma unroll
+    for (int d = 0; d < KS; d += M::DEPTH) {
+#pragma unroll
+      for (int i = 0; i < NI; ++i)
+#pragma unroll
+        for (int j = 0; j < NJ; ++j)
+          acc[i][j] = M::step(&As[(wm + i * M::BLK + lx) * LD + d + lk], &Bs[(wn + j * M::BLK + lx) * LD + d + lk], acc[i][j]);
+    }
+    __syncthreads();
+  }
+
+  T* __restrict__ Y = static_cast<T*>(args.out);
+  const T* __restrict__ bias = static_cast<const T*>(args.bias);
+#pragma unroll
+  for (int i = 0; i < NI; ++i)
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) {
+      const int64_t col = col0 + wn + j * M::BLK + lx;
+#pragma unroll
+      for (int e = 0; e < M::ACC; ++e) {
+        const int64_t row = row0 + wm + i * M::BLK + M::row(lane, e);
+        if (row < args.rows && col < args.cols) {
+          float r = acc[i][j][e];
+          if (bias) r = r + E::to_f32(bias[col]);
+          Y[row * args.cols + col] = round_from_f32<E>(r);
+        }
+      }
+    }
+}
+
+template <typename E, int BM, int BN, bool AC, bool BC>
+hipError_t launch_typed(const GemmArgs& a, hipStream_t stream) {
+  const int64_t blocks = ((a.cols + BN - 1) / BN) * ((a.rows + BM - 1) / BM);
+  if (blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
+  hipLaunchKernelGGL((fast_kernel<E, BM, BN, AC, BC>), dim3(static_cast<unsigned>(blocks)), dim3(THREADS), 0, stream, a);
+  return hipGetLastError();
+}
+
+template <typename E, int BM, int BN>
+hipError_t launch_op(Op op, const GemmArgs& a, hipStream_t stream) {
+  switch (op) {
+    case OP_FWD: return launch_typed<E, BM, BN, true, false>(a, stream);
+    case OP_DX:  return launch_typed<E, BM, BN, true, true>(a, stream);
+    case OP_DW:  return launch_typed<E, BM, BN, false, false>(a, stream);
+  }
+  return hipErrorInvalidValue;
+}
+
+template <typename E>
+hipError_t launch_family(Op op, int family, const GemmArgs& a, hipStream_t stream) {
+  return family == 0 ? launch_op<E, 128, 128>(op, a, stream) : launch_op<E, 64, 64>(op, a, stream);
+}
+
+}  // namespace
+
+// Shape-only choice of the tile family: never reads the row count of fwd/dx.
+int fast_auto_family(Op op, Dt dt, int64_t cols, int64_t red) {
+  (void)op; (void)dt; (void)red;
+  return cols >= 1024 ? 0 : 1;
+}
+
+hipError_t launch_fast(Op op, Dt dt, const GemmArgs& a, int family, hipStream_t stream) {
+  switch (dt) {
+    case DT_F32: return launch_family<F32>(op, family, a, stream);
+    case DT_BF16: return launch_family<BF16>(op, family, a, stream);
+    case DT_F16: return launch_family<F16>(op, family, a, stream);
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace detgemm

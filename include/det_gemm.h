@@ -1,0 +1,126 @@
+/*
+ * det_gemm.h — deterministic, batch-invariant dense GEMM for training linear
+ * layers on AMD Instinct MI355X (gfx950).
+ *
+ * The three operations of a linear layer whose weight is stored [in, out]
+ * (sgemm-bi 0.1.2 PyPI page, "Use": forward, dW and dX; weight kept [in, out],
+ * raw device pointers and an explicit stream at the engine boundary):
+ *
+ *     fwd : Y[m,n]  = X[m,k] · W[k,n] (+ bias[n])      reduction over k
+ *     dx  : dX[m,k] = dY[m,n] · W[k,n]^T                reduction over n
+ *     dw  : dW[k,n] = X[m,k]^T · dY[m,n]                reduction over m
+ *
+ * Shapes are always given as (m, k, n) of the forward problem. Every tensor is
+ * dense, row-major, contiguous, and of the one dtype `dt` (bias included). All
+ * pointers are device pointers on the current HIP device.
+ *
+ * Tiers
+ *   DET_TIER_EXACT — Carbon README (alia-carbon 0.2.0), "How It Works": the
+ *     reduction is cut into tiles of 32 indices anchored at 0; operands are
+ *     upcast to float64; each tile's partial is an fma chain in ascending index
+ *     order from +0; the tile partials are combined in ascending tile order with
+ *     Neumaier's (Kahan-Babushka-Neumaier) compensation; the forward bias is
+ *     added to the compensated sum in float64; the result is rounded once
+ *     (round-to-nearest-even) to `dt`. The bits depend on the reduction length
+ *     alone: never on m (for fwd and dx), the launch, the stream or the device
+ *     state. They equal the CPU oracle's bit for bit.
+ *   DET_TIER_FAST — sgemm-bi page, "Determinism contracts", tensor-core tier:
+ *     matrix-core products with f32 accumulation over a fixed ascending walk of
+ *     the reduction, no split of the reduction for fwd and dx, one rounding to
+ *     `dt` after the bias add. Identical bits on every run; for fwd and dx the
+ *     bits of a row do not depend on m. Two tile families give identical bits;
+ *     the family is chosen from the shape without reading m.
+ *
+ * Ownership and execution
+ *   The caller owns every buffer. The library keeps no reference to any of them
+ *   and allocates no device memory per call. Work is enqueued on `stream`
+ *   (0 = the null stream) and the call returns once it is enqueued; the caller
+ *   keeps the buffers alive until the stream has finished. Outputs must not
+ *   alias inputs. Faults during execution surface at the caller's next
+ *   synchronisation. The library is re-entrant; it never aborts, never prints
+ *   and never changes the current device.
+ *
+ * Errors
+ *   Every entry point returns DET_OK or a negative det_status_t; on error
+ *   nothing is enqueued, and det_gemm_last_error() gives a message for the
+ *   calling thread.
+ */
+#ifndef DET_GEMM_H
+#define DET_GEMM_H
+
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  DET_F32 = 0,   /* IEEE binary32 */
+  DET_BF16 = 1,  /* bfloat16 */
+  DET_F16 = 2    /* IEEE binary16 */
+} det_dtype_t;
+
+typedef enum {
+  DET_TIER_EXACT = 0, /* float64 tiles + Neumaier compensation, oracle bits */
+  DET_TIER_FAST = 1   /* matrix cores, f32 accumulate, within tolerance */
+} det_tier_t;
+
+typedef enum {
+  DET_OK = 0,
+  DET_EINVAL = -1,   /* null required pointer, m/k/n < 1, or a size overflow */
+  DET_EDTYPE = -2,   /* unknown dtype */
+  DET_ETIER = -3,    /* unknown tier */
+  DET_EDEVICE = -4,  /* current device is not gfx950, or no device */
+  DET_ELAUNCH = -5   /* the kernel launch was rejected by the runtime */
+} det_status_t;
+
+/*
+ * Forward: y[m,n] = x[m,k] · w[k,n] (+ bias[n]).
+ * bias may be NULL (no bias). The exact tier adds bias to the float64
+ * compensated sum before the single rounding; the fast tier adds it to the f32
+ * accumulator before the rounding.
+ */
+det_status_t det_gemm_fwd(void* y, const void* x, const void* w, const void* bias,
+                          int64_t m, int64_t k, int64_t n,
+                          det_dtype_t dt, det_tier_t tier, hipStream_t stream);
+
+/*
+ * Input gradient: dx[m,k] = dy[m,n] · w[k,n]^T (reduction over n, in tiles of
+ * 32 for the exact tier). Rows of dx never depend on m.
+ */
+det_status_t det_gemm_dx(void* dx, const void* dy, const void* w,
+                         int64_t m, int64_t k, int64_t n,
+                         det_dtype_t dt, det_tier_t tier, hipStream_t stream);
+
+/*
+ * Weight gradient: dw[k,n] = x[m,k]^T · dy[m,n] (reduction over the m rows,
+ * in tiles of 32 rows for the exact tier). The order is fixed by m alone.
+ * With k = 1 and x a column of ones this is the bias gradient db[n].
+ */
+det_status_t det_gemm_dw(void* dw, const void* x, const void* dy,
+                         int64_t m, int64_t k, int64_t n,
+                         det_dtype_t dt, det_tier_t tier, hipStream_t stream);
+
+/* Static description of a status code. */
+const char* det_gemm_strerror(det_status_t status);
+
+/* Detail of the last error raised on the calling thread ("" if none). */
+const char* det_gemm_last_error(void);
+
+/* Library version, major * 10000 + minor * 100 + patch. */
+int det_gemm_version(void);
+
+/*
+ * Test hook: force the fast tier's tile family (-1 automatic, 0 = the large
+ * family, 1 = the small family) for later calls from any thread. Both families
+ * produce identical bits, so this changes speed only. Returns DET_EINVAL for
+ * other values.
+ */
+det_status_t det_gemm_debug_force_family(int family);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DET_GEMM_H */

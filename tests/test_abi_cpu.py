@@ -1,0 +1,78 @@
+"""The C-ABI library loads and behaves at its boundary, without a GPU.
+
+No computation is launched here: only symbol presence, static strings and the
+argument checks that run before any device call.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+import deterministic_invariant_gemm_det_amd as dg
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "det_gemm.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(det_gemm_\w+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_symbol():
+    L = ctypes.CDLL(dg.LIB_PATH)
+    names = declared_functions()
+    assert {"det_gemm_fwd", "det_gemm_dx", "det_gemm_dw"} <= set(names)
+    for name in names:
+        assert hasattr(L, name), name
+
+
+def test_static_strings_and_version():
+    assert dg.det_gemm_version() >= 100
+    assert dg.det_gemm_strerror(0) == "success"
+    for st in (-1, -2, -3, -4, -5):
+        assert dg.det_gemm_strerror(st) != "unknown status"
+    assert dg.det_gemm_strerror(-99) == "unknown status"
+
+
+def test_force_family_validation():
+    with pytest.raises(dg.DetGemmError):
+        dg.det_gemm_debug_force_family(2)
+    dg.det_gemm_debug_force_family(-1)
+
+
+def _status(fn, *args):
+    return fn(*args)
+
+
+@pytest.mark.parametrize("op", ["fwd", "dx", "dw"])
+def test_argument_checks_before_any_device_call(op):
+    L = dg.lib()
+    p = 0x1000  # never dereferenced: every call below is rejected before launch
+
+    def call(out, a, b, m, k, n, dt, tier):
+        if op == "fwd":
+            return L.det_gemm_fwd(out, a, b, None, m, k, n, dt, tier, None)
+        return getattr(L, "det_gemm_" + op)(out, a, b, m, k, n, dt, tier, None)
+
+    assert call(None, p, p, 4, 4, 4, 0, 0) == -1
+    assert call(p, None, p, 4, 4, 4, 0, 0) == -1
+    assert call(p, p, None, 4, 4, 4, 0, 0) == -1
+    assert call(p, p, p, 0, 4, 4, 0, 0) == -1
+    assert call(p, p, p, 4, -1, 4, 0, 0) == -1
+    assert call(p, p, p, 4, 4, 0, 0, 0) == -1
+    assert call(p, p, p, 1 << 40, 1 << 40, 4, 0, 0) == -1
+    assert call(p, p, p, 4, 4, 4, 7, 0) == -2
+    assert call(p, p, p, 4, 4, 4, 0, 5) == -3
+    assert "m, k and n" in dg.det_gemm_last_error() or dg.det_gemm_last_error()
+
+
+def test_no_device_is_refused_cleanly():
+    import torch
+    if torch.cuda.device_count() > 0:
+        pytest.skip("a GPU is visible; this checks the no-device path only")
+    L = dg.lib()
+    p = 0x1000
+    assert L.det_gemm_fwd(p, p, p, None, 4, 4, 4, 0, 0, None) == -4
+    assert dg.det_gemm_last_error()

@@ -1,0 +1,80 @@
+"""Exact tier on the GPU, bit for bit against the CPU oracle."""
+import numpy as np
+import pytest
+
+import oracle
+import synthetic as syn
+from tests import pins
+from tests.gpu_util import assert_bits_equal, gpu_op, operand_shapes
+
+pytestmark = pytest.mark.gpu
+
+DTS = ("f32", "bf16", "f16")
+SHAPES = [(1, 1, 1), (3, 33, 65), (127, 70, 129), (64, 64, 64), (200, 300, 100), (17, 1000, 5), (65, 31, 63), (2, 97, 250)]
+
+
+def test_config1_fp32_fwd_dx_dw():
+    """M=256 K=512 N=512 f32, X, W ~ N(0,1), bias ~ N(0,0.1), dY ~ N(0,1), seed 42: full outputs."""
+    m, k, n = 256, 512, 512
+    X = syn.normal(42, syn.TID_X, (m, k))
+    W = syn.normal(42, syn.TID_W, (k, n))
+    b = syn.normal(42, syn.TID_B, (n,), sigma=0.1)
+    G = syn.normal(42, syn.TID_DY, (m, n))
+    print("config1 fwd", flush=True)
+    assert_bits_equal(gpu_op("fwd", "f32", X, W, b), oracle.fwd("f32", X, W, b)[0], "fwd")
+    assert_bits_equal(gpu_op("fwd", "f32", X, W), oracle.fwd("f32", X, W)[0], "fwd nobias")
+    print("config1 dx", flush=True)
+    assert_bits_equal(gpu_op("dx", "f32", G, W), oracle.dx("f32", G, W)[0], "dx")
+    print("config1 dw", flush=True)
+    assert_bits_equal(gpu_op("dw", "f32", X, G), oracle.dw("f32", X, G)[0], "dw")
+
+
+@pytest.mark.parametrize("dt", DTS)
+@pytest.mark.parametrize("op", ["fwd", "dx", "dw"])
+def test_ragged_shapes(op, dt):
+    for si, (m, k, n) in enumerate(SHAPES):
+        print(f"exact {op} {dt} {(m, k, n)}", flush=True)
+        sa, sb = operand_shapes(op, m, k, n)
+        A = syn.normal(900 + si, 0, sa, dt=dt)
+        B = syn.normal(900 + si, 1, sb, sigma=0.5, dt=dt)
+        bias = syn.normal(900 + si, 2, (n,), sigma=0.1, dt=dt) if op == "fwd" else None
+        want, _, _ = oracle.gemm(op, dt, A, B, m, k, n, bias=bias)
+        assert_bits_equal(gpu_op(op, dt, A, B, bias), want, f"{op} {dt} {(m, k, n)}")
+
+
+@pytest.mark.parametrize("dt", DTS)
+def test_integer_inputs_exact(dt):
+    for op in ("fwd", "dx", "dw"):
+        for si, (m, k, n) in enumerate(SHAPES):
+            sa, sb = operand_shapes(op, m, k, n)
+            A = syn.integers(950 + si, 0, sa, -8, 8, dt)
+            B = syn.integers(950 + si, 1, sb, -8, 8, dt)
+            want, _, _ = oracle.gemm(op, dt, A, B, m, k, n)
+            assert_bits_equal(gpu_op(op, dt, A, B), want, f"int {op} {dt} {(m, k, n)}")
+
+
+def test_golden_witnesses():
+    for case in pins.golden()["cases"] + pins.golden()["downcast"]:
+        dts = [case["dt"]] if "dt" in case else DTS
+        for op in ("fwd", "dx", "dw"):
+            for dt in dts:
+                A, B, m, k, n = pins._witness_operands(op, dt, case["L"], pins._golden_terms(case))
+                want, r, _ = oracle.gemm(op, dt, A, B, m, k, n, want_r=True)
+                assert r[0, 0] == float.fromhex(case["r"])
+                assert_bits_equal(gpu_op(op, dt, A, B), want, f"{case['name']} {op} {dt}")
+
+
+@pytest.mark.parametrize("dt,scale_x,scale_w", [
+    ("f32", 2.0 ** -70, 2.0 ** -70),    # f32 subnormal outputs
+    ("bf16", 2.0 ** -70, 2.0 ** -65),   # bf16 subnormal outputs
+    ("f16", 2.0 ** -8, 2.0 ** -10),     # f16 subnormal outputs
+    ("bf16", 2.0 ** 100, 2.0 ** 27),    # bf16 overflow to inf
+    ("f16", 2.0 ** 6, 2.0 ** 8),        # f16 overflow to inf
+    ("f32", 2.0 ** 100, 2.0 ** 27),     # f32 overflow to inf
+])
+def test_rounding_edges(dt, scale_x, scale_w):
+    m, k, n = 40, 37, 50
+    X = syn.to_storage(syn.from_storage(syn.normal(990, 0, (m, k), dt=dt), dt) * scale_x, dt)
+    W = syn.to_storage(syn.from_storage(syn.normal(990, 1, (k, n), dt=dt), dt) * scale_w, dt)
+    want, _, _ = oracle.fwd(dt, X, W)
+    assert_bits_equal(gpu_op("fwd", dt, X, W), want, f"edges {dt}")

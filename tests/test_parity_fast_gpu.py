@@ -1,0 +1,53 @@
+"""Fast tier on the GPU: within the stated tolerance of the oracle, exact on
+integer inputs, identical across reruns and across the two tile families."""
+import numpy as np
+import pytest
+
+import oracle
+import synthetic as syn
+from tests.gpu_util import assert_bits_equal, assert_within_tolerance, gpu_op, operand_shapes
+
+pytestmark = pytest.mark.gpu
+
+DTS = ("f32", "bf16", "f16")
+SHAPES = [(1, 1, 1), (3, 33, 65), (127, 70, 129), (64, 64, 64), (200, 300, 100), (17, 1000, 5),
+          (65, 31, 63), (2, 97, 250), (130, 200, 1100), (257, 129, 1030)]
+
+
+@pytest.fixture(autouse=True)
+def _auto_family():
+    import deterministic_invariant_gemm_det_amd as dg
+    dg.det_gemm_debug_force_family(-1)
+    yield
+    dg.det_gemm_debug_force_family(-1)
+
+
+@pytest.mark.parametrize("dt", DTS)
+@pytest.mark.parametrize("op", ["fwd", "dx", "dw"])
+def test_tolerance_and_families(op, dt):
+    import deterministic_invariant_gemm_det_amd as dg
+    for si, (m, k, n) in enumerate(SHAPES):
+        print(f"fast {op} {dt} {(m, k, n)}", flush=True)
+        sa, sb = operand_shapes(op, m, k, n)
+        A = syn.normal(1100 + si, 0, sa, dt=dt)
+        B = syn.normal(1100 + si, 1, sb, sigma=0.5, dt=dt)
+        bias = syn.normal(1100 + si, 2, (n,), sigma=0.1, dt=dt) if op == "fwd" else None
+        _, r, S = oracle.gemm(op, dt, A, B, m, k, n, bias=bias, want_r=True, want_S=True)
+        y = gpu_op(op, dt, A, B, bias, tier="fast")
+        assert_within_tolerance(y, r, S, dt, f"fast {op} {dt} {(m, k, n)}")
+        assert_bits_equal(gpu_op(op, dt, A, B, bias, tier="fast"), y, "rerun")
+        for fam in (0, 1):
+            dg.det_gemm_debug_force_family(fam)
+            assert_bits_equal(gpu_op(op, dt, A, B, bias, tier="fast"), y, f"family {fam}")
+        dg.det_gemm_debug_force_family(-1)
+
+
+@pytest.mark.parametrize("dt", DTS)
+def test_integer_inputs_exact(dt):
+    for op in ("fwd", "dx", "dw"):
+        for si, (m, k, n) in enumerate(SHAPES):
+            sa, sb = operand_shapes(op, m, k, n)
+            A = syn.integers(1200 + si, 0, sa, -8, 8, dt)
+            B = syn.integers(1200 + si, 1, sb, -8, 8, dt)
+            want, _, _ = oracle.gemm(op, dt, A, B, m, k, n)
+            assert_bits_equal(gpu_op(op, dt, A, B, tier="fast"), want, f"int fast {op} {dt} {(m, k, n)}")
