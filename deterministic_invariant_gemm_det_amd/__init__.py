@@ -13,7 +13,7 @@ import os
 
 __all__ = [
     "det_gemm_fwd", "det_gemm_dx", "det_gemm_dw", "det_gemm_strerror", "det_gemm_last_error",
-    "det_gemm_version", "det_gemm_debug_force_family", "DetGemmError", "LIB_PATH",
+    "det_gemm_version", "det_gemm_debug_force_family", "det_gemm_debug_force_exact_kernel", "DetGemmError", "LIB_PATH",
     "fwd", "dx", "dw", "deterministic_linear", "Linear", "DTYPES", "TIERS",
 ]
 
@@ -38,6 +38,13 @@ def lib():
     """The loaded libdetgemm.so (raises if it has not been built)."""
     global _lib
     if _lib is None:
+        # torch bundles its own HIP runtime (same soname). Load it first so that
+        # libdetgemm.so binds to that one runtime instead of a second copy from
+        # /opt/rocm, which would not know torch's device memory or streams.
+        try:
+            import torch  # noqa: F401
+        except ImportError:
+            pass
         if not os.path.exists(LIB_PATH):
             raise ImportError(f"{LIB_PATH} is missing: build it with __graft_entry__.build() "
                               "(hipcc, gfx950); there is no fallback implementation")
@@ -55,6 +62,8 @@ def lib():
         L.det_gemm_version.restype = ci
         L.det_gemm_debug_force_family.argtypes = [ci]
         L.det_gemm_debug_force_family.restype = ci
+        L.det_gemm_debug_force_exact_kernel.argtypes = [ci]
+        L.det_gemm_debug_force_exact_kernel.restype = ci
         _lib = L
     return _lib
 
@@ -111,6 +120,10 @@ def det_gemm_version():
 
 def det_gemm_debug_force_family(family):
     _check(lib().det_gemm_debug_force_family(family))
+
+
+def det_gemm_debug_force_exact_kernel(variant):
+    _check(lib().det_gemm_debug_force_exact_kernel(variant))
 
 
 # ---------------------------------------------------------------- torch layer

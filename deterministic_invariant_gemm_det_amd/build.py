@@ -13,6 +13,10 @@ CSRC = os.path.join(HERE, "csrc")
 ROOT = os.path.dirname(HERE)
 LIB = os.path.join(HERE, "libdetgemm.so")
 SOURCES = ["abi.cpp", "exact.hip", "fast.hip"]
+# Per-source extra flags. The exact tier keeps matrix-core results in ordinary
+# VGPRs: the Neumaier update reads every partial on the vector ALU, and the
+# accumulator-register form would add a copy per partial.
+EXTRA = {"exact.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [
@@ -26,7 +30,7 @@ FLAGS = [
 
 def _compile(src, build_dir):
     obj = os.path.join(build_dir, os.path.basename(src) + ".o")
-    cmd = [HIPCC, *FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [HIPCC, *FLAGS, *EXTRA.get(src, []), "-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed for {src}:\n{r.stdout}\n{r.stderr}")

@@ -14,6 +14,7 @@ namespace {
 
 thread_local char g_last_error[256] = "";
 std::atomic<int> g_force_family{-1};
+std::atomic<int> g_force_exact{-1};
 
 constexpr int kMaxDevices = 64;
 // 0 unknown, 1 gfx950, 2 not supported
@@ -75,10 +76,19 @@ det_status_t run(detgemm::Op op, void* out, const void* A, const void* B, const 
     case detgemm::OP_DX:  a.rows = m; a.cols = k; a.red = n; a.lda = n; a.ldb = n; break;
     case detgemm::OP_DW:  a.rows = k; a.cols = n; a.red = m; a.lda = k; a.ldb = n; break;
   }
+  const uintptr_t align_a = reinterpret_cast<uintptr_t>(A) | static_cast<uintptr_t>(a.lda * esz);
+  const uintptr_t align_b = reinterpret_cast<uintptr_t>(B) | static_cast<uintptr_t>(a.ldb * esz);
+  a.vec_a = (align_a % 16) == 0;
+  a.vec_b = (align_b % 16) == 0;
+  const int64_t a_elems = (op == detgemm::OP_DX) ? m * n : m * k;
+  const int64_t b_elems = (op == detgemm::OP_DW) ? m * n : k * n;
+  a.off32_a = a_elems * esz < (int64_t(1) << 31);
+  a.off32_b = b_elems * esz < (int64_t(1) << 31);
   const detgemm::Dt d = static_cast<detgemm::Dt>(dt);
   hipError_t err;
   if (tier == DET_TIER_EXACT) {
-    err = detgemm::launch_exact(op, d, a, stream);
+    const int v = g_force_exact.load(std::memory_order_relaxed);
+    err = detgemm::launch_exact(op, d, a, v < 0 ? 0 : v, stream);
   } else {
     int fam = g_force_family.load(std::memory_order_relaxed);
     if (fam < 0) fam = detgemm::fast_auto_family(op, d, a.cols, a.red);
@@ -129,6 +139,12 @@ int det_gemm_version(void) { return 100; }
 det_status_t det_gemm_debug_force_family(int family) {
   if (family < -1 || family > 1) return fail(DET_EINVAL, "det_gemm: family must be -1, 0 or 1%s");
   g_force_family.store(family, std::memory_order_relaxed);
+  return DET_OK;
+}
+
+det_status_t det_gemm_debug_force_exact_kernel(int variant) {
+  if (variant < -1 || variant > 3) return fail(DET_EINVAL, "det_gemm: exact kernel must be -1 .. 3%s");
+  g_force_exact.store(variant, std::memory_order_relaxed);
   return DET_OK;
 }
 

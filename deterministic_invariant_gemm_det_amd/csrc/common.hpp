@@ -19,6 +19,8 @@ struct GemmArgs {
   void* out;         // [rows][cols], leading dimension cols
   int64_t lda, ldb;
   int64_t rows, cols, red;
+  bool vec_a, vec_b; // 16-byte vector loads allowed (base and row stride aligned)
+  bool off32_a, off32_b; // every element offset of the operand fits in 32 bits
 };
 
 enum Dt { DT_F32 = 0, DT_BF16 = 1, DT_F16 = 2 };
@@ -78,7 +80,7 @@ template <> __device__ inline uint16_t round_from_f32<BF16>(float r) { return f3
 template <> __device__ inline _Float16 round_from_f32<F16>(float r) { return static_cast<_Float16>(r); }
 
 // Host-side launchers (one per tier), defined next to their kernels.
-hipError_t launch_exact(Op op, Dt dt, const GemmArgs& a, hipStream_t stream);
+hipError_t launch_exact(Op op, Dt dt, const GemmArgs& a, int variant, hipStream_t stream);
 hipError_t launch_fast(Op op, Dt dt, const GemmArgs& a, int family, hipStream_t stream);
 int fast_auto_family(Op op, Dt dt, int64_t cols, int64_t red);
 

@@ -8,24 +8,40 @@
 //     (s, c) <- Neumaier(s, c, p_t) for t ascending, from (+0, +0)
 //     r = s + c (+ bias), then one round-to-nearest-even to the output type.
 //
-// gfx950 mapping
-//   * The fma chains run on the float64 matrix cores: V_MFMA_F64_16X16X4_F64
-//     computes, for each of its 16x16 outputs, acc = fma(a_k, b_k, acc) for
-//     its four k in ascending order, each step rounded to nearest even (checked
-//     bit for bit against a sequential fma chain, subnormals, signed zeros and
-//     ties included). Eight of them in k order, started from +0, are exactly one
-//     tile's chain p_t.
-//   * The Neumaier combine runs on the float64 vector ALU, once per tile and
-//     output, and overlaps with the next tile's matrix-core work.
+// Facts the kernels rely on
 //   * Zero padding past the end of the reduction adds fma(0, 0, p) = p + 0,
 //     which leaves p unchanged because a chain started from +0 is never -0.
 //     So a short last tile is computed as a padded full tile with the same bits.
+//   * Neumaier's update adds to c the exact rounding error of s + p_t. Knuth's
+//     branch-free TwoSum yields the same exact error for all finite operands,
+//     and with f32/bf16/f16 inputs s and p_t are always finite (every partial is
+//     far below the float64 range); a non-finite input makes both forms NaN.
+//     So the kernels use TwoSum (7 float64 adds per output and tile).
 //   * Every output is computed the same way wherever it sits, so a row's bits do
 //     not depend on the number of rows, the tile grid or the launch.
 //
-// Workgroup: 256 threads = 4 waves in 2x2, 64x64 outputs; each wave owns 32x32
-// outputs as 2x2 blocks of 16x16. Operand tiles are staged in LDS as float64,
-// laid out [reduction index][row or column], double buffered.
+// Three kernels implement it, with identical bits (the default is mfma4):
+//   mfma4 — the fma chains on V_MFMA_F64_4X4X4_4B_F64: four independent 4x4
+//           blocks per instruction, each output acc = fma(a_k, b_k, acc) over
+//           its four k in ascending order, one rounding per step (checked bit
+//           for bit against a sequential fma chain, subnormals, signed zeros and
+//           ties included). Eight of them in k order from +0 are one tile's chain.
+//           On gfx950 this shape runs the float64 pipe at close to its peak
+//           (about 1.5x the rate of the 16x16x4 shape). A wave owns 64 rows x 16
+//           columns: four row fragments times the same 16 columns presented in
+//           four block rotations, so that every (row, column) pair meets once.
+//   mfma16 — the same on V_MFMA_F64_16X16X4_F64 (one 16x16 block, same
+//           per-output semantics); a wave owns 32x32 outputs as 2x2 blocks.
+//   valu  — the fma chains on the float64 vector ALU. A wave owns 16 rows x 64
+//           columns; lane l keeps the chains of column l for the 16 rows. The
+//           row operand reaches all lanes through a DPP row broadcast
+//           (V_FMAC_F64 with row_newbcast:n takes src0 from lane n of each row of
+//           16 lanes), so each lane loads one row value and one column value per
+//           reduction index from LDS and issues 16 fmas.
+// The Neumaier combine runs on the float64 vector ALU once per tile and output.
+// All three stage 64x32 operand tiles in LDS as float64, laid out
+// [reduction index][row or column], double buffered, with the next tile's
+// global loads issued before the current tile's arithmetic.
 
 #include "common.hpp"
 
@@ -36,64 +52,328 @@ constexpr int KT = 32;        // the method's tile width along the reduction
 constexpr int BM = 64;        // workgroup output rows
 constexpr int BN = 64;        // workgroup output columns
 constexpr int THREADS = 256;
+constexpr int LS = 80;        // LDS row stride in doubles: 64 + 16 padding keeps the
+                              // four reduction rows read by one wave in distinct bank halves
 
 typedef double v4d __attribute__((ext_vector_type(4)));
 
-// Neumaier's update of the compensated pair (s, c) with one tile partial p.
-// Both branches form the exact rounding error of s + p; the operand selection
-// reproduces the branch on |s| >= |p| exactly, NaN comparisons included.
-__device__ inline void neumaier_add(double& s, double& c, double p) {
-  const double tt = s + p;
-  const bool s_big = __builtin_fabs(s) >= __builtin_fabs(p);
-  const double big = s_big ? s : p;
-  const double small = s_big ? p : s;
-  c = c + ((big - tt) + small);
-  s = tt;
+// (s, c) <- Neumaier(s, c, p): s + p rounded, its exact error added to c.
+__device__ inline void kbn_add(double& s, double& c, double p) {
+  const double t = s + p;
+  const double bp = t - s;
+  const double ap = t - bp;
+  const double e = (s - ap) + (p - bp);
+  c = c + e;
+  s = t;
 }
 
-// Stage a 32-deep slice of an operand into LDS as float64, layout dst[l][x]
-// for l < KT (reduction) and x < 64 (row of A or column of B).
-//   red_contig: element (x, l) is src[(x0 + x) * ld + l0 + l]   (reduction contiguous)
-//   otherwise : element (x, l) is src[(l0 + l) * ld + x0 + x]   (reduction-major)
-// Out-of-range elements are stored as +0.
+// ---- operand staging --------------------------------------------------------
+//
+// One 64 x 32 slice (64 rows of A or columns of B, 32 reduction indices) per
+// tile. Each thread moves 8 elements: x = t % 64 along the non-reduction dim,
+// l = 8 * (t / 64) + j along the reduction. A reduction-contiguous source
+// (element (x, l) at src[x * ld + l]) gives each thread 8 consecutive
+// elements (one vector load); a reduction-major source (element (x, l) at
+// src[l * ld + x]) gives the 64 lanes of a wave 64 consecutive elements per j.
+// LDS layout: dst[l * LS + x], float64; a wave's 64 lanes write 64 consecutive
+// doubles per store, so the stores are free of bank conflicts.
+
+// Eight elements kept as packed 32-bit words until they are written to LDS, so
+// the vector-load and edge paths leave the same registers behind and the
+// loads stay in flight across the arithmetic of the current tile.
+template <typename E> struct alignas(16) Raw8 {
+  static constexpr int NW = static_cast<int>(8 * sizeof(typename E::T) / 4);
+  uint32_t w[NW];
+};
+
+template <typename T> __device__ inline uint32_t bits_of(T v);
+template <> __device__ inline uint32_t bits_of<float>(float v) { return __float_as_uint(v); }
+template <> __device__ inline uint32_t bits_of<uint16_t>(uint16_t v) { return v; }
+template <> __device__ inline uint32_t bits_of<_Float16>(_Float16 v) { return __builtin_bit_cast(uint16_t, v); }
+
+template <typename E> __device__ inline double up_bits(uint32_t b);
+template <> __device__ inline double up_bits<F32>(uint32_t b) { return static_cast<double>(__uint_as_float(b)); }
+template <> __device__ inline double up_bits<BF16>(uint32_t b) { return static_cast<double>(__uint_as_float(b << 16)); }
+template <> __device__ inline double up_bits<F16>(uint32_t b) {
+  return static_cast<double>(static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(b))));
+}
+
+// Element j of a Raw8 as float64.
+template <typename E> __device__ inline double element(const Raw8<E>& r, int j) {
+  if (sizeof(typename E::T) == 4) return up_bits<E>(r.w[j]);
+  return up_bits<E>((r.w[j >> 1] >> (16 * (j & 1))) & 0xffffu);
+}
+
 template <typename E, bool RED_CONTIG>
-__device__ inline void stage(double* __restrict__ dst, const typename E::T* __restrict__ src, int64_t ld,
-                             int64_t x0, int64_t xlen, int64_t l0, int64_t llen) {
-  const int t = threadIdx.x;
-  if (RED_CONTIG) {
-    const int x = t >> 2;             // 64 rows x 4 threads
-    const int lb = (t & 3) * 8;       // 8 consecutive reduction indices each
-    const int64_t gx = x0 + x;
-    const typename E::T* row = src + gx * ld + l0;
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int l = lb + j;
-      double v = 0.0;
-      if (gx < xlen && l0 + l < llen) v = E::up(row[l]);
-      dst[l * BM + x] = v;
+struct Stager {
+  using T = typename E::T;
+  static constexpr int64_t ES = sizeof(T);
+  const T* __restrict__ src;
+  const char* __restrict__ ubase;  // wave-uniform byte base of tile 0 (interior path)
+  int64_t ustep;                   // bytes between consecutive tiles (uniform)
+  int64_t uld;                     // bytes between reduction rows, reduction-major sources
+  uint32_t voff;                   // this lane's byte offset from ubase (interior path)
+  int64_t gx;                      // this thread's index along the non-reduction dim
+  int64_t gl;                      // this thread's first reduction index in tile 0
+  int64_t ld, xlen, llen;
+  bool full;                       // interior path usable for this block (uniform)
+
+  __device__ Stager(const T* src_, int64_t ld_, int64_t x0, int64_t xlen_, int64_t llen_, bool aligned, bool off32) {
+    const int t = threadIdx.x;
+    const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
+    src = src_;
+    ld = ld_;
+    xlen = xlen_;
+    llen = llen_;
+    gx = x0 + (t & 63);
+    gl = wave * 8;
+    full = off32 && (x0 + 64 <= xlen_) && (!RED_CONTIG || aligned);
+    const char* b = reinterpret_cast<const char*>(src_);
+    if (RED_CONTIG) {
+      ubase = b + gl * ES;
+      ustep = KT * ES;
+      uld = 0;
+      voff = static_cast<uint32_t>(gx * ld_ * ES);
+    } else {
+      ubase = b + (gl * ld_ + x0) * ES;
+      ustep = KT * ld_ * ES;
+      uld = ld_ * ES;
+      voff = static_cast<uint32_t>((t & 63) * ES);
     }
-  } else {
-    const int l = t >> 3;             // 32 reduction rows x 8 threads
-    const int xb = (t & 7) * 8;       // 8 consecutive columns each
-    const int64_t gl = l0 + l;
-    const typename E::T* row = src + gl * ld + x0;
+  }
+
+  // Interior tiles (uniform test) load from a wave-uniform base plus a fixed
+  // per-lane 32-bit offset, with no per-tile vector arithmetic; edge tiles load
+  // every element from a clamped, always valid address and zero what lies
+  // outside the operand. No lane-divergent branch, so the loads stay in flight.
+  __device__ inline void load(int tile, Raw8<E>& r) const {
+    const bool interior = full && static_cast<int64_t>(tile + 1) * KT <= llen;
+    if (interior) {
+      const char* tb = ubase + tile * ustep;
+      if (RED_CONTIG) {
+        r = *reinterpret_cast<const Raw8<E>*>(tb + voff);
+        return;
+      }
+      uint32_t e[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) e[j] = bits_of<T>(*reinterpret_cast<const T*>(tb + j * uld + voff));
+#pragma unroll
+      for (int i = 0; i < Raw8<E>::NW; ++i)
+        r.w[i] = (Raw8<E>::NW == 8) ? e[i] : (e[2 * i] | (e[2 * i + 1] << 16));
+      return;
+    }
+    uint32_t e[8];
+    const int64_t l0 = static_cast<int64_t>(tile) * KT + gl;
+    const bool xok = gx < xlen;
+    const int64_t xc = xok ? gx : xlen - 1;
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-      const int x = xb + j;
-      double v = 0.0;
-      if (gl < llen && x0 + x < xlen) v = E::up(row[x]);
-      dst[l * BN + x] = v;
+      const int64_t l = l0 + j;
+      const int64_t lc = l < llen ? l : llen - 1;
+      const uint32_t v = bits_of<T>(RED_CONTIG ? src[xc * ld + lc] : src[lc * ld + xc]);
+      e[j] = (xok && l < llen) ? v : 0u;
+    }
+#pragma unroll
+    for (int i = 0; i < Raw8<E>::NW; ++i)
+      r.w[i] = (Raw8<E>::NW == 8) ? e[i] : (e[2 * i] | (e[2 * i + 1] << 16));
+  }
+
+  __device__ inline void store(double* __restrict__ dst, const Raw8<E>& r) const {
+    const int t = threadIdx.x;
+    const int x = t & 63, l = (t >> 6) * 8;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) dst[(l + j) * LS + x] = element<E>(r, j);
+  }
+};
+
+__device__ inline int tiles_of(int64_t red) { return static_cast<int>((red + KT - 1) / KT); }
+
+// ---- valu kernel ------------------------------------------------------------
+
+// acc = fma(a taken from lane N of this lane's row of 16, b, acc), one rounding.
+template <int N> __device__ inline void fmac_bcast(double& acc, double a, double b) {
+  asm("v_fmac_f64_dpp %0, %1, %2 row_newbcast:%3 row_mask:0xf bank_mask:0xf"
+      : "+v"(acc) : "v"(a), "v"(b), "i"(N));
+}
+template <int N> __device__ inline void fmac_rows(double (&p)[16], double a, double b) {
+  fmac_bcast<N>(p[N], a, b);
+  if constexpr (N + 1 < 16) fmac_rows<N + 1>(p, a, b);
+}
+
+template <typename E, bool A_RED_CONTIG, bool B_RED_CONTIG>
+__global__ void __launch_bounds__(THREADS) exact_valu_kernel(GemmArgs args) {
+  __shared__ double As[2][KT * LS];
+  __shared__ double Bs[2][KT * LS];
+  const int64_t tiles_n = (args.cols + BN - 1) / BN;
+  const int64_t row0 = (static_cast<int64_t>(blockIdx.x) / tiles_n) * BM;
+  const int64_t col0 = (static_cast<int64_t>(blockIdx.x) % tiles_n) * BN;
+  const int wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int wr = wave * 16;          // the wave's 16 rows inside the block
+
+  const Stager<E, A_RED_CONTIG> sa(static_cast<const typename E::T*>(args.A), args.lda, row0, args.rows, args.red, args.vec_a, args.off32_a);
+  const Stager<E, B_RED_CONTIG> sb(static_cast<const typename E::T*>(args.B), args.ldb, col0, args.cols, args.red, args.vec_b, args.off32_b);
+  Raw8<E> ra, rb;
+
+  double s[16], c[16];
+#pragma unroll
+  for (int n = 0; n < 16; ++n) { s[n] = 0.0; c[n] = 0.0; }
+
+  const int ntiles = tiles_of(args.red);
+  sa.load(0, ra);
+  sb.load(0, rb);
+  sa.store(As[0], ra);
+  sb.store(Bs[0], rb);
+  __syncthreads();
+
+  for (int t = 0; t < ntiles; ++t) {
+    const int buf = static_cast<int>(t & 1);
+    const bool more = t + 1 < ntiles;
+    if (more) { sa.load(t + 1, ra); sb.load(t + 1, rb); }
+    const double* __restrict__ as = As[buf] + wr + (lane & 15);
+    const double* __restrict__ bs = Bs[buf] + lane;
+    double p[16];
+#pragma unroll
+    for (int n = 0; n < 16; ++n) p[n] = 0.0;
+#pragma unroll 8
+    for (int k = 0; k < KT; ++k) {
+      const double a = as[k * LS];
+      const double b = bs[k * LS];
+      fmac_rows<0>(p, a, b);
+    }
+#pragma unroll
+    for (int n = 0; n < 16; ++n) kbn_add(s[n], c[n], p[n]);
+    if (more) { sa.store(As[buf ^ 1], ra); sb.store(Bs[buf ^ 1], rb); }
+    __syncthreads();
+  }
+
+  typename E::T* __restrict__ Y = static_cast<typename E::T*>(args.out);
+  const typename E::T* __restrict__ bias = static_cast<const typename E::T*>(args.bias);
+  const int64_t col = col0 + lane;
+  if (col < args.cols) {
+    const double bj = bias ? E::up(bias[col]) : 0.0;
+#pragma unroll
+    for (int n = 0; n < 16; ++n) {
+      const int64_t row = row0 + wr + n;
+      if (row < args.rows) {
+        double r = s[n] + c[n];
+        if (bias) r = r + bj;
+        Y[row * args.cols + col] = round_from_f64<E>(r);
+      }
     }
   }
 }
 
-template <typename E, bool A_RED_CONTIG, bool B_RED_CONTIG>
-__global__ void __launch_bounds__(THREADS) exact_kernel(GemmArgs args) {
-  __shared__ double As[2][KT * BM];
-  __shared__ double Bs[2][KT * BN];
+// ---- mfma4 kernel -----------------------------------------------------------
+//
+// V_MFMA_F64_4X4X4_4B_F64 operand layout (block g = 0..3, lane L):
+//   A: L = 16k + 4g + i holds A_g[i][k];  B: L = 16k + 4g + j holds B_g[k][j];
+//   D: L = 16i + 4g + j holds D_g[i][j].
+// Wave w owns columns 16w .. 16w+15 of the 64-column block and all 64 rows.
+// Row fragment u (u = 0..3) puts row 16u + 4g + i in block g; column fragment
+// r (r = 0..3) puts column 16w + 4((g + r) mod 4) + j in block g. Instruction
+// (u, r) therefore covers rows 16u + 4g + i against columns 4((g + r) mod 4) + j
+// for every block g, and the 16 instructions cover the 64 x 16 outputs once.
 
-  const typename E::T* __restrict__ A = static_cast<const typename E::T*>(args.A);
-  const typename E::T* __restrict__ B = static_cast<const typename E::T*>(args.B);
+template <typename E, bool A_RED_CONTIG, bool B_RED_CONTIG, int NBUF>
+__global__ void __launch_bounds__(THREADS, NBUF == 1 ? 3 : 2) exact_mfma4_kernel(GemmArgs args) {
+  // NBUF == 2: double-buffered LDS (80 KB), one barrier per tile, 2 workgroups per CU.
+  // NBUF == 1: single LDS buffer (40 KB), two barriers per tile, 3 workgroups per CU.
+  __shared__ double As[NBUF][KT * LS];
+  __shared__ double Bs[NBUF][KT * LS];
+  const int64_t tiles_n = (args.cols + BN - 1) / BN;
+  const int64_t row0 = (static_cast<int64_t>(blockIdx.x) / tiles_n) * BM;
+  const int64_t col0 = (static_cast<int64_t>(blockIdx.x) % tiles_n) * BN;
+  const int wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int wn = wave * 16;
+  const int lk = lane >> 4;           // k inside a group of four (operands); i (results)
+  const int lg = (lane >> 2) & 3;     // block g
+  const int le = lane & 3;            // i (A operand) / j (B operand, results)
+
+  const Stager<E, A_RED_CONTIG> sa(static_cast<const typename E::T*>(args.A), args.lda, row0, args.rows, args.red, args.vec_a, args.off32_a);
+  const Stager<E, B_RED_CONTIG> sb(static_cast<const typename E::T*>(args.B), args.ldb, col0, args.cols, args.red, args.vec_b, args.off32_b);
+  Raw8<E> ra, rb;
+
+  int bcol[4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) bcol[r] = wn + 4 * ((lg + r) & 3) + le;
+
+  double s[4][4], c[4][4];
+#pragma unroll
+  for (int u = 0; u < 4; ++u)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) { s[u][r] = 0.0; c[u][r] = 0.0; }
+
+  const int ntiles = tiles_of(args.red);
+  sa.load(0, ra);
+  sb.load(0, rb);
+  sa.store(As[0], ra);
+  sb.store(Bs[0], rb);
+  __syncthreads();
+
+  for (int t = 0; t < ntiles; ++t) {
+    const int buf = NBUF == 2 ? (t & 1) : 0;
+    const bool more = t + 1 < ntiles;
+    if (more) { sa.load(t + 1, ra); sb.load(t + 1, rb); }
+    const double* __restrict__ as = As[buf] + lk * LS + (lane & 15);
+    const double* __restrict__ bs = Bs[buf] + lk * LS;
+    double p[4][4];
+    double a[2][4], b[2][4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) a[0][u] = as[16 * u];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) b[0][r] = bs[bcol[r]];
+#pragma unroll
+    for (int g = 0; g < KT / 4; ++g) {
+      const int cur = g & 1;
+      if (g + 1 < KT / 4) {
+        const int kr = (g + 1) * 4 * LS;
+#pragma unroll
+        for (int u = 0; u < 4; ++u) a[cur ^ 1][u] = as[kr + 16 * u];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) b[cur ^ 1][r] = bs[kr + bcol[r]];
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+#pragma unroll
+        for (int r = 0; r < 4; ++r)   // the chain of each tile starts from +0
+          p[u][r] = __builtin_amdgcn_mfma_f64_4x4x4f64(a[cur][u], b[cur][r], g == 0 ? 0.0 : p[u][r], 0, 0, 0);
+    }
+    if (NBUF == 1) __syncthreads();   // every wave is done reading the single buffer
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) kbn_add(s[u][r], c[u][r], p[u][r]);
+    if (more) { sa.store(As[NBUF == 2 ? buf ^ 1 : 0], ra); sb.store(Bs[NBUF == 2 ? buf ^ 1 : 0], rb); }
+    __syncthreads();
+  }
+
+  typename E::T* __restrict__ Y = static_cast<typename E::T*>(args.out);
+  const typename E::T* __restrict__ bias = static_cast<const typename E::T*>(args.bias);
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int64_t col = col0 + bcol[r];
+    if (col >= args.cols) continue;
+    const double bj = bias ? E::up(bias[col]) : 0.0;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int64_t row = row0 + 16 * u + 4 * lg + lk;   // result lane 16i + 4g + j
+      if (row < args.rows) {
+        double v = s[u][r] + c[u][r];
+        if (bias) v = v + bj;
+        Y[row * args.cols + col] = round_from_f64<E>(v);
+      }
+    }
+  }
+}
+
+// ---- mfma16 kernel ----------------------------------------------------------
+
+template <typename E, bool A_RED_CONTIG, bool B_RED_CONTIG>
+__global__ void __launch_bounds__(THREADS) exact_mfma_kernel(GemmArgs args) {
+  __shared__ double As[2][KT * LS];
+  __shared__ double Bs[2][KT * LS];
   const int64_t tiles_n = (args.cols + BN - 1) / BN;
   const int64_t row0 = (static_cast<int64_t>(blockIdx.x) / tiles_n) * BM;
   const int64_t col0 = (static_cast<int64_t>(blockIdx.x) % tiles_n) * BN;
@@ -104,6 +384,10 @@ __global__ void __launch_bounds__(THREADS) exact_kernel(GemmArgs args) {
   const int lr = lane & 15;   // row (A) / column (B, D) inside a 16x16 block
   const int lk = lane >> 4;   // k inside a group of four
 
+  const Stager<E, A_RED_CONTIG> sa(static_cast<const typename E::T*>(args.A), args.lda, row0, args.rows, args.red, args.vec_a, args.off32_a);
+  const Stager<E, B_RED_CONTIG> sb(static_cast<const typename E::T*>(args.B), args.ldb, col0, args.cols, args.red, args.vec_b, args.off32_b);
+  Raw8<E> ra, rb;
+
   double s[2][2][4], c[2][2][4];
 #pragma unroll
   for (int i = 0; i < 2; ++i)
@@ -112,17 +396,17 @@ __global__ void __launch_bounds__(THREADS) exact_kernel(GemmArgs args) {
 #pragma unroll
       for (int e = 0; e < 4; ++e) { s[i][j][e] = 0.0; c[i][j][e] = 0.0; }
 
-  const int64_t ntiles = (args.red + KT - 1) / KT;
-  stage<E, A_RED_CONTIG>(As[0], A, args.lda, row0, args.rows, 0, args.red);
-  stage<E, B_RED_CONTIG>(Bs[0], B, args.ldb, col0, args.cols, 0, args.red);
+  const int ntiles = tiles_of(args.red);
+  sa.load(0, ra);
+  sb.load(0, rb);
+  sa.store(As[0], ra);
+  sb.store(Bs[0], rb);
   __syncthreads();
 
-  for (int64_t t = 0; t < ntiles; ++t) {
+  for (int t = 0; t < ntiles; ++t) {
     const int buf = static_cast<int>(t & 1);
-    if (t + 1 < ntiles) {
-      stage<E, A_RED_CONTIG>(As[buf ^ 1], A, args.lda, row0, args.rows, (t + 1) * KT, args.red);
-      stage<E, B_RED_CONTIG>(Bs[buf ^ 1], B, args.ldb, col0, args.cols, (t + 1) * KT, args.red);
-    }
+    const bool more = t + 1 < ntiles;
+    if (more) { sa.load(t + 1, ra); sb.load(t + 1, rb); }
     const double* __restrict__ as = As[buf];
     const double* __restrict__ bs = Bs[buf];
     v4d p[2][2];
@@ -132,11 +416,11 @@ __global__ void __launch_bounds__(THREADS) exact_kernel(GemmArgs args) {
       for (int j = 0; j < 2; ++j) p[i][j] = v4d{0.0, 0.0, 0.0, 0.0};
 #pragma unroll
     for (int g = 0; g < KT / 4; ++g) {
-      const int kr = (4 * g + lk);
-      const double a0 = as[kr * BM + wm + lr];
-      const double a1 = as[kr * BM + wm + 16 + lr];
-      const double b0 = bs[kr * BN + wn + lr];
-      const double b1 = bs[kr * BN + wn + 16 + lr];
+      const int kr = 4 * g + lk;
+      const double a0 = as[kr * LS + wm + lr];
+      const double a1 = as[kr * LS + wm + 16 + lr];
+      const double b0 = bs[kr * LS + wn + lr];
+      const double b1 = bs[kr * LS + wn + 16 + lr];
       p[0][0] = __builtin_amdgcn_mfma_f64_16x16x4f64(a0, b0, p[0][0], 0, 0, 0);
       p[0][1] = __builtin_amdgcn_mfma_f64_16x16x4f64(a0, b1, p[0][1], 0, 0, 0);
       p[1][0] = __builtin_amdgcn_mfma_f64_16x16x4f64(a1, b0, p[1][0], 0, 0, 0);
@@ -147,7 +431,8 @@ __global__ void __launch_bounds__(THREADS) exact_kernel(GemmArgs args) {
 #pragma unroll
       for (int j = 0; j < 2; ++j)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) neumaier_add(s[i][j][e], c[i][j][e], p[i][j][e]);
+        for (int e = 0; e < 4; ++e) kbn_add(s[i][j][e], c[i][j][e], p[i][j][e]);
+    if (more) { sa.store(As[buf ^ 1], ra); sb.store(Bs[buf ^ 1], rb); }
     __syncthreads();
   }
 
@@ -160,6 +445,7 @@ __global__ void __launch_bounds__(THREADS) exact_kernel(GemmArgs args) {
       const int64_t col = col0 + wn + 16 * j + lr;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
+        // accumulator e of lane l of a V_MFMA_F64_16X16X4 block is row 4e + l/16, column l%16
         const int64_t row = row0 + wm + 16 * i + 4 * e + lk;
         if (row < args.rows && col < args.cols) {
           double r = s[i][j][e] + c[i][j][e];
@@ -170,31 +456,41 @@ __global__ void __launch_bounds__(THREADS) exact_kernel(GemmArgs args) {
     }
 }
 
+// ---- launch -----------------------------------------------------------------
+
 template <typename E, bool AC, bool BC>
-hipError_t launch_typed(const GemmArgs& a, hipStream_t stream) {
+hipError_t launch_typed(const GemmArgs& a, int variant, hipStream_t stream) {
   const int64_t blocks = ((a.cols + BN - 1) / BN) * ((a.rows + BM - 1) / BM);
   if (blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
-  hipLaunchKernelGGL((exact_kernel<E, AC, BC>), dim3(static_cast<unsigned>(blocks)), dim3(THREADS), 0, stream, a);
+  const dim3 grid(static_cast<unsigned>(blocks));
+  if (variant == 1)
+    hipLaunchKernelGGL((exact_mfma_kernel<E, AC, BC>), grid, dim3(THREADS), 0, stream, a);
+  else if (variant == 2)
+    hipLaunchKernelGGL((exact_valu_kernel<E, AC, BC>), grid, dim3(THREADS), 0, stream, a);
+  else if (variant == 3)
+    hipLaunchKernelGGL((exact_mfma4_kernel<E, AC, BC, 2>), grid, dim3(THREADS), 0, stream, a);
+  else
+    hipLaunchKernelGGL((exact_mfma4_kernel<E, AC, BC, 1>), grid, dim3(THREADS), 0, stream, a);
   return hipGetLastError();
 }
 
 template <typename E>
-hipError_t launch_op(Op op, const GemmArgs& a, hipStream_t stream) {
+hipError_t launch_op(Op op, const GemmArgs& a, int variant, hipStream_t stream) {
   switch (op) {
-    case OP_FWD: return launch_typed<E, true, false>(a, stream);   // X[i][k], W[k][j]
-    case OP_DX:  return launch_typed<E, true, true>(a, stream);    // dY[i][n], W[q][n]
-    case OP_DW:  return launch_typed<E, false, false>(a, stream);  // X[i][q], dY[i][j]
+    case OP_FWD: return launch_typed<E, true, false>(a, variant, stream);   // X[i][k], W[k][j]
+    case OP_DX:  return launch_typed<E, true, true>(a, variant, stream);    // dY[i][n], W[q][n]
+    case OP_DW:  return launch_typed<E, false, false>(a, variant, stream);  // X[i][q], dY[i][j]
   }
   return hipErrorInvalidValue;
 }
 
 }  // namespace
 
-hipError_t launch_exact(Op op, Dt dt, const GemmArgs& a, hipStream_t stream) {
+hipError_t launch_exact(Op op, Dt dt, const GemmArgs& a, int variant, hipStream_t stream) {
   switch (dt) {
-    case DT_F32: return launch_op<F32>(op, a, stream);
-    case DT_BF16: return launch_op<BF16>(op, a, stream);
-    case DT_F16: return launch_op<F16>(op, a, stream);
+    case DT_F32: return launch_op<F32>(op, a, variant, stream);
+    case DT_BF16: return launch_op<BF16>(op, a, variant, stream);
+    case DT_F16: return launch_op<F16>(op, a, variant, stream);
   }
   return hipErrorInvalidValue;
 }

@@ -112,12 +112,21 @@ const char* det_gemm_last_error(void);
 int det_gemm_version(void);
 
 /*
- * Test hook: force the fast tier's tile family (-1 automatic, 0 = the large
- * family, 1 = the small family) for later calls from any thread. Both families
+ * Test hook: force the fast tier's tile family for later calls from any thread
+ * (-1 automatic, 0 = the large family, 1 = the small family). Both families
  * produce identical bits, so this changes speed only. Returns DET_EINVAL for
  * other values.
  */
 det_status_t det_gemm_debug_force_family(int family);
+
+/*
+ * Test hook: force the exact tier's kernel for later calls from any thread
+ * (-1 automatic, 0 = 4x4x4 float64 matrix-core kernel, 1 = 16x16x4 float64
+ * matrix-core kernel, 2 = float64 vector-ALU kernel). All produce the same
+ * bits (the oracle's), so this changes speed only. Returns DET_EINVAL for other
+ * values.
+ */
+det_status_t det_gemm_debug_force_exact_kernel(int variant);
 
 #ifdef __cplusplus
 }

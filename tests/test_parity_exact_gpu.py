@@ -29,11 +29,22 @@ def test_config1_fp32_fwd_dx_dw():
     assert_bits_equal(gpu_op("dw", "f32", X, G), oracle.dw("f32", X, G)[0], "dw")
 
 
+@pytest.fixture(autouse=True)
+def _auto_variant():
+    import deterministic_invariant_gemm_det_amd as dg
+    dg.det_gemm_debug_force_exact_kernel(-1)
+    yield
+    dg.det_gemm_debug_force_exact_kernel(-1)
+
+
+@pytest.mark.parametrize("variant", [0, 1, 2], ids=["mfma4", "mfma16", "valu"])
 @pytest.mark.parametrize("dt", DTS)
 @pytest.mark.parametrize("op", ["fwd", "dx", "dw"])
-def test_ragged_shapes(op, dt):
+def test_ragged_shapes(op, dt, variant):
+    import deterministic_invariant_gemm_det_amd as dg
+    dg.det_gemm_debug_force_exact_kernel(variant)
     for si, (m, k, n) in enumerate(SHAPES):
-        print(f"exact {op} {dt} {(m, k, n)}", flush=True)
+        print(f"exact {op} {dt} {(m, k, n)} variant {variant}", flush=True)
         sa, sb = operand_shapes(op, m, k, n)
         A = syn.normal(900 + si, 0, sa, dt=dt)
         B = syn.normal(900 + si, 1, sb, sigma=0.5, dt=dt)
