@@ -84,6 +84,8 @@ det_status_t run(detgemm::Op op, void* out, const void* A, const void* B, const 
   const int64_t b_elems = (op == detgemm::OP_DW) ? m * n : k * n;
   a.off32_a = a_elems * esz < (int64_t(1) << 31);
   a.off32_b = b_elems * esz < (int64_t(1) << 31);
+  a.a_bytes = a_elems * esz;
+  a.b_bytes = b_elems * esz;
   const detgemm::Dt d = static_cast<detgemm::Dt>(dt);
   hipError_t err;
   if (tier == DET_TIER_EXACT) {

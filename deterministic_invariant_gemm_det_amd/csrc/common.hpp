@@ -21,6 +21,7 @@ struct GemmArgs {
   int64_t rows, cols, red;
   bool vec_a, vec_b; // 16-byte vector loads allowed (base and row stride aligned)
   bool off32_a, off32_b; // every element offset of the operand fits in 32 bits
+  int64_t a_bytes, b_bytes; // size of each operand in bytes
 };
 
 enum Dt { DT_F32 = 0, DT_BF16 = 1, DT_F16 = 2 };
@@ -76,12 +77,15 @@ template <> __device__ inline _Float16 round_from_f64<F16>(double r) { return st
 // Round-to-nearest-even of an f32 accumulator to the output type.
 template <typename E> __device__ inline typename E::T round_from_f32(float r);
 template <> __device__ inline float round_from_f32<F32>(float r) { return r; }
-template <> __device__ inline uint16_t round_from_f32<BF16>(float r) { return f32_to_bf16_rne(r); }
+template <> __device__ inline uint16_t round_from_f32<BF16>(float r) {
+  return __builtin_bit_cast(uint16_t, static_cast<__bf16>(r));   // V_CVT_PK_BF16_F32, round to nearest even
+}
 template <> __device__ inline _Float16 round_from_f32<F16>(float r) { return static_cast<_Float16>(r); }
 
 // Host-side launchers (one per tier), defined next to their kernels.
 hipError_t launch_exact(Op op, Dt dt, const GemmArgs& a, int variant, hipStream_t stream);
 hipError_t launch_fast(Op op, Dt dt, const GemmArgs& a, int family, hipStream_t stream);
+hipError_t launch_fast16(Op op, Dt dt, const GemmArgs& a, int family, hipStream_t stream);
 int fast_auto_family(Op op, Dt dt, int64_t cols, int64_t red);
 
 }  // namespace detgemm

@@ -181,8 +181,8 @@ int fast_auto_family(Op op, Dt dt, int64_t cols, int64_t red) {
 hipError_t launch_fast(Op op, Dt dt, const GemmArgs& a, int family, hipStream_t stream) {
   switch (dt) {
     case DT_F32: return launch_family<F32>(op, family, a, stream);
-    case DT_BF16: return launch_family<BF16>(op, family, a, stream);
-    case DT_F16: return launch_family<F16>(op, family, a, stream);
+    case DT_BF16:
+    case DT_F16: return launch_fast16(op, dt, a, family, stream);
   }
   return hipErrorInvalidValue;
 }
