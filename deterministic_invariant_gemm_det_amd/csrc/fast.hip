@@ -173,16 +173,24 @@ hipError_t launch_family(Op op, int family, const GemmArgs& a, hipStream_t strea
 }  // namespace
 
 // Shape-only choice of the tile family: never reads the row count of fwd/dx.
+// Family choice from the call's shape alone (the families give identical
+// bits, so this only affects speed). f32: wide outputs take the large tiles.
+// 16-bit: the large direct-to-LDS tiles pay off on long reductions outside dW;
+// short reductions and dW run faster on the smaller register-staged tiles.
 int fast_auto_family(Op op, Dt dt, int64_t cols, int64_t red) {
-  (void)op; (void)dt; (void)red;
-  return cols >= 1024 ? 0 : 1;
+  if (dt == DT_F32) return cols >= 1024 ? 0 : 1;
+  return (op != OP_DW && red >= 2048) ? 0 : 1;
 }
 
 hipError_t launch_fast(Op op, Dt dt, const GemmArgs& a, int family, hipStream_t stream) {
   switch (dt) {
     case DT_F32: return launch_family<F32>(op, family, a, stream);
     case DT_BF16:
-    case DT_F16: return launch_fast16(op, dt, a, family, stream);
+    case DT_F16:
+      // family 0: large tiles fed straight into LDS where the shape allows it;
+      // otherwise (and family 1) the register-staged kernel. Identical bits.
+      if (family == 0 && fast16_dl_ok(a)) return launch_fast16_dl(op, dt, a, stream);
+      return launch_fast16(op, dt, a, family, stream);
   }
   return hipErrorInvalidValue;
 }

@@ -11,7 +11,9 @@ pytestmark = pytest.mark.gpu
 
 DTS = ("f32", "bf16", "f16")
 SHAPES = [(1, 1, 1), (3, 33, 65), (127, 70, 129), (64, 64, 64), (200, 300, 100), (17, 1000, 5),
-          (65, 31, 63), (2, 97, 250), (130, 200, 1100), (257, 129, 1030)]
+          (65, 31, 63), (2, 97, 250), (130, 200, 1100), (257, 129, 1030),
+          # reduction lengths that are multiples of 64 for every op (large-tile kernel), ragged edges
+          (320, 128, 192), (512, 256, 136), (192, 640, 1000), (64, 64, 1088), (576, 192, 64)]
 
 
 @pytest.fixture(autouse=True)
