@@ -19,13 +19,14 @@ std::atomic<int> g_force_exact{-1};
 constexpr int kMaxDevices = 64;
 // 0 unknown, 1 gfx950, 2 not supported
 std::atomic<int> g_device_ok[kMaxDevices];
+std::atomic<int> g_device_cus[kMaxDevices];   // compute units, cached with the check
 
 det_status_t fail(det_status_t st, const char* fmt, const char* detail = "") {
   std::snprintf(g_last_error, sizeof(g_last_error), fmt, detail);
   return st;
 }
 
-det_status_t check_device() {
+det_status_t check_device(int* cus) {
   int dev = -1;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0) {
     (void)hipGetLastError();
@@ -40,10 +41,12 @@ det_status_t check_device() {
       return fail(DET_EDEVICE, "det_gemm: cannot query the current device%s");
     }
     state = (std::strncmp(prop.gcnArchName, "gfx950", 6) == 0) ? 1 : 2;
+    g_device_cus[dev].store(prop.multiProcessorCount > 0 ? prop.multiProcessorCount : 1, std::memory_order_relaxed);
     g_device_ok[dev].store(state, std::memory_order_release);
     if (state == 2) return fail(DET_EDEVICE, "det_gemm: device architecture %s is not gfx950 (MI355X); refusing to run", prop.gcnArchName);
   }
   if (state == 2) return fail(DET_EDEVICE, "det_gemm: the current device is not gfx950 (MI355X); refusing to run%s");
+  *cus = g_device_cus[dev].load(std::memory_order_relaxed);
   return DET_OK;
 }
 
@@ -63,7 +66,8 @@ det_status_t run(detgemm::Op op, void* out, const void* A, const void* B, const 
   const int64_t esz = dt == DET_F32 ? 4 : 2;
   if (!mul_ok(m, k, esz) || !mul_ok(k, n, esz) || !mul_ok(m, n, esz))
     return fail(DET_EINVAL, "det_gemm: tensor size overflows int64%s");
-  const det_status_t dev = check_device();
+  int cus = 0;
+  const det_status_t dev = check_device(&cus);
   if (dev != DET_OK) return dev;
 
   detgemm::GemmArgs a;
@@ -71,6 +75,7 @@ det_status_t run(detgemm::Op op, void* out, const void* A, const void* B, const 
   a.B = B;
   a.bias = bias;
   a.out = out;
+  a.num_cu = cus;
   switch (op) {
     case detgemm::OP_FWD: a.rows = m; a.cols = n; a.red = k; a.lda = k; a.ldb = n; break;
     case detgemm::OP_DX:  a.rows = m; a.cols = k; a.red = n; a.lda = n; a.ldb = n; break;
@@ -90,7 +95,7 @@ det_status_t run(detgemm::Op op, void* out, const void* A, const void* B, const 
   hipError_t err;
   if (tier == DET_TIER_EXACT) {
     const int v = g_force_exact.load(std::memory_order_relaxed);
-    err = detgemm::launch_exact(op, d, a, v < 0 ? 0 : v, stream);
+    err = detgemm::launch_exact(op, d, a, v, stream);
   } else {
     int fam = g_force_family.load(std::memory_order_relaxed);
     if (fam < 0) fam = detgemm::fast_auto_family(op, d, a.cols, a.red);
@@ -145,7 +150,7 @@ det_status_t det_gemm_debug_force_family(int family) {
 }
 
 det_status_t det_gemm_debug_force_exact_kernel(int variant) {
-  if (variant < -1 || variant > 3) return fail(DET_EINVAL, "det_gemm: exact kernel must be -1 .. 3%s");
+  if (variant < -1 || variant > 4) return fail(DET_EINVAL, "det_gemm: exact kernel must be -1 .. 4%s");
   g_force_exact.store(variant, std::memory_order_relaxed);
   return DET_OK;
 }

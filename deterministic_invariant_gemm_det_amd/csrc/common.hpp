@@ -22,6 +22,7 @@ struct GemmArgs {
   bool vec_a, vec_b; // 16-byte vector loads allowed (base and row stride aligned)
   bool off32_a, off32_b; // every element offset of the operand fits in 32 bits
   int64_t a_bytes, b_bytes; // size of each operand in bytes
+  int num_cu;        // compute units of the device (launch-shape choice only)
 };
 
 enum Dt { DT_F32 = 0, DT_BF16 = 1, DT_F16 = 2 };

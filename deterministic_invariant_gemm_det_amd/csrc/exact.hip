@@ -20,7 +20,8 @@
 //   * Every output is computed the same way wherever it sits, so a row's bits do
 //     not depend on the number of rows, the tile grid or the launch.
 //
-// Three kernels implement it, with identical bits (the default is mfma4):
+// Three kernels implement it, with identical bits (the default is mfma4, in
+// 64- or 48-row blocks by launch balance):
 //   mfma4 — the fma chains on V_MFMA_F64_4X4X4_4B_F64: four independent 4x4
 //           blocks per instruction, each output acc = fma(a_k, b_k, acc) over
 //           its four k in ascending order, one rounding per step (checked bit
@@ -104,7 +105,9 @@ template <typename E> __device__ inline double element(const Raw8<E>& r, int j) 
   return up_bits<E>((r.w[j >> 1] >> (16 * (j & 1))) & 0xffffu);
 }
 
-template <typename E, bool RED_CONTIG>
+// XW (<= 64) is the slice's width along the non-reduction dimension; lanes
+// past it repeat the last column's loads and fill LDS columns nobody reads.
+template <typename E, bool RED_CONTIG, int XW = 64>
 struct Stager {
   using T = typename E::T;
   static constexpr int64_t ES = sizeof(T);
@@ -125,9 +128,10 @@ struct Stager {
     ld = ld_;
     xlen = xlen_;
     llen = llen_;
-    gx = x0 + (t & 63);
+    const int x = (t & 63) < XW ? (t & 63) : XW - 1;
+    gx = x0 + x;
     gl = wave * 8;
-    full = off32 && (x0 + 64 <= xlen_) && (!RED_CONTIG || aligned);
+    full = off32 && (x0 + XW <= xlen_) && (!RED_CONTIG || aligned);
     const char* b = reinterpret_cast<const char*>(src_);
     if (RED_CONTIG) {
       ubase = b + gl * ES;
@@ -138,7 +142,7 @@ struct Stager {
       ubase = b + (gl * ld_ + x0) * ES;
       ustep = KT * ld_ * ES;
       uld = ld_ * ES;
-      voff = static_cast<uint32_t>((t & 63) * ES);
+      voff = static_cast<uint32_t>(x * ES);
     }
   }
 
@@ -269,20 +273,25 @@ __global__ void __launch_bounds__(THREADS) exact_valu_kernel(GemmArgs args) {
 // V_MFMA_F64_4X4X4_4B_F64 operand layout (block g = 0..3, lane L):
 //   A: L = 16k + 4g + i holds A_g[i][k];  B: L = 16k + 4g + j holds B_g[k][j];
 //   D: L = 16i + 4g + j holds D_g[i][j].
-// Wave w owns columns 16w .. 16w+15 of the 64-column block and all 64 rows.
-// Row fragment u (u = 0..3) puts row 16u + 4g + i in block g; column fragment
-// r (r = 0..3) puts column 16w + 4((g + r) mod 4) + j in block g. Instruction
-// (u, r) therefore covers rows 16u + 4g + i against columns 4((g + r) mod 4) + j
-// for every block g, and the 16 instructions cover the 64 x 16 outputs once.
+// Wave w owns columns 16w .. 16w+15 of the 64-column block and all BMT rows
+// (BMT = 64 or 48). Row fragment u (u < BMT / 16) puts row 16u + 4g + i in
+// block g; column fragment r (r = 0..3) puts column 16w + 4((g + r) mod 4) + j
+// in block g. Instruction (u, r) therefore covers rows 16u + 4g + i against
+// columns 4((g + r) mod 4) + j for every block g, and the instructions cover
+// the BMT x 16 outputs once. The 48-row form exists for launch balance: it
+// turns grids such as 12 x 48 blocks of 64 x 64 (2.25 per compute unit) into
+// 16 x 48 blocks of 48 x 64 (three per compute unit, all resident at once).
 
-template <typename E, bool A_RED_CONTIG, bool B_RED_CONTIG, int NBUF>
+template <typename E, bool A_RED_CONTIG, bool B_RED_CONTIG, int NBUF, int BMT>
 __global__ void __launch_bounds__(THREADS, NBUF == 1 ? 3 : 2) exact_mfma4_kernel(GemmArgs args) {
   // NBUF == 2: double-buffered LDS (80 KB), one barrier per tile, 2 workgroups per CU.
   // NBUF == 1: single LDS buffer (40 KB), two barriers per tile, 3 workgroups per CU.
+  constexpr int NU = BMT / 16;
+  static_assert(BMT % 16 == 0 && BMT <= BM, "row block");
   __shared__ double As[NBUF][KT * LS];
   __shared__ double Bs[NBUF][KT * LS];
   const int64_t tiles_n = (args.cols + BN - 1) / BN;
-  const int64_t row0 = (static_cast<int64_t>(blockIdx.x) / tiles_n) * BM;
+  const int64_t row0 = (static_cast<int64_t>(blockIdx.x) / tiles_n) * BMT;
   const int64_t col0 = (static_cast<int64_t>(blockIdx.x) % tiles_n) * BN;
   const int wave = threadIdx.x >> 6;
   const int lane = threadIdx.x & 63;
@@ -291,7 +300,7 @@ __global__ void __launch_bounds__(THREADS, NBUF == 1 ? 3 : 2) exact_mfma4_kernel
   const int lg = (lane >> 2) & 3;     // block g
   const int le = lane & 3;            // i (A operand) / j (B operand, results)
 
-  const Stager<E, A_RED_CONTIG> sa(static_cast<const typename E::T*>(args.A), args.lda, row0, args.rows, args.red, args.vec_a, args.off32_a);
+  const Stager<E, A_RED_CONTIG, BMT> sa(static_cast<const typename E::T*>(args.A), args.lda, row0, args.rows, args.red, args.vec_a, args.off32_a);
   const Stager<E, B_RED_CONTIG> sb(static_cast<const typename E::T*>(args.B), args.ldb, col0, args.cols, args.red, args.vec_b, args.off32_b);
   Raw8<E> ra, rb;
 
@@ -299,9 +308,9 @@ __global__ void __launch_bounds__(THREADS, NBUF == 1 ? 3 : 2) exact_mfma4_kernel
 #pragma unroll
   for (int r = 0; r < 4; ++r) bcol[r] = wn + 4 * ((lg + r) & 3) + le;
 
-  double s[4][4], c[4][4];
+  double s[NU][4], c[NU][4];
 #pragma unroll
-  for (int u = 0; u < 4; ++u)
+  for (int u = 0; u < NU; ++u)
 #pragma unroll
     for (int r = 0; r < 4; ++r) { s[u][r] = 0.0; c[u][r] = 0.0; }
 
@@ -318,10 +327,10 @@ __global__ void __launch_bounds__(THREADS, NBUF == 1 ? 3 : 2) exact_mfma4_kernel
     if (more) { sa.load(t + 1, ra); sb.load(t + 1, rb); }
     const double* __restrict__ as = As[buf] + lk * LS + (lane & 15);
     const double* __restrict__ bs = Bs[buf] + lk * LS;
-    double p[4][4];
-    double a[2][4], b[2][4];
+    double p[NU][4];
+    double a[2][NU], b[2][4];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) a[0][u] = as[16 * u];
+    for (int u = 0; u < NU; ++u) a[0][u] = as[16 * u];
 #pragma unroll
     for (int r = 0; r < 4; ++r) b[0][r] = bs[bcol[r]];
 #pragma unroll
@@ -330,19 +339,19 @@ __global__ void __launch_bounds__(THREADS, NBUF == 1 ? 3 : 2) exact_mfma4_kernel
       if (g + 1 < KT / 4) {
         const int kr = (g + 1) * 4 * LS;
 #pragma unroll
-        for (int u = 0; u < 4; ++u) a[cur ^ 1][u] = as[kr + 16 * u];
+        for (int u = 0; u < NU; ++u) a[cur ^ 1][u] = as[kr + 16 * u];
 #pragma unroll
         for (int r = 0; r < 4; ++r) b[cur ^ 1][r] = bs[kr + bcol[r]];
       }
 #pragma unroll
-      for (int u = 0; u < 4; ++u)
+      for (int u = 0; u < NU; ++u)
 #pragma unroll
         for (int r = 0; r < 4; ++r)   // the chain of each tile starts from +0
           p[u][r] = __builtin_amdgcn_mfma_f64_4x4x4f64(a[cur][u], b[cur][r], g == 0 ? 0.0 : p[u][r], 0, 0, 0);
     }
     if (NBUF == 1) __syncthreads();   // every wave is done reading the single buffer
 #pragma unroll
-    for (int u = 0; u < 4; ++u)
+    for (int u = 0; u < NU; ++u)
 #pragma unroll
       for (int r = 0; r < 4; ++r) kbn_add(s[u][r], c[u][r], p[u][r]);
     if (more) { sa.store(As[NBUF == 2 ? buf ^ 1 : 0], ra); sb.store(Bs[NBUF == 2 ? buf ^ 1 : 0], rb); }
@@ -357,7 +366,7 @@ __global__ void __launch_bounds__(THREADS, NBUF == 1 ? 3 : 2) exact_mfma4_kernel
     if (col >= args.cols) continue;
     const double bj = bias ? E::up(bias[col]) : 0.0;
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
+    for (int u = 0; u < NU; ++u) {
       const int64_t row = row0 + 16 * u + 4 * lg + lk;   // result lane 16i + 4g + j
       if (row < args.rows) {
         double v = s[u][r] + c[u][r];
@@ -458,8 +467,21 @@ __global__ void __launch_bounds__(THREADS) exact_mfma_kernel(GemmArgs args) {
 
 // ---- launch -----------------------------------------------------------------
 
+// Launch balance of the default kernel: every block of one grid does the same
+// work, proportional to its rows, and three blocks fit on a compute unit. The
+// time of a grid is about (rounds of resident blocks) x (rows per block); take
+// 48-row blocks when that is smaller. Both forms give identical bits.
+bool use_48_rows(const GemmArgs& a) {
+  const int64_t slots = 3 * static_cast<int64_t>(a.num_cu > 0 ? a.num_cu : 1);
+  const int64_t tn = (a.cols + BN - 1) / BN;
+  const int64_t r64 = (tn * ((a.rows + 63) / 64) + slots - 1) / slots;
+  const int64_t r48 = (tn * ((a.rows + 47) / 48) + slots - 1) / slots;
+  return r48 * 48 < r64 * 64;
+}
+
 template <typename E, bool AC, bool BC>
 hipError_t launch_typed(const GemmArgs& a, int variant, hipStream_t stream) {
+  if (variant < 0) variant = use_48_rows(a) ? 4 : 0;
   const int64_t blocks = ((a.cols + BN - 1) / BN) * ((a.rows + BM - 1) / BM);
   if (blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
   const dim3 grid(static_cast<unsigned>(blocks));
@@ -468,9 +490,14 @@ hipError_t launch_typed(const GemmArgs& a, int variant, hipStream_t stream) {
   else if (variant == 2)
     hipLaunchKernelGGL((exact_valu_kernel<E, AC, BC>), grid, dim3(THREADS), 0, stream, a);
   else if (variant == 3)
-    hipLaunchKernelGGL((exact_mfma4_kernel<E, AC, BC, 2>), grid, dim3(THREADS), 0, stream, a);
-  else
-    hipLaunchKernelGGL((exact_mfma4_kernel<E, AC, BC, 1>), grid, dim3(THREADS), 0, stream, a);
+    hipLaunchKernelGGL((exact_mfma4_kernel<E, AC, BC, 2, 64>), grid, dim3(THREADS), 0, stream, a);
+  else if (variant == 4) {
+    const int64_t b48 = ((a.cols + BN - 1) / BN) * ((a.rows + 47) / 48);
+    if (b48 > 0x7fffffff) return hipErrorInvalidConfiguration;
+    hipLaunchKernelGGL((exact_mfma4_kernel<E, AC, BC, 1, 48>), dim3(static_cast<unsigned>(b48)), dim3(THREADS), 0,
+                       stream, a);
+  } else
+    hipLaunchKernelGGL((exact_mfma4_kernel<E, AC, BC, 1, 64>), grid, dim3(THREADS), 0, stream, a);
   return hipGetLastError();
 }
 

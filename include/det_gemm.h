@@ -121,10 +121,11 @@ det_status_t det_gemm_debug_force_family(int family);
 
 /*
  * Test hook: force the exact tier's kernel for later calls from any thread
- * (-1 automatic, 0 = 4x4x4 float64 matrix-core kernel, 1 = 16x16x4 float64
- * matrix-core kernel, 2 = float64 vector-ALU kernel). All produce the same
- * bits (the oracle's), so this changes speed only. Returns DET_EINVAL for other
- * values.
+ * (-1 automatic, 0 = 4x4x4 float64 matrix-core kernel with 64-row blocks,
+ * 1 = 16x16x4 float64 matrix-core kernel, 2 = float64 vector-ALU kernel,
+ * 3 = the 4x4x4 kernel with a double-buffered LDS stage, 4 = the 4x4x4 kernel
+ * with 48-row blocks). All produce the same bits (the oracle's), so this
+ * changes speed only. Returns DET_EINVAL for other values.
  */
 det_status_t det_gemm_debug_force_exact_kernel(int variant);
 

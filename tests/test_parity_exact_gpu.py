@@ -10,7 +10,8 @@ from tests.gpu_util import assert_bits_equal, gpu_op, operand_shapes
 pytestmark = pytest.mark.gpu
 
 DTS = ("f32", "bf16", "f16")
-SHAPES = [(1, 1, 1), (3, 33, 65), (127, 70, 129), (64, 64, 64), (200, 300, 100), (17, 1000, 5), (65, 31, 63), (2, 97, 250)]
+SHAPES = [(1, 1, 1), (3, 33, 65), (127, 70, 129), (64, 64, 64), (200, 300, 100), (17, 1000, 5), (65, 31, 63), (2, 97, 250),
+          (96, 100, 144), (49, 48, 47)]
 
 
 def test_config1_fp32_fwd_dx_dw():
@@ -37,7 +38,7 @@ def _auto_variant():
     dg.det_gemm_debug_force_exact_kernel(-1)
 
 
-@pytest.mark.parametrize("variant", [0, 1, 2], ids=["mfma4", "mfma16", "valu"])
+@pytest.mark.parametrize("variant", [0, 1, 2, 3, 4], ids=["mfma4", "mfma16", "valu", "mfma4db", "mfma4r48"])
 @pytest.mark.parametrize("dt", DTS)
 @pytest.mark.parametrize("op", ["fwd", "dx", "dw"])
 def test_ragged_shapes(op, dt, variant):
