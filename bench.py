@@ -9,7 +9,13 @@ resident in HBM before the timed region.
 Prints one JSON line. `value` is useful TFLOP/s of the whole step
 (2*M*N*K per GEMM over the step time); per-tier and per-op rates, the
 roofline of the dominant kernel (measured with HIP events on the stream the
-kernels run on) and the CPU oracle's rate on a bounded sample are included.
+kernels run on; its HBM traffic comes from the committed counter summary
+under profiles/ while the kernel source is unchanged), skinny-M forward
+bandwidth and the CPU oracle's rate on a bounded sample are included.
+
+Profiling aids (not part of the measured step): --only tier.op runs just
+those launches, --copy-mib N times a plain device copy of N MiB, the known
+size against which memory counters are scaled.
 """
 import argparse
 import json
@@ -36,6 +42,11 @@ def parse():
     p.add_argument("--warmup", type=int, default=3)
     p.add_argument("--cpu-seconds", type=float, default=12.0, help="budget of the CPU-oracle sample")
     p.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline")
+    p.add_argument("--no-skinny", action="store_true", help="skip the skinny-M bandwidth measurements")
+    p.add_argument("--only", default=None,
+                   help="profiling aid: run only the launches of one tier and op (e.g. exact.dw) and print their times")
+    p.add_argument("--copy-mib", type=int, default=0,
+                   help="profiling aid: time a plain device copy of this many MiB instead (counter calibration)")
     return p.parse_args()
 
 
@@ -60,8 +71,8 @@ def make_inputs(dev):
     return data
 
 
-def launches(data):
-    """The step as a list of (tier, layer, op, callable)."""
+def launches(data, only=None):
+    """The step as a list of (tier, layer, op, callable); `only` = "tier.op" keeps those launches."""
     import deterministic_invariant_gemm_det_amd as dg
     out = []
     for tier in ("exact", "fast"):
@@ -70,6 +81,132 @@ def launches(data):
             out.append((tier, name, "fwd", lambda d=d, t=tier: dg.fwd(d["x"], d["w"], None, t, out=d["y"])))
             out.append((tier, name, "dx", lambda d=d, t=tier: dg.dx(d["g"], d["w"], t, out=d["gx"])))
             out.append((tier, name, "dw", lambda d=d, t=tier: dg.dw(d["x"], d["g"], t, out=d["gw"])))
+    if only:
+        out = [l for l in out if f"{l[0]}.{l[2]}" == only]
+        if not out:
+            raise SystemExit(f"bench.py: --only {only!r} matches no launch (use tier.op, e.g. exact.dw)")
+    return out
+
+
+def time_launches(steps, n_steps, warmup, stream):
+    """Warm up, then time n_steps passes over `steps` with an event pair around
+    every launch and one around the whole region, all on `stream`."""
+    import torch
+    for _ in range(warmup):
+        for _, _, _, f in steps:
+            f()
+    torch.cuda.synchronize()
+    ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in steps]
+          for _ in range(n_steps)]
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_start.record(stream)
+    for s in range(n_steps):
+        for i, (_, _, _, f) in enumerate(steps):
+            ev[s][i][0].record(stream)
+            f()
+            ev[s][i][1].record(stream)
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    per_launch_ms = [sum(ev[s][i][0].elapsed_time(ev[s][i][1]) for s in range(n_steps)) / n_steps
+                     for i in range(len(steps))]
+    return t_start.elapsed_time(t_end), per_launch_ms
+
+
+# Kernel sources whose HBM traffic the stored counter summary describes; the
+# stored figure is reported only while these files are unchanged.
+TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "exact_dw_bf16_gpt2mlp_8192tok_traffic.md")
+TRAFFIC_SOURCES = ("deterministic_invariant_gemm_det_amd/csrc/exact.hip",
+                   "deterministic_invariant_gemm_det_amd/csrc/common.hpp")
+
+
+def sources_sha256():
+    import hashlib
+    h = hashlib.sha256()
+    for rel in TRAFFIC_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def stored_traffic():
+    """HBM bytes per launch of the dominant kernel from the committed counter
+    summary (FETCH_SIZE + WRITE_SIZE, scaled by the copy-kernel calibration),
+    or None when the summary is missing or the kernel source changed since."""
+    try:
+        with open(TRAFFIC_SUMMARY) as f:
+            text = f.read()
+    except OSError:
+        return None
+    fields = {}
+    for line in text.splitlines():
+        line = line.strip().lstrip("-* ").replace("`", "")
+        if ":" in line:
+            key, val = line.split(":", 1)
+            fields[key.strip()] = val.strip()
+    if fields.get("kernel_sources_sha256") != sources_sha256():
+        return None
+    try:
+        return float(fields["traffic_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def copy_calibration(dev, mib, n_steps, warmup):
+    """A plain device-to-device copy of known size, for scaling memory counters."""
+    import torch
+    n = mib * (1 << 20)
+    src = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
+    dst = torch.empty(n, dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    steps = [("copy", "copy", "copy", lambda: dst.copy_(src))]
+    total_ms, per = time_launches(steps, n_steps, warmup, stream)
+    print(json.dumps({"copy_bytes_read": n, "copy_bytes_written": n, "us_per_copy": round(per[0] * 1e3, 2),
+                      "GB_per_s": round(2 * n / (per[0] * 1e-3) / 1e9, 1)}))
+
+
+def skinny(data, dev):
+    """Skinny-M forward (M = 1, 3, 17; the first rows of the c_fc input), both
+    tiers: achieved GB/s of algorithmic bytes, warm (200 back-to-back calls
+    with the weight resident in the last-level cache) and cold (a 512 MiB
+    buffer is written between calls so the weight comes from HBM)."""
+    import torch
+    import deterministic_invariant_gemm_det_amd as dg
+    d = data["c_fc"]
+    k, n = d["k"], d["n"]
+    flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    out = {}
+    for m in (1, 3, 17):
+        x = d["x"][:m].clone()
+        y = torch.empty((m, n), dtype=torch.bfloat16, device=dev)
+        algo_bytes = 2 * (m * k + k * n + m * n)
+        for tier in ("exact", "fast"):
+            f = lambda: dg.fwd(x, d["w"], None, tier, out=y)
+            for _ in range(5):
+                f()
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for _ in range(200):
+                f()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            warm_us = e0.elapsed_time(e1) * 1e3 / 200
+            cold = []
+            for _ in range(20):
+                flush.fill_(7)
+                a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                a.record(stream)
+                f()
+                b.record(stream)
+                torch.cuda.synchronize()
+                cold.append(a.elapsed_time(b) * 1e3)
+            cold_us = sorted(cold)[len(cold) // 2]
+            out[f"{tier}.M{m}"] = {"us_warm": round(warm_us, 2), "GBps_warm": round(algo_bytes / (warm_us * 1e-6) / 1e9, 1),
+                                   "us_cold": round(cold_us, 2), "GBps_cold": round(algo_bytes / (cold_us * 1e-6) / 1e9, 1),
+                                   "algo_bytes": algo_bytes}
     return out
 
 
@@ -113,37 +250,24 @@ def main():
         sys.exit(2)
     import torch
     dev = torch.device("cuda:0")
+    if args.copy_mib:
+        copy_calibration(dev, args.copy_mib, args.steps, args.warmup)
+        return
     data = make_inputs(dev)
-    steps = launches(data)
+    steps = launches(data, args.only)
     stream = torch.cuda.current_stream(dev)
-
-    for _ in range(args.warmup):
-        for _, _, _, f in steps:
-            f()
-    torch.cuda.synchronize()
-
-    ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in steps]
-          for _ in range(args.steps)]
-    t_start = torch.cuda.Event(enable_timing=True)
-    t_end = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    t_start.record(stream)
-    for s in range(args.steps):
-        for i, (_, _, _, f) in enumerate(steps):
-            ev[s][i][0].record(stream)
-            f()
-            ev[s][i][1].record(stream)
-    t_end.record(stream)
-    torch.cuda.synchronize()
-    total_ms = t_start.elapsed_time(t_end)
+    total_ms, per_launch_ms = time_launches(steps, args.steps, args.warmup, stream)
     ms_step = total_ms / args.steps
 
     per = {}
     for i, (tier, name, op, _) in enumerate(steps):
-        ms = sum(ev[s][i][0].elapsed_time(ev[s][i][1]) for s in range(args.steps)) / args.steps
+        ms = per_launch_ms[i]
         k, n = data[name]["k"], data[name]["n"]
         fl = 2.0 * TOKENS * k * n
         per[f"{tier}.{name}.{op}"] = {"us": round(ms * 1e3, 2), "tflops": round(fl / (ms * 1e-3) / 1e12, 2)}
+    if args.only:
+        print(json.dumps({"only": args.only, "steps": args.steps, "warmup": args.warmup, "per_gemm": per}))
+        return
 
     def tier_stats(tier, peak):
         keys = [k for k in per if k.startswith(tier + ".")]
@@ -155,13 +279,22 @@ def main():
     total_flops = 2 * sum(2.0 * TOKENS * k * n * len(OPS) for _, k, n in LAYERS)
     value = total_flops / (ms_step * 1e-3) / 1e12
 
-    # dominant kernel: the exact-tier launch with the largest share of the step
-    exact_keys = [k for k in per if k.startswith("exact.")]
-    dom = max(exact_keys, key=lambda k: per[k]["us"])
-    dom_tf = per[dom]["tflops"]
-    roofline = {"bound": "mfma", "achieved": dom_tf, "peak": PEAK_FP64, "unit": "TFLOP/s",
-                "frac": round(dom_tf / PEAK_FP64, 4), "traffic": None, "kernel": dom,
-                "note": "exact tier on FP64 matrix cores; peak is the FP64 (vector = matrix) rate"}
+    # Dominant kernel: the exact-tier dW kernel (its two launches, c_fc and
+    # c_proj, are one kernel with the same flops and the largest share of the
+    # step). achieved = algorithmic flops per launch / its average launch time.
+    dom = [k for k in per if k.startswith("exact.") and k.endswith(".dw")]
+    dom_us = sum(per[k]["us"] for k in dom) / len(dom)
+    dom_flops = 2.0 * TOKENS * LAYERS[0][1] * LAYERS[0][2]
+    dom_tf = dom_flops / (dom_us * 1e-6) / 1e12
+    roofline = {"bound": "mfma", "achieved": round(dom_tf, 2), "peak": PEAK_FP64, "unit": "TFLOP/s",
+                "frac": round(dom_tf / PEAK_FP64, 4), "traffic": stored_traffic(),
+                "kernel": "exact_mfma4_kernel<BF16, dW> (exact.c_fc.dw, exact.c_proj.dw)",
+                "avg_launch_us": round(dom_us, 2), "flops_per_launch": dom_flops,
+                "note": "exact tier on FP64 matrix cores (V_MFMA_F64_4X4X4); peak is MI355X FP64 (vector = matrix)"}
+    fast = tier_stats("fast", PEAK_BF16)
+    roofline_fast = {"bound": "mfma", "achieved": fast["tflops"], "peak": PEAK_BF16, "unit": "TFLOP/s",
+                     "frac": round(fast["tflops"] / PEAK_BF16, 4), "traffic": None,
+                     "kernel": "fast tier, all six launches (bf16 MFMA 32x32x16, f32 accumulate)"}
 
     result = {
         "metric": METRIC, "value": round(value, 3), "unit": "TFLOP/s", "n_gpus": 1,
@@ -171,10 +304,13 @@ def main():
         "config": {"workload": "GPT-2-124M MLP linears (c_fc 768->3072, c_proj 3072->768), 8192 tokens, "
                                "bf16 storage, fwd+dX+dW, exact tier then fast tier (12 GEMMs per step)",
                    "tokens": TOKENS, "layers": [list(l) for l in LAYERS]},
-        "tiers": {"exact": tier_stats("exact", PEAK_FP64), "fast": tier_stats("fast", PEAK_BF16)},
+        "tiers": {"exact": tier_stats("exact", PEAK_FP64), "fast": fast},
         "per_gemm": per,
         "roofline": roofline,
+        "roofline_fast": roofline_fast,
     }
+    if not args.no_skinny:
+        result["skinny_fwd_bf16_K768_N3072"] = skinny(data, dev)
     if not args.no_cpu:
         result["cpu_baseline"] = cpu_baseline(data, args.cpu_seconds)
     print(json.dumps(result))
