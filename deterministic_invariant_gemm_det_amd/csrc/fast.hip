@@ -179,18 +179,21 @@ hipError_t launch_family(Op op, int family, const GemmArgs& a, hipStream_t strea
 // short reductions and dW run faster on the smaller register-staged tiles.
 int fast_auto_family(Op op, Dt dt, int64_t cols, int64_t red) {
   if (dt == DT_F32) return cols >= 1024 ? 0 : 1;
-  return (op != OP_DW && red >= 2048) ? 0 : 1;
+  (void)red;
+  return (op != OP_DW && cols >= 256) ? 0 : 1;
 }
 
 hipError_t launch_fast(Op op, Dt dt, const GemmArgs& a, int family, hipStream_t stream) {
   switch (dt) {
-    case DT_F32: return launch_family<F32>(op, family, a, stream);
+    case DT_F32: return launch_family<F32>(op, family == 1 ? 1 : 0, a, stream);
     case DT_BF16:
     case DT_F16:
-      // family 0: large tiles fed straight into LDS where the shape allows it;
-      // otherwise (and family 1) the register-staged kernel. Identical bits.
-      if (family == 0 && fast16_dl_ok(a)) return launch_fast16_dl(op, dt, a, stream);
-      return launch_fast16(op, dt, a, family, stream);
+      // family 0: eight-wave large tiles where the shape allows it (10 + s:
+      // a given tile shape s of that kernel); otherwise, and family 1, the
+      // four-wave register-staged kernel. Identical bits.
+      if (family == 0 && fast16_w_ok(a)) return launch_fast16_w(op, dt, a, fast16_w_shape(a.cols), stream);
+      if (family >= 10 && fast16_w_ok(a)) return launch_fast16_w(op, dt, a, family - 10, stream);
+      return launch_fast16(op, dt, a, family == 1 ? 1 : 0, stream);
   }
   return hipErrorInvalidValue;
 }

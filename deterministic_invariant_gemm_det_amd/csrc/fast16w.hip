@@ -1,0 +1,477 @@
+// Fast tier, 16-bit inputs: eight waves per workgroup, two per SIMD.
+//
+// Same arithmetic as fast16.hip, hence the same bits for every
+// output element: acc = 0, then acc = V_MFMA_F32_32X32X16_{BF16,F16}(acc,
+// A[row, 16s .. 16s+15], B[16s .. 16s+15, col]) for s = 0, 1, ... in order,
+// then acc + bias rounded once (sgemm-bi 0.1.2 PyPI page, "Determinism
+// contracts"). Only the grouping of outputs into workgroups and the way the
+// operands reach the matrix cores differ.
+//
+// Workgroup: 512 threads = 8 waves in a WR x WC grid over a BM x BN output
+// tile; a wave owns (BM / WR) x (BN / WC) outputs as NI x NJ blocks of 32 x 32.
+// Two waves share each SIMD, so one wave's matrix-core work covers the other's
+// waits. The reduction is walked in stages of 64 indices through two LDS
+// slots: while stage s is multiplied out of one slot, stage s + 1 is written
+// into the other.
+//
+// LDS layout of an operand slot (the same for both source orientations): row
+// x holds the stage's 64 reduction indices of output row (A) or column (B) x,
+// as eight 16-byte pieces. Rows are paired: pair y = x / 2 occupies 256 bytes
+// (all 64 banks once), and piece p of row x sits in 16-byte slot
+// (8 (x mod 2) + p) XOR h(y) of the pair, with
+// h(y) = ((y XOR y / 8) mod 8) + 8 ((y / 4) mod 2). A fragment read (lanes
+// 0..31 rows xb..xb+31 at one piece, lanes 32..63 the next piece) then touches
+// 16 distinct slots in every group of 16 lanes, and so does the transposing
+// write below; both are conflict-free.
+//
+// Filling a slot:
+//   * reduction-contiguous source (A of fwd and dX, B of dX): buffer loads that
+//     write LDS directly, 1 KB (four row pairs) per wave instruction; lane l
+//     fetches the 16-byte source piece that belongs at byte 16 l.
+//   * reduction-major source (the forward weight, both operands of dW): a
+//     thread loads an 8 x 8 block (8 reduction indices x 8 consecutive
+//     columns, eight 16-byte loads) into registers, transposes it with
+//     V_PERM_B32 and writes eight 16-byte pieces, one per column. All fragment
+//     reads are then plain 16-byte LDS reads.
+//
+// Applicability (checked on the host): the reduction length is a multiple of
+// 64; operands are 16-byte aligned with 16-byte aligned rows; every byte
+// offset fits in 31 bits. Pieces past the end of an operand read as zeros
+// (buffer range check); rows or columns past the output's edge only reach
+// outputs that are never stored.
+
+#include <type_traits>
+
+#include "common.hpp"
+
+namespace detgemm {
+namespace w8 {
+
+constexpr int THREADS = 512;
+constexpr int BK = 64;
+
+typedef float v16f __attribute__((ext_vector_type(16)));
+typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
+typedef _Float16 v8h __attribute__((ext_vector_type(8)));
+typedef uint32_t v4u __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void lds_void;
+
+template <typename E> __device__ inline v16f mfma_step(v4u a, v4u b, v16f c);
+template <> __device__ inline v16f mfma_step<BF16>(v4u a, v4u b, v16f c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(v8bf, a), __builtin_bit_cast(v8bf, b), c, 0, 0, 0);
+}
+template <> __device__ inline v16f mfma_step<F16>(v4u a, v4u b, v16f c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(v8h, a), __builtin_bit_cast(v8h, b), c, 0, 0, 0);
+}
+
+// s_waitcnt immediate (gfx9 encoding): at most `vm` vector-memory operations
+// outstanding, no LDS operation outstanding, exports unconstrained.
+constexpr int waitcnt_vm_lgkm0(int vm) { return (vm & 15) | (7 << 4) | (0 << 8) | (((vm >> 4) & 3) << 14); }
+
+// Slot swizzle of row pair y (4 bits).
+__host__ __device__ constexpr int pair_swizzle(int y) { return ((y ^ (y >> 3)) & 7) | (((y >> 2) & 1) << 3); }
+// Byte offset of 16-byte piece p (0..7) of row x within an operand slot.
+__host__ __device__ constexpr uint32_t piece_offset(int x, int p) {
+  return static_cast<uint32_t>((x >> 1) * 256 + 16 * (((x & 1) * 8 + p) ^ pair_swizzle(x >> 1)));
+}
+
+__device__ inline v4u buffer_rsrc(const void* src, int64_t bytes) {
+  // base address, stride 0, size in bytes (reads past it return zeros), 32-bit data format
+  const uint64_t base = reinterpret_cast<uint64_t>(src);
+  return v4u{static_cast<uint32_t>(base), static_cast<uint32_t>(base >> 32) & 0xffffu,
+             static_cast<uint32_t>(bytes), 0x00020000u};
+}
+
+// Reduction-contiguous operand: element (x, l) at src[x * ld + l]; X rows per tile.
+template <int X>
+struct RcOperand {
+  static constexpr int NQ = X / 64;   // 1 KB wave instructions per wave per stage (X * 128 B / 8 waves)
+  static constexpr int LOADS = NQ;    // vector-memory instructions per stage per wave
+  static_assert(X % 64 == 0, "tile extent must be a multiple of 64");
+  v4u rsrc;
+  uint32_t voff[NQ];   // per-lane source byte offset of instruction q, tile origin 0, stage 0
+  uint32_t ld2;        // bytes per source row
+
+  __device__ inline void init(const void* src, int64_t ld, int64_t bytes) {
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    rsrc = buffer_rsrc(src, bytes);
+    ld2 = static_cast<uint32_t>(ld * 2);
+#pragma unroll
+    for (int q = 0; q < NQ; ++q) {
+      const int y = 4 * (wave * NQ + q) + (lane >> 4);      // row pair written by this lane
+      const int v = (lane & 15) ^ pair_swizzle(y);           // (8 (x mod 2) + p) of the slot's piece
+      const int x = 2 * y + (v >> 3), p = v & 7;
+      voff[q] = static_cast<uint32_t>((x * ld + 8 * p) * 2);
+    }
+  }
+  // Request stage st of the tile whose first row is x0 into the operand slot
+  // at `dst`. The loads are inline assembly so that the compiler does not
+  // treat them as LDS writes and drain them before unrelated LDS reads;
+  // completion is awaited explicitly (vmcnt) before the barrier that publishes
+  // the stage. M0 holds the LDS address of the instruction's 1 KB block; the
+  // whole byte offset travels in the VGPR operand, so the buffer range check
+  // covers every piece.
+  __device__ inline void issue(char* dst, int64_t x0, int st) const {
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const uint32_t lds = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_void*)dst));
+    const uint32_t soff = static_cast<uint32_t>(x0) * ld2 + static_cast<uint32_t>(st) * (BK * 2);
+#pragma unroll
+    for (int q = 0; q < NQ; ++q) {
+      const uint32_t m0 = lds + 1024u * static_cast<uint32_t>(wave * NQ + q);
+      const uint32_t off = voff[q] + soff;
+      __asm__ volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+                       :
+                       : "s"(m0), "v"(off), "s"(rsrc)
+                       : "memory", "m0");
+    }
+  }
+};
+
+// Reduction-major operand: element (x, l) at src[l * ld + x]; X columns per tile.
+// Thread t < X owns the 8 x 8 block (reduction rows 8 kb .. 8 kb + 7, columns
+// 8 xb .. 8 xb + 7) with kb = t / (X / 8), xb = t mod (X / 8).
+template <int X>
+struct KmOperand {
+  static constexpr int NX = X / 8;
+  static_assert(X % 64 == 0, "tile extent must be a multiple of 64");
+  __amdgpu_buffer_rsrc_t rsrc;
+  uint32_t voff;    // byte offset of the thread's block, tile origin 0, stage 0
+  uint32_t rstep;   // bytes between reduction rows
+  uint32_t sstep;   // bytes between stages
+  uint32_t dst;     // the thread's block coordinates, kb | xb << 8
+  v4u v[8];
+
+  __device__ inline bool active() const { return static_cast<int>(threadIdx.x) < X; }
+
+  __device__ inline void init(const void* src, int64_t ld, int64_t bytes) {
+    const int t = threadIdx.x;
+    const int kb = t / NX, xb = t % NX;
+    rsrc = __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(src), 0, static_cast<int>(bytes), 0x00020000);
+    voff = static_cast<uint32_t>((8 * kb * ld + 8 * xb) * 2);
+    rstep = static_cast<uint32_t>(ld * 2);
+    sstep = static_cast<uint32_t>(BK * ld * 2);
+    dst = static_cast<uint32_t>(kb | (xb << 8));
+  }
+  // Load stage st of the tile whose first column is x0 into registers. The
+  // whole byte offset goes into the VGPR operand, so the range check covers it.
+  __device__ inline void load(int64_t x0, int st) {
+    const uint32_t off = voff + static_cast<uint32_t>(x0) * 2u + static_cast<uint32_t>(st) * sstep;
+#pragma unroll
+    for (int r = 0; r < 8; ++r)
+      v[r] = __builtin_amdgcn_raw_buffer_load_b128(rsrc, off + static_cast<uint32_t>(r) * rstep, 0, 0);
+  }
+  // Column c of the block: its 8 reduction values packed two per dword.
+  __device__ inline void store(char* slot) const {
+    const int kb = dst & 0xff, xb = dst >> 8;
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+      const uint32_t sel = (c & 1) ? 0x07060302u : 0x05040100u;
+      v4u col;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) col[j] = __builtin_amdgcn_perm(v[2 * j + 1][c >> 1], v[2 * j][c >> 1], sel);
+      *reinterpret_cast<v4u*>(slot + piece_offset(8 * xb + c, kb)) = col;
+    }
+  }
+};
+
+template <int X, bool RC> struct OperandOf;
+template <int X> struct OperandOf<X, true> { using type = RcOperand<X>; };
+template <int X> struct OperandOf<X, false> { using type = KmOperand<X>; };
+
+// The lane's fragment of the 32-row block at xb for reduction step ks of a
+// stage: row xb + lane % 32, piece 2 ks + lane / 32 (elements 16 ks + 8 (lane / 32) + j).
+__device__ inline v4u frag(const char* slot, int xb, int ks) {
+  const int lane = threadIdx.x & 63;
+  return *reinterpret_cast<const v4u*>(slot + piece_offset(xb + (lane & 31), 2 * ks + (lane >> 5)));
+}
+
+// Output tile t -> (first row, first column). Workgroups are dealt to the
+// eight XCDs round-robin, so tile numbers are renumbered to make the tiles
+// that run at the same time on one XCD consecutive; consecutive tiles then
+// walk G row tiles before the next column tile, so that those tiles share A
+// rows and B columns in the XCD's L2.
+template <int BM, int BN>
+__device__ inline void tile_origin(const GemmArgs& a, uint32_t t, int64_t& row0, int64_t& col0) {
+  const uint32_t ntr = static_cast<uint32_t>((a.rows + BM - 1) / BM);
+  const uint32_t ntc = static_cast<uint32_t>((a.cols + BN - 1) / BN);
+  const uint32_t ntiles = ntr * ntc;
+  if (ntiles % 8 == 0) t = (t % 8) * (ntiles / 8) + t / 8;
+  constexpr uint32_t G = 4;
+  const uint32_t grp = t / (G * ntc), first = grp * G;
+  const uint32_t gsz = ntr - first < G ? ntr - first : G;
+  const uint32_t within = t - grp * G * ntc;
+  row0 = static_cast<int64_t>(first + within % gsz) * BM;
+  col0 = static_cast<int64_t>(within / gsz) * BN;
+}
+
+// One output tile per workgroup.
+//
+// Matrix-core operand order: each 32 x 32 block is computed transposed,
+// acc = MFMA(B fragment, A fragment, acc), so that a lane holds one output
+// row and four consecutive output columns per group of four accumulators.
+// Each output element still receives the same 16 products per instruction,
+// in the same instruction order.
+//
+// Reduction steps (16 indices each, four per stage) run in one sequence; the
+// fragments of step t + 2 are read from LDS while step t's MFMAs run (four
+// fragment buffers, step t in buffer t mod 4). Stage g + 1 must therefore be
+// visible before step 4 g + 2 reads it: between steps 4 g + 1 and 4 g + 2 each
+// wave writes its register-staged part of the last requested stage, waits for
+// its own loads of stage g + 1, and meets the others at a barrier. After the
+// barrier every wave has read all of stage g (steps 4 g + 2 and 4 g + 3 are
+// already in registers), so stage g + NS is requested into its slot.
+//
+// Epilogue: acc + bias, one rounding, written through LDS (the stage slots are
+// free by then) as a row-major tile, then copied out with 16-byte stores
+// along whole tile rows.
+template <typename E, bool A_RC, bool B_RC, int BM, int BN, int WR, int WC, int NS>
+__global__ void __launch_bounds__(THREADS, 1) fast16w_kernel(GemmArgs args) {
+  using T = typename E::T;
+  constexpr int WM = BM / WR, WN = BN / WC, NI = WM / 32, NJ = WN / 32;
+  static_assert(WR * WC == 8 && NI * 32 == WM && NJ * 32 == WN, "bad wave grid");
+  constexpr int KS = BK / 16;
+  static_assert(KS == 4, "four reduction steps per stage");
+  constexpr int A_BYTES = BM * BK * 2, B_BYTES = BN * BK * 2, SLOT = A_BYTES + B_BYTES;
+  constexpr int BIAS_BYTES = BN * 2;
+  constexpr int RS = BN * 2 + 16;   // LDS row stride of the output tile (bytes)
+  static_assert(BIAS_BYTES <= 1024, "bias slice must fit one wave instruction");
+  static_assert(BM * RS <= NS * SLOT, "output tile must fit the stage slots");
+  static_assert(NS >= 2 && NS * SLOT + BIAS_BYTES <= 160 * 1024, "LDS");
+  // direct-to-LDS loads per wave per stage (the ones vmcnt must account for)
+  constexpr int DL = (A_RC ? RcOperand<BM>::LOADS : 0) + (B_RC ? RcOperand<BN>::LOADS : 0);
+  static_assert((NS - 2) * DL <= 63, "vmcnt range");
+  constexpr bool KM = !A_RC || !B_RC;
+  __shared__ __attribute__((aligned(1024))) char lds[NS * SLOT + BIAS_BYTES];
+  char* const bias_lds = lds + NS * SLOT;
+
+  int64_t row0, col0;
+  tile_origin<BM, BN>(args, blockIdx.x, row0, col0);
+  const int nst = static_cast<int>(args.red / BK);
+
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  const int wm = (wave / WC) * WM;
+  const int wn = (wave % WC) * WN;
+
+  typename OperandOf<BM, A_RC>::type oa;
+  typename OperandOf<BN, B_RC>::type ob;
+  oa.init(args.A, args.lda, args.a_bytes);
+  ob.init(args.B, args.ldb, args.b_bytes);
+  const bool has_bias = args.bias != nullptr;
+
+  // Everything stage st needs from global memory: the register-staged
+  // operand first, then the direct-to-LDS ones (so that waiting for the
+  // latter covers the former).
+  auto request = [&](int st) {
+    if constexpr (!A_RC) { if (oa.active()) oa.load(row0, st); }
+    if constexpr (!B_RC) { if (ob.active()) ob.load(col0, st); }
+    char* sl = lds + (st % NS) * SLOT;
+    if constexpr (A_RC) oa.issue(sl, row0, st);
+    if constexpr (B_RC) ob.issue(sl + A_BYTES, col0, st);
+  };
+  auto write_km = [&](int st) {
+    char* sl = lds + (st % NS) * SLOT;
+    if constexpr (!A_RC) { if (oa.active()) oa.store(sl); }
+    if constexpr (!B_RC) { if (ob.active()) ob.store(sl + A_BYTES); }
+  };
+  auto read_step = [&](v4u (&af)[NI], v4u (&bf)[NJ], int st, int ks) {
+    const char* As = lds + (st % NS) * SLOT;
+    const char* Bs = As + A_BYTES;
+#pragma unroll
+    for (int i = 0; i < NI; ++i) af[i] = frag(As, wm + 32 * i, ks);
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) bf[j] = frag(Bs, wn + 32 * j, ks);
+  };
+
+  // Prologue: the bias slice and stages 0 .. NS - 1 requested, the
+  // register-staged parts written, stage 0 published.
+  if (has_bias && wave == 0 && lane < BIAS_BYTES / 16) {
+    const v4u brsrc = buffer_rsrc(args.bias, args.cols * 2);
+    const uint32_t dst = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_void*)bias_lds));
+    const uint32_t off = static_cast<uint32_t>(col0) * 2u + 16u * static_cast<uint32_t>(lane);
+    __asm__ volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+                     :
+                     : "s"(dst), "v"(off), "s"(brsrc)
+                     : "memory", "m0");
+  }
+  int requested = 0;   // stages requested so far
+  int pending = -1;    // stage whose register-staged part is still in registers
+  for (; requested < NS && requested < nst; ++requested) {
+    request(requested);
+    if constexpr (KM) {
+      __builtin_amdgcn_s_waitcnt(0);
+      __asm__ volatile("" ::: "memory");
+      write_km(requested);
+    }
+  }
+  __builtin_amdgcn_s_waitcnt(0);
+  __asm__ volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  __asm__ volatile("" ::: "memory");
+
+  v16f acc[NI][NJ];
+#pragma unroll
+  for (int i = 0; i < NI; ++i)
+#pragma unroll
+    for (int j = 0; j < NJ; ++j)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
+  v4u af[4][NI], bf[4][NJ];
+  read_step(af[0], bf[0], 0, 0);
+  read_step(af[1], bf[1], 0, 1);
+
+  // One stage of the sequence. The last stage is a separate copy (LAST), so
+  // that the loop body has no branch around the barrier and the next stage's
+  // fragment reads: the compiler's LDS wait counts then stay exact.
+  auto stage = [&](int g, auto last_tag) {
+    constexpr bool LAST = decltype(last_tag)::value;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      if (ks == 2 && !LAST) {
+        if constexpr (KM) {
+          if (pending >= 0) {
+            // outstanding after the register-staged loads: that stage's direct loads
+            __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(DL));
+            __asm__ volatile("" ::: "memory");
+            write_km(pending);
+            pending = -1;
+          }
+        }
+        // stage g + 1 landed: issued after its loads are the direct loads of
+        // stages g + 2 .. g + NS - 1
+        __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0((NS - 2) * DL));
+        __asm__ volatile("" ::: "memory");
+        __builtin_amdgcn_s_barrier();
+        __asm__ volatile("" ::: "memory");
+        if (requested < nst) {
+          request(requested);
+          if constexpr (KM) pending = requested;
+          ++requested;
+        }
+      }
+      // fragments of step 4 g + ks + 2
+      if (ks < 2) read_step(af[(ks + 2) & 3], bf[(ks + 2) & 3], g, ks + 2);
+      else if (!LAST) read_step(af[(ks + 2) & 3], bf[(ks + 2) & 3], g + 1, ks - 2);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int i = 0; i < NI; ++i)
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) acc[i][j] = mfma_step<E>(bf[ks][j], af[ks][i], acc[i][j]);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+  for (int g = 0; g + 1 < nst; ++g) stage(g, std::false_type{});
+  stage(nst - 1, std::true_type{});
+
+  // Epilogue. Every wave is done with the stage slots after this barrier.
+  __builtin_amdgcn_s_waitcnt(0);
+  __asm__ volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  __asm__ volatile("" ::: "memory");
+  const int lr = lane & 31, lh = lane >> 5;
+#pragma unroll
+  for (int j = 0; j < NJ; ++j) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      // the lane's 4 columns: wn + 32 j + 8 q + 4 (lane / 32) + e of the tile
+      const int cl = wn + 32 * j + 8 * q + 4 * lh;
+      float b[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+      if (has_bias) {
+        const uint2 raw = *reinterpret_cast<const uint2*>(bias_lds + 2 * cl);
+        const T* bt = reinterpret_cast<const T*>(&raw);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) b[e] = E::to_f32(bt[e]);
+      }
+#pragma unroll
+      for (int i = 0; i < NI; ++i) {
+        uint16_t v[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          float r = acc[i][j][4 * q + e];
+          if (has_bias) r = r + b[e];
+          v[e] = __builtin_bit_cast(uint16_t, round_from_f32<E>(r));
+        }
+        uint2 w;
+        w.x = static_cast<uint32_t>(v[0]) | (static_cast<uint32_t>(v[1]) << 16);
+        w.y = static_cast<uint32_t>(v[2]) | (static_cast<uint32_t>(v[3]) << 16);
+        *reinterpret_cast<uint2*>(lds + (wm + 32 * i + lr) * RS + 2 * cl) = w;
+      }
+    }
+  }
+  __builtin_amdgcn_s_waitcnt(0);
+  __asm__ volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  __asm__ volatile("" ::: "memory");
+  // copy-out: 16-byte chunk u of the tile is row u / (BN / 8), columns 8 (u mod (BN / 8)) ..
+  constexpr int CPR = BN / 8;
+  T* __restrict__ Y = static_cast<T*>(args.out);
+  const bool wide = (args.cols % 8) == 0 && (reinterpret_cast<uintptr_t>(args.out) % 16) == 0;
+#pragma unroll 4
+  for (int u = threadIdx.x; u < BM * CPR; u += THREADS) {
+    const int r = u / CPR, c = u - r * CPR;
+    const int64_t row = row0 + r, col = col0 + 8 * c;
+    if (row >= args.rows || col >= args.cols) continue;
+    const v4u val = *reinterpret_cast<const v4u*>(lds + r * RS + 16 * c);
+    T* y = Y + row * args.cols + col;
+    if (wide && col + 8 <= args.cols) {
+      *reinterpret_cast<v4u*>(y) = val;
+    } else {
+      const T* vt = reinterpret_cast<const T*>(&val);
+      for (int e = 0; e < 8 && col + e < args.cols; ++e) y[e] = vt[e];
+    }
+  }
+}
+
+template <typename E, bool AC, bool BC, int BM, int BN, int WR, int WC, int NS>
+hipError_t launch_typed(const GemmArgs& a, hipStream_t stream) {
+  const int64_t tiles = ((a.cols + BN - 1) / BN) * ((a.rows + BM - 1) / BM);
+  // one tile per workgroup: a workgroup's stores then overlap the start of
+  // the next workgroup on its compute unit
+  const int64_t grid = tiles;
+  // the kernel counts tiles and (tile, stage) pairs in 32 bits
+  if (tiles > 0x7fffffff || ((tiles + grid - 1) / grid) * (a.red / BK) > 0x7fffffff) return hipErrorInvalidConfiguration;
+  hipLaunchKernelGGL((fast16w_kernel<E, AC, BC, BM, BN, WR, WC, NS>), dim3(static_cast<unsigned>(grid)), dim3(THREADS),
+                     0, stream, a);
+  return hipGetLastError();
+}
+
+// Tile shape from the output's column count only (never from the row count,
+// which for fwd and dX is the batch): 256 x 192 for wide outputs, 128 x 192
+// for narrow ones, so that an 8192-row batch gives whole rounds of tiles on
+// 256 compute units in both cases.
+template <typename E, bool AC, bool BC>
+hipError_t launch_shape(const GemmArgs& a, int shape, hipStream_t stream) {
+  switch (shape) {
+    case 0: return launch_typed<E, AC, BC, 256, 192, 4, 2, 2>(a, stream);
+    case 1: return launch_typed<E, AC, BC, 128, 192, 4, 2, 2>(a, stream);
+    default: return launch_typed<E, AC, BC, 256, 128, 4, 2, 2>(a, stream);
+  }
+}
+
+template <typename E>
+hipError_t launch_op(Op op, const GemmArgs& a, int shape, hipStream_t stream) {
+  switch (op) {
+    case OP_FWD: return launch_shape<E, true, false>(a, shape, stream);   // X[i][k], W[k][j]
+    case OP_DX:  return launch_shape<E, true, true>(a, shape, stream);    // dY[i][n], W[q][n]
+    case OP_DW:  return launch_shape<E, false, false>(a, shape, stream);  // X[i][q], dY[i][j]
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace w8
+
+bool fast16_w_ok(const GemmArgs& a) {
+  return a.red % w8::BK == 0 && a.vec_a && a.vec_b && a.off32_a && a.off32_b &&
+         reinterpret_cast<uintptr_t>(a.bias) % 16 == 0;
+}
+
+int fast16_w_shape(int64_t cols) { return cols >= 1536 ? 0 : 1; }
+
+hipError_t launch_fast16_w(Op op, Dt dt, const GemmArgs& a, int shape, hipStream_t stream) {
+  if (dt == DT_BF16) return w8::launch_op<BF16>(op, a, shape, stream);
+  if (dt == DT_F16) return w8::launch_op<F16>(op, a, shape, stream);
+  return hipErrorInvalidValue;
+}
+
+}  // namespace detgemm

@@ -113,9 +113,11 @@ int det_gemm_version(void);
 
 /*
  * Test hook: force the fast tier's tile family for later calls from any thread
- * (-1 automatic, 0 = the large family, 1 = the small family). Both families
- * produce identical bits, so this changes speed only. Returns DET_EINVAL for
- * other values.
+ * (-1 automatic, 0 = the large family, 1 = the small family, 10 + s = tile
+ * shape s of the large family's eight-wave kernel: 10 = 256 x 192,
+ * 11 = 128 x 192, 12 = 256 x 128, used where that kernel applies). All
+ * families produce identical bits, so this changes speed only. Returns
+ * DET_EINVAL for other values.
  */
 det_status_t det_gemm_debug_force_family(int family);
 
