@@ -7,6 +7,9 @@
 #include <atomic>
 #include <cstdio>
 #include <cstring>
+#include <map>
+#include <mutex>
+#include <utility>
 
 #include "common.hpp"
 
@@ -76,6 +79,9 @@ det_status_t run(detgemm::Op op, void* out, const void* A, const void* B, const 
   a.bias = bias;
   a.out = out;
   a.num_cu = cus;
+  a.partial = nullptr;
+  a.split = 1;
+  a.chunk_stages = 0;
   switch (op) {
     case detgemm::OP_FWD: a.rows = m; a.cols = n; a.red = k; a.lda = k; a.ldb = n; break;
     case detgemm::OP_DX:  a.rows = m; a.cols = k; a.red = n; a.lda = n; a.ldb = n; break;
@@ -106,6 +112,42 @@ det_status_t run(detgemm::Op op, void* out, const void* A, const void* B, const 
 }
 
 }  // namespace
+
+namespace detgemm {
+
+// Per (device, stream) workspace. Calls on one stream are ordered by the
+// stream, so they may share it; calls on different streams get different
+// ones. Growing waits for the stream's earlier work before freeing the old
+// allocation.
+hipError_t stream_workspace(hipStream_t stream, size_t bytes, void** ptr) {
+  static std::mutex mu;
+  static std::map<std::pair<int, hipStream_t>, std::pair<void*, size_t>> cache;
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  std::lock_guard<std::mutex> lock(mu);
+  auto& slot = cache[{dev, stream}];
+  if (slot.second >= bytes) {
+    *ptr = slot.first;
+    return hipSuccess;
+  }
+  if (slot.first) {
+    e = hipStreamSynchronize(stream);
+    if (e != hipSuccess) return e;
+    (void)hipFree(slot.first);
+    slot = {nullptr, 0};
+  }
+  const size_t grain = size_t(1) << 24;
+  const size_t want = (bytes + grain - 1) / grain * grain;
+  void* p = nullptr;
+  e = hipMalloc(&p, want);
+  if (e != hipSuccess) return e;
+  slot = {p, want};
+  *ptr = p;
+  return hipSuccess;
+}
+
+}  // namespace detgemm
 
 extern "C" {
 
@@ -144,8 +186,8 @@ const char* det_gemm_last_error(void) { return g_last_error; }
 int det_gemm_version(void) { return 100; }
 
 det_status_t det_gemm_debug_force_family(int family) {
-  if (family < -1 || (family > 1 && family < 10) || family > 12)
-    return fail(DET_EINVAL, "det_gemm: family must be -1, 0, 1 or 10 .. 12%s");
+  if (family < -1 || (family > 1 && family < 10) || family > 13)
+    return fail(DET_EINVAL, "det_gemm: family must be -1, 0, 1 or 10 .. 13%s");
   g_force_family.store(family, std::memory_order_relaxed);
   return DET_OK;
 }

@@ -23,6 +23,12 @@ struct GemmArgs {
   bool off32_a, off32_b; // every element offset of the operand fits in 32 bits
   int64_t a_bytes, b_bytes; // size of each operand in bytes
   int num_cu;        // compute units of the device (launch-shape choice only)
+  // Fast tier, dW of 16-bit inputs: the reduction is split into `split` chunks
+  // of `chunk_stages` stages of 64; chunk c writes its f32 partial outputs to
+  // partial + c * rows * cols (row-major). partial == nullptr: no split.
+  float* partial;
+  int split;
+  int chunk_stages;
 };
 
 enum Dt { DT_F32 = 0, DT_BF16 = 1, DT_F16 = 2 };
@@ -91,5 +97,14 @@ bool fast16_w_ok(const GemmArgs& a);
 int fast16_w_shape(int64_t cols);
 hipError_t launch_fast16_w(Op op, Dt dt, const GemmArgs& a, int shape, hipStream_t stream);
 int fast_auto_family(Op op, Dt dt, int64_t cols, int64_t red);
+
+// Split of the fast tier's dW reduction (16-bit inputs), from the shape only:
+// returns the chunk count S >= 1 and sets *chunk_stages.
+int fast_dw_split(int64_t m, int64_t k, int64_t n, int* chunk_stages);
+// out[i] = round(((P_0[i] + P_1[i]) + ...) + P_{S-1}[i]) over `count` elements, P_c = partial + c * count.
+hipError_t launch_combine(Dt dt, const float* partial, int split, int64_t count, void* out, hipStream_t stream);
+// A device workspace of at least `bytes` owned by the library for (current device, stream);
+// grown on demand, kept for later calls on the same stream.
+hipError_t stream_workspace(hipStream_t stream, size_t bytes, void** ptr);
 
 }  // namespace detgemm

@@ -180,10 +180,46 @@ hipError_t launch_family(Op op, int family, const GemmArgs& a, hipStream_t strea
 int fast_auto_family(Op op, Dt dt, int64_t cols, int64_t red) {
   if (dt == DT_F32) return cols >= 1024 ? 0 : 1;
   (void)red;
-  return (op != OP_DW && cols >= 256) ? 0 : 1;
+  return (op == OP_DW || cols >= 256) ? 0 : 1;
+}
+
+// dW of 16-bit inputs has few output tiles when K x N is small, so its
+// reduction over M is split into S chunks of whole 64-row stages, each
+// accumulated from 0 in f32 and combined in ascending chunk order. S follows
+// from the shape alone -- a reference tiling of 256 x 192 outputs and a
+// notional 256 compute units, never the device -- so every kernel and every
+// device gives the same bits; chunks are at least 8 stages long.
+int fast_dw_split(int64_t m, int64_t k, int64_t n, int* chunk_stages) {
+  const int64_t nst = (m + 63) / 64;
+  const int64_t tiles = ((k + 255) / 256) * ((n + 191) / 192);
+  int64_t s = tiles < 128 ? 256 / tiles : 1;
+  if (s > 8) s = 8;
+  if (s > nst / 8) s = nst / 8;
+  if (s < 1) s = 1;
+  const int64_t c = (nst + s - 1) / s;
+  *chunk_stages = static_cast<int>(c);
+  return static_cast<int>((nst + c - 1) / c);
 }
 
 hipError_t launch_fast(Op op, Dt dt, const GemmArgs& a, int family, hipStream_t stream) {
+  if (op == OP_DW && dt != DT_F32 && a.partial == nullptr) {
+    int chunk = 0;
+    const int split = fast_dw_split(a.red, a.rows, a.cols, &chunk);
+    if (split > 1) {
+      // chunk partials into the stream's workspace, then the ordered combine
+      void* ws = nullptr;
+      const size_t count = static_cast<size_t>(a.rows) * static_cast<size_t>(a.cols);
+      hipError_t e = stream_workspace(stream, count * sizeof(float) * static_cast<size_t>(split), &ws);
+      if (e != hipSuccess) return e;
+      GemmArgs p = a;
+      p.partial = static_cast<float*>(ws);
+      p.split = split;
+      p.chunk_stages = chunk;
+      e = launch_fast(op, dt, p, family, stream);
+      if (e != hipSuccess) return e;
+      return launch_combine(dt, p.partial, split, static_cast<int64_t>(count), a.out, stream);
+    }
+  }
   switch (dt) {
     case DT_F32: return launch_family<F32>(op, family == 1 ? 1 : 0, a, stream);
     case DT_BF16:
@@ -191,7 +227,8 @@ hipError_t launch_fast(Op op, Dt dt, const GemmArgs& a, int family, hipStream_t 
       // family 0: eight-wave large tiles where the shape allows it (10 + s:
       // a given tile shape s of that kernel); otherwise, and family 1, the
       // four-wave register-staged kernel. Identical bits.
-      if (family == 0 && fast16_w_ok(a)) return launch_fast16_w(op, dt, a, fast16_w_shape(a.cols), stream);
+      if (family == 0 && fast16_w_ok(a))
+        return launch_fast16_w(op, dt, a, op == OP_DW ? 0 : fast16_w_shape(a.cols), stream);
       if (family >= 10 && fast16_w_ok(a)) return launch_fast16_w(op, dt, a, family - 10, stream);
       return launch_fast16(op, dt, a, family == 1 ? 1 : 0, stream);
   }

@@ -167,8 +167,16 @@ __global__ void __launch_bounds__(THREADS, 2) fast16_kernel(GemmArgs args) {
   const T* __restrict__ A = static_cast<const T*>(args.A);
   const T* __restrict__ B = static_cast<const T*>(args.B);
   const int64_t tiles_n = (args.cols + BN - 1) / BN;
-  const int64_t row0 = (static_cast<int64_t>(blockIdx.x) / tiles_n) * BM;
-  const int64_t col0 = (static_cast<int64_t>(blockIdx.x) % tiles_n) * BN;
+  const int64_t ntiles = tiles_n * ((args.rows + BM - 1) / BM);
+  // for a split reduction, block b is tile b mod ntiles of chunk b / ntiles
+  int64_t tb = blockIdx.x;
+  int chunk = 0;
+  if (args.partial) {
+    chunk = static_cast<int>(tb / ntiles);
+    tb -= chunk * ntiles;
+  }
+  const int64_t row0 = (tb / tiles_n) * BM;
+  const int64_t col0 = (tb % tiles_n) * BN;
   const int wave = threadIdx.x >> 6;
   const int lane = threadIdx.x & 63;
   const int wm = (wave >> 1) * WM;
@@ -193,13 +201,17 @@ __global__ void __launch_bounds__(THREADS, 2) fast16_kernel(GemmArgs args) {
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
 
-  const int nst = static_cast<int>((args.red + BK - 1) / BK);
+  // stages s0 .. nst - 1 (all of them, or one chunk of a split reduction)
+  const int nst_all = static_cast<int>((args.red + BK - 1) / BK);
+  const int s0 = args.partial ? chunk * args.chunk_stages : 0;
+  const int nst = args.partial ? (nst_all - s0 < args.chunk_stages ? nst_all : s0 + args.chunk_stages) : nst_all;
   {
-    const bool kfull = BK <= args.red;
-    if (fast_a && kfull) sa.load_fast(0); else sa.load_edge(A, args.lda, row0, args.rows, 0, args.red);
-    if (fast_b && kfull) sb.load_fast(0); else sb.load_edge(B, args.ldb, col0, args.cols, 0, args.red);
+    const int64_t l0 = static_cast<int64_t>(s0) * BK;
+    const bool kfull = l0 + BK <= args.red;
+    if (fast_a && kfull) sa.load_fast(s0); else sa.load_edge(A, args.lda, row0, args.rows, l0, args.red);
+    if (fast_b && kfull) sb.load_fast(s0); else sb.load_edge(B, args.ldb, col0, args.cols, l0, args.red);
   }
-  for (int st = 0; st < nst; ++st) {
+  for (int st = s0; st < nst; ++st) {
     sa.store(As);
     sb.store(Bs);
     __syncthreads();
@@ -224,9 +236,28 @@ __global__ void __launch_bounds__(THREADS, 2) fast16_kernel(GemmArgs args) {
     __syncthreads();
   }
 
+  const bool interior = rows_full && cols_full;
+  if (args.partial) {
+    // split reduction: this chunk's f32 partials (no bias in dW)
+    float* __restrict__ P = args.partial + static_cast<int64_t>(chunk) * args.rows * args.cols;
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) {
+      const int64_t col = col0 + wn + 32 * j + lx;
+      if (!interior && col >= args.cols) continue;
+#pragma unroll
+      for (int i = 0; i < NI; ++i) {
+        const int64_t rb = row0 + wm + 32 * i + 4 * (lane >> 5);
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const int rr = 8 * (e / 4) + (e % 4);
+          if (interior || rb + rr < args.rows) P[(rb + rr) * args.cols + col] = acc[i][j][e];
+        }
+      }
+    }
+    return;
+  }
   T* __restrict__ Y = static_cast<T*>(args.out);
   const T* __restrict__ bias = static_cast<const T*>(args.bias);
-  const bool interior = rows_full && cols_full;
 #pragma unroll
   for (int j = 0; j < NJ; ++j) {
     const int64_t col = col0 + wn + 32 * j + lx;
@@ -251,7 +282,7 @@ __global__ void __launch_bounds__(THREADS, 2) fast16_kernel(GemmArgs args) {
 
 template <typename E, int BM, int BN, bool AC, bool BC>
 hipError_t launch_typed(const GemmArgs& a, hipStream_t stream) {
-  const int64_t blocks = ((a.cols + BN - 1) / BN) * ((a.rows + BM - 1) / BM);
+  const int64_t blocks = ((a.cols + BN - 1) / BN) * ((a.rows + BM - 1) / BM) * (a.partial ? a.split : 1);
   if (blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
   hipLaunchKernelGGL((fast16_kernel<E, BM, BN, AC, BC>), dim3(static_cast<unsigned>(blocks)), dim3(THREADS), 0, stream, a);
   return hipGetLastError();

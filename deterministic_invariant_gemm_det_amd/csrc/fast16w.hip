@@ -47,7 +47,6 @@
 namespace detgemm {
 namespace w8 {
 
-constexpr int THREADS = 512;
 constexpr int BK = 64;
 
 typedef float v16f __attribute__((ext_vector_type(16)));
@@ -82,12 +81,13 @@ __device__ inline v4u buffer_rsrc(const void* src, int64_t bytes) {
              static_cast<uint32_t>(bytes), 0x00020000u};
 }
 
-// Reduction-contiguous operand: element (x, l) at src[x * ld + l]; X rows per tile.
-template <int X>
+// Reduction-contiguous operand: element (x, l) at src[x * ld + l]; X rows per
+// tile, WAVES waves per workgroup.
+template <int X, int WAVES>
 struct RcOperand {
-  static constexpr int NQ = X / 64;   // 1 KB wave instructions per wave per stage (X * 128 B / 8 waves)
+  static constexpr int NQ = X * 128 / 1024 / WAVES;   // 1 KB wave instructions per wave per stage
+  static_assert(NQ * 1024 * WAVES == X * 128, "tile extent must fill whole wave instructions");
   static constexpr int LOADS = NQ;    // vector-memory instructions per stage per wave
-  static_assert(X % 64 == 0, "tile extent must be a multiple of 64");
   v4u rsrc;
   uint32_t voff[NQ];   // per-lane source byte offset of instruction q, tile origin 0, stage 0
   uint32_t ld2;        // bytes per source row
@@ -128,27 +128,31 @@ struct RcOperand {
   }
 };
 
-// Reduction-major operand: element (x, l) at src[l * ld + x]; X columns per tile.
-// Thread t < X owns the 8 x 8 block (reduction rows 8 kb .. 8 kb + 7, columns
-// 8 xb .. 8 xb + 7) with kb = t / (X / 8), xb = t mod (X / 8).
-template <int X>
+// Reduction-major operand: element (x, l) at src[l * ld + x]; X columns per
+// tile. Thread t < (64 / KH) (X / 8) owns the KH x 8 block (reduction rows
+// KH kb .. KH kb + KH - 1, columns 8 xb .. 8 xb + 7) with kb = t / (X / 8),
+// xb = t mod (X / 8): KH 16-byte loads, a V_PERM_B32 transpose, and one
+// 2 KH-byte LDS write per column (a whole piece for KH = 8, half of one for
+// KH = 4).
+template <int X, int KH>
 struct KmOperand {
   static constexpr int NX = X / 8;
-  static_assert(X % 64 == 0, "tile extent must be a multiple of 64");
+  static constexpr int UNITS = (64 / KH) * NX;
+  static_assert(X % 64 == 0 && (KH == 4 || KH == 8), "tile extent / block height");
   __amdgpu_buffer_rsrc_t rsrc;
   uint32_t voff;    // byte offset of the thread's block, tile origin 0, stage 0
   uint32_t rstep;   // bytes between reduction rows
   uint32_t sstep;   // bytes between stages
   uint32_t dst;     // the thread's block coordinates, kb | xb << 8
-  v4u v[8];
+  v4u v[KH];
 
-  __device__ inline bool active() const { return static_cast<int>(threadIdx.x) < X; }
+  __device__ inline bool active() const { return static_cast<int>(threadIdx.x) < UNITS; }
 
   __device__ inline void init(const void* src, int64_t ld, int64_t bytes) {
     const int t = threadIdx.x;
     const int kb = t / NX, xb = t % NX;
     rsrc = __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(src), 0, static_cast<int>(bytes), 0x00020000);
-    voff = static_cast<uint32_t>((8 * kb * ld + 8 * xb) * 2);
+    voff = static_cast<uint32_t>((KH * kb * ld + 8 * xb) * 2);
     rstep = static_cast<uint32_t>(ld * 2);
     sstep = static_cast<uint32_t>(BK * ld * 2);
     dst = static_cast<uint32_t>(kb | (xb << 8));
@@ -158,26 +162,37 @@ struct KmOperand {
   __device__ inline void load(int64_t x0, int st) {
     const uint32_t off = voff + static_cast<uint32_t>(x0) * 2u + static_cast<uint32_t>(st) * sstep;
 #pragma unroll
-    for (int r = 0; r < 8; ++r)
+    for (int r = 0; r < KH; ++r)
       v[r] = __builtin_amdgcn_raw_buffer_load_b128(rsrc, off + static_cast<uint32_t>(r) * rstep, 0, 0);
   }
-  // Column c of the block: its 8 reduction values packed two per dword.
+  // Column c of the block: its KH reduction values packed two per dword.
   __device__ inline void store(char* slot) const {
     const int kb = dst & 0xff, xb = dst >> 8;
 #pragma unroll
     for (int c = 0; c < 8; ++c) {
       const uint32_t sel = (c & 1) ? 0x07060302u : 0x05040100u;
-      v4u col;
+      if constexpr (KH == 8) {
+        v4u col;
 #pragma unroll
-      for (int j = 0; j < 4; ++j) col[j] = __builtin_amdgcn_perm(v[2 * j + 1][c >> 1], v[2 * j][c >> 1], sel);
-      *reinterpret_cast<v4u*>(slot + piece_offset(8 * xb + c, kb)) = col;
+        for (int j = 0; j < 4; ++j) col[j] = __builtin_amdgcn_perm(v[2 * j + 1][c >> 1], v[2 * j][c >> 1], sel);
+        *reinterpret_cast<v4u*>(slot + piece_offset(8 * xb + c, kb)) = col;
+      } else {
+        uint2 col;
+        col.x = __builtin_amdgcn_perm(v[1][c >> 1], v[0][c >> 1], sel);
+        col.y = __builtin_amdgcn_perm(v[3][c >> 1], v[2][c >> 1], sel);
+        *reinterpret_cast<uint2*>(slot + piece_offset(8 * xb + c, kb >> 1) + 8 * (kb & 1)) = col;
+      }
     }
   }
 };
 
-template <int X, bool RC> struct OperandOf;
-template <int X> struct OperandOf<X, true> { using type = RcOperand<X>; };
-template <int X> struct OperandOf<X, false> { using type = KmOperand<X>; };
+// Block height of the register-staged operand: half blocks when there are
+// threads for them (fewer registers per thread, more threads sharing the work).
+template <int X, int WAVES> constexpr int km_height() { return (64 / 4) * (X / 8) <= 64 * WAVES ? 4 : 8; }
+
+template <int X, int WAVES, bool RC> struct OperandOf;
+template <int X, int WAVES> struct OperandOf<X, WAVES, true> { using type = RcOperand<X, WAVES>; };
+template <int X, int WAVES> struct OperandOf<X, WAVES, false> { using type = KmOperand<X, km_height<X, WAVES>()>; };
 
 // The lane's fragment of the 32-row block at xb for reduction step ks of a
 // stage: row xb + lane % 32, piece 2 ks + lane / 32 (elements 16 ks + 8 (lane / 32) + j).
@@ -226,36 +241,46 @@ __device__ inline void tile_origin(const GemmArgs& a, uint32_t t, int64_t& row0,
 // free by then) as a row-major tile, then copied out with 16-byte stores
 // along whole tile rows.
 template <typename E, bool A_RC, bool B_RC, int BM, int BN, int WR, int WC, int NS>
-__global__ void __launch_bounds__(THREADS, 1) fast16w_kernel(GemmArgs args) {
+__global__ void __launch_bounds__(64 * WR * WC, 8 / (WR * WC)) fast16w_kernel(GemmArgs args) {
   using T = typename E::T;
+  constexpr int WAVES = WR * WC, THREADS = 64 * WAVES;
   constexpr int WM = BM / WR, WN = BN / WC, NI = WM / 32, NJ = WN / 32;
-  static_assert(WR * WC == 8 && NI * 32 == WM && NJ * 32 == WN, "bad wave grid");
+  static_assert((WAVES == 8 || WAVES == 4) && NI * 32 == WM && NJ * 32 == WN, "bad wave grid");
+  static_assert(BM <= THREADS && BN <= THREADS, "register-staged blocks: at most one per thread");
   constexpr int KS = BK / 16;
   static_assert(KS == 4, "four reduction steps per stage");
   constexpr int A_BYTES = BM * BK * 2, B_BYTES = BN * BK * 2, SLOT = A_BYTES + B_BYTES;
-  constexpr int BIAS_BYTES = BN * 2;
   constexpr int RS = BN * 2 + 16;   // LDS row stride of the output tile (bytes)
-  static_assert(BIAS_BYTES <= 1024, "bias slice must fit one wave instruction");
   static_assert(BM * RS <= NS * SLOT, "output tile must fit the stage slots");
-  static_assert(NS >= 2 && NS * SLOT + BIAS_BYTES <= 160 * 1024, "LDS");
+  static_assert(NS >= 2 && NS * SLOT * (8 / WAVES) <= 160 * 1024, "LDS (8 waves per compute unit)");
   // direct-to-LDS loads per wave per stage (the ones vmcnt must account for)
-  constexpr int DL = (A_RC ? RcOperand<BM>::LOADS : 0) + (B_RC ? RcOperand<BN>::LOADS : 0);
+  constexpr int DL = (A_RC ? RcOperand<BM, WAVES>::LOADS : 0) + (B_RC ? RcOperand<BN, WAVES>::LOADS : 0);
   static_assert((NS - 2) * DL <= 63, "vmcnt range");
   constexpr bool KM = !A_RC || !B_RC;
-  __shared__ __attribute__((aligned(1024))) char lds[NS * SLOT + BIAS_BYTES];
-  char* const bias_lds = lds + NS * SLOT;
+  __shared__ __attribute__((aligned(1024))) char lds[NS * SLOT];
 
+  // Tile and, for a split reduction, chunk of this workgroup: chunk c covers
+  // stages s0 .. s0 + nst - 1 and writes f32 partials instead of the output.
+  const uint32_t ntiles = static_cast<uint32_t>(((args.rows + BM - 1) / BM) * ((args.cols + BN - 1) / BN));
+  uint32_t tb = blockIdx.x;
+  int chunk = 0;
+  if (args.partial) {
+    chunk = static_cast<int>(tb / ntiles);
+    tb -= static_cast<uint32_t>(chunk) * ntiles;
+  }
   int64_t row0, col0;
-  tile_origin<BM, BN>(args, blockIdx.x, row0, col0);
-  const int nst = static_cast<int>(args.red / BK);
+  tile_origin<BM, BN>(args, tb, row0, col0);
+  const int nst_all = static_cast<int>(args.red / BK);
+  const int s0 = args.partial ? chunk * args.chunk_stages : 0;
+  const int nst = args.partial ? (nst_all - s0 < args.chunk_stages ? nst_all - s0 : args.chunk_stages) : nst_all;
 
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   const int wm = (wave / WC) * WM;
   const int wn = (wave % WC) * WN;
 
-  typename OperandOf<BM, A_RC>::type oa;
-  typename OperandOf<BN, B_RC>::type ob;
+  typename OperandOf<BM, WAVES, A_RC>::type oa;
+  typename OperandOf<BN, WAVES, B_RC>::type ob;
   oa.init(args.A, args.lda, args.a_bytes);
   ob.init(args.B, args.ldb, args.b_bytes);
   const bool has_bias = args.bias != nullptr;
@@ -264,11 +289,11 @@ __global__ void __launch_bounds__(THREADS, 1) fast16w_kernel(GemmArgs args) {
   // operand first, then the direct-to-LDS ones (so that waiting for the
   // latter covers the former).
   auto request = [&](int st) {
-    if constexpr (!A_RC) { if (oa.active()) oa.load(row0, st); }
-    if constexpr (!B_RC) { if (ob.active()) ob.load(col0, st); }
+    if constexpr (!A_RC) { if (oa.active()) oa.load(row0, s0 + st); }
+    if constexpr (!B_RC) { if (ob.active()) ob.load(col0, s0 + st); }
     char* sl = lds + (st % NS) * SLOT;
-    if constexpr (A_RC) oa.issue(sl, row0, st);
-    if constexpr (B_RC) ob.issue(sl + A_BYTES, col0, st);
+    if constexpr (A_RC) oa.issue(sl, row0, s0 + st);
+    if constexpr (B_RC) ob.issue(sl + A_BYTES, col0, s0 + st);
   };
   auto write_km = [&](int st) {
     char* sl = lds + (st % NS) * SLOT;
@@ -284,17 +309,8 @@ __global__ void __launch_bounds__(THREADS, 1) fast16w_kernel(GemmArgs args) {
     for (int j = 0; j < NJ; ++j) bf[j] = frag(Bs, wn + 32 * j, ks);
   };
 
-  // Prologue: the bias slice and stages 0 .. NS - 1 requested, the
-  // register-staged parts written, stage 0 published.
-  if (has_bias && wave == 0 && lane < BIAS_BYTES / 16) {
-    const v4u brsrc = buffer_rsrc(args.bias, args.cols * 2);
-    const uint32_t dst = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_void*)bias_lds));
-    const uint32_t off = static_cast<uint32_t>(col0) * 2u + 16u * static_cast<uint32_t>(lane);
-    __asm__ volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
-                     :
-                     : "s"(dst), "v"(off), "s"(brsrc)
-                     : "memory", "m0");
-  }
+  // Prologue: stages 0 .. NS - 1 requested, the register-staged parts
+  // written, stage 0 published.
   int requested = 0;   // stages requested so far
   int pending = -1;    // stage whose register-staged part is still in registers
   for (; requested < NS && requested < nst; ++requested) {
@@ -324,8 +340,25 @@ __global__ void __launch_bounds__(THREADS, 1) fast16w_kernel(GemmArgs args) {
   // One stage of the sequence. The last stage is a separate copy (LAST), so
   // that the loop body has no branch around the barrier and the next stage's
   // fragment reads: the compiler's LDS wait counts then stay exact.
+  // The tile's bias slice goes into the LDS slot that stage nst - 2 used
+  // (free from the start of the last stage on; an unused slot when nst < NS)
+  // by one direct load at the start of the last stage.
+  char* const bias_lds = lds + ((nst + NS - 2) % NS) * SLOT;
+  static_assert(BN * 2 <= 1024, "bias slice must fit one wave instruction");
+  auto load_bias = [&]() {
+    if (wave == 0 && lane < BN * 2 / 16) {
+      const v4u brsrc = buffer_rsrc(args.bias, args.cols * 2);
+      const uint32_t dst = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_void*)bias_lds));
+      const uint32_t off = static_cast<uint32_t>(col0) * 2u + 16u * static_cast<uint32_t>(lane);
+      __asm__ volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+                       :
+                       : "s"(dst), "v"(off), "s"(brsrc)
+                       : "memory", "m0");
+    }
+  };
   auto stage = [&](int g, auto last_tag) {
     constexpr bool LAST = decltype(last_tag)::value;
+    if constexpr (LAST) { if (has_bias) load_bias(); }
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
       if (ks == 2 && !LAST) {
@@ -364,12 +397,50 @@ __global__ void __launch_bounds__(THREADS, 1) fast16w_kernel(GemmArgs args) {
   for (int g = 0; g + 1 < nst; ++g) stage(g, std::false_type{});
   stage(nst - 1, std::true_type{});
 
+  const int lr = lane & 31, lh = lane >> 5;
+  if (args.partial) {
+    // split reduction: this chunk's f32 partials, 16 bytes (4 columns) per store
+    float* __restrict__ P = args.partial + static_cast<int64_t>(chunk) * args.rows * args.cols;
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      const int64_t row = row0 + wm + 32 * i + lr;
+      if (row >= args.rows) continue;
+#pragma unroll
+      for (int j = 0; j < NJ; ++j)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int64_t col = col0 + wn + 32 * j + 8 * q + 4 * lh;
+          float* y = P + row * args.cols + col;
+          if (col + 4 <= args.cols) {
+            *reinterpret_cast<v4u*>(y) = v4u{__float_as_uint(acc[i][j][4 * q]), __float_as_uint(acc[i][j][4 * q + 1]),
+                                            __float_as_uint(acc[i][j][4 * q + 2]), __float_as_uint(acc[i][j][4 * q + 3])};
+          } else {
+            for (int e = 0; e < 4 && col + e < args.cols; ++e) y[e] = acc[i][j][4 * q + e];
+          }
+        }
+    }
+    return;
+  }
+
   // Epilogue. Every wave is done with the stage slots after this barrier.
   __builtin_amdgcn_s_waitcnt(0);
   __asm__ volatile("" ::: "memory");
   __builtin_amdgcn_s_barrier();
   __asm__ volatile("" ::: "memory");
-  const int lr = lane & 31, lh = lane >> 5;
+  // the lane's bias values (columns wn + 32 j + 8 q + 4 (lane / 32) + e), read
+  // before the output tile overwrites the slot that holds them
+  uint2 bias_raw[NJ][4];
+  if (has_bias) {
+#pragma unroll
+    for (int j = 0; j < NJ; ++j)
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        bias_raw[j][q] = *reinterpret_cast<const uint2*>(bias_lds + 2 * (wn + 32 * j + 8 * q + 4 * lh));
+    __builtin_amdgcn_s_waitcnt(0);
+    __asm__ volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    __asm__ volatile("" ::: "memory");
+  }
 #pragma unroll
   for (int j = 0; j < NJ; ++j) {
 #pragma unroll
@@ -378,7 +449,7 @@ __global__ void __launch_bounds__(THREADS, 1) fast16w_kernel(GemmArgs args) {
       const int cl = wn + 32 * j + 8 * q + 4 * lh;
       float b[4] = {0.0f, 0.0f, 0.0f, 0.0f};
       if (has_bias) {
-        const uint2 raw = *reinterpret_cast<const uint2*>(bias_lds + 2 * cl);
+        const uint2 raw = bias_raw[j][q];
         const T* bt = reinterpret_cast<const T*>(&raw);
 #pragma unroll
         for (int e = 0; e < 4; ++e) b[e] = E::to_f32(bt[e]);
@@ -426,12 +497,12 @@ __global__ void __launch_bounds__(THREADS, 1) fast16w_kernel(GemmArgs args) {
 template <typename E, bool AC, bool BC, int BM, int BN, int WR, int WC, int NS>
 hipError_t launch_typed(const GemmArgs& a, hipStream_t stream) {
   const int64_t tiles = ((a.cols + BN - 1) / BN) * ((a.rows + BM - 1) / BM);
-  // one tile per workgroup: a workgroup's stores then overlap the start of
-  // the next workgroup on its compute unit
-  const int64_t grid = tiles;
+  // one tile (and reduction chunk) per workgroup: a workgroup's stores then
+  // overlap the start of the next workgroup on its compute unit
+  const int64_t grid = tiles * (a.partial ? a.split : 1);
   // the kernel counts tiles and (tile, stage) pairs in 32 bits
-  if (tiles > 0x7fffffff || ((tiles + grid - 1) / grid) * (a.red / BK) > 0x7fffffff) return hipErrorInvalidConfiguration;
-  hipLaunchKernelGGL((fast16w_kernel<E, AC, BC, BM, BN, WR, WC, NS>), dim3(static_cast<unsigned>(grid)), dim3(THREADS),
+  if (grid > 0x7fffffff || a.red / BK > 0x7fffffff) return hipErrorInvalidConfiguration;
+  hipLaunchKernelGGL((fast16w_kernel<E, AC, BC, BM, BN, WR, WC, NS>), dim3(static_cast<unsigned>(grid)), dim3(64 * WR * WC),
                      0, stream, a);
   return hipGetLastError();
 }
@@ -445,7 +516,8 @@ hipError_t launch_shape(const GemmArgs& a, int shape, hipStream_t stream) {
   switch (shape) {
     case 0: return launch_typed<E, AC, BC, 256, 192, 4, 2, 2>(a, stream);
     case 1: return launch_typed<E, AC, BC, 128, 192, 4, 2, 2>(a, stream);
-    default: return launch_typed<E, AC, BC, 256, 128, 4, 2, 2>(a, stream);
+    case 2: return launch_typed<E, AC, BC, 128, 192, 2, 2, 2>(a, stream);   // four waves, two workgroups per CU
+    default: return launch_typed<E, AC, BC, 64, 192, 2, 2, 2>(a, stream);   // four waves, two workgroups per CU
   }
 }
 
@@ -459,7 +531,57 @@ hipError_t launch_op(Op op, const GemmArgs& a, int shape, hipStream_t stream) {
   return hipErrorInvalidValue;
 }
 
+// Ordered combine of a split reduction: out = round(((P_0 + P_1) + ...) +
+// P_{S-1}) element by element, f32 additions in ascending chunk order, eight
+// elements per thread.
+template <typename E>
+__global__ void __launch_bounds__(256) combine_kernel(const float* __restrict__ P, int split, int64_t count,
+                                                      typename E::T* __restrict__ out, bool vec) {
+  using T = typename E::T;
+  const int64_t i0 = (static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x) * 8;
+  if (i0 >= count) return;
+  if (vec && i0 + 8 <= count) {
+    float acc[8];
+    const v4u a0 = *reinterpret_cast<const v4u*>(P + i0), a1 = *reinterpret_cast<const v4u*>(P + i0 + 4);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) { acc[e] = __uint_as_float(a0[e]); acc[4 + e] = __uint_as_float(a1[e]); }
+    for (int c = 1; c < split; ++c) {
+      const float* Pc = P + static_cast<int64_t>(c) * count + i0;
+      const v4u b0 = *reinterpret_cast<const v4u*>(Pc), b1 = *reinterpret_cast<const v4u*>(Pc + 4);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) { acc[e] = acc[e] + __uint_as_float(b0[e]); acc[4 + e] = acc[4 + e] + __uint_as_float(b1[e]); }
+    }
+    uint16_t v[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) v[e] = __builtin_bit_cast(uint16_t, round_from_f32<E>(acc[e]));
+    v4u w;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) w[e] = static_cast<uint32_t>(v[2 * e]) | (static_cast<uint32_t>(v[2 * e + 1]) << 16);
+    *reinterpret_cast<v4u*>(out + i0) = w;
+    return;
+  }
+  for (int64_t i = i0; i < i0 + 8 && i < count; ++i) {
+    float acc = P[i];
+    for (int c = 1; c < split; ++c) acc = acc + P[static_cast<int64_t>(c) * count + i];
+    out[i] = round_from_f32<E>(acc);
+  }
+}
+
 }  // namespace w8
+
+hipError_t launch_combine(Dt dt, const float* partial, int split, int64_t count, void* out, hipStream_t stream) {
+  const int64_t blocks = (count + 256 * 8 - 1) / (256 * 8);
+  if (blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
+  const bool vec = count % 4 == 0 && reinterpret_cast<uintptr_t>(out) % 16 == 0;
+  const dim3 grid(static_cast<unsigned>(blocks)), block(256);
+  if (dt == DT_BF16)
+    hipLaunchKernelGGL(w8::combine_kernel<BF16>, grid, block, 0, stream, partial, split, count, static_cast<uint16_t*>(out), vec);
+  else if (dt == DT_F16)
+    hipLaunchKernelGGL(w8::combine_kernel<F16>, grid, block, 0, stream, partial, split, count, static_cast<_Float16*>(out), vec);
+  else
+    return hipErrorInvalidValue;
+  return hipGetLastError();
+}
 
 bool fast16_w_ok(const GemmArgs& a) {
   return a.red % w8::BK == 0 && a.vec_a && a.vec_b && a.off32_a && a.off32_b &&

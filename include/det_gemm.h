@@ -29,7 +29,14 @@
  *     the reduction, no split of the reduction for fwd and dx, one rounding to
  *     `dt` after the bias add. Identical bits on every run; for fwd and dx the
  *     bits of a row do not depend on m. Two tile families give identical bits;
- *     the family is chosen from the shape without reading m.
+ *     the family is chosen from the shape without reading m. dW of bf16/f16
+ *     inputs (its reduction is over m, so batch invariance does not apply):
+ *     when k x n gives few output tiles, the m rows are split into S chunks
+ *     of whole 64-row stages, each accumulated from 0 in f32, and the chunk
+ *     results are added in ascending chunk order before the rounding. S and
+ *     the chunk length follow from (m, k, n) alone -- never from the device,
+ *     the family or alignment -- so the bits stay fixed by the shape. For
+ *     f32 inputs S = 1.
  *
  * Ownership and execution
  *   The caller owns every buffer. The library keeps no reference to any of them

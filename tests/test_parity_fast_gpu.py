@@ -53,3 +53,27 @@ def test_integer_inputs_exact(dt):
             B = syn.integers(1200 + si, 1, sb, -8, 8, dt)
             want, _, _ = oracle.gemm(op, dt, A, B, m, k, n)
             assert_bits_equal(gpu_op(op, dt, A, B, tier="fast"), want, f"int fast {op} {dt} {(m, k, n)}")
+
+
+# dW shapes whose reduction (m) is long enough to be split into chunks: the
+# split count comes from the shape alone, so both families (and the eight-wave
+# kernel where the shape allows it) must give the same bits. m = 1100 and
+# 2101 are not multiples of 64 (register-staged kernel only, ragged last chunk).
+SPLIT_SHAPES = [(1088, 100, 136), (2048, 192, 320), (4160, 64, 64), (1100, 72, 200), (2101, 136, 64)]
+
+
+@pytest.mark.parametrize("dt", ["bf16", "f16"])
+def test_dw_split(dt):
+    import deterministic_invariant_gemm_det_amd as dg
+    for si, (m, k, n) in enumerate(SPLIT_SHAPES):
+        print(f"fast dw split {dt} {(m, k, n)}", flush=True)
+        A = syn.normal(1300 + si, 0, (m, k), dt=dt)
+        B = syn.normal(1300 + si, 1, (m, n), sigma=0.5, dt=dt)
+        _, r, S = oracle.gemm("dw", dt, A, B, m, k, n, want_r=True, want_S=True)
+        y = gpu_op("dw", dt, A, B, tier="fast")
+        assert_within_tolerance(y, r, S, dt, f"fast dw {dt} {(m, k, n)}")
+        assert_bits_equal(gpu_op("dw", dt, A, B, tier="fast"), y, "rerun")
+        for fam in (0, 1, 10, 11, 12):
+            dg.det_gemm_debug_force_family(fam)
+            assert_bits_equal(gpu_op("dw", dt, A, B, tier="fast"), y, f"family {fam}")
+        dg.det_gemm_debug_force_family(-1)
