@@ -40,7 +40,12 @@
  *
  * Ownership and execution
  *   The caller owns every buffer. The library keeps no reference to any of them
- *   and allocates no device memory per call. Work is enqueued on `stream`
+ *   and allocates no device memory per call, with one exception: the fast
+ *   tier's split dW (above) needs S * k * n * 4 bytes of f32 partials; the
+ *   library keeps one such workspace per (device, stream), allocated on first
+ *   need and grown (after synchronising that stream) when a larger one is
+ *   needed, and never frees it. Calls on one stream share it in stream order,
+ *   calls on different streams use different ones. Work is enqueued on `stream`
  *   (0 = the null stream) and the call returns once it is enqueued; the caller
  *   keeps the buffers alive until the stream has finished. Outputs must not
  *   alias inputs. Faults during execution surface at the caller's next
@@ -79,7 +84,7 @@ typedef enum {
   DET_EDTYPE = -2,   /* unknown dtype */
   DET_ETIER = -3,    /* unknown tier */
   DET_EDEVICE = -4,  /* current device is not gfx950, or no device */
-  DET_ELAUNCH = -5   /* the kernel launch was rejected by the runtime */
+  DET_ELAUNCH = -5   /* the runtime rejected a kernel launch or the workspace allocation */
 } det_status_t;
 
 /*
@@ -102,8 +107,11 @@ det_status_t det_gemm_dx(void* dx, const void* dy, const void* w,
 
 /*
  * Weight gradient: dw[k,n] = x[m,k]^T · dy[m,n] (reduction over the m rows,
- * in tiles of 32 rows for the exact tier). The order is fixed by m alone.
- * With k = 1 and x a column of ones this is the bias gradient db[n].
+ * in tiles of 32 rows for the exact tier; the order is fixed by m alone). The
+ * fast tier with bf16/f16 inputs may split the m rows into chunks fixed by the
+ * shape (see "Tiers"); a failed workspace allocation returns DET_ELAUNCH and
+ * enqueues nothing. With k = 1 and x a column of ones this is the bias
+ * gradient db[n].
  */
 det_status_t det_gemm_dw(void* dw, const void* x, const void* dy,
                          int64_t m, int64_t k, int64_t n,
