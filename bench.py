@@ -294,7 +294,7 @@ def main():
     fast = tier_stats("fast", PEAK_BF16)
     roofline_fast = {"bound": "mfma", "achieved": fast["tflops"], "peak": PEAK_BF16, "unit": "TFLOP/s",
                      "frac": round(fast["tflops"] / PEAK_BF16, 4), "traffic": None,
-                     "kernel": "fast tier, all six launches (bf16 MFMA 32x32x16, f32 accumulate)"}
+                     "kernel": "fast tier, all six launches (eight-wave bf16 MFMA 32x32x16 kernel, f32 accumulate; dW split into shape-fixed chunks plus an ordered combine)"}
 
     result = {
         "metric": METRIC, "value": round(value, 3), "unit": "TFLOP/s", "n_gpus": 1,

@@ -47,7 +47,7 @@
 namespace detgemm {
 namespace w8 {
 
-constexpr int BK = 64;
+constexpr int BK_MIN = 64;   // every stage depth is a multiple of this
 
 typedef float v16f __attribute__((ext_vector_type(16)));
 typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
@@ -67,12 +67,39 @@ template <> __device__ inline v16f mfma_step<F16>(v4u a, v4u b, v16f c) {
 // outstanding, no LDS operation outstanding, exports unconstrained.
 constexpr int waitcnt_vm_lgkm0(int vm) { return (vm & 15) | (7 << 4) | (0 << 8) | (((vm >> 4) & 3) << 14); }
 
-// Slot swizzle of row pair y (4 bits).
-__host__ __device__ constexpr int pair_swizzle(int y) { return ((y ^ (y >> 3)) & 7) | (((y >> 2) & 1) << 3); }
-// Byte offset of 16-byte piece p (0..7) of row x within an operand slot.
-__host__ __device__ constexpr uint32_t piece_offset(int x, int p) {
-  return static_cast<uint32_t>((x >> 1) * 256 + 16 * (((x & 1) * 8 + p) ^ pair_swizzle(x >> 1)));
-}
+// LDS layouts of an operand region, by stage depth BK (reduction indices per
+// stage): row x holds the stage's BK indices of output row (A) or column (B)
+// x as BK / 8 pieces of 16 bytes.
+template <int BK> struct Lay;
+
+// BK = 64: rows are paired; pair y = x / 2 occupies 256 bytes (all 64 banks
+// once) and piece p of row x sits in 16-byte slot (8 (x mod 2) + p) XOR h(y),
+// h(y) = ((y XOR y / 8) mod 8) + 8 ((y / 4) mod 2).
+template <> struct Lay<64> {
+  __host__ __device__ static constexpr int h(int y) { return ((y ^ (y >> 3)) & 7) | (((y >> 2) & 1) << 3); }
+  __host__ __device__ static constexpr uint32_t off(int x, int p) {
+    return static_cast<uint32_t>((x >> 1) * 256 + 16 * (((x & 1) * 8 + p) ^ h(x >> 1)));
+  }
+  // The piece that a direct-to-LDS wave instruction gi (1 KB at byte 1024 gi)
+  // puts at byte 16 * lane: four row pairs per instruction.
+  __device__ static inline void direct(int gi, int lane, int& x, int& p) {
+    const int y = 4 * gi + (lane >> 4);
+    const int v = (lane & 15) ^ h(y);
+    x = 2 * y + (v >> 3);
+    p = v & 7;
+  }
+};
+
+// BK = 128: row x occupies 256 bytes and piece p sits in slot p XOR f(x),
+// f(x) = (x XOR x / 8) mod 16.
+template <> struct Lay<128> {
+  __host__ __device__ static constexpr int f(int x) { return (x ^ (x >> 3)) & 15; }
+  __host__ __device__ static constexpr uint32_t off(int x, int p) { return static_cast<uint32_t>(x * 256 + 16 * (p ^ f(x))); }
+  __device__ static inline void direct(int gi, int lane, int& x, int& p) {
+    x = 4 * gi + (lane >> 4);
+    p = (lane & 15) ^ f(x);
+  }
+};
 
 __device__ inline v4u buffer_rsrc(const void* src, int64_t bytes) {
   // base address, stride 0, size in bytes (reads past it return zeros), 32-bit data format
@@ -83,10 +110,10 @@ __device__ inline v4u buffer_rsrc(const void* src, int64_t bytes) {
 
 // Reduction-contiguous operand: element (x, l) at src[x * ld + l]; X rows per
 // tile, WAVES waves per workgroup.
-template <int X, int WAVES>
+template <int X, int WAVES, int BK>
 struct RcOperand {
-  static constexpr int NQ = X * 128 / 1024 / WAVES;   // 1 KB wave instructions per wave per stage
-  static_assert(NQ * 1024 * WAVES == X * 128, "tile extent must fill whole wave instructions");
+  static constexpr int NQ = X * BK * 2 / 1024 / WAVES;   // 1 KB wave instructions per wave per stage
+  static_assert(NQ * 1024 * WAVES == X * BK * 2, "tile extent must fill whole wave instructions");
   static constexpr int LOADS = NQ;    // vector-memory instructions per stage per wave
   v4u rsrc;
   uint32_t voff[NQ];   // per-lane source byte offset of instruction q, tile origin 0, stage 0
@@ -99,9 +126,8 @@ struct RcOperand {
     ld2 = static_cast<uint32_t>(ld * 2);
 #pragma unroll
     for (int q = 0; q < NQ; ++q) {
-      const int y = 4 * (wave * NQ + q) + (lane >> 4);      // row pair written by this lane
-      const int v = (lane & 15) ^ pair_swizzle(y);           // (8 (x mod 2) + p) of the slot's piece
-      const int x = 2 * y + (v >> 3), p = v & 7;
+      int x, p;
+      Lay<BK>::direct(wave * NQ + q, lane, x, p);
       voff[q] = static_cast<uint32_t>((x * ld + 8 * p) * 2);
     }
   }
@@ -134,10 +160,10 @@ struct RcOperand {
 // xb = t mod (X / 8): KH 16-byte loads, a V_PERM_B32 transpose, and one
 // 2 KH-byte LDS write per column (a whole piece for KH = 8, half of one for
 // KH = 4).
-template <int X, int KH>
+template <int X, int KH, int BK>
 struct KmOperand {
   static constexpr int NX = X / 8;
-  static constexpr int UNITS = (64 / KH) * NX;
+  static constexpr int UNITS = (BK / KH) * NX;
   static_assert(X % 64 == 0 && (KH == 4 || KH == 8), "tile extent / block height");
   __amdgpu_buffer_rsrc_t rsrc;
   uint32_t voff;    // byte offset of the thread's block, tile origin 0, stage 0
@@ -175,12 +201,12 @@ struct KmOperand {
         v4u col;
 #pragma unroll
         for (int j = 0; j < 4; ++j) col[j] = __builtin_amdgcn_perm(v[2 * j + 1][c >> 1], v[2 * j][c >> 1], sel);
-        *reinterpret_cast<v4u*>(slot + piece_offset(8 * xb + c, kb)) = col;
+        *reinterpret_cast<v4u*>(slot + Lay<BK>::off(8 * xb + c, kb)) = col;
       } else {
         uint2 col;
         col.x = __builtin_amdgcn_perm(v[1][c >> 1], v[0][c >> 1], sel);
         col.y = __builtin_amdgcn_perm(v[3][c >> 1], v[2][c >> 1], sel);
-        *reinterpret_cast<uint2*>(slot + piece_offset(8 * xb + c, kb >> 1) + 8 * (kb & 1)) = col;
+        *reinterpret_cast<uint2*>(slot + Lay<BK>::off(8 * xb + c, kb >> 1) + 8 * (kb & 1)) = col;
       }
     }
   }
@@ -188,17 +214,21 @@ struct KmOperand {
 
 // Block height of the register-staged operand: half blocks when there are
 // threads for them (fewer registers per thread, more threads sharing the work).
-template <int X, int WAVES> constexpr int km_height() { return (64 / 4) * (X / 8) <= 64 * WAVES ? 4 : 8; }
+template <int X, int WAVES, int BK> constexpr int km_height() { return (BK / 4) * (X / 8) <= 64 * WAVES ? 4 : 8; }
 
-template <int X, int WAVES, bool RC> struct OperandOf;
-template <int X, int WAVES> struct OperandOf<X, WAVES, true> { using type = RcOperand<X, WAVES>; };
-template <int X, int WAVES> struct OperandOf<X, WAVES, false> { using type = KmOperand<X, km_height<X, WAVES>()>; };
+template <int X, int WAVES, int BK, bool RC> struct OperandOf;
+template <int X, int WAVES, int BK> struct OperandOf<X, WAVES, BK, true> { using type = RcOperand<X, WAVES, BK>; };
+template <int X, int WAVES, int BK> struct OperandOf<X, WAVES, BK, false> {
+  using type = KmOperand<X, km_height<X, WAVES, BK>(), BK>;
+  static_assert(type::UNITS <= 64 * WAVES, "register-staged blocks: at most one per thread");
+};
 
 // The lane's fragment of the 32-row block at xb for reduction step ks of a
 // stage: row xb + lane % 32, piece 2 ks + lane / 32 (elements 16 ks + 8 (lane / 32) + j).
+template <int BK>
 __device__ inline v4u frag(const char* slot, int xb, int ks) {
   const int lane = threadIdx.x & 63;
-  return *reinterpret_cast<const v4u*>(slot + piece_offset(xb + (lane & 31), 2 * ks + (lane >> 5)));
+  return *reinterpret_cast<const v4u*>(slot + Lay<BK>::off(xb + (lane & 31), 2 * ks + (lane >> 5)));
 }
 
 // Output tile t -> (first row, first column). Workgroups are dealt to the
@@ -240,21 +270,20 @@ __device__ inline void tile_origin(const GemmArgs& a, uint32_t t, int64_t& row0,
 // Epilogue: acc + bias, one rounding, written through LDS (the stage slots are
 // free by then) as a row-major tile, then copied out with 16-byte stores
 // along whole tile rows.
-template <typename E, bool A_RC, bool B_RC, int BM, int BN, int WR, int WC, int NS>
+template <typename E, bool A_RC, bool B_RC, int BM, int BN, int WR, int WC, int NS, int BK>
 __global__ void __launch_bounds__(64 * WR * WC, 8 / (WR * WC)) fast16w_kernel(GemmArgs args) {
   using T = typename E::T;
   constexpr int WAVES = WR * WC, THREADS = 64 * WAVES;
   constexpr int WM = BM / WR, WN = BN / WC, NI = WM / 32, NJ = WN / 32;
   static_assert((WAVES == 8 || WAVES == 4) && NI * 32 == WM && NJ * 32 == WN, "bad wave grid");
-  static_assert(BM <= THREADS && BN <= THREADS, "register-staged blocks: at most one per thread");
-  constexpr int KS = BK / 16;
-  static_assert(KS == 4, "four reduction steps per stage");
+  constexpr int KS = BK / 16;   // reduction steps per stage
+  static_assert(KS % 4 == 0, "whole groups of four reduction steps per stage");
   constexpr int A_BYTES = BM * BK * 2, B_BYTES = BN * BK * 2, SLOT = A_BYTES + B_BYTES;
   constexpr int RS = BN * 2 + 16;   // LDS row stride of the output tile (bytes)
   static_assert(BM * RS <= NS * SLOT, "output tile must fit the stage slots");
   static_assert(NS >= 2 && NS * SLOT * (8 / WAVES) <= 160 * 1024, "LDS (8 waves per compute unit)");
   // direct-to-LDS loads per wave per stage (the ones vmcnt must account for)
-  constexpr int DL = (A_RC ? RcOperand<BM, WAVES>::LOADS : 0) + (B_RC ? RcOperand<BN, WAVES>::LOADS : 0);
+  constexpr int DL = (A_RC ? RcOperand<BM, WAVES, BK>::LOADS : 0) + (B_RC ? RcOperand<BN, WAVES, BK>::LOADS : 0);
   static_assert((NS - 2) * DL <= 63, "vmcnt range");
   constexpr bool KM = !A_RC || !B_RC;
   __shared__ __attribute__((aligned(1024))) char lds[NS * SLOT];
@@ -279,8 +308,8 @@ __global__ void __launch_bounds__(64 * WR * WC, 8 / (WR * WC)) fast16w_kernel(Ge
   const int wm = (wave / WC) * WM;
   const int wn = (wave % WC) * WN;
 
-  typename OperandOf<BM, WAVES, A_RC>::type oa;
-  typename OperandOf<BN, WAVES, B_RC>::type ob;
+  typename OperandOf<BM, WAVES, BK, A_RC>::type oa;
+  typename OperandOf<BN, WAVES, BK, B_RC>::type ob;
   oa.init(args.A, args.lda, args.a_bytes);
   ob.init(args.B, args.ldb, args.b_bytes);
   const bool has_bias = args.bias != nullptr;
@@ -304,24 +333,40 @@ __global__ void __launch_bounds__(64 * WR * WC, 8 / (WR * WC)) fast16w_kernel(Ge
     const char* As = lds + (st % NS) * SLOT;
     const char* Bs = As + A_BYTES;
 #pragma unroll
-    for (int i = 0; i < NI; ++i) af[i] = frag(As, wm + 32 * i, ks);
+    for (int i = 0; i < NI; ++i) af[i] = frag<BK>(As, wm + 32 * i, ks);
 #pragma unroll
-    for (int j = 0; j < NJ; ++j) bf[j] = frag(Bs, wn + 32 * j, ks);
+    for (int j = 0; j < NJ; ++j) bf[j] = frag<BK>(Bs, wn + 32 * j, ks);
   };
 
-  // Prologue: stages 0 .. NS - 1 requested, the register-staged parts
-  // written, stage 0 published.
-  int requested = 0;   // stages requested so far
+  // Prologue: stages 0 .. NS - 1 requested and stage 0 published; the last
+  // requested stage may still be in flight (its register-staged part is then
+  // written before the first barrier of the loop).
   int pending = -1;    // stage whose register-staged part is still in registers
-  for (; requested < NS && requested < nst; ++requested) {
-    request(requested);
-    if constexpr (KM) {
+  const int pro = nst < NS ? nst : NS;
+  if constexpr (KM) {
+    // the registers hold one stage: complete stages one by one, leave the last one pending
+    for (int st = 0; st + 1 < pro; ++st) {
+      request(st);
       __builtin_amdgcn_s_waitcnt(0);
       __asm__ volatile("" ::: "memory");
-      write_km(requested);
+      write_km(st);
     }
+    request(pro - 1);
+    if (pro == 1) {
+      __builtin_amdgcn_s_waitcnt(0);
+      __asm__ volatile("" ::: "memory");
+      write_km(0);
+    } else {
+      pending = pro - 1;
+    }
+  } else {
+    for (int st = 0; st < pro; ++st) request(st);
+    // stage 0 landed; the direct loads of stages 1 .. pro - 1 may still fly
+    if (pro == NS) __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0((NS - 1) * DL));
+    else __builtin_amdgcn_s_waitcnt(0);
   }
-  __builtin_amdgcn_s_waitcnt(0);
+  int requested = pro;   // stages requested so far
+  __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(63));
   __asm__ volatile("" ::: "memory");
   __builtin_amdgcn_s_barrier();
   __asm__ volatile("" ::: "memory");
@@ -361,7 +406,7 @@ __global__ void __launch_bounds__(64 * WR * WC, 8 / (WR * WC)) fast16w_kernel(Ge
     if constexpr (LAST) { if (has_bias) load_bias(); }
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
-      if (ks == 2 && !LAST) {
+      if (ks == KS - 2 && !LAST) {
         if constexpr (KM) {
           if (pending >= 0) {
             // outstanding after the register-staged loads: that stage's direct loads
@@ -384,13 +429,13 @@ __global__ void __launch_bounds__(64 * WR * WC, 8 / (WR * WC)) fast16w_kernel(Ge
         }
       }
       // fragments of step 4 g + ks + 2
-      if (ks < 2) read_step(af[(ks + 2) & 3], bf[(ks + 2) & 3], g, ks + 2);
-      else if (!LAST) read_step(af[(ks + 2) & 3], bf[(ks + 2) & 3], g + 1, ks - 2);
+      if (ks < KS - 2) read_step(af[(ks + 2) & 3], bf[(ks + 2) & 3], g, ks + 2);
+      else if (!LAST) read_step(af[(ks + 2) & 3], bf[(ks + 2) & 3], g + 1, ks + 2 - KS);
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int i = 0; i < NI; ++i)
 #pragma unroll
-        for (int j = 0; j < NJ; ++j) acc[i][j] = mfma_step<E>(bf[ks][j], af[ks][i], acc[i][j]);
+        for (int j = 0; j < NJ; ++j) acc[i][j] = mfma_step<E>(bf[ks & 3][j], af[ks & 3][i], acc[i][j]);
       __builtin_amdgcn_sched_barrier(0);
     }
   };
@@ -494,15 +539,17 @@ __global__ void __launch_bounds__(64 * WR * WC, 8 / (WR * WC)) fast16w_kernel(Ge
   }
 }
 
-template <typename E, bool AC, bool BC, int BM, int BN, int WR, int WC, int NS>
+template <typename E, bool AC, bool BC, int BM, int BN, int WR, int WC, int NS, int BK = 64>
 hipError_t launch_typed(const GemmArgs& a, hipStream_t stream) {
+  // a split reduction counts its chunks in stages of 64
+  if (a.red % BK != 0 || (a.partial && BK != 64)) return hipErrorInvalidValue;
   const int64_t tiles = ((a.cols + BN - 1) / BN) * ((a.rows + BM - 1) / BM);
   // one tile (and reduction chunk) per workgroup: a workgroup's stores then
   // overlap the start of the next workgroup on its compute unit
   const int64_t grid = tiles * (a.partial ? a.split : 1);
   // the kernel counts tiles and (tile, stage) pairs in 32 bits
   if (grid > 0x7fffffff || a.red / BK > 0x7fffffff) return hipErrorInvalidConfiguration;
-  hipLaunchKernelGGL((fast16w_kernel<E, AC, BC, BM, BN, WR, WC, NS>), dim3(static_cast<unsigned>(grid)), dim3(64 * WR * WC),
+  hipLaunchKernelGGL((fast16w_kernel<E, AC, BC, BM, BN, WR, WC, NS, BK>), dim3(static_cast<unsigned>(grid)), dim3(64 * WR * WC),
                      0, stream, a);
   return hipGetLastError();
 }
@@ -517,7 +564,10 @@ hipError_t launch_shape(const GemmArgs& a, int shape, hipStream_t stream) {
     case 0: return launch_typed<E, AC, BC, 256, 192, 4, 2, 2>(a, stream);
     case 1: return launch_typed<E, AC, BC, 128, 192, 4, 2, 2>(a, stream);
     case 2: return launch_typed<E, AC, BC, 128, 192, 2, 2, 2>(a, stream);   // four waves, two workgroups per CU
-    default: return launch_typed<E, AC, BC, 64, 192, 2, 2, 2>(a, stream);   // four waves, two workgroups per CU
+    case 3: return launch_typed<E, AC, BC, 64, 192, 2, 2, 2>(a, stream);    // four waves, two workgroups per CU
+    default:   // stages of 128 (half the barriers) where the reduction allows it
+      if (a.red % 128 != 0 || a.partial) return launch_typed<E, AC, BC, 128, 192, 4, 2, 2>(a, stream);
+      return launch_typed<E, AC, BC, 128, 192, 4, 2, 2, 128>(a, stream);
   }
 }
 
@@ -584,11 +634,14 @@ hipError_t launch_combine(Dt dt, const float* partial, int split, int64_t count,
 }
 
 bool fast16_w_ok(const GemmArgs& a) {
-  return a.red % w8::BK == 0 && a.vec_a && a.vec_b && a.off32_a && a.off32_b &&
+  return a.red % w8::BK_MIN == 0 && a.vec_a && a.vec_b && a.off32_a && a.off32_b &&
          reinterpret_cast<uintptr_t>(a.bias) % 16 == 0;
 }
 
-int fast16_w_shape(int64_t cols) { return cols >= 1536 ? 0 : 1; }
+// Wide outputs: 256 x 192 tiles; narrow ones: 128 x 192 tiles with stages of
+// 128 reduction indices where the reduction allows it (shape 4 falls back to
+// stages of 64 otherwise). Chosen from the column count only.
+int fast16_w_shape(int64_t cols) { return cols >= 1536 ? 0 : 4; }
 
 hipError_t launch_fast16_w(Op op, Dt dt, const GemmArgs& a, int shape, hipStream_t stream) {
   if (dt == DT_BF16) return w8::launch_op<BF16>(op, a, shape, stream);

@@ -129,8 +129,9 @@ int det_gemm_version(void);
 /*
  * Test hook: force the fast tier's tile family for later calls from any thread
  * (-1 automatic, 0 = the large family, 1 = the small family, 10 + s = tile
- * shape s of the large family's eight-wave kernel: 10 = 256 x 192,
- * 11 = 128 x 192, 12 = 256 x 128, used where that kernel applies). All
+ * shape s of the large family's kernel where it applies: 10 = 256 x 192,
+ * 11 = 128 x 192, 12 = 128 x 192 in two four-wave workgroups per compute
+ * unit, 13 = 64 x 192 likewise, 14 = 128 x 192 in stages of 128). All
  * families produce identical bits, so this changes speed only. Returns
  * DET_EINVAL for other values.
  */

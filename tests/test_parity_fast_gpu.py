@@ -73,7 +73,7 @@ def test_dw_split(dt):
         y = gpu_op("dw", dt, A, B, tier="fast")
         assert_within_tolerance(y, r, S, dt, f"fast dw {dt} {(m, k, n)}")
         assert_bits_equal(gpu_op("dw", dt, A, B, tier="fast"), y, "rerun")
-        for fam in (0, 1, 10, 11, 12):
+        for fam in (0, 1, 10, 11, 12, 13, 14):
             dg.det_gemm_debug_force_family(fam)
             assert_bits_equal(gpu_op("dw", dt, A, B, tier="fast"), y, f"family {fam}")
         dg.det_gemm_debug_force_family(-1)
