@@ -80,6 +80,22 @@ class Oracle:
         m, k = x.shape
         return self.gemm("dw", dt, x, dy, m, k, dy.shape[1], rows=rows, **kw)
 
+    def dw_out(self, dt, out_dt, x, dy, rows=None, **kw):
+        """dW rounded once to out_dt (dt itself, or "f32" for f32 master weights): the float64
+        value r of dw, then one RNE rounding to out_dt. Returns (y, r, S) like gemm."""
+        _, r, S = self.dw(dt, x, dy, rows=rows, want_r=True, want_S=kw.get("want_S", False))
+        return self.round_to(out_dt, r), (r if kw.get("want_r") else None), S
+
+    def db(self, dt, dy, out_dt=None, want_r=False, want_S=False):
+        """Bias gradient db[n] = sum_i dy[i, n], defined as dW of a column of ones (the
+        reduction over i in tiles of 32 rows, Neumaier across tiles), rounded once to out_dt
+        (default dt). Returns (y[n], r[n] or None, S[n] or None)."""
+        m, n = dy.shape
+        ones = self.round_to(dt, np.ones((m, 1)))
+        _, r, S = self.gemm("dw", dt, ones, dy, m, 1, n, want_r=True, want_S=want_S)
+        y = self.round_to(out_dt or dt, r[0])
+        return y, (r[0] if want_r else None), (S[0] if want_S else None)
+
     def round_to(self, dt, r):
         """Single RNE rounding of float64 values to dt (raw storage out)."""
         r = np.ascontiguousarray(r, dtype=np.float64)
@@ -129,3 +145,11 @@ def dw(*a, **kw):
 
 def round_to(*a, **kw):
     return default().round_to(*a, **kw)
+
+
+def dw_out(*a, **kw):
+    return default().dw_out(*a, **kw)
+
+
+def db(*a, **kw):
+    return default().db(*a, **kw)
