@@ -12,9 +12,9 @@ import ctypes
 import os
 
 __all__ = [
-    "det_gemm_fwd", "det_gemm_dx", "det_gemm_dw", "det_gemm_strerror", "det_gemm_last_error",
-    "det_gemm_version", "det_gemm_debug_force_family", "det_gemm_debug_force_exact_kernel", "DetGemmError", "LIB_PATH",
-    "fwd", "dx", "dw", "deterministic_linear", "Linear", "DTYPES", "TIERS",
+    "det_gemm_fwd", "det_gemm_dx", "det_gemm_dw", "det_gemm_dw_out", "det_gemm_db", "det_gemm_strerror",
+    "det_gemm_last_error", "det_gemm_version", "det_gemm_debug_force_family", "det_gemm_debug_force_exact_kernel",
+    "DetGemmError", "LIB_PATH", "fwd", "dx", "dw", "db", "deterministic_linear", "Linear", "DTYPES", "TIERS",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -53,7 +53,9 @@ def lib():
         L.det_gemm_fwd.argtypes = [vp, vp, vp, vp, i64, i64, i64, ci, ci, vp]
         L.det_gemm_dx.argtypes = [vp, vp, vp, i64, i64, i64, ci, ci, vp]
         L.det_gemm_dw.argtypes = [vp, vp, vp, i64, i64, i64, ci, ci, vp]
-        for f in (L.det_gemm_fwd, L.det_gemm_dx, L.det_gemm_dw):
+        L.det_gemm_dw_out.argtypes = [vp, ci, vp, vp, i64, i64, i64, ci, ci, vp]
+        L.det_gemm_db.argtypes = [vp, ci, vp, i64, i64, ci, ci, vp]
+        for f in (L.det_gemm_fwd, L.det_gemm_dx, L.det_gemm_dw, L.det_gemm_dw_out, L.det_gemm_db):
             f.restype = ci
         L.det_gemm_strerror.argtypes = [ci]
         L.det_gemm_strerror.restype = ctypes.c_char_p
@@ -103,6 +105,16 @@ def det_gemm_dx(dx_, dy, w, m, k, n, dtype, tier, stream=0):
 
 def det_gemm_dw(dw_, x, dy, m, k, n, dtype, tier, stream=0):
     _check(lib().det_gemm_dw(_p(dw_), _p(x), _p(dy), m, k, n,
+                             _code(DTYPES, dtype, "dtype"), _code(TIERS, tier, "tier"), _p(stream)))
+
+
+def det_gemm_dw_out(dw_, dw_dtype, x, dy, m, k, n, dtype, tier, stream=0):
+    _check(lib().det_gemm_dw_out(_p(dw_), _code(DTYPES, dw_dtype, "dtype"), _p(x), _p(dy), m, k, n,
+                                 _code(DTYPES, dtype, "dtype"), _code(TIERS, tier, "tier"), _p(stream)))
+
+
+def det_gemm_db(db_, db_dtype, dy, m, n, dtype, tier, stream=0):
+    _check(lib().det_gemm_db(_p(db_), _code(DTYPES, db_dtype, "dtype"), _p(dy), m, n,
                              _code(DTYPES, dtype, "dtype"), _code(TIERS, tier, "tier"), _p(stream)))
 
 
@@ -182,16 +194,37 @@ def dx(dy, w, tier="exact", out=None):
     return g
 
 
-def dw(x, dy, tier="exact", out=None):
-    """dw[k,n] = x[m,k]^T @ dy[m,n] on the current stream."""
+def dw(x, dy, tier="exact", out=None, out_dtype=None):
+    """dw[k,n] = x[m,k]^T @ dy[m,n] on the current stream; out_dtype=torch.float32 writes
+    f32 gradients (for f32 master weights) from bf16/f16 inputs."""
     import torch
     (x, dy), stream = _prep(x, dy)
     m, k = x.shape
     m2, n = dy.shape
     if m2 != m:
         raise ValueError("shape mismatch")
-    g = out if out is not None else torch.empty((k, n), dtype=x.dtype, device=x.device)
-    det_gemm_dw(g, x, dy, m, k, n, _torch_dtype_name(x), tier, stream)
+    odt = out_dtype or x.dtype
+    g = out if out is not None else torch.empty((k, n), dtype=odt, device=x.device)
+    if g.dtype != odt or not g.is_contiguous() or tuple(g.shape) != (k, n):
+        raise ValueError("out must be a contiguous (k, n) tensor of the output dtype")
+    if odt == x.dtype:
+        det_gemm_dw(g, x, dy, m, k, n, _torch_dtype_name(x), tier, stream)
+    else:
+        det_gemm_dw_out(g, _torch_dtype_name(g), x, dy, m, k, n, _torch_dtype_name(x), tier, stream)
+    return g
+
+
+def db(dy, tier="exact", out=None, out_dtype=None):
+    """db[n] = sum_i dy[i,n] on the current stream (the exact tier's column sum in either tier);
+    out_dtype=torch.float32 writes f32 from bf16/f16 inputs."""
+    import torch
+    (dy,), stream = _prep(dy)
+    m, n = dy.shape
+    odt = out_dtype or dy.dtype
+    g = out if out is not None else torch.empty((n,), dtype=odt, device=dy.device)
+    if g.dtype != odt or not g.is_contiguous() or g.numel() != n:
+        raise ValueError("out must be a contiguous tensor of n elements of the output dtype")
+    det_gemm_db(g, _torch_dtype_name(g), dy, m, n, _torch_dtype_name(dy), tier, stream)
     return g
 
 
@@ -214,8 +247,7 @@ def _autograd_fn():
             gw = dw(x, gy, ctx.tier) if ctx.needs_input_grad[1] else None
             gb = None
             if ctx.has_bias and ctx.needs_input_grad[2]:
-                ones = torch.ones((x.shape[0], 1), dtype=x.dtype, device=x.device)
-                gb = dw(ones, gy, ctx.tier).reshape(-1)   # column sum in the tier's fixed order
+                gb = db(gy, ctx.tier)   # column sum in the exact tier's fixed order
             return gx, gw, gb, None
 
     return DeterministicLinearFn

@@ -60,7 +60,8 @@ bool mul_ok(int64_t a, int64_t b, int64_t elem) {
 }
 
 det_status_t run(detgemm::Op op, void* out, const void* A, const void* B, const void* bias,
-                 int64_t m, int64_t k, int64_t n, det_dtype_t dt, det_tier_t tier, hipStream_t stream) {
+                 int64_t m, int64_t k, int64_t n, det_dtype_t dt, det_tier_t tier, hipStream_t stream,
+                 bool out_f32 = false) {
   g_last_error[0] = '\0';
   if (dt != DET_F32 && dt != DET_BF16 && dt != DET_F16) return fail(DET_EDTYPE, "det_gemm: unknown dtype%s");
   if (tier != DET_TIER_EXACT && tier != DET_TIER_FAST) return fail(DET_ETIER, "det_gemm: unknown tier%s");
@@ -82,6 +83,7 @@ det_status_t run(detgemm::Op op, void* out, const void* A, const void* B, const 
   a.partial = nullptr;
   a.split = 1;
   a.chunk_stages = 0;
+  a.out_f32 = out_f32 && dt != DET_F32;
   switch (op) {
     case detgemm::OP_FWD: a.rows = m; a.cols = n; a.red = k; a.lda = k; a.ldb = n; break;
     case detgemm::OP_DX:  a.rows = m; a.cols = k; a.red = n; a.lda = n; a.ldb = n; break;
@@ -169,6 +171,36 @@ det_status_t det_gemm_dw(void* dw, const void* x, const void* dy,
   return run(detgemm::OP_DW, dw, x, dy, nullptr, m, k, n, dt, tier, stream);
 }
 
+det_status_t det_gemm_dw_out(void* dw, det_dtype_t dw_dt, const void* x, const void* dy,
+                             int64_t m, int64_t k, int64_t n,
+                             det_dtype_t dt, det_tier_t tier, hipStream_t stream) {
+  if (dw_dt != dt && dw_dt != DET_F32) {
+    g_last_error[0] = '\0';
+    return fail(DET_EDTYPE, "det_gemm_dw_out: the output dtype must be the input dtype or DET_F32%s");
+  }
+  return run(detgemm::OP_DW, dw, x, dy, nullptr, m, k, n, dt, tier, stream, dw_dt == DET_F32);
+}
+
+det_status_t det_gemm_db(void* db, det_dtype_t db_dt, const void* dy, int64_t m, int64_t n,
+                         det_dtype_t dt, det_tier_t tier, hipStream_t stream) {
+  g_last_error[0] = '\0';
+  if (dt != DET_F32 && dt != DET_BF16 && dt != DET_F16) return fail(DET_EDTYPE, "det_gemm: unknown dtype%s");
+  if (db_dt != dt && db_dt != DET_F32)
+    return fail(DET_EDTYPE, "det_gemm_db: the output dtype must be the input dtype or DET_F32%s");
+  if (tier != DET_TIER_EXACT && tier != DET_TIER_FAST) return fail(DET_ETIER, "det_gemm: unknown tier%s");
+  if (!db || !dy) return fail(DET_EINVAL, "det_gemm: null %s pointer", !db ? "output" : "input");
+  if (m < 1 || n < 1) return fail(DET_EINVAL, "det_gemm: m and n must both be >= 1%s");
+  const int64_t esz = dt == DET_F32 ? 4 : 2;
+  if (!mul_ok(m, n, esz)) return fail(DET_EINVAL, "det_gemm: tensor size overflows int64%s");
+  int cus = 0;
+  const det_status_t dev = check_device(&cus);
+  if (dev != DET_OK) return dev;
+  const hipError_t err = detgemm::launch_db(static_cast<detgemm::Dt>(dt), db_dt == DET_F32 && dt != DET_F32, dy, m, n,
+                                            db, stream);
+  if (err != hipSuccess) return fail(DET_ELAUNCH, "det_gemm: kernel launch failed: %s", hipGetErrorString(err));
+  return DET_OK;
+}
+
 const char* det_gemm_strerror(det_status_t status) {
   switch (status) {
     case DET_OK: return "success";
@@ -183,7 +215,7 @@ const char* det_gemm_strerror(det_status_t status) {
 
 const char* det_gemm_last_error(void) { return g_last_error; }
 
-int det_gemm_version(void) { return 100; }
+int det_gemm_version(void) { return 200; }
 
 det_status_t det_gemm_debug_force_family(int family) {
   if (family < -1 || (family > 1 && family < 10) || family > 14)

@@ -29,6 +29,9 @@ struct GemmArgs {
   float* partial;
   int split;
   int chunk_stages;
+  // dW only: write f32 outputs (rounded once from the tier's wide value)
+  // instead of the input dtype
+  bool out_f32;
 };
 
 enum Dt { DT_F32 = 0, DT_BF16 = 1, DT_F16 = 2 };
@@ -102,7 +105,10 @@ int fast_auto_family(Op op, Dt dt, int64_t cols, int64_t red);
 // returns the chunk count S >= 1 and sets *chunk_stages.
 int fast_dw_split(int64_t m, int64_t k, int64_t n, int* chunk_stages);
 // out[i] = round(((P_0[i] + P_1[i]) + ...) + P_{S-1}[i]) over `count` elements, P_c = partial + c * count.
-hipError_t launch_combine(Dt dt, const float* partial, int split, int64_t count, void* out, hipStream_t stream);
+hipError_t launch_combine(Dt dt, bool out_f32, const float* partial, int split, int64_t count, void* out,
+                          hipStream_t stream);
+// db[n] = sum_i dy[i, n] with the exact tier's arithmetic (the dW of a column of ones).
+hipError_t launch_db(Dt dt, bool out_f32, const void* dy, int64_t m, int64_t n, void* db, hipStream_t stream);
 // A device workspace of at least `bytes` owned by the library for (current device, stream);
 // grown on demand, kept for later calls on the same stream.
 hipError_t stream_workspace(hipStream_t stream, size_t bytes, void** ptr);

@@ -44,6 +44,8 @@
 // [reduction index][row or column], double buffered, with the next tile's
 // global loads issued before the current tile's arithmetic.
 
+#include <type_traits>
+
 #include "common.hpp"
 
 namespace detgemm {
@@ -282,7 +284,8 @@ __global__ void __launch_bounds__(THREADS) exact_valu_kernel(GemmArgs args) {
 // turns grids such as 12 x 48 blocks of 64 x 64 (2.25 per compute unit) into
 // 16 x 48 blocks of 48 x 64 (three per compute unit, all resident at once).
 
-template <typename E, bool A_RED_CONTIG, bool B_RED_CONTIG, int NBUF, int BMT>
+// O: the output type (E, or F32 for dW written as f32).
+template <typename E, bool A_RED_CONTIG, bool B_RED_CONTIG, int NBUF, int BMT, typename O = E>
 __global__ void __launch_bounds__(THREADS, NBUF == 1 ? 3 : 2) exact_mfma4_kernel(GemmArgs args) {
   // NBUF == 2: double-buffered LDS (80 KB), one barrier per tile, 2 workgroups per CU.
   // NBUF == 1: single LDS buffer (40 KB), two barriers per tile, 3 workgroups per CU.
@@ -358,7 +361,7 @@ __global__ void __launch_bounds__(THREADS, NBUF == 1 ? 3 : 2) exact_mfma4_kernel
     __syncthreads();
   }
 
-  typename E::T* __restrict__ Y = static_cast<typename E::T*>(args.out);
+  typename O::T* __restrict__ Y = static_cast<typename O::T*>(args.out);
   const typename E::T* __restrict__ bias = static_cast<const typename E::T*>(args.bias);
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
@@ -371,7 +374,7 @@ __global__ void __launch_bounds__(THREADS, NBUF == 1 ? 3 : 2) exact_mfma4_kernel
       if (row < args.rows) {
         double v = s[u][r] + c[u][r];
         if (bias) v = v + bj;
-        Y[row * args.cols + col] = round_from_f64<E>(v);
+        Y[row * args.cols + col] = round_from_f64<O>(v);
       }
     }
   }
@@ -479,12 +482,17 @@ bool use_48_rows(const GemmArgs& a) {
   return r48 * 48 < r64 * 64;
 }
 
-template <typename E, bool AC, bool BC>
+template <typename E, bool AC, bool BC, typename O = E>
 hipError_t launch_typed(const GemmArgs& a, int variant, hipStream_t stream) {
   if (variant < 0) variant = use_48_rows(a) ? 4 : 0;
+  // f32 output: the default kernel in its two row-block forms (identical bits)
+  if constexpr (!std::is_same<O, E>::value) {
+    if (variant != 4) variant = 0;
+  }
   const int64_t blocks = ((a.cols + BN - 1) / BN) * ((a.rows + BM - 1) / BM);
   if (blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
   const dim3 grid(static_cast<unsigned>(blocks));
+  // (variants 1 .. 3 write the input type only; for f32 output variant is 0 or 4 here)
   if (variant == 1)
     hipLaunchKernelGGL((exact_mfma_kernel<E, AC, BC>), grid, dim3(THREADS), 0, stream, a);
   else if (variant == 2)
@@ -494,10 +502,10 @@ hipError_t launch_typed(const GemmArgs& a, int variant, hipStream_t stream) {
   else if (variant == 4) {
     const int64_t b48 = ((a.cols + BN - 1) / BN) * ((a.rows + 47) / 48);
     if (b48 > 0x7fffffff) return hipErrorInvalidConfiguration;
-    hipLaunchKernelGGL((exact_mfma4_kernel<E, AC, BC, 1, 48>), dim3(static_cast<unsigned>(b48)), dim3(THREADS), 0,
+    hipLaunchKernelGGL((exact_mfma4_kernel<E, AC, BC, 1, 48, O>), dim3(static_cast<unsigned>(b48)), dim3(THREADS), 0,
                        stream, a);
   } else
-    hipLaunchKernelGGL((exact_mfma4_kernel<E, AC, BC, 1, 64>), grid, dim3(THREADS), 0, stream, a);
+    hipLaunchKernelGGL((exact_mfma4_kernel<E, AC, BC, 1, 64, O>), grid, dim3(THREADS), 0, stream, a);
   return hipGetLastError();
 }
 
@@ -506,7 +514,9 @@ hipError_t launch_op(Op op, const GemmArgs& a, int variant, hipStream_t stream) 
   switch (op) {
     case OP_FWD: return launch_typed<E, true, false>(a, variant, stream);   // X[i][k], W[k][j]
     case OP_DX:  return launch_typed<E, true, true>(a, variant, stream);    // dY[i][n], W[q][n]
-    case OP_DW:  return launch_typed<E, false, false>(a, variant, stream);  // X[i][q], dY[i][j]
+    case OP_DW:   // X[i][q], dY[i][j]
+      if (a.out_f32) return launch_typed<E, false, false, F32>(a, variant, stream);
+      return launch_typed<E, false, false>(a, variant, stream);
   }
   return hipErrorInvalidValue;
 }

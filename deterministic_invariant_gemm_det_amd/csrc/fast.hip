@@ -217,7 +217,7 @@ hipError_t launch_fast(Op op, Dt dt, const GemmArgs& a, int family, hipStream_t 
       p.chunk_stages = chunk;
       e = launch_fast(op, dt, p, family, stream);
       if (e != hipSuccess) return e;
-      return launch_combine(dt, p.partial, split, static_cast<int64_t>(count), a.out, stream);
+      return launch_combine(dt, a.out_f32, p.partial, split, static_cast<int64_t>(count), a.out, stream);
     }
   }
   switch (dt) {

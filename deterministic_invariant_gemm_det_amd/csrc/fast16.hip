@@ -237,9 +237,11 @@ __global__ void __launch_bounds__(THREADS, 2) fast16_kernel(GemmArgs args) {
   }
 
   const bool interior = rows_full && cols_full;
-  if (args.partial) {
-    // split reduction: this chunk's f32 partials (no bias in dW)
-    float* __restrict__ P = args.partial + static_cast<int64_t>(chunk) * args.rows * args.cols;
+  if (args.partial || args.out_f32) {
+    // split reduction: this chunk's f32 partials; f32 output: the accumulators
+    // themselves (no bias in dW)
+    float* __restrict__ P = args.partial ? args.partial + static_cast<int64_t>(chunk) * args.rows * args.cols
+                                         : static_cast<float*>(args.out);
 #pragma unroll
     for (int j = 0; j < NJ; ++j) {
       const int64_t col = col0 + wn + 32 * j + lx;

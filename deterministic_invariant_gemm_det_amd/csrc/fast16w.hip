@@ -443,9 +443,11 @@ __global__ void __launch_bounds__(64 * WR * WC, 8 / (WR * WC)) fast16w_kernel(Ge
   stage(nst - 1, std::true_type{});
 
   const int lr = lane & 31, lh = lane >> 5;
-  if (args.partial) {
-    // split reduction: this chunk's f32 partials, 16 bytes (4 columns) per store
-    float* __restrict__ P = args.partial + static_cast<int64_t>(chunk) * args.rows * args.cols;
+  if (args.partial || args.out_f32) {
+    // split reduction: this chunk's f32 partials; f32 output: the accumulators
+    // themselves (no bias in dW); 16 bytes (4 columns) per store
+    float* __restrict__ P = args.partial ? args.partial + static_cast<int64_t>(chunk) * args.rows * args.cols
+                                         : static_cast<float*>(args.out);
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
       const int64_t row = row0 + wm + 32 * i + lr;
@@ -588,6 +590,7 @@ template <typename E>
 __global__ void __launch_bounds__(256) combine_kernel(const float* __restrict__ P, int split, int64_t count,
                                                       typename E::T* __restrict__ out, bool vec) {
   using T = typename E::T;
+  static_assert(sizeof(T) == 2 || sizeof(T) == 4, "16- or 32-bit output");
   const int64_t i0 = (static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x) * 8;
   if (i0 >= count) return;
   if (vec && i0 + 8 <= count) {
@@ -601,13 +604,18 @@ __global__ void __launch_bounds__(256) combine_kernel(const float* __restrict__ 
 #pragma unroll
       for (int e = 0; e < 4; ++e) { acc[e] = acc[e] + __uint_as_float(b0[e]); acc[4 + e] = acc[4 + e] + __uint_as_float(b1[e]); }
     }
-    uint16_t v[8];
+    if constexpr (sizeof(T) == 2) {
+      uint16_t v[8];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) v[e] = __builtin_bit_cast(uint16_t, round_from_f32<E>(acc[e]));
-    v4u w;
+      for (int e = 0; e < 8; ++e) v[e] = __builtin_bit_cast(uint16_t, round_from_f32<E>(acc[e]));
+      v4u w;
 #pragma unroll
-    for (int e = 0; e < 4; ++e) w[e] = static_cast<uint32_t>(v[2 * e]) | (static_cast<uint32_t>(v[2 * e + 1]) << 16);
-    *reinterpret_cast<v4u*>(out + i0) = w;
+      for (int e = 0; e < 4; ++e) w[e] = static_cast<uint32_t>(v[2 * e]) | (static_cast<uint32_t>(v[2 * e + 1]) << 16);
+      *reinterpret_cast<v4u*>(out + i0) = w;
+    } else {
+      *reinterpret_cast<v4u*>(out + i0) = v4u{__float_as_uint(acc[0]), __float_as_uint(acc[1]), __float_as_uint(acc[2]), __float_as_uint(acc[3])};
+      *reinterpret_cast<v4u*>(out + i0 + 4) = v4u{__float_as_uint(acc[4]), __float_as_uint(acc[5]), __float_as_uint(acc[6]), __float_as_uint(acc[7])};
+    }
     return;
   }
   for (int64_t i = i0; i < i0 + 8 && i < count; ++i) {
@@ -619,12 +627,15 @@ __global__ void __launch_bounds__(256) combine_kernel(const float* __restrict__ 
 
 }  // namespace w8
 
-hipError_t launch_combine(Dt dt, const float* partial, int split, int64_t count, void* out, hipStream_t stream) {
+hipError_t launch_combine(Dt dt, bool out_f32, const float* partial, int split, int64_t count, void* out,
+                          hipStream_t stream) {
   const int64_t blocks = (count + 256 * 8 - 1) / (256 * 8);
   if (blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
   const bool vec = count % 4 == 0 && reinterpret_cast<uintptr_t>(out) % 16 == 0;
   const dim3 grid(static_cast<unsigned>(blocks)), block(256);
-  if (dt == DT_BF16)
+  if (out_f32)
+    hipLaunchKernelGGL(w8::combine_kernel<F32>, grid, block, 0, stream, partial, split, count, static_cast<float*>(out), vec);
+  else if (dt == DT_BF16)
     hipLaunchKernelGGL(w8::combine_kernel<BF16>, grid, block, 0, stream, partial, split, count, static_cast<uint16_t*>(out), vec);
   else if (dt == DT_F16)
     hipLaunchKernelGGL(w8::combine_kernel<F16>, grid, block, 0, stream, partial, split, count, static_cast<_Float16*>(out), vec);

@@ -117,6 +117,34 @@ det_status_t det_gemm_dw(void* dw, const void* x, const void* dy,
                          int64_t m, int64_t k, int64_t n,
                          det_dtype_t dt, det_tier_t tier, hipStream_t stream);
 
+/*
+ * Weight gradient with an explicit output dtype: as det_gemm_dw, with dw of
+ * dtype dw_dt, which must be dt or DET_F32 (f32 gradients for bf16/f16
+ * training against f32 master weights: Carbon README, alia-carbon 0.2.0,
+ * "Roadmap", v0.3 mixed precision). The tier's wide value is
+ * rounded once to dw_dt: the exact tier's float64 compensated sum to f32, the
+ * fast tier's f32 accumulation (after the ordered chunk combine when the
+ * reduction is split) stored as is. dw is k x n, row-major, in dw_dt.
+ * DET_EDTYPE for any other dw_dt.
+ */
+det_status_t det_gemm_dw_out(void* dw, det_dtype_t dw_dt, const void* x, const void* dy,
+                             int64_t m, int64_t k, int64_t n,
+                             det_dtype_t dt, det_tier_t tier, hipStream_t stream);
+
+/*
+ * Bias gradient: db[n] = sum over i < m of dy[i, n] (sgemm-bi 0.1.2 PyPI page,
+ * note after "Determinism contracts": a column sum of dY, which that engine
+ * leaves to the framework). Defined here as the exact tier's
+ * det_gemm_dw of a column of ones -- rows in tiles of 32, an ascending
+ * float64 chain per tile, Neumaier across tiles, one rounding to db_dt (dt or
+ * DET_F32) -- and computed with that arithmetic in both tiers: the operation
+ * is bound by memory, so the exact sum costs nothing extra. dy is m x n,
+ * row-major, dtype dt; db has n elements of db_dt. Same errors as the other
+ * entry points (DET_EDTYPE for a db_dt other than dt and DET_F32).
+ */
+det_status_t det_gemm_db(void* db, det_dtype_t db_dt, const void* dy, int64_t m, int64_t n,
+                         det_dtype_t dt, det_tier_t tier, hipStream_t stream);
+
 /* Static description of a status code. */
 const char* det_gemm_strerror(det_status_t status);
 

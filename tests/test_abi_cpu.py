@@ -76,3 +76,26 @@ def test_no_device_is_refused_cleanly():
     p = 0x1000
     assert L.det_gemm_fwd(p, p, p, None, 4, 4, 4, 0, 0, None) == -4
     assert dg.det_gemm_last_error()
+
+
+def test_dw_out_and_db_argument_checks():
+    L = dg.lib()
+    p = 0x1000  # never dereferenced: every call below is rejected before launch
+    F32, BF16, F16 = 0, 1, 2
+    # the output dtype is the input dtype or f32; nothing else
+    assert L.det_gemm_dw_out(p, F16, p, p, 4, 4, 4, BF16, 0, None) == -2
+    assert L.det_gemm_dw_out(p, BF16, p, p, 4, 4, 4, F32, 0, None) == -2
+    assert L.det_gemm_dw_out(p, 7, p, p, 4, 4, 4, BF16, 0, None) == -2
+    assert L.det_gemm_dw_out(None, F32, p, p, 4, 4, 4, BF16, 0, None) == -1
+    assert L.det_gemm_dw_out(p, F32, p, p, 0, 4, 4, BF16, 0, None) == -1
+    assert L.det_gemm_dw_out(p, F32, p, p, 4, 4, 4, BF16, 5, None) == -3
+    assert L.det_gemm_db(p, F16, p, 4, 4, BF16, 0, None) == -2
+    assert L.det_gemm_db(p, BF16, p, 4, 4, F16, 0, None) == -2
+    assert L.det_gemm_db(p, F32, p, 4, 4, 9, 0, None) == -2
+    assert L.det_gemm_db(p, F32, p, 4, 4, BF16, 2, None) == -3
+    assert L.det_gemm_db(None, F32, p, 4, 4, BF16, 0, None) == -1
+    assert L.det_gemm_db(p, F32, None, 4, 4, BF16, 0, None) == -1
+    assert L.det_gemm_db(p, F32, p, 0, 4, BF16, 0, None) == -1
+    assert L.det_gemm_db(p, F32, p, 4, -3, BF16, 0, None) == -1
+    assert L.det_gemm_db(p, F32, p, 1 << 40, 1 << 40, BF16, 0, None) == -1
+    assert "dtype" in dg.det_gemm_last_error() or dg.det_gemm_last_error()

@@ -4,9 +4,10 @@ the method's error bound, the hand-derived order witnesses laid along a column,
 and a brute-force f32 rounding.
 
 db[n] = sum_i dy[i, n] is the dW of a column of ones (the reduction over i in
-tiles of 32 rows, Neumaier across tiles; sgemm-bi 0.1.2 PyPI page, "Use":
-the bias gradient is the column sum of dY). dW for f32 master weights is the
-same float64 value rounded once to f32 instead of the input dtype.
+tiles of 32 rows, Neumaier across tiles; sgemm-bi 0.1.2 PyPI page, note after
+"Determinism contracts": the bias gradient is a column sum of dY). dW for f32
+master weights (Carbon README, "Roadmap", v0.3 mixed precision) is the same
+float64 value rounded once to f32 instead of the input dtype.
 """
 from fractions import Fraction
 
