@@ -14,6 +14,7 @@ import os
 __all__ = [
     "det_gemm_fwd", "det_gemm_dx", "det_gemm_dw", "det_gemm_dw_out", "det_gemm_db", "det_gemm_strerror",
     "det_gemm_last_error", "det_gemm_version", "det_gemm_debug_force_family", "det_gemm_debug_force_exact_kernel",
+    "det_gemm_debug_force_db_chunk",
     "DetGemmError", "LIB_PATH", "fwd", "dx", "dw", "db", "deterministic_linear", "Linear", "DTYPES", "TIERS",
 ]
 
@@ -66,6 +67,8 @@ def lib():
         L.det_gemm_debug_force_family.restype = ci
         L.det_gemm_debug_force_exact_kernel.argtypes = [ci]
         L.det_gemm_debug_force_exact_kernel.restype = ci
+        L.det_gemm_debug_force_db_chunk.argtypes = [i64]
+        L.det_gemm_debug_force_db_chunk.restype = ci
         _lib = L
     return _lib
 
@@ -136,6 +139,10 @@ def det_gemm_debug_force_family(family):
 
 def det_gemm_debug_force_exact_kernel(variant):
     _check(lib().det_gemm_debug_force_exact_kernel(variant))
+
+
+def det_gemm_debug_force_db_chunk(tiles):
+    _check(lib().det_gemm_debug_force_db_chunk(tiles))
 
 
 # ---------------------------------------------------------------- torch layer

@@ -18,6 +18,7 @@ namespace {
 thread_local char g_last_error[256] = "";
 std::atomic<int> g_force_family{-1};
 std::atomic<int> g_force_exact{-1};
+std::atomic<int64_t> g_force_db_chunk{0};
 
 constexpr int kMaxDevices = 64;
 // 0 unknown, 1 gfx950, 2 not supported
@@ -196,7 +197,7 @@ det_status_t det_gemm_db(void* db, det_dtype_t db_dt, const void* dy, int64_t m,
   const det_status_t dev = check_device(&cus);
   if (dev != DET_OK) return dev;
   const hipError_t err = detgemm::launch_db(static_cast<detgemm::Dt>(dt), db_dt == DET_F32 && dt != DET_F32, dy, m, n,
-                                            db, stream);
+                                            db, g_force_db_chunk.load(std::memory_order_relaxed), stream);
   if (err != hipSuccess) return fail(DET_ELAUNCH, "det_gemm: kernel launch failed: %s", hipGetErrorString(err));
   return DET_OK;
 }
@@ -227,6 +228,12 @@ det_status_t det_gemm_debug_force_family(int family) {
 det_status_t det_gemm_debug_force_exact_kernel(int variant) {
   if (variant < -1 || variant > 4) return fail(DET_EINVAL, "det_gemm: exact kernel must be -1 .. 4%s");
   g_force_exact.store(variant, std::memory_order_relaxed);
+  return DET_OK;
+}
+
+det_status_t det_gemm_debug_force_db_chunk(int64_t tiles) {
+  if (tiles < 0) return fail(DET_EINVAL, "det_gemm: db chunk must be >= 0%s");
+  g_force_db_chunk.store(tiles, std::memory_order_relaxed);
   return DET_OK;
 }
 

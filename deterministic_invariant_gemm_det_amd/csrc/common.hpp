@@ -108,7 +108,9 @@ int fast_dw_split(int64_t m, int64_t k, int64_t n, int* chunk_stages);
 hipError_t launch_combine(Dt dt, bool out_f32, const float* partial, int split, int64_t count, void* out,
                           hipStream_t stream);
 // db[n] = sum_i dy[i, n] with the exact tier's arithmetic (the dW of a column of ones).
-hipError_t launch_db(Dt dt, bool out_f32, const void* dy, int64_t m, int64_t n, void* db, hipStream_t stream);
+// chunk_tiles > 0 forces the tiles per chunk of the column sum (bits unchanged)
+hipError_t launch_db(Dt dt, bool out_f32, const void* dy, int64_t m, int64_t n, void* db, int64_t chunk_tiles,
+                     hipStream_t stream);
 // A device workspace of at least `bytes` owned by the library for (current device, stream);
 // grown on demand, kept for later calls on the same stream.
 hipError_t stream_workspace(hipStream_t stream, size_t bytes, void** ptr);

@@ -40,8 +40,10 @@
  *
  * Ownership and execution
  *   The caller owns every buffer. The library keeps no reference to any of them
- *   and allocates no device memory per call, with one exception: the fast
- *   tier's split dW (above) needs S * k * n * 4 bytes of f32 partials; the
+ *   and allocates no device memory per call, with two exceptions: the fast
+ *   tier's split dW (above) needs S * k * n * 4 bytes of f32 partials, and
+ *   det_gemm_db needs the float64 tile partials of up to max(2^23, 128 * n)
+ *   values (m / 32 * n of them when that is less) plus 2 * n; the
  *   library keeps one such workspace per (device, stream), allocated on first
  *   need and grown (after synchronising that stream) when a larger one is
  *   needed, and never frees it. Calls on one stream share it in stream order,
@@ -138,9 +140,10 @@ det_status_t det_gemm_dw_out(void* dw, det_dtype_t dw_dt, const void* x, const v
  * det_gemm_dw of a column of ones -- rows in tiles of 32, an ascending
  * float64 chain per tile, Neumaier across tiles, one rounding to db_dt (dt or
  * DET_F32) -- and computed with that arithmetic in both tiers: the operation
- * is bound by memory, so the exact sum costs nothing extra. dy is m x n,
- * row-major, dtype dt; db has n elements of db_dt. Same errors as the other
- * entry points (DET_EDTYPE for a db_dt other than dt and DET_F32).
+ * is bound by memory, so the exact sum costs nothing extra. The tile partials
+ * go through the stream's workspace (see "Ownership and execution"). dy is
+ * m x n, row-major, dtype dt; db has n elements of db_dt. Same errors as the
+ * other entry points (DET_EDTYPE for a db_dt other than dt and DET_F32).
  */
 det_status_t det_gemm_db(void* db, det_dtype_t db_dt, const void* dy, int64_t m, int64_t n,
                          det_dtype_t dt, det_tier_t tier, hipStream_t stream);
@@ -174,6 +177,14 @@ det_status_t det_gemm_debug_force_family(int family);
  * changes speed only. Returns DET_EINVAL for other values.
  */
 det_status_t det_gemm_debug_force_exact_kernel(int variant);
+
+/*
+ * Test hook: force the number of 32-row tiles per chunk of det_gemm_db for
+ * later calls from any thread (0 = automatic: as many as fit 64 MiB of
+ * float64 partials, at least 128). The chunks only bound the workspace; the
+ * sum and its bits do not depend on them. Returns DET_EINVAL for tiles < 0.
+ */
+det_status_t det_gemm_debug_force_db_chunk(int64_t tiles);
 
 #ifdef __cplusplus
 }

@@ -18,8 +18,10 @@ DB_SHAPES = [(1, 1), (31, 5), (32, 33), (33, 70), (200, 130), (1000, 3), (8300, 
 def _auto_family():
     import deterministic_invariant_gemm_det_amd as dg
     dg.det_gemm_debug_force_family(-1)
+    dg.det_gemm_debug_force_db_chunk(0)
     yield
     dg.det_gemm_debug_force_family(-1)
+    dg.det_gemm_debug_force_db_chunk(0)
 
 
 def _db_gpu(G, dt, out_dt, tier):
@@ -41,6 +43,35 @@ def test_db_bit_exact(dt):
             want, _, _ = oracle.db(dt, G, out_dt=out_dt)
             for tier in ("exact", "fast"):
                 assert_bits_equal(_db_gpu(G, dt, out_dt, tier), want, f"db {dt}->{out_dt} {tier} {(m, n)}")
+
+
+@pytest.mark.parametrize("chunk", [1, 3, 128])
+def test_db_chunked(chunk):
+    """Tiles handled in several chunks (the pass state carried between them) give the same bits."""
+    import deterministic_invariant_gemm_det_amd as dg
+    m, n = 8300, 260   # 260 tiles, the last one short
+    G = syn.normal(1440, syn.TID_DY, (m, n), dt="bf16")
+    want, _, _ = oracle.db("bf16", G, out_dt="f32")
+    dg.det_gemm_debug_force_db_chunk(chunk)
+    assert_bits_equal(_db_gpu(G, "bf16", "f32", "exact"), want, f"db chunk {chunk}")
+
+
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+def test_db_unaligned_base(dt):
+    """dY starting one element past an aligned address takes the per-element load path."""
+    import torch
+    import deterministic_invariant_gemm_det_amd as dg
+    from tests.gpu_util import torch_dtype
+    m, n = 100, 64
+    G = syn.normal(1445, syn.TID_DY, (m, n), dt=dt)
+    want, _, _ = oracle.db(dt, G)
+    flat = to_dev(np.concatenate([G.reshape(-1)[:1], G.reshape(-1)]), dt)
+    g = flat[1:].view(m, n)
+    assert g.data_ptr() % 16 != 0
+    out = dg.db(g, "exact")
+    torch.cuda.synchronize()
+    assert_bits_equal(to_host(out, dt), want, f"db unaligned {dt}")
+    assert out.dtype == torch_dtype(dt)
 
 
 def test_db_integer_columns():
