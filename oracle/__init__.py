@@ -34,6 +34,11 @@ class Oracle:
         L.oracle_round.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_void_p]
         L.oracle_env_ok.restype = ctypes.c_int
         L.oracle_version.restype = ctypes.c_int
+        vp, i64 = ctypes.c_void_p, ctypes.c_int64
+        L.oracle_layernorm_fwd.restype = ctypes.c_int
+        L.oracle_layernorm_fwd.argtypes = [ctypes.c_int, vp, vp, vp, i64, i64, ctypes.c_double, vp, vp, vp, vp]
+        L.oracle_layernorm_bwd.restype = ctypes.c_int
+        L.oracle_layernorm_bwd.argtypes = [ctypes.c_int, ctypes.c_int, vp, vp, vp, vp, vp, i64, i64, vp, vp, vp, vp]
         if L.oracle_env_ok() != 1:
             raise RuntimeError("oracle: floating-point environment is not IEEE RNE without FTZ/DAZ")
         self.L = L
@@ -96,6 +101,44 @@ class Oracle:
         y = self.round_to(out_dt or dt, r[0])
         return y, (r[0] if want_r else None), (S[0] if want_S else None)
 
+    def layernorm_fwd(self, dt, x, gamma=None, beta=None, eps=1e-5, want_r=False):
+        """LayerNorm over the last dim of x[rows, h] with float64 statistics (the row sums are
+        the matmul's tiled compensated sum). Returns (y, mean, rstd, r or None)."""
+        rows, h = x.shape
+        _check(x, dt, (rows, h), "x")
+        for v, name in ((gamma, "gamma"), (beta, "beta")):
+            if v is not None:
+                _check(v, dt, (h,), name)
+        y = np.zeros((rows, h), dtype=STORAGE[dt])
+        mean = np.zeros(rows)
+        rstd = np.zeros(rows)
+        r = np.zeros((rows, h)) if want_r else None
+        if self.L.oracle_layernorm_fwd(DTYPES[dt], _ptr(x), _ptr(gamma), _ptr(beta), rows, h, float(eps),
+                                       _ptr(y), _ptr(mean), _ptr(rstd), _ptr(r)) != 0:
+            raise ValueError("oracle_layernorm_fwd rejected its arguments")
+        return y, mean, rstd, r
+
+    def layernorm_bwd(self, dt, dy, x, mean, rstd, gamma=None, pdt=None, want_r=False):
+        """Gradients of layernorm_fwd: (dx in dt, dgamma and dbeta in pdt (default dt), r of dx or None)."""
+        rows, h = x.shape
+        _check(x, dt, (rows, h), "x")
+        _check(dy, dt, (rows, h), "dy")
+        if gamma is not None:
+            _check(gamma, dt, (h,), "gamma")
+        mean = np.ascontiguousarray(mean, dtype=np.float64)
+        rstd = np.ascontiguousarray(rstd, dtype=np.float64)
+        if mean.shape != (rows,) or rstd.shape != (rows,):
+            raise ValueError("oracle: mean and rstd must have one value per row")
+        pdt = pdt or dt
+        dx = np.zeros((rows, h), dtype=STORAGE[dt])
+        dg = np.zeros(h, dtype=STORAGE[pdt])
+        dbt = np.zeros(h, dtype=STORAGE[pdt])
+        r = np.zeros((rows, h)) if want_r else None
+        if self.L.oracle_layernorm_bwd(DTYPES[dt], DTYPES[pdt], _ptr(dy), _ptr(x), _ptr(mean), _ptr(rstd),
+                                       _ptr(gamma), rows, h, _ptr(dx), _ptr(dg), _ptr(dbt), _ptr(r)) != 0:
+            raise ValueError("oracle_layernorm_bwd rejected its arguments")
+        return dx, dg, dbt, r
+
     def round_to(self, dt, r):
         """Single RNE rounding of float64 values to dt (raw storage out)."""
         r = np.ascontiguousarray(r, dtype=np.float64)
@@ -153,3 +196,11 @@ def dw_out(*a, **kw):
 
 def db(*a, **kw):
     return default().db(*a, **kw)
+
+
+def layernorm_fwd(*a, **kw):
+    return default().layernorm_fwd(*a, **kw)
+
+
+def layernorm_bwd(*a, **kw):
+    return default().layernorm_bwd(*a, **kw)

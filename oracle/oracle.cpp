@@ -36,6 +36,10 @@
 //
 // Alongside each output the oracle can return r (the float64 value before the
 // downcast) and S = sum |a_k * b_k| + |b_j|, which bound the fast tier's error.
+//
+// LayerNorm (Carbon README, "How It Works", the LayerNorm row: mean and
+// variance in float64 instead of a thread-dependent parallel reduction) is
+// defined on top of the same summation; see oracle_layernorm_fwd/_bwd below.
 
 #include <cfenv>
 #include <cmath>
@@ -186,7 +190,7 @@ double kbn_dot(const double* a, const double* b, int64_t L, double* S) {
 
 extern "C" {
 
-int oracle_version(void) { return 1; }
+int oracle_version(void) { return 2; }
 
 // 1 when the floating-point environment is the IEEE default this oracle needs:
 // round-to-nearest-even, no flush-to-zero, no denormals-are-zero.
@@ -266,4 +270,104 @@ int oracle_gemm(int op, int dt, const void* A, const void* B, const void* bias,
   return 0;
 }
 
+
+// ---- LayerNorm over the last dimension, float64 statistics ------------------
+//
+// Readings (the page gives only "float64 mean and variance"):
+//   * every row sum is the matmul's tiled, compensated, fixed-order sum:
+//     kbn_dot(v, ones) for a plain sum (fma(v, 1, p) = p + v, one rounding)
+//     and kbn_dot(u, v) for a sum of products;
+//   * mean = sum(x) / H; d_j = x_j - mean; var = sum(d_j * d_j) / H (the
+//     biased variance, as a LayerNorm normalises); rstd = 1 / sqrt(var + eps);
+//   * y_j = (d_j * rstd) * gamma_j + beta_j in float64, one rounding per
+//     operation and no fusion; gamma or beta absent: that operation is
+//     skipped; then one RNE rounding to the output dtype.
+// Backward, with xhat_j = d_j * rstd (d_j recomputed from the stored mean) and
+// g_j = dy_j * gamma_j (exact; g = dy without gamma):
+//     a = sum(g) / H, b = sum(g_j * xhat_j) / H,
+//     dx_j = rstd * ((g_j - a) - xhat_j * b)        then one rounding,
+//     dgamma_j = sum over rows i of dy_ij * xhat_ij  (rows in tiles of 32, KBN),
+//     dbeta_j  = sum over rows i of dy_ij            (the same column sum),
+// which is the derivative of the forward's real-number definition.
+
+namespace {
+
+// mean, rstd and the float64 d_j of one row
+void ln_stats(const void* x, int64_t row, int64_t h, double eps, int dt, std::vector<double>& d,
+              double* mean, double* rstd) {
+  std::vector<double> ones(static_cast<size_t>(h), 1.0);
+  d.resize(static_cast<size_t>(h));
+  for (int64_t j = 0; j < h; ++j) d[j] = decode(x, row * h + j, dt);
+  double S;
+  const double mu = kbn_dot(d.data(), ones.data(), h, &S) / static_cast<double>(h);
+  for (int64_t j = 0; j < h; ++j) d[j] = d[j] - mu;
+  const double var = kbn_dot(d.data(), d.data(), h, &S) / static_cast<double>(h);
+  *mean = mu;
+  *rstd = 1.0 / std::sqrt(var + eps);
+}
+
+}  // namespace
+
+// Forward. x: rows x h in dt; gamma, beta: h in dt, nullable; y: rows x h in dt.
+// mean, rstd: nullable float64[rows]; r: nullable float64 rows x h (y before rounding).
+// Returns 0, or -1 on invalid arguments.
+int oracle_layernorm_fwd(int dt, const void* x, const void* gamma, const void* beta, int64_t rows,
+                         int64_t h, double eps, void* y, double* mean, double* rstd, double* r) {
+  if (dt < DT_F32 || dt > DT_F16 || rows < 1 || h < 1 || !x || !y || !(eps >= 0.0)) return -1;
+  std::vector<double> d;
+  for (int64_t i = 0; i < rows; ++i) {
+    double mu, rs;
+    ln_stats(x, i, h, eps, dt, d, &mu, &rs);
+    if (mean) mean[i] = mu;
+    if (rstd) rstd[i] = rs;
+    for (int64_t j = 0; j < h; ++j) {
+      double v = d[j] * rs;
+      if (gamma) v = v * decode(gamma, j, dt);
+      if (beta) v = v + decode(beta, j, dt);
+      store(y, i * h + j, v, dt);
+      if (r) r[i * h + j] = v;
+    }
+  }
+  return 0;
+}
+
+// Backward. dy, x: rows x h in dt; mean, rstd: float64[rows] from the forward;
+// gamma: h in dt, nullable. dx: rows x h in dt (nullable); dgamma, dbeta: h in
+// pdt (dt or f32), nullable; rdx: nullable float64 rows x h (dx before rounding).
+int oracle_layernorm_bwd(int dt, int pdt, const void* dy, const void* x, const double* mean,
+                         const double* rstd, const void* gamma, int64_t rows, int64_t h, void* dx,
+                         void* dgamma, void* dbeta, double* rdx) {
+  if (dt < DT_F32 || dt > DT_F16 || (pdt != dt && pdt != DT_F32)) return -1;
+  if (rows < 1 || h < 1 || !dy || !x || !mean || !rstd) return -1;
+  const double H = static_cast<double>(h);
+  std::vector<double> xhat(static_cast<size_t>(h)), g(static_cast<size_t>(h));
+  std::vector<double> ones(static_cast<size_t>(std::max(h, rows)), 1.0);
+  std::vector<double> colx(static_cast<size_t>(rows * h)), coly(static_cast<size_t>(rows * h));
+  for (int64_t i = 0; i < rows; ++i) {
+    for (int64_t j = 0; j < h; ++j) {
+      const double dyv = decode(dy, i * h + j, dt);
+      xhat[j] = (decode(x, i * h + j, dt) - mean[i]) * rstd[i];
+      g[j] = gamma ? dyv * decode(gamma, j, dt) : dyv;
+      colx[j * rows + i] = xhat[j];   // column-major copies for the sums over rows
+      coly[j * rows + i] = dyv;
+    }
+    if (!dx) continue;
+    double S;
+    const double a = kbn_dot(g.data(), ones.data(), h, &S) / H;
+    const double b = kbn_dot(g.data(), xhat.data(), h, &S) / H;
+    for (int64_t j = 0; j < h; ++j) {
+      const double v = rstd[i] * ((g[j] - a) - xhat[j] * b);
+      store(dx, i * h + j, v, dt);
+      if (rdx) rdx[i * h + j] = v;
+    }
+  }
+  for (int64_t j = 0; j < h; ++j) {
+    double S;
+    if (dgamma) store(dgamma, j, kbn_dot(&coly[j * rows], &colx[j * rows], rows, &S), pdt);
+    if (dbeta) store(dbeta, j, kbn_dot(&coly[j * rows], ones.data(), rows, &S), pdt);
+  }
+  return 0;
+}
+
 }  // extern "C"
+
