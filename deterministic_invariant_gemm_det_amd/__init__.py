@@ -16,6 +16,7 @@ __all__ = [
     "det_gemm_last_error", "det_gemm_version", "det_gemm_debug_force_family", "det_gemm_debug_force_exact_kernel",
     "det_gemm_debug_force_db_chunk",
     "DetGemmError", "LIB_PATH", "fwd", "dx", "dw", "db", "deterministic_linear", "Linear", "DTYPES", "TIERS",
+    "det_layernorm_fwd", "det_layernorm_bwd", "layer_norm", "layer_norm_backward", "deterministic_layer_norm",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -56,7 +57,10 @@ def lib():
         L.det_gemm_dw.argtypes = [vp, vp, vp, i64, i64, i64, ci, ci, vp]
         L.det_gemm_dw_out.argtypes = [vp, ci, vp, vp, i64, i64, i64, ci, ci, vp]
         L.det_gemm_db.argtypes = [vp, ci, vp, i64, i64, ci, ci, vp]
-        for f in (L.det_gemm_fwd, L.det_gemm_dx, L.det_gemm_dw, L.det_gemm_dw_out, L.det_gemm_db):
+        L.det_layernorm_fwd.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, ctypes.c_double, ci, vp]
+        L.det_layernorm_bwd.argtypes = [vp, vp, vp, ci, vp, vp, vp, vp, vp, i64, i64, ci, vp]
+        for f in (L.det_gemm_fwd, L.det_gemm_dx, L.det_gemm_dw, L.det_gemm_dw_out, L.det_gemm_db,
+                  L.det_layernorm_fwd, L.det_layernorm_bwd):
             f.restype = ci
         L.det_gemm_strerror.argtypes = [ci]
         L.det_gemm_strerror.restype = ctypes.c_char_p
@@ -119,6 +123,16 @@ def det_gemm_dw_out(dw_, dw_dtype, x, dy, m, k, n, dtype, tier, stream=0):
 def det_gemm_db(db_, db_dtype, dy, m, n, dtype, tier, stream=0):
     _check(lib().det_gemm_db(_p(db_), _code(DTYPES, db_dtype, "dtype"), _p(dy), m, n,
                              _code(DTYPES, dtype, "dtype"), _code(TIERS, tier, "tier"), _p(stream)))
+
+
+def det_layernorm_fwd(y, mean, rstd, x, gamma, beta, rows, h, eps, dtype, stream=0):
+    _check(lib().det_layernorm_fwd(_p(y), _p(mean), _p(rstd), _p(x), _p(gamma), _p(beta), rows, h, float(eps),
+                                   _code(DTYPES, dtype, "dtype"), _p(stream)))
+
+
+def det_layernorm_bwd(dx, dgamma, dbeta, param_dtype, dy, x, mean, rstd, gamma, rows, h, dtype, stream=0):
+    _check(lib().det_layernorm_bwd(_p(dx), _p(dgamma), _p(dbeta), _code(DTYPES, param_dtype, "dtype"), _p(dy), _p(x),
+                                   _p(mean), _p(rstd), _p(gamma), rows, h, _code(DTYPES, dtype, "dtype"), _p(stream)))
 
 
 def det_gemm_strerror(status):
@@ -235,6 +249,41 @@ def db(dy, tier="exact", out=None, out_dtype=None):
     return g
 
 
+def layer_norm(x, gamma=None, beta=None, eps=1e-5, out=None):
+    """LayerNorm over the last dim of x[rows, h] with float64 statistics on the current stream.
+    Returns (y, mean, rstd); mean and rstd are float64 [rows] for layer_norm_backward."""
+    import torch
+    (x, gamma, beta), stream = _prep(x, gamma, beta)
+    rows, h = x.shape
+    for v in (gamma, beta):
+        if v is not None and tuple(v.shape) != (h,):
+            raise ValueError("gamma and beta must have h elements")
+    y = out if out is not None else torch.empty_like(x)
+    if y.dtype != x.dtype or not y.is_contiguous() or tuple(y.shape) != (rows, h):
+        raise ValueError("out must be a contiguous tensor like x")
+    mean = torch.empty(rows, dtype=torch.float64, device=x.device)
+    rstd = torch.empty(rows, dtype=torch.float64, device=x.device)
+    det_layernorm_fwd(y, mean, rstd, x, gamma, beta, rows, h, eps, _torch_dtype_name(x), stream)
+    return y, mean, rstd
+
+
+def layer_norm_backward(dy, x, mean, rstd, gamma=None, param_dtype=None, need_dx=True, need_params=True):
+    """(dx, dgamma, dbeta) of layer_norm; dgamma/dbeta in param_dtype (x's dtype or torch.float32)."""
+    import torch
+    (dy, x, gamma), stream = _prep(dy, x, gamma)
+    rows, h = x.shape
+    if tuple(dy.shape) != (rows, h) or mean.dtype != torch.float64 or rstd.dtype != torch.float64:
+        raise ValueError("dy must match x; mean and rstd must be float64")
+    mean, rstd = mean.contiguous(), rstd.contiguous()
+    pdt = param_dtype or x.dtype
+    gx = torch.empty_like(x) if need_dx else None
+    gg = torch.empty(h, dtype=pdt, device=x.device) if need_params and gamma is not None else None
+    gb = torch.empty(h, dtype=pdt, device=x.device) if need_params else None
+    det_layernorm_bwd(gx, gg, gb, _torch_dtype_name(gb if gb is not None else x), dy, x, mean, rstd, gamma,
+                      rows, h, _torch_dtype_name(x), stream)
+    return gx, gg, gb
+
+
 def _autograd_fn():
     import torch
 
@@ -261,6 +310,38 @@ def _autograd_fn():
 
 
 _FN = None
+_LN = None
+
+
+def _ln_fn():
+    import torch
+
+    class DeterministicLayerNormFn(torch.autograd.Function):
+        @staticmethod
+        def forward(ctx, x, gamma, beta, eps):
+            y, mean, rstd = layer_norm(x, gamma, beta, eps)
+            ctx.save_for_backward(x, gamma, mean, rstd)
+            ctx.has_beta = beta is not None
+            return y
+
+        @staticmethod
+        def backward(ctx, gy):
+            x, gamma, mean, rstd = ctx.saved_tensors
+            need_params = ctx.needs_input_grad[1] or ctx.needs_input_grad[2]
+            gx, gg, gb = layer_norm_backward(gy.contiguous(), x, mean, rstd, gamma,
+                                             need_dx=ctx.needs_input_grad[0], need_params=need_params)
+            return gx, gg, (gb if ctx.has_beta else None), None
+
+    return DeterministicLayerNormFn
+
+
+def deterministic_layer_norm(x, gamma=None, beta=None, eps=1e-5):
+    """LayerNorm over the last dim (leading dims flattened) with float64 statistics, differentiable."""
+    global _LN
+    if _LN is None:
+        _LN = _ln_fn()
+    lead = x.shape[:-1]
+    return _LN.apply(x.reshape(-1, x.shape[-1]), gamma, beta, eps).reshape(*lead, x.shape[-1])
 
 
 def deterministic_linear(x, weight, bias=None, tier="exact"):

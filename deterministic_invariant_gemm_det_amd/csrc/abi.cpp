@@ -202,6 +202,45 @@ det_status_t det_gemm_db(void* db, det_dtype_t db_dt, const void* dy, int64_t m,
   return DET_OK;
 }
 
+det_status_t det_layernorm_fwd(void* y, double* mean, double* rstd, const void* x, const void* gamma,
+                               const void* beta, int64_t rows, int64_t h, double eps, det_dtype_t dt,
+                               hipStream_t stream) {
+  g_last_error[0] = '\0';
+  if (dt != DET_F32 && dt != DET_BF16 && dt != DET_F16) return fail(DET_EDTYPE, "det_layernorm: unknown dtype%s");
+  if (!y || !x) return fail(DET_EINVAL, "det_layernorm: null %s pointer", !y ? "output" : "input");
+  if (rows < 1 || h < 1 || h > DET_LAYERNORM_MAX_H)
+    return fail(DET_EINVAL, "det_layernorm: rows must be >= 1 and h in 1 .. 65536%s");
+  if (!(eps >= 0.0) || eps > 1e300) return fail(DET_EINVAL, "det_layernorm: eps must be finite and >= 0%s");
+  if (!mul_ok(rows, h, dt == DET_F32 ? 4 : 2)) return fail(DET_EINVAL, "det_layernorm: tensor size overflows int64%s");
+  int cus = 0;
+  const det_status_t dev = check_device(&cus);
+  if (dev != DET_OK) return dev;
+  const hipError_t err = detgemm::launch_layernorm_fwd(static_cast<detgemm::Dt>(dt), x, gamma, beta, rows, h, eps, y,
+                                                       mean, rstd, stream);
+  if (err != hipSuccess) return fail(DET_ELAUNCH, "det_layernorm: kernel launch failed: %s", hipGetErrorString(err));
+  return DET_OK;
+}
+
+det_status_t det_layernorm_bwd(void* dx, void* dgamma, void* dbeta, det_dtype_t param_dt, const void* dy,
+                               const void* x, const double* mean, const double* rstd, const void* gamma,
+                               int64_t rows, int64_t h, det_dtype_t dt, hipStream_t stream) {
+  g_last_error[0] = '\0';
+  if (dt != DET_F32 && dt != DET_BF16 && dt != DET_F16) return fail(DET_EDTYPE, "det_layernorm: unknown dtype%s");
+  if (param_dt != dt && param_dt != DET_F32)
+    return fail(DET_EDTYPE, "det_layernorm_bwd: the parameter-gradient dtype must be the input dtype or DET_F32%s");
+  if (!dy || !x || !mean || !rstd) return fail(DET_EINVAL, "det_layernorm_bwd: null %s pointer", "input");
+  if (rows < 1 || h < 1 || h > DET_LAYERNORM_MAX_H)
+    return fail(DET_EINVAL, "det_layernorm: rows must be >= 1 and h in 1 .. 65536%s");
+  if (!mul_ok(rows, h, dt == DET_F32 ? 4 : 2)) return fail(DET_EINVAL, "det_layernorm: tensor size overflows int64%s");
+  int cus = 0;
+  const det_status_t dev = check_device(&cus);
+  if (dev != DET_OK) return dev;
+  const hipError_t err = detgemm::launch_layernorm_bwd(static_cast<detgemm::Dt>(dt), param_dt == DET_F32 && dt != DET_F32,
+                                                       dy, x, mean, rstd, gamma, rows, h, dx, dgamma, dbeta, stream);
+  if (err != hipSuccess) return fail(DET_ELAUNCH, "det_layernorm: kernel launch failed: %s", hipGetErrorString(err));
+  return DET_OK;
+}
+
 const char* det_gemm_strerror(det_status_t status) {
   switch (status) {
     case DET_OK: return "success";

@@ -113,6 +113,12 @@ hipError_t launch_db(Dt dt, bool out_f32, const void* dy, int64_t m, int64_t n, 
                      hipStream_t stream);
 // A device workspace of at least `bytes` owned by the library for (current device, stream);
 // grown on demand, kept for later calls on the same stream.
+// LayerNorm over rows of h elements (h <= 65536), float64 statistics.
+hipError_t launch_layernorm_fwd(Dt dt, const void* x, const void* gamma, const void* beta, int64_t rows, int64_t h,
+                                double eps, void* y, double* mean, double* rstd, hipStream_t stream);
+hipError_t launch_layernorm_bwd(Dt dt, bool param_f32, const void* dy, const void* x, const double* mean,
+                                const double* rstd, const void* gamma, int64_t rows, int64_t h, void* dx,
+                                void* dgamma, void* dbeta, hipStream_t stream);
 hipError_t stream_workspace(hipStream_t stream, size_t bytes, void** ptr);
 
 }  // namespace detgemm

@@ -1,0 +1,471 @@
+// LayerNorm over the last dimension with float64 statistics (Carbon README,
+// alia-carbon 0.2.0, "How It Works", the LayerNorm row: mean and variance in
+// float64 instead of a parallel reduction whose order depends on the threads).
+// Every row sum is the matmul's exact-tier sum -- 32-element tiles, an
+// ascending float64 chain per tile from +0, Neumaier across tiles in order:
+//   mean = sum(x) / H;  d_j = x_j - mean;  var = sum(d_j * d_j) / H  (biased);
+//   rstd = 1 / sqrt(var + eps);
+//   y_j  = RNE((d_j * rstd) * gamma_j + beta_j)   (float64 steps, no fusion;
+//          an absent gamma or beta skips its step).
+// Backward, xhat_j = d_j * rstd (d_j from the stored mean), g_j = dy_j * gamma_j:
+//   a = sum(g) / H;  b = sum(g_j * xhat_j) / H;
+//   dx_j = RNE(rstd * ((g_j - a) - xhat_j * b));
+//   dgamma_j = sum_i dy_ij * xhat_ij,  dbeta_j = sum_i dy_ij  over rows i, in
+//   32-row tiles with Neumaier across them (the column sums of colsum.hpp).
+// Every float64 operation is IEEE-rounded (division and square root included),
+// so the results are the same bits on any device that follows the order.
+//
+// Row kernels: a row belongs to G = min(T, 64) lanes of one wave (T = tiles
+// per row); lane g owns tiles g, g + G, ... and keeps their values in
+// registers (up to TPL tiles, else it reads them again from memory). Each pass
+// writes the lane's tile partials to LDS; one lane per row runs the Neumaier
+// pass over them in tile order and shares the result through LDS. 64 / G rows
+// share a wave (two rows of 24 tiles for H = 768).
+
+#include "colsum.hpp"
+
+namespace detgemm {
+namespace ln {
+
+constexpr int KT = 32;
+
+// Row geometry for H = h: T tiles, G lanes per row, RW rows per wave, NW waves
+// per workgroup, TPL tiles kept in registers per lane (0: re-read).
+struct Geom {
+  int T, G, RW, NW, TPL;
+};
+
+inline Geom geom(int64_t h) {
+  Geom g;
+  g.T = static_cast<int>((h + KT - 1) / KT);
+  g.G = g.T < 64 ? g.T : 64;
+  g.RW = 64 / g.G;
+  const int per_lane = (g.T + g.G - 1) / g.G;
+  g.TPL = per_lane <= 1 ? 1 : per_lane <= 2 ? 2 : 0;
+  g.NW = g.T <= 512 ? 4 : 1;
+  return g;
+}
+
+// The 32 (or fewer, in the last tile) values of tile t of one row, upcast
+// exactly to float. VEC: the row start and every 16 bytes are aligned.
+template <typename E, bool VEC>
+__device__ inline void load_tile(const typename E::T* __restrict__ row, int h, int t, float (&v)[KT]) {
+  using T = typename E::T;
+  const int c0 = t * KT;
+  if constexpr (VEC) {
+    constexpr int PER = 16 / sizeof(T);
+#pragma unroll
+    for (int q = 0; q < KT / PER; ++q) {
+      if (c0 + q * PER < h) {
+        const uint4 w = *reinterpret_cast<const uint4*>(row + c0 + q * PER);
+        T x[PER];
+        __builtin_memcpy(x, &w, 16);
+#pragma unroll
+        for (int e = 0; e < PER; ++e) v[q * PER + e] = E::to_f32(x[e]);
+      } else {
+#pragma unroll
+        for (int e = 0; e < PER; ++e) v[q * PER + e] = 0.0f;
+      }
+    }
+  } else {
+#pragma unroll
+    for (int e = 0; e < KT; ++e) v[e] = c0 + e < h ? E::to_f32(row[c0 + e]) : 0.0f;
+  }
+}
+
+template <typename E, bool VEC>
+__device__ inline void store_tile(typename E::T* __restrict__ row, int h, int t, const double (&r)[KT]) {
+  using T = typename E::T;
+  const int c0 = t * KT;
+  if constexpr (VEC) {
+    constexpr int PER = 16 / sizeof(T);
+#pragma unroll
+    for (int q = 0; q < KT / PER; ++q) {
+      if (c0 + q * PER < h) {
+        T x[PER];
+#pragma unroll
+        for (int e = 0; e < PER; ++e) x[e] = round_from_f64<E>(r[q * PER + e]);
+        uint4 w;
+        __builtin_memcpy(&w, x, 16);
+        *reinterpret_cast<uint4*>(row + c0 + q * PER) = w;
+      }
+    }
+  } else {
+#pragma unroll
+    for (int e = 0; e < KT; ++e)
+      if (c0 + e < h) row[c0 + e] = round_from_f64<E>(r[e]);
+  }
+}
+
+// Neumaier pass over P[0 .. T-1] in order (one lane).
+__device__ inline double ordered_sum(const double* P, int T) {
+  double s = 0.0, c = 0.0;
+  for (int t = 0; t < T; ++t) colsum::kbn_add(s, c, P[t]);
+  return s + c;
+}
+
+// A lane's tiles g, g + G, ... (nk of them): kept in registers (TPL > 0; the
+// loops over them are unrolled so that every register index is static) or read
+// again on each visit (TPL == 0).
+template <typename E, bool VEC, int TPL>
+struct Tiles {
+  float v[TPL > 0 ? TPL : 1][KT];
+  const typename E::T* row;
+  int h, g, G, nk;
+  __device__ void init(const typename E::T* r, int hh, int gg, int GG, int T) {
+    row = r;
+    h = hh;
+    g = gg;
+    G = GG;
+    nk = (T - g + G - 1) / G;
+    if constexpr (TPL > 0) {
+#pragma unroll
+      for (int k = 0; k < TPL; ++k)
+        if (k < nk) load_tile<E, VEC>(row, h, g + k * G, v[k]);
+    }
+  }
+  // f(t, values) for each of the lane's tiles in ascending order
+  template <typename F>
+  __device__ void each(F&& f) {
+    if constexpr (TPL > 0) {
+#pragma unroll
+      for (int k = 0; k < TPL; ++k)
+        if (k < nk) f(g + k * G, v[k]);
+    } else {
+      float tmp[KT];
+      for (int k = 0; k < nk; ++k) {
+        load_tile<E, VEC>(row, h, g + k * G, tmp);
+        f(g + k * G, tmp);
+      }
+    }
+  }
+};
+
+// Two rows' worth of tiles visited together (x and dy of the backward).
+template <typename E, bool VEC, int TPL, typename F>
+__device__ inline void each2(Tiles<E, VEC, TPL>& a, Tiles<E, VEC, TPL>& b, F&& f) {
+  if constexpr (TPL > 0) {
+#pragma unroll
+    for (int k = 0; k < TPL; ++k)
+      if (k < a.nk) f(a.g + k * a.G, a.v[k], b.v[k]);
+  } else {
+    float ta[KT], tb[KT];
+    for (int k = 0; k < a.nk; ++k) {
+      load_tile<E, VEC>(a.row, a.h, a.g + k * a.G, ta);
+      load_tile<E, VEC>(b.row, b.h, b.g + k * b.G, tb);
+      f(a.g + k * a.G, ta, tb);
+    }
+  }
+}
+
+template <typename E, int TPL, bool VEC>
+__global__ void __launch_bounds__(256) fwd_kernel(const typename E::T* __restrict__ x,
+                                                  const typename E::T* __restrict__ gamma,
+                                                  const typename E::T* __restrict__ beta, int64_t rows, int h,
+                                                  Geom gm, double eps, typename E::T* __restrict__ y,
+                                                  double* __restrict__ mean_out, double* __restrict__ rstd_out) {
+  extern __shared__ double sm[];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int rg = lane / gm.G, g = lane % gm.G;
+  const int slot = wave * gm.RW + rg;
+  const int64_t row = static_cast<int64_t>(blockIdx.x) * (gm.NW * gm.RW) + slot;
+  const bool ok = rg < gm.RW && row < rows;
+  const int T = gm.T, G = gm.G;
+  double* P = sm + slot * T;
+  double* stat = sm + gm.NW * gm.RW * T;   // [slot] mean, [NW RW + slot] rstd
+  Tiles<E, VEC, TPL> tl;
+  if (ok) tl.init(x + row * h, h, g, G, T);
+
+  // pass 1: tile sums of x (elements past the row's end are skipped, so a
+  // short last tile is the chain over its own elements)
+  if (ok) {
+    tl.each([&](int t, const float(&v)[KT]) {
+      double p = 0.0;
+#pragma unroll
+      for (int e = 0; e < KT; ++e)
+        if (t * KT + e < h) p = p + static_cast<double>(v[e]);
+      P[t] = p;
+    });
+  }
+  __syncthreads();
+  if (ok && g == 0) stat[slot] = ordered_sum(P, T) / static_cast<double>(h);
+  __syncthreads();
+  const double mu = ok ? stat[slot] : 0.0;
+
+  // pass 2: tile sums of (x - mean)^2
+  if (ok) {
+    tl.each([&](int t, const float(&v)[KT]) {
+      double p = 0.0;
+#pragma unroll
+      for (int e = 0; e < KT; ++e) {
+        if (t * KT + e < h) {
+          const double d = static_cast<double>(v[e]) - mu;
+          p = __builtin_fma(d, d, p);
+        }
+      }
+      P[t] = p;
+    });
+  }
+  __syncthreads();
+  if (ok && g == 0) {
+    const double var = ordered_sum(P, T) / static_cast<double>(h);
+    const double rs = 1.0 / __builtin_sqrt(var + eps);
+    stat[gm.NW * gm.RW + slot] = rs;
+    if (mean_out) mean_out[row] = mu;
+    if (rstd_out) rstd_out[row] = rs;
+  }
+  __syncthreads();
+  if (!ok) return;
+  const double rs = stat[gm.NW * gm.RW + slot];
+
+  // pass 3: y = (d * rstd) * gamma + beta, one rounding
+  tl.each([&](int t, const float(&v)[KT]) {
+    double r[KT];
+#pragma unroll
+    for (int e = 0; e < KT; ++e) {
+      const int c = t * KT + e;
+      const int cc = c < h ? c : h - 1;
+      double u = (static_cast<double>(v[e]) - mu) * rs;
+      if (gamma) u = u * E::up(gamma[cc]);
+      if (beta) u = u + E::up(beta[cc]);
+      r[e] = u;
+    }
+    store_tile<E, VEC>(y + row * h, h, t, r);
+  });
+}
+
+template <typename E, int TPL, bool VEC>
+__global__ void __launch_bounds__(256) bwd_dx_kernel(const typename E::T* __restrict__ dy,
+                                                     const typename E::T* __restrict__ x,
+                                                     const double* __restrict__ mean, const double* __restrict__ rstd,
+                                                     const typename E::T* __restrict__ gamma, int64_t rows, int h,
+                                                     Geom gm, typename E::T* __restrict__ dx) {
+  extern __shared__ double sm[];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int rg = lane / gm.G, g = lane % gm.G;
+  const int slot = wave * gm.RW + rg;
+  const int64_t row = static_cast<int64_t>(blockIdx.x) * (gm.NW * gm.RW) + slot;
+  const bool ok = rg < gm.RW && row < rows;
+  const int T = gm.T, G = gm.G, S = gm.NW * gm.RW;
+  double* Pa = sm + slot * T;
+  double* Pb = sm + (S + slot) * T;
+  double* stat = sm + 2 * S * T;   // [slot] a, [S + slot] b
+  Tiles<E, VEC, TPL> tx, tg;
+  double mu = 0.0, rs = 0.0;
+  if (ok) {
+    tx.init(x + row * h, h, g, G, T);
+    tg.init(dy + row * h, h, g, G, T);
+    mu = mean[row];
+    rs = rstd[row];
+  }
+  if (ok) {
+    each2(tx, tg, [&](int t, const float(&vx)[KT], const float(&vg)[KT]) {
+      double pa = 0.0, pb = 0.0;
+#pragma unroll
+      for (int e = 0; e < KT; ++e) {
+        const int c = t * KT + e;
+        if (c < h) {
+          const double gv = gamma ? static_cast<double>(vg[e]) * E::up(gamma[c]) : static_cast<double>(vg[e]);
+          const double xh = (static_cast<double>(vx[e]) - mu) * rs;
+          pa = pa + gv;
+          pb = __builtin_fma(gv, xh, pb);
+        }
+      }
+      Pa[t] = pa;
+      Pb[t] = pb;
+    });
+  }
+  __syncthreads();
+  if (ok && g == 0) {
+    stat[slot] = ordered_sum(Pa, T) / static_cast<double>(h);
+    stat[S + slot] = ordered_sum(Pb, T) / static_cast<double>(h);
+  }
+  __syncthreads();
+  if (!ok) return;
+  const double a = stat[slot], b = stat[S + slot];
+  each2(tx, tg, [&](int t, const float(&vx)[KT], const float(&vg)[KT]) {
+    double r[KT];
+#pragma unroll
+    for (int e = 0; e < KT; ++e) {
+      const int c = t * KT + e;
+      const int cc = c < h ? c : h - 1;
+      const double gv = gamma ? static_cast<double>(vg[e]) * E::up(gamma[cc]) : static_cast<double>(vg[e]);
+      const double xh = (static_cast<double>(vx[e]) - mu) * rs;
+      r[e] = rs * ((gv - a) - xh * b);
+    }
+    store_tile<E, VEC>(dx + row * h, h, t, r);
+  });
+}
+
+// Column tile partials for dgamma and dbeta: one wave per (row tile, 64 * 4
+// columns); lane chains over the tile's rows for 4 adjacent columns.
+constexpr int CV = 4;
+constexpr int CWPB = 4;
+
+template <typename E>
+__global__ void __launch_bounds__(64 * CWPB) param_tile_kernel(const typename E::T* __restrict__ dy,
+                                                               const typename E::T* __restrict__ x,
+                                                               const double* __restrict__ mean,
+                                                               const double* __restrict__ rstd, int64_t rows,
+                                                               int64_t h, int64_t t0, int64_t nt, int ncb,
+                                                               double* __restrict__ Pg, double* __restrict__ Pb) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int cb = static_cast<int>(blockIdx.x % static_cast<unsigned>(ncb));
+  const int64_t tb = blockIdx.x / static_cast<unsigned>(ncb);
+  const int64_t tl = tb * CWPB + w;
+  const int64_t c0 = static_cast<int64_t>(cb) * 64 * CV + lane * CV;
+  if (tl >= nt || c0 >= h) return;   // no barrier in this kernel
+  const int64_t r0 = (t0 + tl) * KT;
+  const int cnt = static_cast<int>(rows - r0 < KT ? rows - r0 : KT);
+  double pg[CV], pb[CV];
+#pragma unroll
+  for (int v = 0; v < CV; ++v) pg[v] = pb[v] = 0.0;
+  for (int i = 0; i < cnt; ++i) {
+    const int64_t r = r0 + i;
+    const double mu = mean[r], rs = rstd[r];
+#pragma unroll
+    for (int v = 0; v < CV; ++v) {
+      if (c0 + v < h) {
+        const double d = E::up(dy[r * h + c0 + v]);
+        const double xh = (E::up(x[r * h + c0 + v]) - mu) * rs;
+        pg[v] = __builtin_fma(d, xh, pg[v]);
+        pb[v] = pb[v] + d;
+      }
+    }
+  }
+#pragma unroll
+  for (int v = 0; v < CV; ++v)
+    if (c0 + v < h) {
+      Pg[tl * h + c0 + v] = pg[v];
+      Pb[tl * h + c0 + v] = pb[v];
+    }
+}
+
+template <typename E>
+hipError_t launch_fwd_e(const void* x, const void* gamma, const void* beta, int64_t rows, int64_t h, double eps,
+                        void* y, double* mean, double* rstd, hipStream_t stream) {
+  using T = typename E::T;
+  const Geom gm = geom(h);
+  const int64_t per_wg = gm.NW * gm.RW;
+  const int64_t blocks = (rows + per_wg - 1) / per_wg;
+  if (blocks > INT_MAX) return hipErrorInvalidConfiguration;
+  const size_t lds = sizeof(double) * static_cast<size_t>(per_wg * gm.T + 2 * per_wg);
+  const bool vec = h % (16 / sizeof(T)) == 0 && reinterpret_cast<uintptr_t>(x) % 16 == 0 &&
+                   reinterpret_cast<uintptr_t>(y) % 16 == 0;
+  const dim3 grid(static_cast<unsigned>(blocks)), block(64 * gm.NW);
+  auto xs = static_cast<const T*>(x), gs = static_cast<const T*>(gamma), bs = static_cast<const T*>(beta);
+  auto ys = static_cast<T*>(y);
+  const int hi = static_cast<int>(h);
+#define LN_FWD(TPL, VEC) \
+  hipLaunchKernelGGL((fwd_kernel<E, TPL, VEC>), grid, block, lds, stream, xs, gs, bs, rows, hi, gm, eps, ys, mean, rstd)
+  if (vec) {
+    switch (gm.TPL) {
+      case 1: LN_FWD(1, true); break;
+      case 2: LN_FWD(2, true); break;
+      default: LN_FWD(0, true); break;
+    }
+  } else {
+    switch (gm.TPL) {
+      case 1: LN_FWD(1, false); break;
+      case 2: LN_FWD(2, false); break;
+      default: LN_FWD(0, false); break;
+    }
+  }
+#undef LN_FWD
+  return hipGetLastError();
+}
+
+template <typename E, typename O>
+hipError_t launch_params(const void* dy, const void* x, const double* mean, const double* rstd, int64_t rows,
+                         int64_t h, void* dgamma, void* dbeta, hipStream_t stream) {
+  using T = typename E::T;
+  const colsum::Chunks ck = colsum::plan_chunks(rows, h, 0);
+  const int64_t ncb = (h + 64 * CV - 1) / (64 * CV);
+  if (ncb > INT_MAX || ncb * ((ck.tck + CWPB - 1) / CWPB) > INT_MAX) return hipErrorInvalidConfiguration;
+  void* ws = nullptr;
+  hipError_t e = stream_workspace(stream, ck.bytes(h, 2), &ws);
+  if (e != hipSuccess) return e;
+  double* Pg = ck.partials(ws, h, 0);
+  double* Pb = ck.partials(ws, h, 1);
+  double* Sg = ck.state(ws, h, 2, 0);
+  double* Sb = ck.state(ws, h, 2, 1);
+  for (int64_t ch = 0; ch < ck.nch; ++ch) {
+    const int64_t t0 = ch * ck.tck, nt = ck.tiles - t0 < ck.tck ? ck.tiles - t0 : ck.tck;
+    const dim3 g1(static_cast<unsigned>(ncb * ((nt + CWPB - 1) / CWPB))), b1(64 * CWPB);
+    hipLaunchKernelGGL((param_tile_kernel<E>), g1, b1, 0, stream, static_cast<const T*>(dy),
+                       static_cast<const T*>(x), mean, rstd, rows, h, t0, nt, static_cast<int>(ncb), Pg, Pb);
+    const bool first = ch == 0, last = ch == ck.nch - 1;
+    if (dgamma) colsum::launch_pass<O>(Pg, h, nt, Sg, first, last, static_cast<typename O::T*>(dgamma), stream);
+    if (dbeta) colsum::launch_pass<O>(Pb, h, nt, Sb, first, last, static_cast<typename O::T*>(dbeta), stream);
+  }
+  return hipGetLastError();
+}
+
+template <typename E>
+hipError_t launch_bwd_e(bool pf32, const void* dy, const void* x, const double* mean, const double* rstd,
+                        const void* gamma, int64_t rows, int64_t h, void* dx, void* dgamma, void* dbeta,
+                        hipStream_t stream) {
+  using T = typename E::T;
+  if (dx) {
+    const Geom gm = geom(h);
+    const int64_t per_wg = gm.NW * gm.RW;
+    const int64_t blocks = (rows + per_wg - 1) / per_wg;
+    if (blocks > INT_MAX) return hipErrorInvalidConfiguration;
+    const size_t lds = sizeof(double) * static_cast<size_t>(2 * per_wg * gm.T + 2 * per_wg);
+    const bool vec = h % (16 / sizeof(T)) == 0 && reinterpret_cast<uintptr_t>(x) % 16 == 0 &&
+                     reinterpret_cast<uintptr_t>(dy) % 16 == 0 && reinterpret_cast<uintptr_t>(dx) % 16 == 0;
+    const dim3 grid(static_cast<unsigned>(blocks)), block(64 * gm.NW);
+    auto dys = static_cast<const T*>(dy), xs = static_cast<const T*>(x), gs = static_cast<const T*>(gamma);
+    auto dxs = static_cast<T*>(dx);
+    const int hi = static_cast<int>(h);
+#define LN_BWD(TPL, VEC)                                                                                       \
+  hipLaunchKernelGGL((bwd_dx_kernel<E, TPL, VEC>), grid, block, lds, stream, dys, xs, mean, rstd, gs, rows, hi, \
+                     gm, dxs)
+    if (vec) {
+      switch (gm.TPL) {
+        case 1: LN_BWD(1, true); break;
+        case 2: LN_BWD(2, true); break;
+        default: LN_BWD(0, true); break;
+      }
+    } else {
+      switch (gm.TPL) {
+        case 1: LN_BWD(1, false); break;
+        case 2: LN_BWD(2, false); break;
+        default: LN_BWD(0, false); break;
+      }
+    }
+#undef LN_BWD
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  if (!dgamma && !dbeta) return hipSuccess;
+  return pf32 ? launch_params<E, F32>(dy, x, mean, rstd, rows, h, dgamma, dbeta, stream)
+              : launch_params<E, E>(dy, x, mean, rstd, rows, h, dgamma, dbeta, stream);
+}
+
+}  // namespace ln
+
+hipError_t launch_layernorm_fwd(Dt dt, const void* x, const void* gamma, const void* beta, int64_t rows, int64_t h,
+                                double eps, void* y, double* mean, double* rstd, hipStream_t stream) {
+  switch (dt) {
+    case DT_F32: return ln::launch_fwd_e<F32>(x, gamma, beta, rows, h, eps, y, mean, rstd, stream);
+    case DT_BF16: return ln::launch_fwd_e<BF16>(x, gamma, beta, rows, h, eps, y, mean, rstd, stream);
+    case DT_F16: return ln::launch_fwd_e<F16>(x, gamma, beta, rows, h, eps, y, mean, rstd, stream);
+  }
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_layernorm_bwd(Dt dt, bool param_f32, const void* dy, const void* x, const double* mean,
+                                const double* rstd, const void* gamma, int64_t rows, int64_t h, void* dx,
+                                void* dgamma, void* dbeta, hipStream_t stream) {
+  switch (dt) {
+    case DT_F32: return ln::launch_bwd_e<F32>(false, dy, x, mean, rstd, gamma, rows, h, dx, dgamma, dbeta, stream);
+    case DT_BF16:
+      return ln::launch_bwd_e<BF16>(param_f32, dy, x, mean, rstd, gamma, rows, h, dx, dgamma, dbeta, stream);
+    case DT_F16:
+      return ln::launch_bwd_e<F16>(param_f32, dy, x, mean, rstd, gamma, rows, h, dx, dgamma, dbeta, stream);
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace detgemm

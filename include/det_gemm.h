@@ -43,7 +43,8 @@
  *   and allocates no device memory per call, with two exceptions: the fast
  *   tier's split dW (above) needs S * k * n * 4 bytes of f32 partials, and
  *   det_gemm_db needs the float64 tile partials of up to max(2^23, 128 * n)
- *   values (m / 32 * n of them when that is less) plus 2 * n; the
+ *   values (m / 32 * n of them when that is less) plus 2 * n, and
+ *   det_layernorm_bwd twice that for its two parameter gradients; the
  *   library keeps one such workspace per (device, stream), allocated on first
  *   need and grown (after synchronising that stream) when a larger one is
  *   needed, and never frees it. Calls on one stream share it in stream order,
@@ -147,6 +148,48 @@ det_status_t det_gemm_dw_out(void* dw, det_dtype_t dw_dt, const void* x, const v
  */
 det_status_t det_gemm_db(void* db, det_dtype_t db_dt, const void* dy, int64_t m, int64_t n,
                          det_dtype_t dt, det_tier_t tier, hipStream_t stream);
+
+/* Largest row length det_layernorm_fwd/_bwd accept. */
+#define DET_LAYERNORM_MAX_H 65536
+
+/*
+ * LayerNorm over the last dimension with float64 statistics (Carbon README,
+ * alia-carbon 0.2.0, "How It Works", the LayerNorm row: mean and variance in
+ * float64 instead of a thread-dependent parallel reduction). For each of the
+ * `rows` rows of x (h elements, row-major, dtype dt):
+ *   mean = S(x) / h,  d_j = x_j - mean,  var = S(d_j * d_j) / h   (biased),
+ *   rstd = 1 / sqrt(var + eps),
+ *   y_j  = round_dt((d_j * rstd) * gamma_j + beta_j),
+ * where S is the exact tier's fixed-order sum (32-element tiles, an ascending
+ * float64 chain in each, Neumaier across tiles) and every step is one IEEE
+ * float64 operation (no fusion); a null gamma or beta skips its step. One
+ * rounding to dt; the bits are fixed by the inputs alone (any row count,
+ * launch or device). gamma, beta: h elements of dt, nullable. y: rows x h of
+ * dt. mean, rstd: nullable float64 arrays of `rows` values (the backward
+ * takes them). 1 <= h <= DET_LAYERNORM_MAX_H; eps finite and >= 0. There is
+ * one arithmetic, so no tier argument. Errors as for the GEMM entry points.
+ */
+det_status_t det_layernorm_fwd(void* y, double* mean, double* rstd, const void* x, const void* gamma,
+                               const void* beta, int64_t rows, int64_t h, double eps, det_dtype_t dt,
+                               hipStream_t stream);
+
+/*
+ * Gradients of det_layernorm_fwd for the incoming gradient dy (rows x h, dt),
+ * with mean and rstd as the forward returned them and xhat_j = (x_j - mean) *
+ * rstd, g_j = dy_j * gamma_j (g = dy when gamma is null):
+ *   dx_j     = round_dt(rstd * ((g_j - S(g) / h) - xhat_j * (S(g * xhat) / h))),
+ *   dgamma_j = round_pdt(sum over rows of dy_j * xhat_j),
+ *   dbeta_j  = round_pdt(sum over rows of dy_j),
+ * the sums over a row (S) and over rows (in 32-row tiles, Neumaier across
+ * them, as det_gemm_db) in the exact tier's fixed order. dx: rows x h of dt;
+ * dgamma, dbeta: h values of param_dt (dt or DET_F32). Each output pointer is
+ * nullable (that output is not computed). The parameter gradients use the
+ * stream's workspace (2 * min(rows / 32, max(128, 2^23 / h)) * h float64
+ * values, plus 4h between chunks). DET_EDTYPE for any other param_dt.
+ */
+det_status_t det_layernorm_bwd(void* dx, void* dgamma, void* dbeta, det_dtype_t param_dt, const void* dy,
+                               const void* x, const double* mean, const double* rstd, const void* gamma,
+                               int64_t rows, int64_t h, det_dtype_t dt, hipStream_t stream);
 
 /* Static description of a status code. */
 const char* det_gemm_strerror(det_status_t status);
