@@ -43,6 +43,8 @@ def parse():
     p.add_argument("--cpu-seconds", type=float, default=12.0, help="budget of the CPU-oracle sample")
     p.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline")
     p.add_argument("--no-skinny", action="store_true", help="skip the skinny-M bandwidth measurements")
+    p.add_argument("--no-next", action="store_true",
+                   help="skip the bias-gradient, f32-dW and LayerNorm measurements")
     p.add_argument("--only", default=None,
                    help="profiling aid: run only the launches of one tier and op (e.g. exact.dw) and print their times")
     p.add_argument("--copy-mib", type=int, default=0,
@@ -210,6 +212,68 @@ def skinny(data, dev):
     return out
 
 
+PEAK_HBM = 8000.0   # GB/s, MI355X HBM3E
+
+
+def _time_calls(f, stream, reps=50, warmup=5):
+    """Average microseconds per call of f, HIP events on `stream` around `reps` back-to-back calls."""
+    import torch
+    for _ in range(warmup):
+        f()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(reps):
+        f()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) * 1e3 / reps
+
+
+def next_rows(data, dev):
+    """The ops beside the GEMMs, on the step's own tensors: the bias gradient of both layers
+    (f32 out), dW of c_fc written as f32 in both tiers, and the GPT-2 LayerNorm (8192 x 768,
+    bf16, float64 statistics) forward and backward. HBM-bound ops report GB/s of algorithmic
+    bytes against the HBM peak."""
+    import torch
+    import deterministic_invariant_gemm_det_amd as dg
+    stream = torch.cuda.current_stream(dev)
+    out = {}
+
+    def hbm(us, nbytes):
+        gbps = nbytes / (us * 1e-6) / 1e9
+        return {"us": round(us, 2), "algo_bytes": nbytes,
+                "roofline": {"bound": "hbm", "achieved": round(gbps, 1), "peak": PEAK_HBM, "unit": "GB/s",
+                             "frac": round(gbps / PEAK_HBM, 4)}}
+
+    for name, k, n in LAYERS:
+        g = data[name]["g"]
+        db = torch.empty(n, dtype=torch.float32, device=dev)
+        us = _time_calls(lambda: dg.db(g, "exact", out=db, out_dtype=torch.float32), stream)
+        out[f"db.{name}"] = hbm(us, TOKENS * n * 2 + n * 4)
+    d = data["c_fc"]
+    gw32 = torch.empty((d["k"], d["n"]), dtype=torch.float32, device=dev)
+    fl = 2.0 * TOKENS * d["k"] * d["n"]
+    for tier, peak in (("exact", PEAK_FP64), ("fast", PEAK_BF16)):
+        us = _time_calls(lambda: dg.dw(d["x"], d["g"], tier, out=gw32, out_dtype=torch.float32), stream, reps=10)
+        tf = fl / (us * 1e-6) / 1e12
+        out[f"dw_f32.c_fc.{tier}"] = {"us": round(us, 2), "tflops": round(tf, 2),
+                                      "roofline": {"bound": "mfma", "achieved": round(tf, 2), "peak": peak,
+                                                   "unit": "TFLOP/s", "frac": round(tf / peak, 4)}}
+    h = 768
+    x = data["c_fc"]["x"]                      # 8192 x 768 bf16
+    gy = data["c_proj"]["g"]                   # 8192 x 768 bf16, the LayerNorm's incoming gradient
+    gamma = torch.ones(h, dtype=torch.bfloat16, device=dev).add_(x[0] * 0.01)
+    beta = (x[1] * 0.1).contiguous()
+    y = torch.empty_like(x)
+    _, mean, rstd = dg.layer_norm(x, gamma, beta, 1e-5, out=y)
+    us = _time_calls(lambda: dg.layer_norm(x, gamma, beta, 1e-5, out=y), stream)
+    out["layernorm_fwd.8192x768"] = hbm(us, 2 * TOKENS * h * 2 + 2 * h * 2 + 16 * TOKENS)
+    us = _time_calls(lambda: dg.layer_norm_backward(gy, x, mean, rstd, gamma, param_dtype=torch.float32), stream)
+    out["layernorm_bwd.8192x768"] = hbm(us, 3 * TOKENS * h * 2 + 16 * TOKENS + h * 2 + 2 * h * 4)
+    return out
+
+
 def cpu_baseline(data, budget_s):
     """The oracle, as it stands, on a bounded sample of the step's exact-tier GEMMs (one core)."""
     import numpy as np
@@ -311,6 +375,8 @@ def main():
     }
     if not args.no_skinny:
         result["skinny_fwd_bf16_K768_N3072"] = skinny(data, dev)
+    if not args.no_next:
+        result["next_rows"] = next_rows(data, dev)
     if not args.no_cpu:
         result["cpu_baseline"] = cpu_baseline(data, args.cpu_seconds)
     print(json.dumps(result))

@@ -63,9 +63,17 @@ __global__ void __launch_bounds__(THREADS2) pass_kernel(const double* __restrict
     for (int j = 0; j < LPT; ++j) L[lr + j * (THREADS2 / CB)][lc] = r[j];
     __syncthreads();
     if (k + 1 < rounds) load((k + 1) * TCH);   // in flight during the pass below
-    if (tid < CB) {
+    if (tid < CB) {   // partials read eight at a time ahead of the dependent updates
       const int cnt = static_cast<int>(nt - k * TCH < TCH ? nt - k * TCH : TCH);
-      for (int t = 0; t < cnt; ++t) kbn_add(s, c, L[t][lc]);
+      int t = 0;
+      for (; t + 8 <= cnt; t += 8) {
+        double v[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) v[j] = L[t + j][lc];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) kbn_add(s, c, v[j]);
+      }
+      for (; t < cnt; ++t) kbn_add(s, c, L[t][lc]);
     }
     __syncthreads();
   }

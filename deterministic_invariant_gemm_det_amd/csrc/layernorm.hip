@@ -42,7 +42,7 @@ inline Geom geom(int64_t h) {
   g.RW = 64 / g.G;
   const int per_lane = (g.T + g.G - 1) / g.G;
   g.TPL = per_lane <= 1 ? 1 : per_lane <= 2 ? 2 : 0;
-  g.NW = g.T <= 512 ? 4 : 1;
+  g.NW = 1;   // rows never span waves, so a one-wave workgroup needs no cross-wave barrier
   return g;
 }
 
@@ -98,9 +98,18 @@ __device__ inline void store_tile(typename E::T* __restrict__ row, int h, int t,
 }
 
 // Neumaier pass over P[0 .. T-1] in order (one lane).
+// The partials are read eight at a time ahead of the dependent updates.
 __device__ inline double ordered_sum(const double* P, int T) {
   double s = 0.0, c = 0.0;
-  for (int t = 0; t < T; ++t) colsum::kbn_add(s, c, P[t]);
+  int t = 0;
+  for (; t + 8 <= T; t += 8) {
+    double v[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) v[j] = P[t + j];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) colsum::kbn_add(s, c, v[j]);
+  }
+  for (; t < T; ++t) colsum::kbn_add(s, c, P[t]);
   return s + c;
 }
 
@@ -220,14 +229,15 @@ __global__ void __launch_bounds__(256) fwd_kernel(const typename E::T* __restric
 
   // pass 3: y = (d * rstd) * gamma + beta, one rounding
   tl.each([&](int t, const float(&v)[KT]) {
+    float gv[KT], bv[KT];
+    if (gamma) load_tile<E, VEC>(gamma, h, t, gv);
+    if (beta) load_tile<E, VEC>(beta, h, t, bv);
     double r[KT];
 #pragma unroll
     for (int e = 0; e < KT; ++e) {
-      const int c = t * KT + e;
-      const int cc = c < h ? c : h - 1;
       double u = (static_cast<double>(v[e]) - mu) * rs;
-      if (gamma) u = u * E::up(gamma[cc]);
-      if (beta) u = u + E::up(beta[cc]);
+      if (gamma) u = u * static_cast<double>(gv[e]);
+      if (beta) u = u + static_cast<double>(bv[e]);
       r[e] = u;
     }
     store_tile<E, VEC>(y + row * h, h, t, r);
@@ -260,12 +270,14 @@ __global__ void __launch_bounds__(256) bwd_dx_kernel(const typename E::T* __rest
   }
   if (ok) {
     each2(tx, tg, [&](int t, const float(&vx)[KT], const float(&vg)[KT]) {
+      float gm_[KT];
+      if (gamma) load_tile<E, VEC>(gamma, h, t, gm_);
       double pa = 0.0, pb = 0.0;
 #pragma unroll
       for (int e = 0; e < KT; ++e) {
         const int c = t * KT + e;
         if (c < h) {
-          const double gv = gamma ? static_cast<double>(vg[e]) * E::up(gamma[c]) : static_cast<double>(vg[e]);
+          const double gv = gamma ? static_cast<double>(vg[e]) * static_cast<double>(gm_[e]) : static_cast<double>(vg[e]);
           const double xh = (static_cast<double>(vx[e]) - mu) * rs;
           pa = pa + gv;
           pb = __builtin_fma(gv, xh, pb);
@@ -284,12 +296,12 @@ __global__ void __launch_bounds__(256) bwd_dx_kernel(const typename E::T* __rest
   if (!ok) return;
   const double a = stat[slot], b = stat[S + slot];
   each2(tx, tg, [&](int t, const float(&vx)[KT], const float(&vg)[KT]) {
+    float gm_[KT];
+    if (gamma) load_tile<E, VEC>(gamma, h, t, gm_);
     double r[KT];
 #pragma unroll
     for (int e = 0; e < KT; ++e) {
-      const int c = t * KT + e;
-      const int cc = c < h ? c : h - 1;
-      const double gv = gamma ? static_cast<double>(vg[e]) * E::up(gamma[cc]) : static_cast<double>(vg[e]);
+      const double gv = gamma ? static_cast<double>(vg[e]) * static_cast<double>(gm_[e]) : static_cast<double>(vg[e]);
       const double xh = (static_cast<double>(vx[e]) - mu) * rs;
       r[e] = rs * ((gv - a) - xh * b);
     }
@@ -298,17 +310,24 @@ __global__ void __launch_bounds__(256) bwd_dx_kernel(const typename E::T* __rest
 }
 
 // Column tile partials for dgamma and dbeta: one wave per (row tile, 64 * 4
-// columns); lane chains over the tile's rows for 4 adjacent columns.
+// columns); each lane chains over the tile's rows for 4 adjacent columns. VEC:
+// h % 4 == 0 and both bases aligned to 4 elements (one 8- or 16-byte load per
+// row and operand).
 constexpr int CV = 4;
 constexpr int CWPB = 4;
 
-template <typename E>
+template <int BYTES> struct VecOf;
+template <> struct VecOf<8> { using type = uint2; };
+template <> struct VecOf<16> { using type = uint4; };
+
+template <typename E, bool VEC>
 __global__ void __launch_bounds__(64 * CWPB) param_tile_kernel(const typename E::T* __restrict__ dy,
                                                                const typename E::T* __restrict__ x,
                                                                const double* __restrict__ mean,
                                                                const double* __restrict__ rstd, int64_t rows,
                                                                int64_t h, int64_t t0, int64_t nt, int ncb,
                                                                double* __restrict__ Pg, double* __restrict__ Pb) {
+  using T = typename E::T;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int cb = static_cast<int>(blockIdx.x % static_cast<unsigned>(ncb));
   const int64_t tb = blockIdx.x / static_cast<unsigned>(ncb);
@@ -320,22 +339,43 @@ __global__ void __launch_bounds__(64 * CWPB) param_tile_kernel(const typename E:
   double pg[CV], pb[CV];
 #pragma unroll
   for (int v = 0; v < CV; ++v) pg[v] = pb[v] = 0.0;
-  for (int i = 0; i < cnt; ++i) {
+  auto step = [&](int i) {
     const int64_t r = r0 + i;
     const double mu = mean[r], rs = rstd[r];
+    T dv[CV], xv[CV];
+    if constexpr (VEC) {
+      using Vec = typename VecOf<CV * sizeof(T)>::type;
+      const Vec qd = *reinterpret_cast<const Vec*>(dy + r * h + c0);
+      const Vec qx = *reinterpret_cast<const Vec*>(x + r * h + c0);
+      __builtin_memcpy(dv, &qd, sizeof(qd));
+      __builtin_memcpy(xv, &qx, sizeof(qx));
+    } else {
+#pragma unroll
+      for (int v = 0; v < CV; ++v) {
+        const int64_t c = c0 + v < h ? c0 + v : h - 1;   // clamped reads are never used
+        dv[v] = dy[r * h + c];
+        xv[v] = x[r * h + c];
+      }
+    }
 #pragma unroll
     for (int v = 0; v < CV; ++v) {
-      if (c0 + v < h) {
-        const double d = E::up(dy[r * h + c0 + v]);
-        const double xh = (E::up(x[r * h + c0 + v]) - mu) * rs;
+      if (VEC || c0 + v < h) {
+        const double d = E::up(dv[v]);
+        const double xh = (E::up(xv[v]) - mu) * rs;
         pg[v] = __builtin_fma(d, xh, pg[v]);
         pb[v] = pb[v] + d;
       }
     }
+  };
+  if (cnt == KT) {
+#pragma unroll 8
+    for (int i = 0; i < KT; ++i) step(i);
+  } else {
+    for (int i = 0; i < cnt; ++i) step(i);
   }
 #pragma unroll
   for (int v = 0; v < CV; ++v)
-    if (c0 + v < h) {
+    if (VEC || c0 + v < h) {
       Pg[tl * h + c0 + v] = pg[v];
       Pb[tl * h + c0 + v] = pb[v];
     }
@@ -351,7 +391,8 @@ hipError_t launch_fwd_e(const void* x, const void* gamma, const void* beta, int6
   if (blocks > INT_MAX) return hipErrorInvalidConfiguration;
   const size_t lds = sizeof(double) * static_cast<size_t>(per_wg * gm.T + 2 * per_wg);
   const bool vec = h % (16 / sizeof(T)) == 0 && reinterpret_cast<uintptr_t>(x) % 16 == 0 &&
-                   reinterpret_cast<uintptr_t>(y) % 16 == 0;
+                   reinterpret_cast<uintptr_t>(y) % 16 == 0 && reinterpret_cast<uintptr_t>(gamma) % 16 == 0 &&
+                   reinterpret_cast<uintptr_t>(beta) % 16 == 0;
   const dim3 grid(static_cast<unsigned>(blocks)), block(64 * gm.NW);
   auto xs = static_cast<const T*>(x), gs = static_cast<const T*>(gamma), bs = static_cast<const T*>(beta);
   auto ys = static_cast<T*>(y);
@@ -389,11 +430,17 @@ hipError_t launch_params(const void* dy, const void* x, const double* mean, cons
   double* Pb = ck.partials(ws, h, 1);
   double* Sg = ck.state(ws, h, 2, 0);
   double* Sb = ck.state(ws, h, 2, 1);
+  const bool vec = h % CV == 0 && reinterpret_cast<uintptr_t>(dy) % (CV * sizeof(T)) == 0 &&
+                   reinterpret_cast<uintptr_t>(x) % (CV * sizeof(T)) == 0;
   for (int64_t ch = 0; ch < ck.nch; ++ch) {
     const int64_t t0 = ch * ck.tck, nt = ck.tiles - t0 < ck.tck ? ck.tiles - t0 : ck.tck;
     const dim3 g1(static_cast<unsigned>(ncb * ((nt + CWPB - 1) / CWPB))), b1(64 * CWPB);
-    hipLaunchKernelGGL((param_tile_kernel<E>), g1, b1, 0, stream, static_cast<const T*>(dy),
-                       static_cast<const T*>(x), mean, rstd, rows, h, t0, nt, static_cast<int>(ncb), Pg, Pb);
+    if (vec)
+      hipLaunchKernelGGL((param_tile_kernel<E, true>), g1, b1, 0, stream, static_cast<const T*>(dy),
+                         static_cast<const T*>(x), mean, rstd, rows, h, t0, nt, static_cast<int>(ncb), Pg, Pb);
+    else
+      hipLaunchKernelGGL((param_tile_kernel<E, false>), g1, b1, 0, stream, static_cast<const T*>(dy),
+                         static_cast<const T*>(x), mean, rstd, rows, h, t0, nt, static_cast<int>(ncb), Pg, Pb);
     const bool first = ch == 0, last = ch == ck.nch - 1;
     if (dgamma) colsum::launch_pass<O>(Pg, h, nt, Sg, first, last, static_cast<typename O::T*>(dgamma), stream);
     if (dbeta) colsum::launch_pass<O>(Pb, h, nt, Sb, first, last, static_cast<typename O::T*>(dbeta), stream);
@@ -413,7 +460,8 @@ hipError_t launch_bwd_e(bool pf32, const void* dy, const void* x, const double* 
     if (blocks > INT_MAX) return hipErrorInvalidConfiguration;
     const size_t lds = sizeof(double) * static_cast<size_t>(2 * per_wg * gm.T + 2 * per_wg);
     const bool vec = h % (16 / sizeof(T)) == 0 && reinterpret_cast<uintptr_t>(x) % 16 == 0 &&
-                     reinterpret_cast<uintptr_t>(dy) % 16 == 0 && reinterpret_cast<uintptr_t>(dx) % 16 == 0;
+                     reinterpret_cast<uintptr_t>(dy) % 16 == 0 && reinterpret_cast<uintptr_t>(dx) % 16 == 0 &&
+                     reinterpret_cast<uintptr_t>(gamma) % 16 == 0;
     const dim3 grid(static_cast<unsigned>(blocks)), block(64 * gm.NW);
     auto dys = static_cast<const T*>(dy), xs = static_cast<const T*>(x), gs = static_cast<const T*>(gamma);
     auto dxs = static_cast<T*>(dx);
