@@ -35,6 +35,10 @@ class Oracle:
         L.oracle_env_ok.restype = ctypes.c_int
         L.oracle_version.restype = ctypes.c_int
         vp, i64 = ctypes.c_void_p, ctypes.c_int64
+        L.oracle_gemm_cr.restype = ctypes.c_int
+        L.oracle_gemm_cr.argtypes = [ctypes.c_int, ctypes.c_int, vp, vp, vp, i64, i64, i64, vp, i64, vp]
+        L.oracle_exact_sum.restype = ctypes.c_int
+        L.oracle_exact_sum.argtypes = [vp, i64, ctypes.c_int, vp]
         L.oracle_layernorm_fwd.restype = ctypes.c_int
         L.oracle_layernorm_fwd.argtypes = [ctypes.c_int, vp, vp, vp, i64, i64, ctypes.c_double, vp, vp, vp, vp]
         L.oracle_layernorm_bwd.restype = ctypes.c_int
@@ -100,6 +104,36 @@ class Oracle:
         _, r, S = self.gemm("dw", dt, ones, dy, m, 1, n, want_r=True, want_S=want_S)
         y = self.round_to(out_dt or dt, r[0])
         return y, (r[0] if want_r else None), (S[0] if want_S else None)
+
+    def gemm_cr(self, op, dt, A, B, m, k, n, bias=None, rows=None):
+        """Correctly rounded tier: each output is the exact value of its dot product (+ bias)
+        rounded once (RNE) to dt. Shapes and operands as gemm; returns y."""
+        a_shape = (m, k) if op in ("fwd", "dw") else (m, n)
+        b_shape = (k, n) if op in ("fwd", "dx") else (m, n)
+        _check(A, dt, a_shape, "A")
+        _check(B, dt, b_shape, "B")
+        if bias is not None:
+            _check(bias, dt, (n,), "bias")
+        out_rows = k if op == "dw" else m
+        cols = k if op == "dx" else n
+        if rows is not None:
+            rows = np.ascontiguousarray(rows, dtype=np.int64)
+            nrows = rows.shape[0]
+        else:
+            nrows = out_rows
+        y = np.zeros((nrows, cols), dtype=STORAGE[dt])
+        if self.L.oracle_gemm_cr(OPS[op], DTYPES[dt], _ptr(A), _ptr(B), _ptr(bias), m, k, n, _ptr(rows), nrows,
+                                 _ptr(y)) != 0:
+            raise ValueError("oracle_gemm_cr rejected its arguments")
+        return y
+
+    def exact_sum(self, dt, values):
+        """The exact sum of float64 values rounded once to dt (raw storage scalar)."""
+        v = np.ascontiguousarray(values, dtype=np.float64)
+        out = np.zeros(1, dtype=STORAGE[dt])
+        if self.L.oracle_exact_sum(_ptr(v) if v.size else None, v.size, DTYPES[dt], _ptr(out)) != 0:
+            raise ValueError("oracle_exact_sum rejected its arguments")
+        return out[0]
 
     def layernorm_fwd(self, dt, x, gamma=None, beta=None, eps=1e-5, want_r=False):
         """LayerNorm over the last dim of x[rows, h] with float64 statistics (the row sums are
@@ -204,3 +238,11 @@ def layernorm_fwd(*a, **kw):
 
 def layernorm_bwd(*a, **kw):
     return default().layernorm_bwd(*a, **kw)
+
+
+def gemm_cr(*a, **kw):
+    return default().gemm_cr(*a, **kw)
+
+
+def exact_sum(*a, **kw):
+    return default().exact_sum(*a, **kw)

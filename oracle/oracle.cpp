@@ -37,6 +37,10 @@
 // Alongside each output the oracle can return r (the float64 value before the
 // downcast) and S = sum |a_k * b_k| + |b_j|, which bound the fast tier's error.
 //
+// The correctly rounded tier (Carbon README, "Roadmap", v0.2: exact summation
+// with a superaccumulator, independent of order) is defined separately below:
+// oracle_gemm_cr rounds the exact value of each dot product once.
+//
 // LayerNorm (Carbon README, "How It Works", the LayerNorm row: mean and
 // variance in float64 instead of a thread-dependent parallel reduction) is
 // defined on top of the same summation; see oracle_layernorm_fwd/_bwd below.
@@ -190,7 +194,7 @@ double kbn_dot(const double* a, const double* b, int64_t L, double* S) {
 
 extern "C" {
 
-int oracle_version(void) { return 2; }
+int oracle_version(void) { return 3; }
 
 // 1 when the floating-point environment is the IEEE default this oracle needs:
 // round-to-nearest-even, no flush-to-zero, no denormals-are-zero.
@@ -366,6 +370,171 @@ int oracle_layernorm_bwd(int dt, int pdt, const void* dy, const void* x, const d
     if (dgamma) store(dgamma, j, kbn_dot(&coly[j * rows], &colx[j * rows], rows, &S), pdt);
     if (dbeta) store(dbeta, j, kbn_dot(&coly[j * rows], ones.data(), rows, &S), pdt);
   }
+  return 0;
+}
+
+
+// ---- correctly rounded tier -------------------------------------------------
+//
+// Carbon README (alia-carbon 0.2.0), "Roadmap", v0.2: the Kahan accumulation
+// replaced by a superaccumulator, i.e. an exact sum whose value does not
+// depend on the order of the terms. Reading taken: every output is the exact
+// real value of sum_k a_k * b_k (+ b_j), rounded once to the output dtype with
+// round-to-nearest-even (ties to the even code; beyond the largest finite
+// value to infinity). An exact zero gives +0. If any term involves an infinity
+// or a NaN, the result is the float64 sum of the terms (NaN or an infinity).
+//
+// The exact value is kept as a big integer: a sign and a magnitude in 32-bit
+// limbs, counting units of 2^-BIG_LOW (below the lowest bit of any float64).
+// Each float64 term m * 2^e (m an integer of at most 53 bits) is added to the
+// positive or the negative magnitude at bit e + BIG_LOW; the two are
+// subtracted at the end.
+
+namespace {
+
+constexpr int BIG_LOW = 1120;               // the unit is 2^-1120
+constexpr int BIG_LIMBS = (BIG_LOW + 1100) / 32 + 2;
+
+struct BigMag {
+  std::vector<uint64_t> limb = std::vector<uint64_t>(BIG_LIMBS, 0);   // 32 bits used per limb
+  void add_shifted(uint64_t m, int bit) {   // += m * 2^bit
+    int li = bit / 32, sh = bit % 32;
+    // m < 2^53: m << sh spans at most three 32-bit limbs
+    unsigned __int128 v = static_cast<unsigned __int128>(m) << sh;
+    uint64_t carry = 0;
+    for (int i = li; i < BIG_LIMBS; ++i) {
+      const uint64_t part = static_cast<uint64_t>(v & 0xffffffffu);
+      v >>= 32;
+      const uint64_t t = limb[i] + part + carry;
+      limb[i] = t & 0xffffffffu;
+      carry = t >> 32;
+      if (v == 0 && carry == 0) break;
+    }
+  }
+  int cmp(const BigMag& o) const {
+    for (int i = BIG_LIMBS - 1; i >= 0; --i)
+      if (limb[i] != o.limb[i]) return limb[i] < o.limb[i] ? -1 : 1;
+    return 0;
+  }
+  void sub(const BigMag& o) {   // *this -= o, requires *this >= o
+    int64_t borrow = 0;
+    for (int i = 0; i < BIG_LIMBS; ++i) {
+      int64_t t = static_cast<int64_t>(limb[i]) - static_cast<int64_t>(o.limb[i]) - borrow;
+      borrow = t < 0 ? 1 : 0;
+      if (t < 0) t += int64_t(1) << 32;
+      limb[i] = static_cast<uint64_t>(t);
+    }
+  }
+  int top_bit() const {   // index of the highest set bit, -1 for zero
+    for (int i = BIG_LIMBS - 1; i >= 0; --i)
+      if (limb[i]) return i * 32 + 63 - __builtin_clzll(limb[i]);
+    return -1;
+  }
+  int bit(int b) const { return b < 0 ? 0 : static_cast<int>((limb[b / 32] >> (b % 32)) & 1u); }
+  bool any_below(int b) const {   // any set bit with index < b
+    for (int i = 0; i < b; ++i)
+      if (bit(i)) return true;
+    return false;
+  }
+};
+
+struct ExactSum {
+  BigMag pos, neg;
+  double nonfinite = 0.0;
+  bool has_nonfinite = false;
+  void add(double v) {
+    if (!std::isfinite(v)) {
+      nonfinite = has_nonfinite ? nonfinite + v : v;
+      has_nonfinite = true;
+      return;
+    }
+    if (v == 0.0) return;
+    int e;
+    const double m = std::frexp(std::fabs(v), &e);            // |v| = m * 2^e, m in [0.5, 1)
+    const uint64_t M = static_cast<uint64_t>(std::ldexp(m, 53));   // exact: 53-bit integer
+    const int bit = e - 53 + BIG_LOW;                             // |v| = M * 2^(bit - BIG_LOW)
+    (v > 0 ? pos : neg).add_shifted(M, bit);
+  }
+};
+
+// Precision p (significand bits) and the exponent of the smallest normal value.
+void dtype_format(int dt, int* p, int* emin) {
+  if (dt == DT_F32) { *p = 24; *emin = -126; }
+  else if (dt == DT_BF16) { *p = 8; *emin = -126; }
+  else { *p = 11; *emin = -14; }
+}
+
+// The exact sum rounded once to dt (RNE), returned as a float64 that dt holds
+// exactly (or an infinity past dt's range), then stored.
+double round_exact(ExactSum& x, int dt) {
+  if (x.has_nonfinite) return x.nonfinite;
+  BigMag mag = x.pos;
+  double sign = 1.0;
+  const int c = x.pos.cmp(x.neg);
+  if (c == 0) return 0.0;
+  if (c > 0) {
+    mag.sub(x.neg);
+  } else {
+    mag = x.neg;
+    mag.sub(x.pos);
+    sign = -1.0;
+  }
+  int p, emin;
+  dtype_format(dt, &p, &emin);
+  const int h = mag.top_bit();
+  // the result's last bit: p - 1 bits below the top, but not below dt's smallest subnormal bit
+  int lsb = h - (p - 1);
+  const int lsb_min = (emin - (p - 1)) + BIG_LOW;
+  if (lsb < lsb_min) lsb = lsb_min;
+  uint64_t keep = 0;
+  for (int b = h; b >= lsb; --b) keep = (keep << 1) | static_cast<uint64_t>(mag.bit(b));
+  const int round = mag.bit(lsb - 1);
+  const bool sticky = mag.any_below(lsb - 1);
+  if (round && (sticky || (keep & 1u))) keep += 1;
+  return sign * std::ldexp(static_cast<double>(keep), lsb - BIG_LOW);
+}
+
+}  // namespace
+
+// Correctly rounded GEMM rows; arguments as oracle_gemm (no S).
+int oracle_gemm_cr(int op, int dt, const void* A, const void* B, const void* bias,
+                   int64_t m, int64_t k, int64_t n, const int64_t* rows, int64_t nrows, void* y) {
+  if (op < OP_FWD || op > OP_DW || dt < DT_F32 || dt > DT_F16) return -1;
+  if (m < 1 || k < 1 || n < 1 || !A || !B || !y) return -1;
+  if (op != OP_FWD && bias) return -1;
+  const int64_t out_rows = (op == OP_DW) ? k : m;
+  const int64_t cols = (op == OP_DX) ? k : n;
+  const int64_t L = (op == OP_FWD) ? k : (op == OP_DX ? n : m);
+  if (!rows) nrows = out_rows;
+  for (int64_t ii = 0; ii < nrows; ++ii) {
+    const int64_t row = rows ? rows[ii] : ii;
+    if (row < 0 || row >= out_rows) return -1;
+  }
+  for (int64_t ii = 0; ii < nrows; ++ii) {
+    const int64_t row = rows ? rows[ii] : ii;
+    for (int64_t col = 0; col < cols; ++col) {
+      ExactSum x;
+      for (int64_t l = 0; l < L; ++l) {
+        double a, b;
+        if (op == OP_FWD) { a = decode(A, row * k + l, dt); b = decode(B, l * n + col, dt); }
+        else if (op == OP_DX) { a = decode(A, row * n + l, dt); b = decode(B, col * n + l, dt); }
+        else { a = decode(A, l * k + row, dt); b = decode(B, l * n + col, dt); }
+        x.add(a * b);   // exact: the product of two f32/bf16/f16 values fits float64
+      }
+      if (bias) x.add(decode(bias, col, dt));
+      store(y, ii * cols + col, round_exact(x, dt), dt);
+    }
+  }
+  return 0;
+}
+
+// The exact sum of cnt float64 values, rounded once to dt (pins the rounding of
+// the correctly rounded tier on values chosen by the caller).
+int oracle_exact_sum(const double* v, int64_t cnt, int dt, void* out) {
+  if (dt < DT_F32 || dt > DT_F16 || cnt < 0 || (cnt > 0 && !v) || !out) return -1;
+  ExactSum x;
+  for (int64_t i = 0; i < cnt; ++i) x.add(v[i]);
+  store(out, 0, round_exact(x, dt), dt);
   return 0;
 }
 
