@@ -14,7 +14,7 @@ import os
 __all__ = [
     "det_gemm_fwd", "det_gemm_dx", "det_gemm_dw", "det_gemm_dw_out", "det_gemm_db", "det_gemm_strerror",
     "det_gemm_last_error", "det_gemm_version", "det_gemm_debug_force_family", "det_gemm_debug_force_exact_kernel",
-    "det_gemm_debug_force_db_chunk",
+    "det_gemm_debug_force_db_chunk", "det_gemm_debug_force_cr_fallback",
     "DetGemmError", "LIB_PATH", "fwd", "dx", "dw", "db", "deterministic_linear", "Linear", "DTYPES", "TIERS",
     "det_layernorm_fwd", "det_layernorm_bwd", "layer_norm", "layer_norm_backward", "deterministic_layer_norm",
 ]
@@ -23,7 +23,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libdetgemm.so")
 
 DTYPES = {"f32": 0, "bf16": 1, "f16": 2}
-TIERS = {"exact": 0, "fast": 1}
+TIERS = {"exact": 0, "fast": 1, "cr": 2}
 STATUS = {0: "DET_OK", -1: "DET_EINVAL", -2: "DET_EDTYPE", -3: "DET_ETIER", -4: "DET_EDEVICE", -5: "DET_ELAUNCH"}
 
 
@@ -73,6 +73,8 @@ def lib():
         L.det_gemm_debug_force_exact_kernel.restype = ci
         L.det_gemm_debug_force_db_chunk.argtypes = [i64]
         L.det_gemm_debug_force_db_chunk.restype = ci
+        L.det_gemm_debug_force_cr_fallback.argtypes = [ci]
+        L.det_gemm_debug_force_cr_fallback.restype = ci
         _lib = L
     return _lib
 
@@ -157,6 +159,10 @@ def det_gemm_debug_force_exact_kernel(variant):
 
 def det_gemm_debug_force_db_chunk(tiles):
     _check(lib().det_gemm_debug_force_db_chunk(tiles))
+
+
+def det_gemm_debug_force_cr_fallback(on):
+    _check(lib().det_gemm_debug_force_cr_fallback(int(bool(on))))
 
 
 # ---------------------------------------------------------------- torch layer

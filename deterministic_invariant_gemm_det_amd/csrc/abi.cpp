@@ -19,6 +19,10 @@ thread_local char g_last_error[256] = "";
 std::atomic<int> g_force_family{-1};
 std::atomic<int> g_force_exact{-1};
 std::atomic<int64_t> g_force_db_chunk{0};
+std::atomic<int> g_force_cr_fallback{0};
+// longest reduction (with the bias index) of the correctly rounded tier: its
+// int128 accumulator stays below 2^126 for up to 2^27 indices
+constexpr int64_t kMaxCrReduction = int64_t(1) << 27;
 
 constexpr int kMaxDevices = 64;
 // 0 unknown, 1 gfx950, 2 not supported
@@ -65,12 +69,18 @@ det_status_t run(detgemm::Op op, void* out, const void* A, const void* B, const 
                  bool out_f32 = false) {
   g_last_error[0] = '\0';
   if (dt != DET_F32 && dt != DET_BF16 && dt != DET_F16) return fail(DET_EDTYPE, "det_gemm: unknown dtype%s");
-  if (tier != DET_TIER_EXACT && tier != DET_TIER_FAST) return fail(DET_ETIER, "det_gemm: unknown tier%s");
+  if (tier != DET_TIER_EXACT && tier != DET_TIER_FAST && tier != DET_TIER_CR)
+    return fail(DET_ETIER, "det_gemm: unknown tier%s");
   if (!out || !A || !B) return fail(DET_EINVAL, "det_gemm: null %s pointer", !out ? "output" : "input");
   if (m < 1 || k < 1 || n < 1) return fail(DET_EINVAL, "det_gemm: m, k and n must all be >= 1%s");
   const int64_t esz = dt == DET_F32 ? 4 : 2;
   if (!mul_ok(m, k, esz) || !mul_ok(k, n, esz) || !mul_ok(m, n, esz))
     return fail(DET_EINVAL, "det_gemm: tensor size overflows int64%s");
+  if (tier == DET_TIER_CR) {
+    const int64_t red = (op == detgemm::OP_FWD) ? k : (op == detgemm::OP_DX ? n : m);
+    if (red + 1 > kMaxCrReduction)
+      return fail(DET_EINVAL, "det_gemm: the correctly rounded tier takes reductions of at most 2^27 - 1%s");
+  }
   int cus = 0;
   const det_status_t dev = check_device(&cus);
   if (dev != DET_OK) return dev;
@@ -105,6 +115,8 @@ det_status_t run(detgemm::Op op, void* out, const void* A, const void* B, const 
   if (tier == DET_TIER_EXACT) {
     const int v = g_force_exact.load(std::memory_order_relaxed);
     err = detgemm::launch_exact(op, d, a, v, stream);
+  } else if (tier == DET_TIER_CR) {
+    err = detgemm::launch_cr(op, d, a, g_force_cr_fallback.load(std::memory_order_relaxed), stream);
   } else {
     int fam = g_force_family.load(std::memory_order_relaxed);
     if (fam < 0) fam = detgemm::fast_auto_family(op, d, a.cols, a.red);
@@ -188,14 +200,36 @@ det_status_t det_gemm_db(void* db, det_dtype_t db_dt, const void* dy, int64_t m,
   if (dt != DET_F32 && dt != DET_BF16 && dt != DET_F16) return fail(DET_EDTYPE, "det_gemm: unknown dtype%s");
   if (db_dt != dt && db_dt != DET_F32)
     return fail(DET_EDTYPE, "det_gemm_db: the output dtype must be the input dtype or DET_F32%s");
-  if (tier != DET_TIER_EXACT && tier != DET_TIER_FAST) return fail(DET_ETIER, "det_gemm: unknown tier%s");
+  if (tier != DET_TIER_EXACT && tier != DET_TIER_FAST && tier != DET_TIER_CR)
+    return fail(DET_ETIER, "det_gemm: unknown tier%s");
   if (!db || !dy) return fail(DET_EINVAL, "det_gemm: null %s pointer", !db ? "output" : "input");
   if (m < 1 || n < 1) return fail(DET_EINVAL, "det_gemm: m and n must both be >= 1%s");
   const int64_t esz = dt == DET_F32 ? 4 : 2;
   if (!mul_ok(m, n, esz)) return fail(DET_EINVAL, "det_gemm: tensor size overflows int64%s");
+  if (tier == DET_TIER_CR && m + 1 > kMaxCrReduction)
+    return fail(DET_EINVAL, "det_gemm: the correctly rounded tier takes reductions of at most 2^27 - 1%s");
   int cus = 0;
   const det_status_t dev = check_device(&cus);
   if (dev != DET_OK) return dev;
+  if (tier == DET_TIER_CR) {   // the correctly rounded column sum: dW of a column of ones
+    detgemm::GemmArgs a;
+    std::memset(&a, 0, sizeof(a));
+    a.A = nullptr;
+    a.B = dy;
+    a.out = db;
+    a.rows = 1;
+    a.cols = n;
+    a.red = m;
+    a.lda = 1;
+    a.ldb = n;
+    a.num_cu = cus;
+    a.split = 1;
+    a.out_f32 = db_dt == DET_F32 && dt != DET_F32;
+    const hipError_t e = detgemm::launch_cr(detgemm::OP_DW, static_cast<detgemm::Dt>(dt), a,
+                                            g_force_cr_fallback.load(std::memory_order_relaxed), stream);
+    if (e != hipSuccess) return fail(DET_ELAUNCH, "det_gemm: kernel launch failed: %s", hipGetErrorString(e));
+    return DET_OK;
+  }
   const hipError_t err = detgemm::launch_db(static_cast<detgemm::Dt>(dt), db_dt == DET_F32 && dt != DET_F32, dy, m, n,
                                             db, g_force_db_chunk.load(std::memory_order_relaxed), stream);
   if (err != hipSuccess) return fail(DET_ELAUNCH, "det_gemm: kernel launch failed: %s", hipGetErrorString(err));
@@ -267,6 +301,12 @@ det_status_t det_gemm_debug_force_family(int family) {
 det_status_t det_gemm_debug_force_exact_kernel(int variant) {
   if (variant < -1 || variant > 4) return fail(DET_EINVAL, "det_gemm: exact kernel must be -1 .. 4%s");
   g_force_exact.store(variant, std::memory_order_relaxed);
+  return DET_OK;
+}
+
+det_status_t det_gemm_debug_force_cr_fallback(int on) {
+  if (on != 0 && on != 1) return fail(DET_EINVAL, "det_gemm: cr fallback switch must be 0 or 1%s");
+  g_force_cr_fallback.store(on, std::memory_order_relaxed);
   return DET_OK;
 }
 

@@ -119,6 +119,8 @@ hipError_t launch_layernorm_fwd(Dt dt, const void* x, const void* gamma, const v
 hipError_t launch_layernorm_bwd(Dt dt, bool param_f32, const void* dy, const void* x, const double* mean,
                                 const double* rstd, const void* gamma, int64_t rows, int64_t h, void* dx,
                                 void* dgamma, void* dbeta, hipStream_t stream);
+// Correctly rounded tier; a null A stands for a column of ones.
+hipError_t launch_cr(Op op, Dt dt, const GemmArgs& a, int force_fallback, hipStream_t stream);
 hipError_t stream_workspace(hipStream_t stream, size_t bytes, void** ptr);
 
 }  // namespace detgemm

@@ -1,0 +1,580 @@
+// Correctly rounded tier: every output is the exact value of its dot product
+// (+ bias) rounded once to the output type (Carbon README, alia-carbon 0.2.0,
+// "Roadmap", v0.2: exact summation with a superaccumulator, so that the result
+// no longer depends on any order). Exactness makes the result independent of
+// the reduction order, the tiling and the launch.
+//
+// How the exact value is reached on the matrix of the GEMM, in three launches:
+//
+//  1. stats: for every row r of A (the output-row operand, over the reduction)
+//     the highest set bit top_r and the lowest set bit low_r of its nonzero
+//     values, and for every column c of B the same; with a forward bias the
+//     rows also count the value 1 and the columns their bias (the bias is the
+//     product 1 * b_c at one extra reduction index). Maximum and minimum are
+//     order-free, so the partial results of the workgroups meet in global
+//     atomics. Non-finite values set a flag.
+//
+//  2. sliced tiles: a value v of row r is cut into 24-bit slices at fixed
+//     positions below top_r: slice s holds the bits of v with weights
+//     2^(top_r - 24 s - 23) .. 2^(top_r - 24 s), as a signed integer a_s below
+//     2^24 (so v = sum_s a_s 2^(top_r - 24 s - 23), exactly). The same for the
+//     columns of B. For one slice pair (s, t) the integer products a_s b_t are
+//     below 2^48, so a float64 fma chain over 32 reduction indices stays below
+//     2^53 and is exact; each such block sum is added to an int64, and the
+//     pairs are combined in an int128 at their offsets 24 (s + t). A tile whose
+//     rows or columns need at most two slices (span of set bits <= 48) and hold
+//     only finite values is finished here: the int128 is rounded to odd at 53
+//     bits (truncate, set the last bit when anything was dropped), scaled by
+//     its power of two, and rounded to the output type by the same single-
+//     rounding path as the other tiers; rounding to odd first and then to a
+//     format at least two bits narrower is one correct rounding (Boldo and
+//     Melquiond, IEEE TC 2008).
+//
+// A null A operand stands for a column of ones (the bias gradient as the
+// correctly rounded column sum of dY).
+//
+//  3. fallback: tiles flagged by 2 (wide spans or non-finite values) are
+//     summed one output at a time in a superaccumulator: 21 int64 chunks of 32
+//     bits each in LDS, covering every bit a product or bias can carry (2^-350
+//     .. 2^632), each float64 product added at its bit position; carries are
+//     propagated once at the end, and the integer is rounded as in 2. Sums with
+//     an infinity or a NaN give the float64 sum of those terms.
+//
+// Both ways give the same bits for a tile (they compute the same exact value),
+// so the split between them changes only the speed.
+
+#include <climits>
+
+#include "common.hpp"
+
+namespace detgemm {
+namespace cr {
+
+constexpr int TILE = 64;
+constexpr int KB = 32;                 // reduction indices per exact float64 block
+constexpr int SLICE = 24;              // bits per slice
+constexpr int NOBITS = -100000;        // "no set bit" markers of an all-zero row or column
+constexpr int NOLOW = 100000;
+constexpr int NCH = 21;                // superaccumulator chunks
+constexpr int OFF = 352;               // bit index of 2^0 in the superaccumulator
+
+// Sign, integer significand and the weight of its last bit of one stored value.
+struct Parts {
+  uint32_t sig;
+  int lsb;
+  bool neg, finite;
+};
+
+template <typename E> __device__ inline Parts parts(typename E::T v);
+template <> __device__ inline Parts parts<F32>(float v) {
+  const uint32_t u = __float_as_uint(v);
+  const uint32_t e = (u >> 23) & 0xffu, f = u & 0x7fffffu;
+  Parts p;
+  p.neg = (u >> 31) != 0;
+  p.finite = e != 0xffu;
+  p.sig = e ? (f | 0x800000u) : f;
+  p.lsb = e ? static_cast<int>(e) - 150 : -149;
+  return p;
+}
+template <> __device__ inline Parts parts<BF16>(uint16_t v) {
+  const uint32_t e = (v >> 7) & 0xffu, f = v & 0x7fu;
+  Parts p;
+  p.neg = (v >> 15) != 0;
+  p.finite = e != 0xffu;
+  p.sig = e ? (f | 0x80u) : f;
+  p.lsb = e ? static_cast<int>(e) - 134 : -133;
+  return p;
+}
+template <> __device__ inline Parts parts<F16>(_Float16 v) {
+  uint16_t u;
+  __builtin_memcpy(&u, &v, 2);
+  const uint32_t e = (u >> 10) & 0x1fu, f = u & 0x3ffu;
+  Parts p;
+  p.neg = (u >> 15) != 0;
+  p.finite = e != 0x1fu;
+  p.sig = e ? (f | 0x400u) : f;
+  p.lsb = e ? static_cast<int>(e) - 25 : -24;
+  return p;
+}
+
+// highest and lowest set bit of a nonzero significand at weight 2^lsb
+__device__ inline int top_bit(const Parts& p) { return p.lsb + 31 - __builtin_clz(p.sig); }
+__device__ inline int low_bit(const Parts& p) { return p.lsb + __builtin_ctz(p.sig); }
+
+// Slice s of a value whose row or column has top bit `top`: the bits with
+// weights 2^(top - 24 s - 23) .. 2^(top - 24 s) as a signed integer.
+__device__ inline double slice(const Parts& p, int top, int s) {
+  if (p.sig == 0) return 0.0;
+  const int low = top - SLICE * s - (SLICE - 1);
+  const int sh = p.lsb - low;
+  uint64_t part;
+  if (sh >= 0)
+    part = sh >= SLICE ? 0 : ((static_cast<uint64_t>(p.sig) << sh) & 0xffffffull);
+  else
+    part = -sh >= SLICE ? 0 : ((static_cast<uint64_t>(p.sig) >> (-sh)) & 0xffffffull);
+  const double d = static_cast<double>(part);
+  return p.neg ? -d : d;
+}
+
+// 2^x as a float64, -1022 <= x <= 1023
+__device__ inline double pow2(int x) { return __longlong_as_double(static_cast<long long>(x + 1023) << 52); }
+
+// Round to odd at 53 bits of the integer z (two's complement, |z| < 2^126),
+// times 2^scale. The result is a float64 from which one further rounding to a
+// format of at most 51 bits is the correct rounding of z * 2^scale.
+__device__ inline double round_odd53(__int128 z, int scale) {
+  if (z == 0) return 0.0;
+  const bool neg = z < 0;
+  unsigned __int128 mag = neg ? static_cast<unsigned __int128>(-z) : static_cast<unsigned __int128>(z);
+  const uint64_t hi = static_cast<uint64_t>(mag >> 64), lo = static_cast<uint64_t>(mag);
+  const int n = hi ? 128 - __builtin_clzll(hi) : 64 - __builtin_clzll(lo);
+  uint64_t top;
+  int sh = 0;
+  if (n <= 53) {
+    top = lo;
+  } else {
+    sh = n - 53;
+    top = static_cast<uint64_t>(mag >> sh);
+    const unsigned __int128 rest = mag - (static_cast<unsigned __int128>(top) << sh);
+    if (rest != 0) top |= 1u;
+  }
+  const double d = static_cast<double>(top) * pow2(scale + sh);   // exact: top < 2^53, power of two in range
+  return neg ? -d : d;
+}
+
+// ---- 1. stats ---------------------------------------------------------------
+
+// Stats of a 2D array X[outer][inner] (inner contiguous) per outer index
+// (PER_OUTER: reduced over inner) or per inner index (reduced over outer).
+// Each thread folds a strip and meets the others in atomics.
+template <typename E, bool PER_OUTER>
+__global__ void __launch_bounds__(256) stats_kernel(const typename E::T* __restrict__ X, int64_t outer, int64_t inner,
+                                                    int64_t strip, int* __restrict__ top, int* __restrict__ low,
+                                                    int* __restrict__ bad) {
+  const int64_t nidx = PER_OUTER ? outer : inner;     // indices the stats are kept for
+  const int64_t red = PER_OUTER ? inner : outer;      // length reduced over
+  int t = NOBITS, lo = NOLOW, nf = 0;
+  int64_t idx;
+  if constexpr (PER_OUTER) {
+    // a wave per outer index and strip; lanes along the contiguous dimension
+    const int lane = threadIdx.x & 63;
+    const int64_t w = (static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x) >> 6;
+    const int64_t strips = (red + strip - 1) / strip;
+    idx = w / strips;
+    if (idx >= nidx) return;
+    const int64_t r0 = (w % strips) * strip, r1 = r0 + strip < red ? r0 + strip : red;
+    for (int64_t r = r0 + lane; r < r1; r += 64) {
+      const Parts p = parts<E>(X[idx * inner + r]);
+      if (!p.finite) nf = 1;
+      else if (p.sig) {
+        t = max(t, top_bit(p));
+        lo = min(lo, low_bit(p));
+      }
+    }
+    for (int o = 32; o > 0; o >>= 1) {
+      t = max(t, __shfl_xor(t, o));
+      lo = min(lo, __shfl_xor(lo, o));
+      nf |= __shfl_xor(nf, o);
+    }
+    if (lane != 0) return;
+  } else {
+    // a thread per inner index and strip of outer rows; lanes along the contiguous dimension
+    const int64_t tid = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+    idx = tid % inner;
+    const int64_t s = tid / inner;
+    const int64_t r0 = s * strip;
+    if (r0 >= red) return;
+    const int64_t r1 = r0 + strip < red ? r0 + strip : red;
+    for (int64_t r = r0; r < r1; ++r) {
+      const Parts p = parts<E>(X[r * inner + idx]);
+      if (!p.finite) nf = 1;
+      else if (p.sig) {
+        t = max(t, top_bit(p));
+        lo = min(lo, low_bit(p));
+      }
+    }
+  }
+  if (t != NOBITS) {
+    atomicMax(top + idx, t);
+    atomicMin(low + idx, lo);
+  }
+  if (nf) atomicOr(bad + idx, 1);
+}
+
+// Initial values of the stats, plus the extra values: 1 for every A row, the
+// bias for every B column (when `extra` is set for that side).
+template <typename E>
+__global__ void __launch_bounds__(256) stats_init_kernel(int64_t rows, int64_t cols, int* __restrict__ topA,
+                                                         int* __restrict__ lowA, int* __restrict__ badA,
+                                                         int* __restrict__ topB, int* __restrict__ lowB,
+                                                         int* __restrict__ badB,
+                                                         const typename E::T* __restrict__ bias, int ones_a) {
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (i < rows) {
+    topA[i] = (bias || ones_a) ? 0 : NOBITS;   // the value 1 at the bias index, or A all ones
+    lowA[i] = (bias || ones_a) ? 0 : NOLOW;
+    badA[i] = 0;
+  }
+  if (i < cols) {
+    int t = NOBITS, lo = NOLOW, nf = 0;
+    if (bias) {
+      const Parts p = parts<E>(bias[i]);
+      if (!p.finite) nf = 1;
+      else if (p.sig) {
+        t = top_bit(p);
+        lo = low_bit(p);
+      }
+    }
+    topB[i] = t;
+    lowB[i] = lo;
+    badB[i] = nf;
+  }
+}
+
+__device__ inline int slices_of(int t, int lo) { return t == NOBITS ? 0 : (t - lo + SLICE) / SLICE; }
+
+// ---- operand access ---------------------------------------------------------
+
+// A(r, l) and B(l, c) of the GEMM, with the bias index l == red: A = 1, B = bias.
+template <typename E, bool A_RC>
+__device__ inline Parts a_at(const GemmArgs& g, int64_t r, int64_t l) {
+  using T = typename E::T;
+  const T* A = static_cast<const T*>(g.A);
+  if (l == g.red || !A) {   // bias index, or A a column of ones
+    Parts p;
+    p.neg = false;
+    p.finite = true;
+    p.sig = 1;
+    p.lsb = 0;
+    return p;
+  }
+  return parts<E>(A_RC ? A[r * g.lda + l] : A[l * g.lda + r]);
+}
+template <typename E, bool B_RC>
+__device__ inline Parts b_at(const GemmArgs& g, int64_t l, int64_t c) {
+  using T = typename E::T;
+  if (l == g.red) return parts<E>(static_cast<const T*>(g.bias)[c]);
+  const T* B = static_cast<const T*>(g.B);
+  return parts<E>(B_RC ? B[c * g.ldb + l] : B[l * g.ldb + c]);
+}
+
+struct Stats {
+  const int *topA, *lowA, *badA, *topB, *lowB, *badB;
+  int* flag;   // per tile: 1 when the fallback must finish it
+};
+
+// ---- 2. sliced tiles ---------------------------------------------------------
+
+template <typename E, typename O, bool A_RC, bool B_RC>
+__global__ void __launch_bounds__(256) sliced_kernel(GemmArgs g, Stats st, int tiles_c, int force_fallback) {
+  __shared__ double As[KB][TILE];
+  __shared__ double Bs[KB][TILE];
+  __shared__ int red_s[4];
+  const int tid = threadIdx.x;
+  const int tile = blockIdx.x;
+  const int64_t r0 = static_cast<int64_t>(tile / tiles_c) * TILE, c0 = static_cast<int64_t>(tile % tiles_c) * TILE;
+  const int64_t kt = g.red + (g.bias ? 1 : 0);   // reduction with the bias index
+
+  // the tile's slice counts and non-finite flag
+  if (tid < 4) red_s[tid] = 0;
+  __syncthreads();
+  {
+    const int i = tid & 63;
+    if (tid < 64 && r0 + i < g.rows) {
+      atomicMax(&red_s[0], slices_of(st.topA[r0 + i], st.lowA[r0 + i]));
+      if (st.badA[r0 + i]) atomicOr(&red_s[2], 1);
+    } else if (tid >= 64 && tid < 128 && c0 + i < g.cols) {
+      atomicMax(&red_s[1], slices_of(st.topB[c0 + i], st.lowB[c0 + i]));
+      if (st.badB[c0 + i]) atomicOr(&red_s[2], 1);
+    }
+  }
+  __syncthreads();
+  const int LA = red_s[0], LB = red_s[1];
+  const bool fallback = force_fallback || red_s[2] || LA > 2 || LB > 2;
+  if (tid == 0) st.flag[tile] = fallback ? 1 : 0;
+  if (fallback) return;   // uniform over the workgroup
+
+  const int ty = tid / 16, tx = tid % 16;   // outputs rows r0 + 4 ty + i, cols c0 + 4 tx + j
+  int trow[4], tcol[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int64_t r = r0 + 4 * ty + i, c = c0 + 4 * tx + i;
+    trow[i] = r < g.rows ? st.topA[r] : NOBITS;
+    tcol[i] = c < g.cols ? st.topB[c] : NOBITS;
+  }
+  // staging: element (x = tid % 64, l = 8 (tid / 64) + j) of each operand tile
+  const int sx = tid % 64, sl = 8 * (tid / 64);
+  const int64_t sr = r0 + sx, sc = c0 + sx;
+  const int stop_a = sr < g.rows ? st.topA[sr] : NOBITS;
+  const int stop_b = sc < g.cols ? st.topB[sc] : NOBITS;
+
+  __int128 Z[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) Z[i][j] = 0;
+
+  for (int s = 0; s < LA; ++s) {
+    for (int t = 0; t < LB; ++t) {
+      int64_t I[4][4];
+      double acc[4][4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          I[i][j] = 0;
+          acc[i][j] = 0.0;
+        }
+      int blocks = 0;
+      for (int64_t kb = 0; kb < kt; kb += KB) {
+        __syncthreads();
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const int64_t l = kb + sl + j;
+          double av = 0.0, bv = 0.0;
+          if (l < kt) {
+            if (sr < g.rows) av = slice(a_at<E, A_RC>(g, sr, l), stop_a, s);
+            if (sc < g.cols) bv = slice(b_at<E, B_RC>(g, l, sc), stop_b, t);
+          }
+          As[sl + j][sx] = av;
+          Bs[sl + j][sx] = bv;
+        }
+        __syncthreads();
+#pragma unroll 4
+        for (int l = 0; l < KB; ++l) {
+          double a[4], b[4];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            a[i] = As[l][4 * ty + i];
+            b[i] = Bs[l][4 * tx + i];
+          }
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) acc[i][j] = __builtin_fma(a[i], b[j], acc[i][j]);
+        }
+        // each block sum is an integer below 2^53: exact in int64
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            I[i][j] += static_cast<int64_t>(acc[i][j]);
+            acc[i][j] = 0.0;
+          }
+        if (++blocks == 1024) {   // keep the int64 below 2^63
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+              Z[i][j] += static_cast<__int128>(I[i][j]) << (48 - SLICE * (s + t));
+              I[i][j] = 0;
+            }
+          blocks = 0;
+        }
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) Z[i][j] += static_cast<__int128>(I[i][j]) << (48 - SLICE * (s + t));
+    }
+  }
+  // Z counts units of 2^(top_r + top_c - 94): slice pair (s, t) has unit
+  // 2^(top_r - 24 s - 23 + top_c - 24 t - 23) and sits 48 - 24 (s + t) bits up.
+  using OT = typename O::T;
+  OT* out = static_cast<OT*>(g.out);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int64_t r = r0 + 4 * ty + i;
+    if (r >= g.rows) continue;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int64_t c = c0 + 4 * tx + j;
+      if (c >= g.cols) continue;
+      const double v = Z[i][j] == 0 ? 0.0 : round_odd53(Z[i][j], trow[i] + tcol[j] - 94);
+      out[r * g.cols + c] = round_from_f64<O>(v);
+    }
+  }
+}
+
+// ---- 3. fallback ---------------------------------------------------------------
+
+// Adds the finite float64 term v to the chunks (each chunk counts 32 bits;
+// the int64 leaves room for 2^31 additions before a carry is needed).
+__device__ inline void sacc_add(int64_t* ch, double v) {
+  const uint64_t u = static_cast<uint64_t>(__double_as_longlong(v));
+  const int e = static_cast<int>((u >> 52) & 0x7ffu);
+  if (e == 0) return;   // zero (subnormal float64 terms do not occur: |products| >= 2^-298)
+  const uint64_t M = (u & 0xfffffffffffffull) | (1ull << 52);   // |v| = M * 2^(e - 1075)
+  const int bit = e - 1075 + OFF;
+  const int ci = bit >> 5, sh = bit & 31;
+  const unsigned __int128 w = static_cast<unsigned __int128>(M) << sh;
+  const int64_t p0 = static_cast<int64_t>(static_cast<uint64_t>(w) & 0xffffffffu);
+  const int64_t p1 = static_cast<int64_t>(static_cast<uint64_t>(w >> 32) & 0xffffffffu);
+  const int64_t p2 = static_cast<int64_t>(static_cast<uint64_t>(w >> 64));
+  if (u >> 63) {
+    ch[ci] -= p0;
+    ch[ci + 1] -= p1;
+    ch[ci + 2] -= p2;
+  } else {
+    ch[ci] += p0;
+    ch[ci + 1] += p1;
+    ch[ci + 2] += p2;
+  }
+}
+
+// The chunks' exact value rounded to odd at 53 bits (see round_odd53).
+__device__ inline double sacc_round_odd53(int64_t* ch) {
+  // carry-propagate into 32-bit digits; the final carry is the sign extension
+  int64_t carry = 0;
+  for (int i = 0; i < NCH; ++i) {
+    const int64_t v = ch[i] + carry;
+    ch[i] = v & 0xffffffff;
+    carry = v >> 32;   // arithmetic shift
+  }
+  const bool neg = carry < 0;
+  if (neg) {   // magnitude = two's complement of the digits
+    int64_t c = 1;
+    for (int i = 0; i < NCH; ++i) {
+      const int64_t v = ((~ch[i]) & 0xffffffff) + c;
+      ch[i] = v & 0xffffffff;
+      c = v >> 32;
+    }
+  }
+  int hi = -1;
+  for (int i = NCH - 1; i >= 0; --i)
+    if (ch[i]) {
+      hi = i;
+      break;
+    }
+  if (hi < 0) return 0.0;
+  // the top 96 bits from three digits, and whether anything below them is set
+  const uint64_t d2 = static_cast<uint64_t>(ch[hi]);
+  const uint64_t d1 = hi >= 1 ? static_cast<uint64_t>(ch[hi - 1]) : 0;
+  const uint64_t d0 = hi >= 2 ? static_cast<uint64_t>(ch[hi - 2]) : 0;
+  bool sticky = false;
+  for (int i = 0; i < hi - 2; ++i) sticky |= ch[i] != 0;
+  const unsigned __int128 w = (static_cast<unsigned __int128>(d2) << 64) | (d1 << 32) | d0;   // < 2^96
+  const int n = 64 - __builtin_clzll(d2) + 64;   // bit length of w
+  const int sh = n - 53;                        // >= 12
+  uint64_t top = static_cast<uint64_t>(w >> sh);
+  if (sticky || (w & ((static_cast<unsigned __int128>(1) << sh) - 1)) != 0) top |= 1u;
+  const int scale = 32 * (hi - 2) + sh - OFF;   // weight of top's last bit
+  const double d = static_cast<double>(top) * pow2(scale);
+  return neg ? -d : d;
+}
+
+template <typename E, typename O, bool A_RC, bool B_RC>
+__global__ void __launch_bounds__(256) fallback_kernel(GemmArgs g, Stats st, int tiles_c) {
+  __shared__ int64_t acc[256][NCH + 1];
+  const int tile = blockIdx.x;
+  if (!st.flag[tile]) return;   // uniform over the workgroup
+  const int tid = threadIdx.x;
+  const int64_t r0 = static_cast<int64_t>(tile / tiles_c) * TILE, c0 = static_cast<int64_t>(tile % tiles_c) * TILE;
+  const int64_t kt = g.red + (g.bias ? 1 : 0);
+  int64_t* ch = acc[tid];
+  using OT = typename O::T;
+  OT* out = static_cast<OT*>(g.out);
+  const int64_t c = c0 + tid % 64;
+  for (int q = 0; q < 16; ++q) {
+    const int64_t r = r0 + tid / 64 + 4 * q;
+    if (r >= g.rows || c >= g.cols) continue;
+    for (int i = 0; i < NCH; ++i) ch[i] = 0;
+    double nonfinite = 0.0;
+    bool has_nf = false;
+    for (int64_t l = 0; l < kt; ++l) {
+      // the stored values, upcast exactly (A is a column of ones when absent)
+      const typename E::T* A = static_cast<const typename E::T*>(g.A);
+      const typename E::T* B = static_cast<const typename E::T*>(g.B);
+      const double a = (l == g.red || !A) ? 1.0 : E::up(A_RC ? A[r * g.lda + l] : A[l * g.lda + r]);
+      const double b = E::up(l == g.red ? static_cast<const typename E::T*>(g.bias)[c]
+                                        : (B_RC ? B[c * g.ldb + l] : B[l * g.ldb + c]));
+      const double p = a * b;   // exact: products of f32/bf16/f16 values fit float64
+      if (!__builtin_isfinite(p)) {
+        nonfinite = has_nf ? nonfinite + p : p;
+        has_nf = true;
+      } else {
+        sacc_add(ch, p);
+      }
+    }
+    const double v = has_nf ? nonfinite : sacc_round_odd53(ch);
+    out[r * g.cols + c] = round_from_f64<O>(v);
+  }
+}
+
+// ---- launch -----------------------------------------------------------------
+
+template <typename E, typename O, bool A_RC, bool B_RC>
+hipError_t launch_typed(const GemmArgs& a, int force_fallback, hipStream_t stream) {
+  using T = typename E::T;
+  const int64_t tiles_r = (a.rows + TILE - 1) / TILE, tiles_c = (a.cols + TILE - 1) / TILE;
+  const int64_t tiles = tiles_r * tiles_c;
+  if (tiles > INT_MAX || tiles_c > INT_MAX) return hipErrorInvalidConfiguration;
+  const size_t ints = static_cast<size_t>(3 * a.rows + 3 * a.cols + tiles);
+  void* ws = nullptr;
+  hipError_t e = stream_workspace(stream, ints * sizeof(int), &ws);
+  if (e != hipSuccess) return e;
+  int* p = static_cast<int*>(ws);
+  Stats st;
+  int* topA = p;
+  int* lowA = topA + a.rows;
+  int* badA = lowA + a.rows;
+  int* topB = badA + a.rows;
+  int* lowB = topB + a.cols;
+  int* badB = lowB + a.cols;
+  int* flag = badB + a.cols;
+  st.topA = topA; st.lowA = lowA; st.badA = badA;
+  st.topB = topB; st.lowB = lowB; st.badB = badB;
+  st.flag = flag;
+  const int64_t nmax = a.rows > a.cols ? a.rows : a.cols;
+  hipLaunchKernelGGL((stats_init_kernel<E>), dim3(static_cast<unsigned>((nmax + 255) / 256)), dim3(256), 0, stream,
+                     a.rows, a.cols, topA, lowA, badA, topB, lowB, badB, static_cast<const T*>(a.bias),
+                     a.A ? 0 : 1);
+  // A(r, l): rows x red when reduction-contiguous (stats per outer), else red x rows (per inner)
+  const int64_t strip = 256;
+  auto stats = [&](const void* X, bool rc, int64_t n_idx, int64_t red, int64_t ld, int* top, int* low, int* bad) {
+    // the array is [n_idx][ld] (rc) or [red][ld] (!rc); ld is its contiguous length
+    if (rc) {
+      const int64_t waves = n_idx * ((red + strip - 1) / strip);
+      hipLaunchKernelGGL((stats_kernel<E, true>), dim3(static_cast<unsigned>((waves * 64 + 255) / 256)), dim3(256), 0,
+                         stream, static_cast<const T*>(X), n_idx, ld, strip, top, low, bad);
+    } else {
+      const int64_t threads = ld * ((red + strip - 1) / strip);
+      hipLaunchKernelGGL((stats_kernel<E, false>), dim3(static_cast<unsigned>((threads + 255) / 256)), dim3(256), 0,
+                         stream, static_cast<const T*>(X), red, ld, strip, top, low, bad);
+    }
+  };
+  if (a.A) stats(a.A, A_RC, a.rows, a.red, a.lda, topA, lowA, badA);
+  stats(a.B, B_RC, a.cols, a.red, a.ldb, topB, lowB, badB);
+  hipLaunchKernelGGL((sliced_kernel<E, O, A_RC, B_RC>), dim3(static_cast<unsigned>(tiles)), dim3(256), 0, stream, a,
+                     st, static_cast<int>(tiles_c), force_fallback);
+  hipLaunchKernelGGL((fallback_kernel<E, O, A_RC, B_RC>), dim3(static_cast<unsigned>(tiles)), dim3(256), 0, stream, a,
+                     st, static_cast<int>(tiles_c));
+  return hipGetLastError();
+}
+
+template <typename E, typename O>
+hipError_t launch_eo(Op op, const GemmArgs& a, int force_fallback, hipStream_t stream) {
+  switch (op) {
+    case OP_FWD: return launch_typed<E, O, true, false>(a, force_fallback, stream);
+    case OP_DX: return launch_typed<E, O, true, true>(a, force_fallback, stream);
+    case OP_DW: return launch_typed<E, O, false, false>(a, force_fallback, stream);
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace cr
+
+hipError_t launch_cr(Op op, Dt dt, const GemmArgs& a, int force_fallback, hipStream_t stream) {
+  switch (dt) {
+    case DT_F32: return cr::launch_eo<F32, F32>(op, a, force_fallback, stream);
+    case DT_BF16:
+      return a.out_f32 ? cr::launch_eo<BF16, F32>(op, a, force_fallback, stream)
+                       : cr::launch_eo<BF16, BF16>(op, a, force_fallback, stream);
+    case DT_F16:
+      return a.out_f32 ? cr::launch_eo<F16, F32>(op, a, force_fallback, stream)
+                       : cr::launch_eo<F16, F16>(op, a, force_fallback, stream);
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace detgemm

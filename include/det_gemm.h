@@ -37,6 +37,16 @@
  *     the chunk length follow from (m, k, n) alone -- never from the device,
  *     the family or alignment -- so the bits stay fixed by the shape. For
  *     f32 inputs S = 1.
+ *   DET_TIER_CR — Carbon README, "Roadmap", v0.2 (exact summation with a
+ *     superaccumulator, independent of any order): every output is the exact
+ *     real value of its dot product (plus the bias) rounded once to the output
+ *     type, ties to even; an exact zero is +0; terms with an infinity or a NaN
+ *     give the float64 sum of those terms. The bits are those of the exact
+ *     value, so they depend on no order, tiling, m or device. Reductions of at
+ *     most 2^27 - 1 (2^27 with the bias); longer ones return DET_EINVAL. The
+ *     tier keeps per-row and per-column statistics and per-tile flags in the
+ *     stream's workspace (4 bytes per row of each operand and per 64 x 64
+ *     output tile, times 3).
  *
  * Ownership and execution
  *   The caller owns every buffer. The library keeps no reference to any of them
@@ -78,7 +88,8 @@ typedef enum {
 
 typedef enum {
   DET_TIER_EXACT = 0, /* float64 tiles + Neumaier compensation, oracle bits */
-  DET_TIER_FAST = 1   /* matrix cores, f32 accumulate, within tolerance */
+  DET_TIER_FAST = 1,  /* matrix cores, f32 accumulate, within tolerance */
+  DET_TIER_CR = 2     /* the exact value rounded once: correctly rounded, order-free */
 } det_tier_t;
 
 typedef enum {
@@ -228,6 +239,14 @@ det_status_t det_gemm_debug_force_exact_kernel(int variant);
  * sum and its bits do not depend on them. Returns DET_EINVAL for tiles < 0.
  */
 det_status_t det_gemm_debug_force_db_chunk(int64_t tiles);
+
+/*
+ * Test hook: 1 sends every output tile of the correctly rounded tier to its
+ * per-output superaccumulator path, 0 restores the shape-and-data choice. Both
+ * paths compute the exact value, so this changes speed only. DET_EINVAL for
+ * other values.
+ */
+det_status_t det_gemm_debug_force_cr_fallback(int on);
 
 #ifdef __cplusplus
 }

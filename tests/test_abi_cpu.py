@@ -92,10 +92,22 @@ def test_dw_out_and_db_argument_checks():
     assert L.det_gemm_db(p, F16, p, 4, 4, BF16, 0, None) == -2
     assert L.det_gemm_db(p, BF16, p, 4, 4, F16, 0, None) == -2
     assert L.det_gemm_db(p, F32, p, 4, 4, 9, 0, None) == -2
-    assert L.det_gemm_db(p, F32, p, 4, 4, BF16, 2, None) == -3
+    assert L.det_gemm_db(p, F32, p, 4, 4, BF16, 7, None) == -3
     assert L.det_gemm_db(None, F32, p, 4, 4, BF16, 0, None) == -1
     assert L.det_gemm_db(p, F32, None, 4, 4, BF16, 0, None) == -1
     assert L.det_gemm_db(p, F32, p, 0, 4, BF16, 0, None) == -1
     assert L.det_gemm_db(p, F32, p, 4, -3, BF16, 0, None) == -1
     assert L.det_gemm_db(p, F32, p, 1 << 40, 1 << 40, BF16, 0, None) == -1
     assert "dtype" in dg.det_gemm_last_error() or dg.det_gemm_last_error()
+
+
+def test_cr_tier_checks():
+    L = dg.lib()
+    p = 0x1000  # never dereferenced: every call below is rejected before launch
+    BF16, CR = 1, 2
+    assert L.det_gemm_fwd(p, p, p, None, 4, 1 << 27, 4, BF16, CR, None) == -1   # reduction too long
+    assert L.det_gemm_dw(p, p, p, 1 << 27, 4, 4, BF16, CR, None) == -1
+    assert L.det_gemm_db(p, BF16, p, 1 << 27, 4, BF16, CR, None) == -1
+    assert L.det_gemm_fwd(p, p, p, None, 4, 4, 4, BF16, 3, None) == -3
+    assert dg.lib().det_gemm_debug_force_cr_fallback(2) == -1
+    assert dg.lib().det_gemm_debug_force_cr_fallback(0) == 0

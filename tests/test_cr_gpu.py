@@ -1,0 +1,141 @@
+"""Correctly rounded tier on the GPU against the oracle, bit for bit: every op and dtype
+on ragged multi-tile shapes (the sliced path), the same forced through the per-output
+superaccumulator path, wide exponent ranges and non-finite values (which take that path
+by themselves), cancellation witnesses, permutation invariance, the column sum and f32
+outputs, and sampled rows of the GPT-2 c_fc forward."""
+import numpy as np
+import pytest
+
+import oracle
+import synthetic as syn
+from tests.gpu_util import assert_bits_equal, to_dev, to_host
+from tests.pins import stor, vals, wide_f32
+
+pytestmark = pytest.mark.gpu
+
+SHAPES = [(1, 1, 1), (5, 37, 9), (64, 64, 64), (100, 70, 130), (130, 33, 65), (3, 300, 2)]
+
+
+@pytest.fixture(autouse=True)
+def _paths():
+    import deterministic_invariant_gemm_det_amd as dg
+    dg.det_gemm_debug_force_cr_fallback(0)
+    yield
+    dg.det_gemm_debug_force_cr_fallback(0)
+
+
+def _gpu(op, dt, A, B, bias=None, out_dtype=None):
+    import torch
+    import deterministic_invariant_gemm_det_amd as dg
+    a, b = to_dev(A, dt), to_dev(B, dt)
+    if op == "fwd":
+        y = dg.fwd(a, b, None if bias is None else to_dev(bias, dt), "cr")
+    elif op == "dx":
+        y = dg.dx(a, b, "cr")
+    else:
+        y = dg.dw(a, b, "cr", out_dtype=out_dtype)
+    torch.cuda.synchronize()
+    return to_host(y, "f32" if out_dtype is not None else dt)
+
+
+def _operands(seed, op, dt, m, k, n, wide=False):
+    sa = (m, k) if op != "dx" else (m, n)
+    sb = (k, n) if op != "dw" else (m, n)
+    if wide:
+        A = syn.to_storage(vals(wide_f32(seed, 0, sa, -40, 40), "f32"), dt)
+        B = syn.to_storage(vals(wide_f32(seed, 1, sb, -40, 40), "f32"), dt)
+    else:
+        A = syn.normal(seed, 0, sa, dt=dt)
+        B = syn.normal(seed, 1, sb, sigma=0.5, dt=dt)
+    bias = syn.normal(seed, 2, (n,), sigma=0.3, dt=dt) if op == "fwd" else None
+    return A, B, bias
+
+
+@pytest.mark.parametrize("dt", ["f32", "bf16", "f16"])
+@pytest.mark.parametrize("op", ["fwd", "dx", "dw"])
+def test_cr_parity(op, dt):
+    import deterministic_invariant_gemm_det_amd as dg
+    for si, (m, k, n) in enumerate(SHAPES):
+        for wide in (False, True):
+            if wide and dt == "f16":
+                continue   # f16's range is covered by the oracle pins; wide f32 exponents overflow it
+            print(f"cr {op} {dt} {(m, k, n)} wide={wide}", flush=True)
+            A, B, bias = _operands(1500 + si, op, dt, m, k, n, wide)
+            want = oracle.gemm_cr(op, dt, A, B, m, k, n, bias=bias)
+            got = _gpu(op, dt, A, B, bias)
+            assert_bits_equal(got, want, f"cr {op} {dt} {(m, k, n)} wide={wide}")
+            dg.det_gemm_debug_force_cr_fallback(1)
+            got2 = _gpu(op, dt, A, B, bias)
+            dg.det_gemm_debug_force_cr_fallback(0)
+            assert_bits_equal(got2, want, f"cr fallback {op} {dt} {(m, k, n)} wide={wide}")
+
+
+def test_cr_nonfinite():
+    dt, m, k, n = "f32", 70, 40, 66
+    A, B, bias = _operands(1550, "fwd", dt, m, k, n)
+    A = A.copy()
+    A[3, 5] = np.inf
+    A[10, 7] = np.nan
+    B = B.copy()
+    B[9, 20] = -np.inf
+    want = oracle.gemm_cr("fwd", dt, A, B, m, k, n, bias=bias)
+    got = _gpu("fwd", dt, A, B, bias)
+    wn, gn = np.isnan(want), np.isnan(got)
+    assert np.array_equal(wn, gn)
+    assert_bits_equal(np.where(gn, 0, got).astype(np.float32), np.where(wn, 0, want).astype(np.float32), "non-finite")
+
+
+def test_cr_cancellation_and_permutation():
+    dt = "f32"
+    # 2^100 + 1 - 2^100 in one reduction tile, per output row
+    X = stor(np.array([[2.0 ** 100, 1.0, -(2.0 ** 100)] * 11]), dt)
+    W = stor(np.ones((33, 3)), dt)
+    got = _gpu("fwd", dt, X, W)
+    assert np.all(got == 11.0), got
+    # any permutation of the reduction index gives the same bits
+    m, k, n = 40, 500, 70
+    A, B, bias = _operands(1560, "fwd", "bf16", m, k, n)
+    y = _gpu("fwd", "bf16", A, B, bias)
+    perm = np.random.default_rng(1560).permutation(k)
+    yp = _gpu("fwd", "bf16", np.ascontiguousarray(A[:, perm]), np.ascontiguousarray(B[perm, :]), bias)
+    assert_bits_equal(yp, y, "permuted reduction")
+
+
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+def test_cr_column_sum_and_f32_out(dt):
+    import torch
+    import deterministic_invariant_gemm_det_amd as dg
+    from tests.gpu_util import torch_dtype
+    for si, (m, n) in enumerate(((1, 1), (33, 70), (1000, 130), (4100, 65))):
+        G = syn.normal(1570 + si, 3, (m, n), dt=dt)
+        ones = syn.to_storage(np.ones((m, 1)), dt)
+        for out_dt in sorted({dt, "f32"}):
+            want = oracle.gemm_cr("dw", dt, ones, G, m, 1, n)[0]
+            if out_dt != dt:   # the exact sum rounded to f32: round the oracle's f32-typed result
+                want = oracle.gemm_cr("dw", "f32", syn.to_storage(np.ones((m, 1)), "f32"),
+                                      syn.to_storage(vals(G, dt), "f32"), m, 1, n)[0]
+            db = dg.db(to_dev(G, dt), "cr", out_dtype=torch_dtype(out_dt))
+            torch.cuda.synchronize()
+            assert_bits_equal(to_host(db, out_dt), want, f"cr db {dt}->{out_dt} {(m, n)}")
+    if dt == "bf16":
+        m, k, n = 300, 70, 90
+        X = syn.normal(1580, 0, (m, k), dt=dt)
+        G = syn.normal(1580, 3, (m, n), dt=dt)
+        want = oracle.gemm_cr("dw", "f32", syn.to_storage(vals(X, dt), "f32"), syn.to_storage(vals(G, dt), "f32"),
+                              m, k, n)
+        assert_bits_equal(_gpu("dw", dt, X, G, out_dtype=torch.float32), want, "cr dw -> f32")
+
+
+def test_cr_gpt2_c_fc_rows():
+    """The GPT-2 c_fc forward (8192 x 768 -> 3072, bf16): sampled rows against the oracle."""
+    import torch
+    import deterministic_invariant_gemm_det_amd as dg
+    dt, m, k, n = "bf16", 8192, 768, 3072
+    X = syn.normal(42, syn.TID_X, (m, k), dt=dt)
+    W = syn.normal(42, syn.TID_W, (k, n), sigma=0.02, dt=dt)
+    b = syn.normal(42, syn.TID_B, (n,), sigma=0.1, dt=dt)
+    rows = np.array([0, 1, 63, 64, 4095, 8191])
+    want = oracle.gemm_cr("fwd", dt, X, W, m, k, n, bias=b, rows=rows)
+    y = dg.fwd(to_dev(X, dt), to_dev(W, dt), to_dev(b, dt), "cr")
+    torch.cuda.synchronize()
+    assert_bits_equal(to_host(y, dt)[rows], want, "cr gpt2 c_fc rows")
