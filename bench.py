@@ -260,6 +260,15 @@ def next_rows(data, dev):
         out[f"dw_f32.c_fc.{tier}"] = {"us": round(us, 2), "tflops": round(tf, 2),
                                       "roofline": {"bound": "mfma", "achieved": round(tf, 2), "peak": peak,
                                                    "unit": "TFLOP/s", "frac": round(tf / peak, 4)}}
+    # the correctly rounded tier on c_fc (useful flops 2MNK; the kernels run one pass per slice pair)
+    for op, f in (("fwd", lambda: dg.fwd(d["x"], d["w"], None, "cr", out=d["y"])),
+                  ("dx", lambda: dg.dx(d["g"], d["w"], "cr", out=d["gx"])),
+                  ("dw", lambda: dg.dw(d["x"], d["g"], "cr", out=d["gw"]))):
+        us = _time_calls(f, stream, reps=3, warmup=1)
+        tf = fl / (us * 1e-6) / 1e12
+        out[f"cr.c_fc.{op}"] = {"us": round(us, 2), "tflops": round(tf, 2),
+                                "roofline": {"bound": "mfma", "achieved": round(tf, 2), "peak": PEAK_FP64,
+                                             "unit": "TFLOP/s", "frac": round(tf / PEAK_FP64, 4)}}
     h = 768
     x = data["c_fc"]["x"]                      # 8192 x 768 bf16
     gy = data["c_proj"]["g"]                   # 8192 x 768 bf16, the LayerNorm's incoming gradient

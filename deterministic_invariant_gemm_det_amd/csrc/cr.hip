@@ -14,21 +14,23 @@
 //     order-free, so the partial results of the workgroups meet in global
 //     atomics. Non-finite values set a flag.
 //
-//  2. sliced tiles: a value v of row r is cut into 24-bit slices at fixed
+//  2. sliced tiles: a value v of row r is cut into 23-bit slices at fixed
 //     positions below top_r: slice s holds the bits of v with weights
-//     2^(top_r - 24 s - 23) .. 2^(top_r - 24 s), as a signed integer a_s below
-//     2^24 (so v = sum_s a_s 2^(top_r - 24 s - 23), exactly). The same for the
-//     columns of B. For one slice pair (s, t) the integer products a_s b_t are
-//     below 2^48, so a float64 fma chain over 32 reduction indices stays below
-//     2^53 and is exact; each such block sum is added to an int64, and the
-//     pairs are combined in an int128 at their offsets 24 (s + t). A tile whose
-//     rows or columns need at most two slices (span of set bits <= 48) and hold
-//     only finite values is finished here: the int128 is rounded to odd at 53
-//     bits (truncate, set the last bit when anything was dropped), scaled by
-//     its power of two, and rounded to the output type by the same single-
-//     rounding path as the other tiers; rounding to odd first and then to a
-//     format at least two bits narrower is one correct rounding (Boldo and
-//     Melquiond, IEEE TC 2008).
+//     2^(top_r - 23 s - 22) .. 2^(top_r - 23 s), as a signed integer a_s below
+//     2^23 (so v = sum_s a_s 2^(top_r - 23 s - 22), exactly). The same for the
+//     columns of B. A prepass writes the first two slices of every value as
+//     float32 (exact) in a K-major, zero-padded layout. For one slice pair
+//     (s, t) the integer products a_s b_t are below 2^46, so the float64 matrix
+//     instructions summing 128 of them stay below 2^53 and are exact in any
+//     order; each such block sum is added to an int64, and the pairs are
+//     combined in an int128 at their offsets 23 (s + t). A tile whose rows or
+//     columns need at most two slices (span of set bits <= 46) and hold only
+//     finite values is finished here: the int128 is rounded to odd at 53 bits
+//     (truncate, set the last bit when anything was dropped), scaled by its
+//     power of two, and rounded to the output type by the same single-rounding
+//     path as the other tiers; rounding to odd first and then to a format at
+//     least two bits narrower is one correct rounding (Boldo and Melquiond,
+//     IEEE TC 2008).
 //
 // A null A operand stands for a column of ones (the bias gradient as the
 // correctly rounded column sum of dY).
@@ -52,7 +54,7 @@ namespace cr {
 
 constexpr int TILE = 64;
 constexpr int KB = 32;                 // reduction indices per exact float64 block
-constexpr int SLICE = 24;              // bits per slice
+constexpr int SLICE = 23;              // bits per slice
 constexpr int NOBITS = -100000;        // "no set bit" markers of an all-zero row or column
 constexpr int NOLOW = 100000;
 constexpr int NCH = 21;                // superaccumulator chunks
@@ -102,16 +104,17 @@ __device__ inline int top_bit(const Parts& p) { return p.lsb + 31 - __builtin_cl
 __device__ inline int low_bit(const Parts& p) { return p.lsb + __builtin_ctz(p.sig); }
 
 // Slice s of a value whose row or column has top bit `top`: the bits with
-// weights 2^(top - 24 s - 23) .. 2^(top - 24 s) as a signed integer.
+// weights 2^(top - SLICE s - SLICE + 1) .. 2^(top - SLICE s) as a signed integer.
 __device__ inline double slice(const Parts& p, int top, int s) {
   if (p.sig == 0) return 0.0;
   const int low = top - SLICE * s - (SLICE - 1);
   const int sh = p.lsb - low;
+  constexpr uint64_t mask = (uint64_t(1) << SLICE) - 1;
   uint64_t part;
   if (sh >= 0)
-    part = sh >= SLICE ? 0 : ((static_cast<uint64_t>(p.sig) << sh) & 0xffffffull);
+    part = sh >= SLICE ? 0 : ((static_cast<uint64_t>(p.sig) << sh) & mask);
   else
-    part = -sh >= SLICE ? 0 : ((static_cast<uint64_t>(p.sig) >> (-sh)) & 0xffffffull);
+    part = -sh >= 32 ? 0 : ((static_cast<uint64_t>(p.sig) >> (-sh)) & mask);
   const double d = static_cast<double>(part);
   return p.neg ? -d : d;
 }
@@ -265,15 +268,46 @@ struct Stats {
 
 // ---- 2. sliced tiles ---------------------------------------------------------
 
-template <typename E, typename O, bool A_RC, bool B_RC>
-__global__ void __launch_bounds__(256) sliced_kernel(GemmArgs g, Stats st, int tiles_c, int force_fallback) {
-  __shared__ double As[KB][TILE];
-  __shared__ double Bs[KB][TILE];
+// The two leading slices of every operand value, as float32 (exact: integers
+// below 2^23), laid out K-major and zero-padded: S[s][l][x] for l < ktp (the
+// reduction with the bias index, rounded up to 32) and x < np (rows of A or
+// columns of B, rounded up to 64), so that a tile's block is one aligned,
+// unconditional read. Rows or columns that need more slices are finished by
+// the fallback, so two suffice here.
+template <typename E, bool IS_A, bool RC>
+__global__ void __launch_bounds__(256) slice_prep_kernel(GemmArgs g, const int* __restrict__ top, int64_t n,
+                                                         int64_t np, int64_t ktp, float* __restrict__ S) {
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (i >= ktp * np) return;
+  const int64_t l = i / np, x = i % np;
+  float s0 = 0.0f, s1 = 0.0f;
+  const int64_t kt = g.red + (g.bias ? 1 : 0);
+  if (x < n && l < kt) {
+    const Parts p = IS_A ? a_at<E, RC>(g, x, l) : b_at<E, RC>(g, l, x);
+    if (p.finite && p.sig) {
+      const int t = top[x];
+      s0 = static_cast<float>(slice(p, t, 0));
+      s1 = static_cast<float>(slice(p, t, 1));
+    }
+  }
+  S[l * np + x] = s0;
+  S[ktp * np + l * np + x] = s1;
+}
+
+typedef double v4d __attribute__((ext_vector_type(4)));
+constexpr int LSD = 80;   // LDS row stride in doubles: the four k rows a wave reads per step land in alternate bank halves
+constexpr int SUBS = 4;   // 32-index stages per exact block (128 indices: 128 products below 2^46 stay below 2^53)
+
+template <typename O>
+__global__ void __launch_bounds__(256) sliced_kernel(GemmArgs g, Stats st, int tiles_c, int force_fallback,
+                                                     const float* __restrict__ SA, const float* __restrict__ SB,
+                                                     int64_t npa, int64_t npb, int64_t ktp) {
+  __shared__ double As[KB][LSD];
+  __shared__ double Bs[KB][LSD];
   __shared__ int red_s[4];
   const int tid = threadIdx.x;
   const int tile = blockIdx.x;
   const int64_t r0 = static_cast<int64_t>(tile / tiles_c) * TILE, c0 = static_cast<int64_t>(tile % tiles_c) * TILE;
-  const int64_t kt = g.red + (g.bias ? 1 : 0);   // reduction with the bias index
 
   // the tile's slice counts and non-finite flag
   if (tid < 4) red_s[tid] = 0;
@@ -294,106 +328,130 @@ __global__ void __launch_bounds__(256) sliced_kernel(GemmArgs g, Stats st, int t
   if (tid == 0) st.flag[tile] = fallback ? 1 : 0;
   if (fallback) return;   // uniform over the workgroup
 
-  const int ty = tid / 16, tx = tid % 16;   // outputs rows r0 + 4 ty + i, cols c0 + 4 tx + j
-  int trow[4], tcol[4];
+  // A wave owns 32 x 32 outputs as 2 x 2 blocks of V_MFMA_F64_16X16X4 (accumulator e
+  // of lane l: row 4e + l/16, column l%16 of its block).
+  const int wave = tid >> 6, lane = tid & 63;
+  const int wm = (wave >> 1) * 32, wn = (wave & 1) * 32;
+  const int lr = lane & 15, lk = lane >> 4;
+  int trow[2][4], tcol[2];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int64_t r = r0 + 4 * ty + i, c = c0 + 4 * tx + i;
-    trow[i] = r < g.rows ? st.topA[r] : NOBITS;
+  for (int i = 0; i < 2; ++i) {
+    const int64_t c = c0 + wn + 16 * i + lr;
     tcol[i] = c < g.cols ? st.topB[c] : NOBITS;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int64_t r = r0 + wm + 16 * i + 4 * e + lk;
+      trow[i][e] = r < g.rows ? st.topA[r] : NOBITS;
+    }
   }
-  // staging: element (x = tid % 64, l = 8 (tid / 64) + j) of each operand tile
-  const int sx = tid % 64, sl = 8 * (tid / 64);
-  const int64_t sr = r0 + sx, sc = c0 + sx;
-  const int stop_a = sr < g.rows ? st.topA[sr] : NOBITS;
-  const int stop_b = sc < g.cols ? st.topB[sc] : NOBITS;
+  // staging: thread copies 4 consecutive x at reduction rows lq and lq + 16 of the stage
+  const int sx = 4 * (tid % 16), lq = tid / 16;
 
-  __int128 Z[4][4];
+  __int128 Z[2][2][4];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < 2; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) Z[i][j] = 0;
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) Z[i][j][e] = 0;
 
+  const int64_t nstages = ktp / KB;
   for (int s = 0; s < LA; ++s) {
     for (int t = 0; t < LB; ++t) {
-      int64_t I[4][4];
-      double acc[4][4];
+      const float* sa = SA + s * ktp * npa + r0 + sx;
+      const float* sb = SB + t * ktp * npb + c0 + sx;
+      const int shift = 2 * SLICE - SLICE * (s + t);
+      float4 ra[2], rb[2];
+      auto load = [&](int64_t kb) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
+        for (int h = 0; h < 2; ++h) {
+          ra[h] = *reinterpret_cast<const float4*>(sa + (kb + lq + 16 * h) * npa);
+          rb[h] = *reinterpret_cast<const float4*>(sb + (kb + lq + 16 * h) * npb);
+        }
+      };
+      int64_t I[2][2][4];
+      v4d p[2][2];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          I[i][j] = 0;
-          acc[i][j] = 0.0;
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          p[i][j] = v4d{0.0, 0.0, 0.0, 0.0};
+#pragma unroll
+          for (int e = 0; e < 4; ++e) I[i][j][e] = 0;
         }
       int blocks = 0;
-      for (int64_t kb = 0; kb < kt; kb += KB) {
-        __syncthreads();
+      load(0);
+      for (int64_t st_i = 0; st_i < nstages; ++st_i) {
+        __syncthreads();   // the previous stage's reads of As, Bs are done
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          const int64_t l = kb + sl + j;
-          double av = 0.0, bv = 0.0;
-          if (l < kt) {
-            if (sr < g.rows) av = slice(a_at<E, A_RC>(g, sr, l), stop_a, s);
-            if (sc < g.cols) bv = slice(b_at<E, B_RC>(g, l, sc), stop_b, t);
-          }
-          As[sl + j][sx] = av;
-          Bs[sl + j][sx] = bv;
+        for (int h = 0; h < 2; ++h) {
+          double* da = &As[lq + 16 * h][sx];
+          double* db = &Bs[lq + 16 * h][sx];
+          da[0] = ra[h].x; da[1] = ra[h].y; da[2] = ra[h].z; da[3] = ra[h].w;
+          db[0] = rb[h].x; db[1] = rb[h].y; db[2] = rb[h].z; db[3] = rb[h].w;
         }
         __syncthreads();
-#pragma unroll 4
-        for (int l = 0; l < KB; ++l) {
-          double a[4], b[4];
+        if (st_i + 1 < nstages) load((st_i + 1) * KB);   // in flight during the stage below
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            a[i] = As[l][4 * ty + i];
-            b[i] = Bs[l][4 * tx + i];
-          }
-#pragma unroll
-          for (int i = 0; i < 4; ++i)
-#pragma unroll
-            for (int j = 0; j < 4; ++j) acc[i][j] = __builtin_fma(a[i], b[j], acc[i][j]);
+        for (int gk = 0; gk < KB / 4; ++gk) {
+          const int kr = 4 * gk + lk;
+          const double a0 = As[kr][wm + lr], a1 = As[kr][wm + 16 + lr];
+          const double b0 = Bs[kr][wn + lr], b1 = Bs[kr][wn + 16 + lr];
+          p[0][0] = __builtin_amdgcn_mfma_f64_16x16x4f64(a0, b0, p[0][0], 0, 0, 0);
+          p[0][1] = __builtin_amdgcn_mfma_f64_16x16x4f64(a0, b1, p[0][1], 0, 0, 0);
+          p[1][0] = __builtin_amdgcn_mfma_f64_16x16x4f64(a1, b0, p[1][0], 0, 0, 0);
+          p[1][1] = __builtin_amdgcn_mfma_f64_16x16x4f64(a1, b1, p[1][1], 0, 0, 0);
         }
-        // each block sum is an integer below 2^53: exact in int64
+        // every SUBS stages (and at the end) the block sums, integers below 2^53, go to int64
+        if ((st_i + 1) % SUBS == 0 || st_i + 1 == nstages) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
+          for (int i = 0; i < 2; ++i)
 #pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            I[i][j] += static_cast<int64_t>(acc[i][j]);
-            acc[i][j] = 0.0;
-          }
-        if (++blocks == 1024) {   // keep the int64 below 2^63
+            for (int j = 0; j < 2; ++j) {
 #pragma unroll
-          for (int i = 0; i < 4; ++i)
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-              Z[i][j] += static_cast<__int128>(I[i][j]) << (48 - SLICE * (s + t));
-              I[i][j] = 0;
+              for (int e = 0; e < 4; ++e) I[i][j][e] += static_cast<int64_t>(p[i][j][e]);
+              p[i][j] = v4d{0.0, 0.0, 0.0, 0.0};
             }
-          blocks = 0;
+          if (++blocks == 1024) {   // keep the int64 below 2^63
+#pragma unroll
+            for (int i = 0; i < 2; ++i)
+#pragma unroll
+              for (int j = 0; j < 2; ++j)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                  Z[i][j][e] += static_cast<__int128>(I[i][j][e]) << shift;
+                  I[i][j][e] = 0;
+                }
+            blocks = 0;
+          }
         }
       }
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
+      for (int i = 0; i < 2; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) Z[i][j] += static_cast<__int128>(I[i][j]) << (48 - SLICE * (s + t));
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) Z[i][j][e] += static_cast<__int128>(I[i][j][e]) << shift;
     }
   }
-  // Z counts units of 2^(top_r + top_c - 94): slice pair (s, t) has unit
-  // 2^(top_r - 24 s - 23 + top_c - 24 t - 23) and sits 48 - 24 (s + t) bits up.
+  // Z counts units of 2^(top_r + top_c - 4 SLICE + 2): slice pair (s, t) has unit
+  // 2^(top_r - SLICE (s + 1) + 1 + top_c - SLICE (t + 1) + 1) and sits SLICE (2 - s - t) bits up.
   using OT = typename O::T;
   OT* out = static_cast<OT*>(g.out);
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int64_t r = r0 + 4 * ty + i;
-    if (r >= g.rows) continue;
+  for (int i = 0; i < 2; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int64_t c = c0 + 4 * tx + j;
-      if (c >= g.cols) continue;
-      const double v = Z[i][j] == 0 ? 0.0 : round_odd53(Z[i][j], trow[i] + tcol[j] - 94);
-      out[r * g.cols + c] = round_from_f64<O>(v);
+    for (int j = 0; j < 2; ++j) {
+      const int64_t c = c0 + wn + 16 * j + lr;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int64_t r = r0 + wm + 16 * i + 4 * e + lk;
+        if (r < g.rows && c < g.cols) {
+          const double v = Z[i][j][e] == 0 ? 0.0 : round_odd53(Z[i][j][e], trow[i][e] + tcol[j] - 4 * SLICE + 2);
+          out[r * g.cols + c] = round_from_f64<O>(v);
+        }
+      }
     }
-  }
 }
 
 // ---- 3. fallback ---------------------------------------------------------------
@@ -509,11 +567,19 @@ hipError_t launch_typed(const GemmArgs& a, int force_fallback, hipStream_t strea
   const int64_t tiles_r = (a.rows + TILE - 1) / TILE, tiles_c = (a.cols + TILE - 1) / TILE;
   const int64_t tiles = tiles_r * tiles_c;
   if (tiles > INT_MAX || tiles_c > INT_MAX) return hipErrorInvalidConfiguration;
+  const int64_t kt = a.red + (a.bias ? 1 : 0);
+  const int64_t ktp = (kt + KB - 1) / KB * KB;
+  const int64_t npa = tiles_r * TILE, npb = tiles_c * TILE;
+  // workspace: int stats and flags, then (256-byte aligned) the float slices of A and B
   const size_t ints = static_cast<size_t>(3 * a.rows + 3 * a.cols + tiles);
+  const size_t off_slices = (ints * sizeof(int) + 255) / 256 * 256;
+  const size_t sa_floats = static_cast<size_t>(2 * ktp * npa), sb_floats = static_cast<size_t>(2 * ktp * npb);
   void* ws = nullptr;
-  hipError_t e = stream_workspace(stream, ints * sizeof(int), &ws);
+  hipError_t e = stream_workspace(stream, off_slices + (sa_floats + sb_floats) * sizeof(float), &ws);
   if (e != hipSuccess) return e;
   int* p = static_cast<int*>(ws);
+  float* SA = reinterpret_cast<float*>(static_cast<char*>(ws) + off_slices);
+  float* SB = SA + sa_floats;
   Stats st;
   int* topA = p;
   int* lowA = topA + a.rows;
@@ -529,7 +595,6 @@ hipError_t launch_typed(const GemmArgs& a, int force_fallback, hipStream_t strea
   hipLaunchKernelGGL((stats_init_kernel<E>), dim3(static_cast<unsigned>((nmax + 255) / 256)), dim3(256), 0, stream,
                      a.rows, a.cols, topA, lowA, badA, topB, lowB, badB, static_cast<const T*>(a.bias),
                      a.A ? 0 : 1);
-  // A(r, l): rows x red when reduction-contiguous (stats per outer), else red x rows (per inner)
   const int64_t strip = 256;
   auto stats = [&](const void* X, bool rc, int64_t n_idx, int64_t red, int64_t ld, int* top, int* low, int* bad) {
     // the array is [n_idx][ld] (rc) or [red][ld] (!rc); ld is its contiguous length
@@ -545,8 +610,12 @@ hipError_t launch_typed(const GemmArgs& a, int force_fallback, hipStream_t strea
   };
   if (a.A) stats(a.A, A_RC, a.rows, a.red, a.lda, topA, lowA, badA);
   stats(a.B, B_RC, a.cols, a.red, a.ldb, topB, lowB, badB);
-  hipLaunchKernelGGL((sliced_kernel<E, O, A_RC, B_RC>), dim3(static_cast<unsigned>(tiles)), dim3(256), 0, stream, a,
-                     st, static_cast<int>(tiles_c), force_fallback);
+  hipLaunchKernelGGL((slice_prep_kernel<E, true, A_RC>), dim3(static_cast<unsigned>((ktp * npa + 255) / 256)),
+                     dim3(256), 0, stream, a, topA, a.rows, npa, ktp, SA);
+  hipLaunchKernelGGL((slice_prep_kernel<E, false, B_RC>), dim3(static_cast<unsigned>((ktp * npb + 255) / 256)),
+                     dim3(256), 0, stream, a, topB, a.cols, npb, ktp, SB);
+  hipLaunchKernelGGL((sliced_kernel<O>), dim3(static_cast<unsigned>(tiles)), dim3(256), 0, stream, a, st,
+                     static_cast<int>(tiles_c), force_fallback, SA, SB, npa, npb, ktp);
   hipLaunchKernelGGL((fallback_kernel<E, O, A_RC, B_RC>), dim3(static_cast<unsigned>(tiles)), dim3(256), 0, stream, a,
                      st, static_cast<int>(tiles_c));
   return hipGetLastError();

@@ -139,3 +139,23 @@ def test_cr_gpt2_c_fc_rows():
     y = dg.fwd(to_dev(X, dt), to_dev(W, dt), to_dev(b, dt), "cr")
     torch.cuda.synchronize()
     assert_bits_equal(to_host(y, dt)[rows], want, "cr gpt2 c_fc rows")
+
+
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+def test_cr_two_slices(dt):
+    """Rows and columns whose set bits span 24..46 positions take two slices on the sliced path
+    (one tiny value per row of A and per column of B); the bits still match the oracle and the
+    superaccumulator path."""
+    import deterministic_invariant_gemm_det_amd as dg
+    m, k, n = 130, 100, 70
+    Av = vals(syn.normal(1590, 0, (m, k), dt=dt), dt)
+    Bv = vals(syn.normal(1590, 1, (k, n), sigma=0.5, dt=dt), dt)
+    Av[:, 7] = 1.5 * 2.0 ** -30
+    Bv[11, :] = -1.25 * 2.0 ** -28
+    A, B = stor(Av, dt), stor(Bv, dt)
+    bias = syn.normal(1590, 2, (n,), dt=dt)
+    want = oracle.gemm_cr("fwd", dt, A, B, m, k, n, bias=bias)
+    assert_bits_equal(_gpu("fwd", dt, A, B, bias), want, f"two slices {dt}")
+    dg.det_gemm_debug_force_cr_fallback(1)
+    assert_bits_equal(_gpu("fwd", dt, A, B, bias), want, f"two slices {dt}, superaccumulator")
+    dg.det_gemm_debug_force_cr_fallback(0)
