@@ -46,11 +46,22 @@ def uniform(seed, tid, start, count):
 
 def normal_f64(seed, tid, count, sigma=1.0):
     out = np.empty(count, dtype=np.float64)
-    for c0 in range(0, count, CHUNK):
+
+    def fill(c0):   # chunks are independent: their values do not depend on the threads
         c = min(CHUNK, count - c0)
         u = uniform(seed, tid, 2 * c0, 2 * c)
         u1, u2 = u[0::2], u[1::2]
         out[c0:c0 + c] = np.sqrt(-2.0 * np.log(1.0 - u1)) * np.cos(2.0 * np.pi * u2) * sigma
+
+    starts = range(0, count, CHUNK)
+    if count <= CHUNK:
+        for c0 in starts:
+            fill(c0)
+    else:
+        import os
+        from concurrent.futures import ThreadPoolExecutor
+        with ThreadPoolExecutor(max_workers=max(1, min(8, os.cpu_count() or 1))) as ex:
+            list(ex.map(fill, starts))
     return out
 
 
