@@ -61,21 +61,21 @@ struct F16 {
 // two fewer significand bits equals a single rounding from float64.
 __device__ inline float f64_to_f32_odd(double r) {
   const float f = static_cast<float>(r);  // round to nearest even
-  uint32_t u = __float_as_uint(f);
+  const uint32_t u = __float_as_uint(f);
   const double back = static_cast<double>(f);
-  if (back != r) {                        // inexact (NaN keeps its NaN-ness)
-    if (__builtin_fabs(back) > __builtin_fabs(r)) u -= 1u;  // step to the neighbour toward zero
-    u |= 1u;
-  }
-  return __uint_as_float(u);
+  // inexact: step to the neighbour toward zero if the rounding went away from
+  // zero, then set the last bit (selects rather than branches; a NaN stays NaN)
+  const bool inexact = back != r;
+  const uint32_t down = (inexact && __builtin_fabs(back) > __builtin_fabs(r)) ? 1u : 0u;
+  return __uint_as_float((u - down) | (inexact ? 1u : 0u));
 }
 
 // float32 -> bfloat16 bits, round to nearest even.
 __device__ inline uint16_t f32_to_bf16_rne(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return static_cast<uint16_t>((u >> 16) | 0x40u);  // quiet NaN
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return static_cast<uint16_t>(u >> 16);
+  const uint32_t u = __float_as_uint(f);
+  const uint32_t rounded = (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+  const uint32_t quiet_nan = (u >> 16) | 0x40u;
+  return static_cast<uint16_t>((u & 0x7fffffffu) > 0x7f800000u ? quiet_nan : rounded);   // a select, not a branch
 }
 
 // Single round-to-nearest-even of a float64 value to the output type.

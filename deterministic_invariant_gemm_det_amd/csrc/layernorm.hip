@@ -22,6 +22,8 @@
 // pass over them in tile order and shares the result through LDS. 64 / G rows
 // share a wave (two rows of 24 tiles for H = 768).
 
+#include <type_traits>
+
 #include "colsum.hpp"
 
 namespace detgemm {
@@ -115,10 +117,11 @@ __device__ inline double ordered_sum(const double* P, int T) {
 
 // A lane's tiles g, g + G, ... (nk of them): kept in registers (TPL > 0; the
 // loops over them are unrolled so that every register index is static) or read
-// again on each visit (TPL == 0).
-template <typename E, bool VEC, int TPL>
+// again on each visit (TPL == 0). VT: the register type of the kept values
+// (float64 converts them once; float halves the registers).
+template <typename E, bool VEC, int TPL, typename VT = float>
 struct Tiles {
-  float v[TPL > 0 ? TPL : 1][KT];
+  VT v[TPL > 0 ? TPL : 1][KT];
   const typename E::T* row;
   int h, g, G, nk;
   __device__ void init(const typename E::T* r, int hh, int gg, int GG, int T) {
@@ -130,7 +133,12 @@ struct Tiles {
     if constexpr (TPL > 0) {
 #pragma unroll
       for (int k = 0; k < TPL; ++k)
-        if (k < nk) load_tile<E, VEC>(row, h, g + k * G, v[k]);
+        if (k < nk) {
+          float tmp[KT];
+          load_tile<E, VEC>(row, h, g + k * G, tmp);
+#pragma unroll
+          for (int e = 0; e < KT; ++e) v[k][e] = static_cast<VT>(tmp[e]);
+        }
     }
   }
   // f(t, values) for each of the lane's tiles in ascending order
@@ -152,7 +160,7 @@ struct Tiles {
 
 // Two rows' worth of tiles visited together (x and dy of the backward).
 template <typename E, bool VEC, int TPL, typename F>
-__device__ inline void each2(Tiles<E, VEC, TPL>& a, Tiles<E, VEC, TPL>& b, F&& f) {
+__device__ inline void each2(Tiles<E, VEC, TPL, float>& a, Tiles<E, VEC, TPL, float>& b, F&& f) {
   if constexpr (TPL > 0) {
 #pragma unroll
     for (int k = 0; k < TPL; ++k)
@@ -182,13 +190,13 @@ __global__ void __launch_bounds__(256) fwd_kernel(const typename E::T* __restric
   const int T = gm.T, G = gm.G;
   double* P = sm + slot * T;
   double* stat = sm + gm.NW * gm.RW * T;   // [slot] mean, [NW RW + slot] rstd
-  Tiles<E, VEC, TPL> tl;
+  Tiles<E, VEC, TPL, typename std::conditional<TPL == 1, double, float>::type> tl;
   if (ok) tl.init(x + row * h, h, g, G, T);
 
   // pass 1: tile sums of x (elements past the row's end are skipped, so a
   // short last tile is the chain over its own elements)
   if (ok) {
-    tl.each([&](int t, const float(&v)[KT]) {
+    tl.each([&](int t, const auto& v) {
       double p = 0.0;
 #pragma unroll
       for (int e = 0; e < KT; ++e)
@@ -203,7 +211,7 @@ __global__ void __launch_bounds__(256) fwd_kernel(const typename E::T* __restric
 
   // pass 2: tile sums of (x - mean)^2
   if (ok) {
-    tl.each([&](int t, const float(&v)[KT]) {
+    tl.each([&](int t, const auto& v) {
       double p = 0.0;
 #pragma unroll
       for (int e = 0; e < KT; ++e) {
@@ -228,7 +236,7 @@ __global__ void __launch_bounds__(256) fwd_kernel(const typename E::T* __restric
   const double rs = stat[gm.NW * gm.RW + slot];
 
   // pass 3: y = (d * rstd) * gamma + beta, one rounding
-  tl.each([&](int t, const float(&v)[KT]) {
+  tl.each([&](int t, const auto& v) {
     float gv[KT], bv[KT];
     if (gamma) load_tile<E, VEC>(gamma, h, t, gv);
     if (beta) load_tile<E, VEC>(beta, h, t, bv);
