@@ -284,7 +284,7 @@ __global__ void __launch_bounds__(64 * WR * WC, 8 / (WR * WC)) fast16w_kernel(Ge
   static_assert(NS >= 2 && NS * SLOT * (8 / WAVES) <= 160 * 1024, "LDS (8 waves per compute unit)");
   // direct-to-LDS loads per wave per stage (the ones vmcnt must account for)
   constexpr int DL = (A_RC ? RcOperand<BM, WAVES, BK>::LOADS : 0) + (B_RC ? RcOperand<BN, WAVES, BK>::LOADS : 0);
-  static_assert((NS - 2) * DL <= 63, "vmcnt range");
+  static_assert((NS - 2) * DL <= 63 && NS <= 4, "vmcnt range; the stage wait below handles up to four stages");
   constexpr bool KM = !A_RC || !B_RC;
   __shared__ __attribute__((aligned(1024))) char lds[NS * SLOT];
 
@@ -416,9 +416,15 @@ __global__ void __launch_bounds__(64 * WR * WC, 8 / (WR * WC)) fast16w_kernel(Ge
             pending = -1;
           }
         }
-        // stage g + 1 landed: issued after its loads are the direct loads of
-        // stages g + 2 .. g + NS - 1
-        __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0((NS - 2) * DL));
+        // stage g + 1 landed: issued after its loads are only the direct loads
+        // of the stages requested after it, g + 2 .. requested - 1 (NS - 2 of
+        // them in the steady state, fewer near the end of the reduction)
+        {
+          const int after = requested - (g + 2);
+          if (NS >= 4 && after >= 2) __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(2 * DL));
+          else if (NS >= 3 && after >= 1) __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(DL));
+          else __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(0));
+        }
         __asm__ volatile("" ::: "memory");
         __builtin_amdgcn_s_barrier();
         __asm__ volatile("" ::: "memory");

@@ -38,7 +38,7 @@ def test_tolerance_and_families(op, dt):
         y = gpu_op(op, dt, A, B, bias, tier="fast")
         assert_within_tolerance(y, r, S, dt, f"fast {op} {dt} {(m, k, n)}")
         assert_bits_equal(gpu_op(op, dt, A, B, bias, tier="fast"), y, "rerun")
-        for fam in (0, 1):
+        for fam in (0, 1, 10, 12, 14):
             dg.det_gemm_debug_force_family(fam)
             assert_bits_equal(gpu_op(op, dt, A, B, bias, tier="fast"), y, f"family {fam}")
         dg.det_gemm_debug_force_family(-1)
