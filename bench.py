@@ -13,6 +13,11 @@ kernels run on; its HBM traffic comes from the committed counter summary
 under profiles/ while the kernel source is unchanged), skinny-M forward
 bandwidth and the CPU oracle's rate on a bounded sample are included.
 
+Per launch the median time gives the reported rate (minimum and mean beside
+it); the SHA-256 of every output is recorded. For context only, the vendor
+BLAS behind torch.matmul is timed on the same tensors (it carries no
+determinism contract and is not the product path).
+
 Profiling aids (not part of the measured step): --only tier.op runs just
 those launches, --copy-mib N times a plain device copy of N MiB, the known
 size against which memory counters are scaled.
@@ -43,6 +48,7 @@ def parse():
     p.add_argument("--cpu-seconds", type=float, default=12.0, help="budget of the CPU-oracle sample")
     p.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline")
     p.add_argument("--no-skinny", action="store_true", help="skip the skinny-M bandwidth measurements")
+    p.add_argument("--no-vendor", action="store_true", help="skip the vendor-BLAS context timings")
     p.add_argument("--no-next", action="store_true",
                    help="skip the bias-gradient, f32-dW and LayerNorm measurements")
     p.add_argument("--only", default=None,
@@ -111,8 +117,7 @@ def time_launches(steps, n_steps, warmup, stream):
             ev[s][i][1].record(stream)
     t_end.record(stream)
     torch.cuda.synchronize()
-    per_launch_ms = [sum(ev[s][i][0].elapsed_time(ev[s][i][1]) for s in range(n_steps)) / n_steps
-                     for i in range(len(steps))]
+    per_launch_ms = [[ev[s][i][0].elapsed_time(ev[s][i][1]) for s in range(n_steps)] for i in range(len(steps))]
     return t_start.elapsed_time(t_end), per_launch_ms
 
 
@@ -164,8 +169,9 @@ def copy_calibration(dev, mib, n_steps, warmup):
     stream = torch.cuda.current_stream(dev)
     steps = [("copy", "copy", "copy", lambda: dst.copy_(src))]
     total_ms, per = time_launches(steps, n_steps, warmup, stream)
-    print(json.dumps({"copy_bytes_read": n, "copy_bytes_written": n, "us_per_copy": round(per[0] * 1e3, 2),
-                      "GB_per_s": round(2 * n / (per[0] * 1e-3) / 1e9, 1)}))
+    ms = sum(per[0]) / len(per[0])
+    print(json.dumps({"copy_bytes_read": n, "copy_bytes_written": n, "us_per_copy": round(ms * 1e3, 2),
+                      "GB_per_s": round(2 * n / (ms * 1e-3) / 1e9, 1)}))
 
 
 def skinny(data, dev):
@@ -283,6 +289,58 @@ def next_rows(data, dev):
     return out
 
 
+def output_hashes(data, steps):
+    """SHA-256 (first 16 hex digits) of every GEMM output of one more pass of the step, so runs
+    on different boxes and days can be compared bit for bit."""
+    import hashlib
+    import torch
+    out = {}
+    for tier, name, op, f in steps:
+        f()
+        t = data[name][{"fwd": "y", "dx": "gx", "dw": "gw"}[op]]
+        torch.cuda.synchronize()
+        out[f"{tier}.{name}.{op}"] = hashlib.sha256(t.view(torch.int16).cpu().numpy().tobytes()).hexdigest()[:16]
+    return out
+
+
+def host_cpu():
+    """The host's CPU model name and logical CPU count."""
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return model, os.cpu_count()
+
+
+def vendor_context(data, dev, fast_per):
+    """Context only, not the product path: the vendor BLAS behind torch.matmul (hipBLASLt)
+    on the step's own bf16 tensors in their natural layouts (X @ W, dY @ W^T, X^T @ dY, the
+    transposes as views), with no determinism or batch-invariance contract. Each fast-tier
+    launch's time is reported beside it."""
+    import torch
+    stream = torch.cuda.current_stream(dev)
+    out = {}
+    for name, k, n in LAYERS:
+        d = data[name]
+        x, w, g = d["x"], d["w"], d["g"]
+        fl = 2.0 * TOKENS * k * n
+        for op, f in (("fwd", lambda: torch.matmul(x, w)), ("dx", lambda: torch.matmul(g, w.t())),
+                      ("dw", lambda: torch.matmul(x.t(), g))):
+            us = _time_calls(f, stream)
+            ours = fast_per[f"fast.{name}.{op}"]["us"]
+            out[f"{name}.{op}"] = {"us": round(us, 2), "tflops": round(fl / (us * 1e-6) / 1e12, 1),
+                                   "fast_tier_us": ours, "fast_over_vendor_time": round(ours / us, 3)}
+    tot_v = sum(v["us"] for v in out.values())
+    tot_f = sum(v["fast_tier_us"] for v in out.values())
+    out["total"] = {"us": round(tot_v, 1), "fast_tier_us": round(tot_f, 1), "fast_over_vendor_time": round(tot_f / tot_v, 3)}
+    return out
+
+
 def cpu_baseline(data, budget_s):
     """The oracle, as it stands, on a bounded sample of the step's exact-tier GEMMs (one core)."""
     import numpy as np
@@ -311,7 +369,9 @@ def cpu_baseline(data, budget_s):
                 rows_done += chunk
             pieces.append(f"{name}.{op}:{rows_done} rows")
     secs = time.perf_counter() - t0
+    model, ncpu = host_cpu()
     return {"value": flops / secs / 1e12, "unit": "TFLOP/s", "cores": 1, "kind": "oracle",
+            "host_cpu": model, "host_logical_cpus": ncpu,
             "sample": "exact-tier output rows of the step's six GEMMs (" + ", ".join(pieces) +
                       f"), {secs:.1f} s single-threaded, useful 2*M*N*K flops per row"}
 
@@ -332,12 +392,19 @@ def main():
     total_ms, per_launch_ms = time_launches(steps, args.steps, args.warmup, stream)
     ms_step = total_ms / args.steps
 
+    # per launch: mean over the timed steps (the figure rocprofv3's average duration
+    # is compared with), median and minimum beside it
     per = {}
     for i, (tier, name, op, _) in enumerate(steps):
-        ms = per_launch_ms[i]
+        times = sorted(per_launch_ms[i])
+        h = len(times) // 2
+        med = times[h] if len(times) % 2 else 0.5 * (times[h - 1] + times[h])
+        mean = sum(times) / len(times)
         k, n = data[name]["k"], data[name]["n"]
         fl = 2.0 * TOKENS * k * n
-        per[f"{tier}.{name}.{op}"] = {"us": round(ms * 1e3, 2), "tflops": round(fl / (ms * 1e-3) / 1e12, 2)}
+        per[f"{tier}.{name}.{op}"] = {"us": round(mean * 1e3, 2), "tflops": round(fl / (mean * 1e-3) / 1e12, 2),
+                                      "us_median": round(med * 1e3, 2), "us_min": round(times[0] * 1e3, 2),
+                                      "tflops_median": round(fl / (med * 1e-3) / 1e12, 2)}
     if args.only:
         print(json.dumps({"only": args.only, "steps": args.steps, "warmup": args.warmup, "per_gemm": per}))
         return
@@ -346,8 +413,10 @@ def main():
         keys = [k for k in per if k.startswith(tier + ".")]
         fl = sum(2.0 * TOKENS * data[k.split(".")[1]]["k"] * data[k.split(".")[1]]["n"] for k in keys)
         us = sum(per[k]["us"] for k in keys)
-        tf = fl / (us * 1e-6) / 1e12
-        return {"tflops": round(tf, 2), "pct_of_peak": round(100 * tf / peak, 2), "peak_tflops": peak, "us": round(us, 1)}
+        us_med = sum(per[k]["us_median"] for k in keys)
+        tf, tf_med = fl / (us * 1e-6) / 1e12, fl / (us_med * 1e-6) / 1e12
+        return {"tflops": round(tf, 2), "pct_of_peak": round(100 * tf / peak, 2), "peak_tflops": peak, "us": round(us, 1),
+                "tflops_median": round(tf_med, 2), "pct_of_peak_median": round(100 * tf_med / peak, 2)}
 
     total_flops = 2 * sum(2.0 * TOKENS * k * n * len(OPS) for _, k, n in LAYERS)
     value = total_flops / (ms_step * 1e-3) / 1e12
@@ -382,10 +451,13 @@ def main():
         "roofline": roofline,
         "roofline_fast": roofline_fast,
     }
+    result["output_sha256"] = output_hashes(data, steps)
     if not args.no_skinny:
         result["skinny_fwd_bf16_K768_N3072"] = skinny(data, dev)
     if not args.no_next:
         result["next_rows"] = next_rows(data, dev)
+    if not args.no_vendor:
+        result["vendor_blas_context"] = vendor_context(data, dev, per)
     if not args.no_cpu:
         result["cpu_baseline"] = cpu_baseline(data, args.cpu_seconds)
     print(json.dumps(result))
