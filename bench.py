@@ -13,8 +13,9 @@ kernels run on; its HBM traffic comes from the committed counter summary
 under profiles/ while the kernel source is unchanged), skinny-M forward
 bandwidth and the CPU oracle's rate on a bounded sample are included.
 
-Per launch the median time gives the reported rate (minimum and mean beside
-it); the SHA-256 of every output is recorded. For context only, the vendor
+Per launch the mean time gives the reported rate (median and minimum beside
+it); the SHA-256 of every output is recorded, and each tier is also stated as
+a fraction of the peak the library's own microkernels measure on the box. For context only, the vendor
 BLAS behind torch.matmul is timed on the same tensors (it carries no
 determinism contract and is not the product path).
 
@@ -49,6 +50,7 @@ def parse():
     p.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline")
     p.add_argument("--no-skinny", action="store_true", help="skip the skinny-M bandwidth measurements")
     p.add_argument("--no-vendor", action="store_true", help="skip the vendor-BLAS context timings")
+    p.add_argument("--no-peak", action="store_true", help="skip the measured-peak microkernels")
     p.add_argument("--no-next", action="store_true",
                    help="skip the bias-gradient, f32-dW and LayerNorm measurements")
     p.add_argument("--only", default=None,
@@ -452,6 +454,14 @@ def main():
         "roofline_fast": roofline_fast,
     }
     result["output_sha256"] = output_hashes(data, steps)
+    if not args.no_peak:
+        import deterministic_invariant_gemm_det_amd as dg
+        peaks = {"fp64_mfma_4x4x4": round(dg.measure_peak(0, 4000), 2), "fp64_fma_valu": round(dg.measure_peak(1, 4000), 2),
+                 "bf16_mfma_32x32x16": round(dg.measure_peak(2, 2000), 2), "unit": "TFLOP/s",
+                 "note": "the library's peak-rate microkernels at the box's running clock (no memory traffic)"}
+        result["measured_peak"] = peaks
+        result["tiers"]["exact"]["pct_of_measured_peak"] = round(100 * result["tiers"]["exact"]["tflops"] / peaks["fp64_mfma_4x4x4"], 2)
+        result["tiers"]["fast"]["pct_of_measured_peak"] = round(100 * result["tiers"]["fast"]["tflops"] / peaks["bf16_mfma_32x32x16"], 2)
     if not args.no_skinny:
         result["skinny_fwd_bf16_K768_N3072"] = skinny(data, dev)
     if not args.no_next:

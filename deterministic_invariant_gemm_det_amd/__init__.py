@@ -14,7 +14,7 @@ import os
 __all__ = [
     "det_gemm_fwd", "det_gemm_dx", "det_gemm_dw", "det_gemm_dw_out", "det_gemm_db", "det_gemm_strerror",
     "det_gemm_last_error", "det_gemm_version", "det_gemm_debug_force_family", "det_gemm_debug_force_exact_kernel",
-    "det_gemm_debug_force_db_chunk", "det_gemm_debug_force_cr_fallback",
+    "det_gemm_debug_force_db_chunk", "det_gemm_debug_force_cr_fallback", "det_gemm_measure_peak", "measure_peak",
     "DetGemmError", "LIB_PATH", "fwd", "dx", "dw", "db", "deterministic_linear", "Linear", "DTYPES", "TIERS",
     "det_layernorm_fwd", "det_layernorm_bwd", "layer_norm", "layer_norm_backward", "deterministic_layer_norm",
 ]
@@ -75,6 +75,8 @@ def lib():
         L.det_gemm_debug_force_db_chunk.restype = ci
         L.det_gemm_debug_force_cr_fallback.argtypes = [ci]
         L.det_gemm_debug_force_cr_fallback.restype = ci
+        L.det_gemm_measure_peak.argtypes = [ci, ci, vp, i64, ctypes.POINTER(ctypes.c_double), vp]
+        L.det_gemm_measure_peak.restype = ci
         _lib = L
     return _lib
 
@@ -163,6 +165,33 @@ def det_gemm_debug_force_db_chunk(tiles):
 
 def det_gemm_debug_force_cr_fallback(on):
     _check(lib().det_gemm_debug_force_cr_fallback(int(bool(on))))
+
+
+def det_gemm_measure_peak(kind, iters, out, out_len, stream):
+    """One peak-rate microkernel launch (measurement aid); returns the flops it performs."""
+    fl = ctypes.c_double(0.0)
+    _check(lib().det_gemm_measure_peak(kind, iters, _p(out), out_len, ctypes.byref(fl), stream))
+    return fl.value
+
+
+def measure_peak(kind, iters, reps=5, device=None):
+    """Sustained TFLOP/s of peak-rate microkernel `kind` (0: float64 4x4x4 MFMA, 1: float64
+    vector fma, 2: bf16 32x32x16 MFMA) on the current stream: one warm-up launch, then `reps`
+    launches between two events."""
+    import torch
+    dev = torch.device("cuda", torch.cuda.current_device()) if device is None else torch.device(device)
+    cus = torch.cuda.get_device_properties(dev).multi_processor_count
+    out = torch.empty(cus * 512, dtype=torch.float64, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    det_gemm_measure_peak(kind, iters, out, out.numel(), stream.cuda_stream)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    flops = 0.0
+    for _ in range(reps):
+        flops += det_gemm_measure_peak(kind, iters, out, out.numel(), stream.cuda_stream)
+    e1.record(stream)
+    torch.cuda.synchronize(dev)
+    return flops / (e0.elapsed_time(e1) * 1e-3) / 1e12
 
 
 # ---------------------------------------------------------------- torch layer

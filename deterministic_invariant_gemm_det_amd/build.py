@@ -12,7 +12,8 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 ROOT = os.path.dirname(HERE)
 LIB = os.path.join(HERE, "libdetgemm.so")
-SOURCES = ["abi.cpp", "exact.hip", "fast.hip", "fast16.hip", "fast16w.hip", "colsum.hip", "layernorm.hip", "cr.hip"]
+SOURCES = ["abi.cpp", "exact.hip", "fast.hip", "fast16.hip", "fast16w.hip", "colsum.hip", "layernorm.hip", "cr.hip",
+           "peak.hip"]
 # Per-source extra flags. The exact tier keeps matrix-core results in ordinary
 # VGPRs: the Neumaier update reads every partial on the vector ALU, and the
 # accumulator-register form would add a copy per partial.

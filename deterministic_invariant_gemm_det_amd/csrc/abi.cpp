@@ -13,6 +13,15 @@
 
 #include "common.hpp"
 
+namespace detgemm {
+// Peak-rate microkernels (measurement only, peak.hip): threads launched for
+// num_cu compute units, and the launch of kind 0 (float64 4x4x4 MFMA), 1
+// (float64 vector fma) or 2 (bf16 32x32x16 MFMA); *flops receives the flops
+// the launch performs.
+int64_t peak_threads(int num_cu);
+hipError_t launch_peak(int kind, int num_cu, int iters, double* out, double* flops, hipStream_t stream);
+}  // namespace detgemm
+
 namespace {
 
 thread_local char g_last_error[256] = "";
@@ -313,6 +322,23 @@ det_status_t det_gemm_debug_force_cr_fallback(int on) {
 det_status_t det_gemm_debug_force_db_chunk(int64_t tiles) {
   if (tiles < 0) return fail(DET_EINVAL, "det_gemm: db chunk must be >= 0%s");
   g_force_db_chunk.store(tiles, std::memory_order_relaxed);
+  return DET_OK;
+}
+
+det_status_t det_gemm_measure_peak(int kind, int iters, double* out, int64_t out_len, double* flops,
+                                   hipStream_t stream) {
+  if (kind < 0 || kind > 2) return fail(DET_EINVAL, "det_gemm_measure_peak: kind must be 0, 1 or 2%s");
+  if (iters < 1 || out == nullptr || flops == nullptr)
+    return fail(DET_EINVAL, "det_gemm_measure_peak: iters >= 1 and non-null out and flops required%s");
+  int cus = 0;
+  const det_status_t st = check_device(&cus);
+  if (st != DET_OK) return st;
+  if (out_len < detgemm::peak_threads(cus))
+    return fail(DET_EINVAL, "det_gemm_measure_peak: out must hold one double per thread (compute units x 512)%s");
+  if (detgemm::launch_peak(kind, cus, iters, out, flops, stream) != hipSuccess) {
+    (void)hipGetLastError();
+    return fail(DET_ELAUNCH, "det_gemm_measure_peak: kernel launch failed%s");
+  }
   return DET_OK;
 }
 

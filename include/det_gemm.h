@@ -248,6 +248,24 @@ det_status_t det_gemm_debug_force_db_chunk(int64_t tiles);
  */
 det_status_t det_gemm_debug_force_cr_fallback(int on);
 
+/*
+ * Measurement aid, not an operation of the method: runs one peak-rate
+ * microkernel on `stream`, so that a tier's rate can be compared with what the
+ * device sustains at its running clock as well as with the datasheet peak.
+ *   kind 0: V_MFMA_F64_4X4X4_4B_F64 back to back (the exact tier's chains);
+ *   kind 1: float64 vector fma (the exact tier's other float64 work);
+ *   kind 2: V_MFMA_F32_32X32X16_BF16 back to back (the fast tier).
+ * Two workgroups of 256 threads per compute unit, `iters` (>= 1) iterations
+ * each, no memory traffic. out: device buffer of out_len doubles, at least
+ * (compute units x 512); every thread writes one meaningless value (so the
+ * arithmetic is not optimised away). *flops (host) receives the flops the
+ * launch performs; time it with events on `stream`. DET_EINVAL for a bad
+ * kind, iters < 1, null pointers or a short buffer; DET_EDEVICE off gfx950;
+ * DET_ELAUNCH if the launch fails. The library allocates nothing.
+ */
+det_status_t det_gemm_measure_peak(int kind, int iters, double* out, int64_t out_len, double* flops,
+                                   hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -111,3 +111,14 @@ def test_cr_tier_checks():
     assert L.det_gemm_fwd(p, p, p, None, 4, 4, 4, BF16, 3, None) == -3
     assert dg.lib().det_gemm_debug_force_cr_fallback(2) == -1
     assert dg.lib().det_gemm_debug_force_cr_fallback(0) == 0
+
+
+def test_measure_peak_argument_checks():
+    L = dg.lib()
+    fl = ctypes.c_double(0.0)
+    p = 0x1000  # never dereferenced: rejected before any launch
+    assert L.det_gemm_measure_peak(3, 10, p, 1 << 20, ctypes.byref(fl), None) == -1
+    assert L.det_gemm_measure_peak(-1, 10, p, 1 << 20, ctypes.byref(fl), None) == -1
+    assert L.det_gemm_measure_peak(0, 0, p, 1 << 20, ctypes.byref(fl), None) == -1
+    assert L.det_gemm_measure_peak(0, 10, None, 1 << 20, ctypes.byref(fl), None) == -1
+    assert L.det_gemm_measure_peak(0, 10, p, 1 << 20, None, None) == -1
