@@ -122,6 +122,8 @@ struct Stager {
   int64_t gl;                      // this thread's first reduction index in tile 0
   int64_t ld, xlen, llen;
   bool full;                       // interior path usable for this block (uniform)
+  __amdgpu_buffer_rsrc_t rsrc;     // reduction-major interior path: the operand as a buffer
+  uint32_t lane_off;               // reduction-major interior path: byte offset of the lane's column
 
   __device__ Stager(const T* src_, int64_t ld_, int64_t x0, int64_t xlen_, int64_t llen_, bool aligned, bool off32) {
     const int t = threadIdx.x;
@@ -145,11 +147,18 @@ struct Stager {
       ustep = KT * ld_ * ES;
       uld = ld_ * ES;
       voff = static_cast<uint32_t>(x * ES);
+      // the buffer spans the operand (clamped to 31 bits: the interior path
+      // only runs when every element offset fits, off32)
+      const int64_t nbytes = ((llen_ - 1) * ld_ + xlen_) * ES;
+      rsrc = __builtin_amdgcn_make_buffer_rsrc(const_cast<T*>(src_), 0,
+                                               static_cast<int>(nbytes < 0x7fffffff ? nbytes : 0x7fffffff), 0x00020000);
+      lane_off = static_cast<uint32_t>(gx * ES);
     }
   }
 
   // Interior tiles (uniform test) load from a wave-uniform base plus a fixed
-  // per-lane 32-bit offset, with no per-tile vector arithmetic; edge tiles load
+  // per-lane 32-bit offset, with no per-tile vector arithmetic (reduction-major
+  // sources: buffer loads, the row offset in a scalar register); edge tiles load
   // every element from a clamped, always valid address and zero what lies
   // outside the operand. No lane-divergent branch, so the loads stay in flight.
   __device__ inline void load(int tile, Raw8<E>& r) const {
@@ -160,9 +169,19 @@ struct Stager {
         r = *reinterpret_cast<const Raw8<E>*>(tb + voff);
         return;
       }
+      // reduction-major: a per-lane column offset (vector) plus a per-row
+      // offset (scalar), so the eight loads need no vector address arithmetic
       uint32_t e[8];
+      const int row0 = static_cast<int>(static_cast<int64_t>(tile) * KT + gl);
+      const int rstep = static_cast<int>(uld);
 #pragma unroll
-      for (int j = 0; j < 8; ++j) e[j] = bits_of<T>(*reinterpret_cast<const T*>(tb + j * uld + voff));
+      for (int j = 0; j < 8; ++j) {
+        const int soff = (row0 + j) * rstep;
+        if constexpr (ES == 4)
+          e[j] = __builtin_amdgcn_raw_buffer_load_b32(rsrc, static_cast<int>(lane_off), soff, 0);
+        else
+          e[j] = __builtin_amdgcn_raw_buffer_load_b16(rsrc, static_cast<int>(lane_off), soff, 0);
+      }
 #pragma unroll
       for (int i = 0; i < Raw8<E>::NW; ++i)
         r.w[i] = (Raw8<E>::NW == 8) ? e[i] : (e[2 * i] | (e[2 * i + 1] << 16));
