@@ -81,11 +81,14 @@ __device__ inline void kbn_add(double& s, double& c, double p) {
 // LDS layout: dst[l * LS + x], float64; a wave's 64 lanes write 64 consecutive
 // doubles per store, so the stores are free of bank conflicts.
 
-// Eight elements kept as packed 32-bit words until they are written to LDS, so
-// the vector-load and edge paths leave the same registers behind and the
-// loads stay in flight across the arithmetic of the current tile.
-template <typename E> struct alignas(16) Raw8 {
-  static constexpr int NW = static_cast<int>(8 * sizeof(typename E::T) / 4);
+// Eight elements kept in registers as loaded until they are written to LDS, so
+// that the vector-load and edge paths leave the same registers behind and the
+// loads stay in flight across the arithmetic of the current tile. PACKED (a
+// reduction-contiguous source, one vector load): 32-bit words as in memory.
+// Otherwise one element per word (16-bit elements zero-extended): packing them
+// right after eight separate loads would wait for those loads at once.
+template <typename E, bool PACKED = true> struct alignas(16) Raw8 {
+  static constexpr int NW = PACKED ? static_cast<int>(8 * sizeof(typename E::T) / 4) : 8;
   uint32_t w[NW];
 };
 
@@ -102,8 +105,8 @@ template <> __device__ inline double up_bits<F16>(uint32_t b) {
 }
 
 // Element j of a Raw8 as float64.
-template <typename E> __device__ inline double element(const Raw8<E>& r, int j) {
-  if (sizeof(typename E::T) == 4) return up_bits<E>(r.w[j]);
+template <typename E, bool PACKED> __device__ inline double element(const Raw8<E, PACKED>& r, int j) {
+  if constexpr (Raw8<E, PACKED>::NW == 8) return up_bits<E>(r.w[j]);
   return up_bits<E>((r.w[j >> 1] >> (16 * (j & 1))) & 0xffffu);
 }
 
@@ -161,12 +164,14 @@ struct Stager {
   // sources: buffer loads, the row offset in a scalar register); edge tiles load
   // every element from a clamped, always valid address and zero what lies
   // outside the operand. No lane-divergent branch, so the loads stay in flight.
-  __device__ inline void load(int tile, Raw8<E>& r) const {
+  using Raw = Raw8<E, RED_CONTIG>;
+
+  __device__ inline void load(int tile, Raw& r) const {
     const bool interior = full && static_cast<int64_t>(tile + 1) * KT <= llen;
     if (interior) {
       const char* tb = ubase + tile * ustep;
       if (RED_CONTIG) {
-        r = *reinterpret_cast<const Raw8<E>*>(tb + voff);
+        r = *reinterpret_cast<const Raw*>(tb + voff);
         return;
       }
       // reduction-major: a per-lane column offset (vector) plus a per-row
@@ -183,8 +188,8 @@ struct Stager {
           e[j] = __builtin_amdgcn_raw_buffer_load_b16(rsrc, static_cast<int>(lane_off), soff, 0);
       }
 #pragma unroll
-      for (int i = 0; i < Raw8<E>::NW; ++i)
-        r.w[i] = (Raw8<E>::NW == 8) ? e[i] : (e[2 * i] | (e[2 * i + 1] << 16));
+      for (int i = 0; i < Raw::NW; ++i)
+        r.w[i] = (Raw::NW == 8) ? e[i] : (e[2 * i] | (e[2 * i + 1] << 16));
       return;
     }
     uint32_t e[8];
@@ -199,11 +204,11 @@ struct Stager {
       e[j] = (xok && l < llen) ? v : 0u;
     }
 #pragma unroll
-    for (int i = 0; i < Raw8<E>::NW; ++i)
-      r.w[i] = (Raw8<E>::NW == 8) ? e[i] : (e[2 * i] | (e[2 * i + 1] << 16));
+    for (int i = 0; i < Raw::NW; ++i)
+      r.w[i] = (Raw::NW == 8) ? e[i] : (e[2 * i] | (e[2 * i + 1] << 16));
   }
 
-  __device__ inline void store(double* __restrict__ dst, const Raw8<E>& r) const {
+  __device__ inline void store(double* __restrict__ dst, const Raw& r) const {
     const int t = threadIdx.x;
     const int x = t & 63, l = (t >> 6) * 8;
 #pragma unroll
@@ -238,7 +243,8 @@ __global__ void __launch_bounds__(THREADS) exact_valu_kernel(GemmArgs args) {
 
   const Stager<E, A_RED_CONTIG> sa(static_cast<const typename E::T*>(args.A), args.lda, row0, args.rows, args.red, args.vec_a, args.off32_a);
   const Stager<E, B_RED_CONTIG> sb(static_cast<const typename E::T*>(args.B), args.ldb, col0, args.cols, args.red, args.vec_b, args.off32_b);
-  Raw8<E> ra, rb;
+  typename decltype(sa)::Raw ra;
+  typename decltype(sb)::Raw rb;
 
   double s[16], c[16];
 #pragma unroll
@@ -324,7 +330,8 @@ __global__ void __launch_bounds__(THREADS, NBUF == 1 ? 3 : 2) exact_mfma4_kernel
 
   const Stager<E, A_RED_CONTIG, BMT> sa(static_cast<const typename E::T*>(args.A), args.lda, row0, args.rows, args.red, args.vec_a, args.off32_a);
   const Stager<E, B_RED_CONTIG> sb(static_cast<const typename E::T*>(args.B), args.ldb, col0, args.cols, args.red, args.vec_b, args.off32_b);
-  Raw8<E> ra, rb;
+  typename decltype(sa)::Raw ra;
+  typename decltype(sb)::Raw rb;
 
   int bcol[4];
 #pragma unroll
@@ -417,7 +424,8 @@ __global__ void __launch_bounds__(THREADS) exact_mfma_kernel(GemmArgs args) {
 
   const Stager<E, A_RED_CONTIG> sa(static_cast<const typename E::T*>(args.A), args.lda, row0, args.rows, args.red, args.vec_a, args.off32_a);
   const Stager<E, B_RED_CONTIG> sb(static_cast<const typename E::T*>(args.B), args.ldb, col0, args.cols, args.red, args.vec_b, args.off32_b);
-  Raw8<E> ra, rb;
+  typename decltype(sa)::Raw ra;
+  typename decltype(sb)::Raw rb;
 
   double s[2][2][4], c[2][2][4];
 #pragma unroll
