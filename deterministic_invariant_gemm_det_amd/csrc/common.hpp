@@ -70,18 +70,14 @@ __device__ inline float f64_to_f32_odd(double r) {
   return __uint_as_float((u - down) | (inexact ? 1u : 0u));
 }
 
-// float32 -> bfloat16 bits, round to nearest even.
-__device__ inline uint16_t f32_to_bf16_rne(float f) {
-  const uint32_t u = __float_as_uint(f);
-  const uint32_t rounded = (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
-  const uint32_t quiet_nan = (u >> 16) | 0x40u;
-  return static_cast<uint16_t>((u & 0x7fffffffu) > 0x7f800000u ? quiet_nan : rounded);   // a select, not a branch
-}
-
-// Single round-to-nearest-even of a float64 value to the output type.
+// Single round-to-nearest-even of a float64 value to the output type: for
+// bf16 and f16 round to odd at float32, then the hardware conversion
+// (V_CVT_PK_BF16_F32 / V_CVT_F16_F32, round to nearest even, subnormals kept).
 template <typename E> __device__ inline typename E::T round_from_f64(double r);
 template <> __device__ inline float round_from_f64<F32>(double r) { return static_cast<float>(r); }
-template <> __device__ inline uint16_t round_from_f64<BF16>(double r) { return f32_to_bf16_rne(f64_to_f32_odd(r)); }
+template <> __device__ inline uint16_t round_from_f64<BF16>(double r) {
+  return __builtin_bit_cast(uint16_t, static_cast<__bf16>(f64_to_f32_odd(r)));
+}
 template <> __device__ inline _Float16 round_from_f64<F16>(double r) { return static_cast<_Float16>(f64_to_f32_odd(r)); }
 
 // Round-to-nearest-even of an f32 accumulator to the output type.

@@ -15,7 +15,9 @@
 // Every float64 operation is IEEE-rounded (division and square root included),
 // so the results are the same bits on any device that follows the order.
 //
-// Row kernels: a row belongs to G = min(T, 64) lanes of one wave (T = tiles
+// Row kernels (at least four waves per SIMD, at most 128 registers, except the
+// backward with more than one tile per lane): a row belongs to G = min(T, 64)
+// lanes of one wave (T = tiles
 // per row); lane g owns tiles g, g + G, ... and keeps their values in
 // registers (up to TPL tiles, else it reads them again from memory). Each pass
 // writes the lane's tile partials to LDS; one lane per row runs the Neumaier
@@ -99,6 +101,57 @@ __device__ inline void store_tile(typename E::T* __restrict__ row, int h, int t,
   }
 }
 
+// Elements c0 .. c0 + 7 of a row (c0 a multiple of 8), upcast exactly to
+// float; elements past h read as 0. VEC: as load_tile (h is a multiple of the
+// elements per 16 bytes, so every 16-byte piece lies wholly inside or outside).
+template <typename E, bool VEC>
+__device__ inline void load8(const typename E::T* __restrict__ row, int h, int c0, float (&v)[8]) {
+  using T = typename E::T;
+  if constexpr (VEC) {
+    constexpr int PER = 16 / sizeof(T);
+#pragma unroll
+    for (int q = 0; q < 8 / PER; ++q) {
+      if (c0 + q * PER < h) {
+        const uint4 w = *reinterpret_cast<const uint4*>(row + c0 + q * PER);
+        T x[PER];
+        __builtin_memcpy(x, &w, 16);
+#pragma unroll
+        for (int e = 0; e < PER; ++e) v[q * PER + e] = E::to_f32(x[e]);
+      } else {
+#pragma unroll
+        for (int e = 0; e < PER; ++e) v[q * PER + e] = 0.0f;
+      }
+    }
+  } else {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) v[e] = c0 + e < h ? E::to_f32(row[c0 + e]) : 0.0f;
+  }
+}
+
+// Elements c0 .. c0 + 7 of a row, each rounded once; nothing is written past h.
+template <typename E, bool VEC>
+__device__ inline void store8(typename E::T* __restrict__ row, int h, int c0, const double (&r)[8]) {
+  using T = typename E::T;
+  if constexpr (VEC) {
+    constexpr int PER = 16 / sizeof(T);
+#pragma unroll
+    for (int q = 0; q < 8 / PER; ++q) {
+      if (c0 + q * PER < h) {
+        T x[PER];
+#pragma unroll
+        for (int e = 0; e < PER; ++e) x[e] = round_from_f64<E>(r[q * PER + e]);
+        uint4 w;
+        __builtin_memcpy(&w, x, 16);
+        *reinterpret_cast<uint4*>(row + c0 + q * PER) = w;
+      }
+    }
+  } else {
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+      if (c0 + e < h) row[c0 + e] = round_from_f64<E>(r[e]);
+  }
+}
+
 // Neumaier pass over P[0 .. T-1] in order (one lane).
 // The partials are read eight at a time ahead of the dependent updates.
 __device__ inline double ordered_sum(const double* P, int T) {
@@ -176,7 +229,7 @@ __device__ inline void each2(Tiles<E, VEC, TPL, float>& a, Tiles<E, VEC, TPL, fl
 }
 
 template <typename E, int TPL, bool VEC>
-__global__ void __launch_bounds__(256) fwd_kernel(const typename E::T* __restrict__ x,
+__global__ void __launch_bounds__(256, 4) fwd_kernel(const typename E::T* __restrict__ x,
                                                   const typename E::T* __restrict__ gamma,
                                                   const typename E::T* __restrict__ beta, int64_t rows, int h,
                                                   Geom gm, double eps, typename E::T* __restrict__ y,
@@ -235,25 +288,30 @@ __global__ void __launch_bounds__(256) fwd_kernel(const typename E::T* __restric
   if (!ok) return;
   const double rs = stat[gm.NW * gm.RW + slot];
 
-  // pass 3: y = (d * rstd) * gamma + beta, one rounding
+  // pass 3: y = (d * rstd) * gamma + beta, one rounding; eight elements at a
+  // time (few live registers, so that four waves fit on a SIMD)
   tl.each([&](int t, const auto& v) {
-    float gv[KT], bv[KT];
-    if (gamma) load_tile<E, VEC>(gamma, h, t, gv);
-    if (beta) load_tile<E, VEC>(beta, h, t, bv);
-    double r[KT];
 #pragma unroll
-    for (int e = 0; e < KT; ++e) {
-      double u = (static_cast<double>(v[e]) - mu) * rs;
-      if (gamma) u = u * static_cast<double>(gv[e]);
-      if (beta) u = u + static_cast<double>(bv[e]);
-      r[e] = u;
+    for (int q = 0; q < KT / 8; ++q) {
+      const int c0 = t * KT + 8 * q;
+      float gv[8], bv[8];
+      if (gamma) load8<E, VEC>(gamma, h, c0, gv);
+      if (beta) load8<E, VEC>(beta, h, c0, bv);
+      double r[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        double u = (static_cast<double>(v[8 * q + e]) - mu) * rs;
+        if (gamma) u = u * static_cast<double>(gv[e]);
+        if (beta) u = u + static_cast<double>(bv[e]);
+        r[e] = u;
+      }
+      store8<E, VEC>(y + row * h, h, c0, r);
     }
-    store_tile<E, VEC>(y + row * h, h, t, r);
   });
 }
 
 template <typename E, int TPL, bool VEC>
-__global__ void __launch_bounds__(256) bwd_dx_kernel(const typename E::T* __restrict__ dy,
+__global__ void __launch_bounds__(256, TPL == 1 ? 4 : 2) bwd_dx_kernel(const typename E::T* __restrict__ dy,
                                                      const typename E::T* __restrict__ x,
                                                      const double* __restrict__ mean, const double* __restrict__ rstd,
                                                      const typename E::T* __restrict__ gamma, int64_t rows, int h,
@@ -304,16 +362,21 @@ __global__ void __launch_bounds__(256) bwd_dx_kernel(const typename E::T* __rest
   if (!ok) return;
   const double a = stat[slot], b = stat[S + slot];
   each2(tx, tg, [&](int t, const float(&vx)[KT], const float(&vg)[KT]) {
-    float gm_[KT];
-    if (gamma) load_tile<E, VEC>(gamma, h, t, gm_);
-    double r[KT];
 #pragma unroll
-    for (int e = 0; e < KT; ++e) {
-      const double gv = gamma ? static_cast<double>(vg[e]) * static_cast<double>(gm_[e]) : static_cast<double>(vg[e]);
-      const double xh = (static_cast<double>(vx[e]) - mu) * rs;
-      r[e] = rs * ((gv - a) - xh * b);
+    for (int q = 0; q < KT / 8; ++q) {   // eight elements at a time (few live registers)
+      const int c0 = t * KT + 8 * q;
+      float gm_[8];
+      if (gamma) load8<E, VEC>(gamma, h, c0, gm_);
+      double r[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const double gv = gamma ? static_cast<double>(vg[8 * q + e]) * static_cast<double>(gm_[e])
+                                : static_cast<double>(vg[8 * q + e]);
+        const double xh = (static_cast<double>(vx[8 * q + e]) - mu) * rs;
+        r[e] = rs * ((gv - a) - xh * b);
+      }
+      store8<E, VEC>(dx + row * h, h, c0, r);
     }
-    store_tile<E, VEC>(dx + row * h, h, t, r);
   });
 }
 
