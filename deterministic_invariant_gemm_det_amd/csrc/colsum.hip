@@ -104,7 +104,7 @@ hipError_t launch_eo(const void* dy, int64_t m, int64_t n, void* db, int64_t chu
       hipLaunchKernelGGL((tile_kernel<E, true>), g1, b1, 0, stream, src, m, n, t0, nt, static_cast<int>(ncb), P);
     else
       hipLaunchKernelGGL((tile_kernel<E, false>), g1, b1, 0, stream, src, m, n, t0, nt, static_cast<int>(ncb), P);
-    launch_pass<O>(P, n, nt, state, ch == 0, ch == ck.nch - 1, out, stream);
+    launch_pass<O>(P, state, out, nullptr, nullptr, nullptr, n, nt, ch == 0, ch == ck.nch - 1, stream);
   }
   return hipGetLastError();
 }

@@ -3,10 +3,10 @@
 // 32-row tile and column, in a workspace), shared by the bias gradient and the
 // LayerNorm parameter gradients.
 //
-// The ordered pass: one workgroup per 64 columns; 8 waves stage 128 tiles of
-// partials at a time in LDS while wave 0 (one lane per column) runs the
-// Neumaier pass over them in tile order, the next 128 being loaded while it
-// does. Long reductions are cut into chunks of whole tiles whose partials fit
+// The ordered pass: one workgroup per 64 columns (and per array, when one
+// launch carries two column sums); 8 waves stage 128 tiles of partials at a
+// time in LDS while wave 0 (one lane per column) runs the Neumaier pass over
+// them in tile order, the next 128 being loaded while it does. Long reductions are cut into chunks of whole tiles whose partials fit
 // the workspace; the pass state (s, c) is kept there between chunks.
 #pragma once
 
@@ -33,13 +33,25 @@ __device__ inline void kbn_add(double& s, double& c, double p) {
   s = t;
 }
 
-// Neumaier pass over P[0 .. nt-1][col] in order, continuing (s, c) from state
-// unless first; writes db when last, else the state.
+// Up to two column-sum arrays handled by one launch (blockIdx.y picks one):
+// partials P[a], state[a], output out[a] (null: that array is skipped).
 template <typename O>
-__global__ void __launch_bounds__(THREADS2) pass_kernel(const double* __restrict__ P, int64_t n, int64_t nt,
-                                                        double* __restrict__ state, int first, int last,
-                                                        typename O::T* __restrict__ db) {
+struct PassArrays {
+  const double* P[2];
+  double* state[2];
+  typename O::T* out[2];
+};
+
+// Neumaier pass over P[0 .. nt-1][col] in order, continuing (s, c) from state
+// unless first; writes the output when last, else the state.
+template <typename O>
+__global__ void __launch_bounds__(THREADS2) pass_kernel(PassArrays<O> arr, int64_t n, int64_t nt, int first, int last) {
   __shared__ double L[TCH][CB];
+  const int a = blockIdx.y;
+  const double* __restrict__ P = arr.P[a];
+  double* __restrict__ state = arr.state[a];
+  typename O::T* __restrict__ out = arr.out[a];
+  if (out == nullptr) return;   // uniform over the workgroup: no barrier is skipped by part of it
   const int tid = threadIdx.x, lc = tid % CB, lr = tid / CB;
   const int64_t col = static_cast<int64_t>(blockIdx.x) * CB + lc;
   const bool ok = col < n;
@@ -79,7 +91,7 @@ __global__ void __launch_bounds__(THREADS2) pass_kernel(const double* __restrict
   }
   if (tid < CB && ok) {
     if (last) {
-      db[col] = round_from_f64<O>(s + c);
+      out[col] = round_from_f64<O>(s + c);
     } else {
       state[col] = s;
       state[n + col] = c;
@@ -113,12 +125,14 @@ inline Chunks plan_chunks(int64_t m, int64_t n, int64_t chunk_tiles) {
   return c;
 }
 
+// One launch for up to two arrays (P1, state1, out1 may be null).
 template <typename O>
-inline void launch_pass(const double* P, int64_t n, int64_t nt, double* state, bool first, bool last,
-                        typename O::T* out, hipStream_t stream) {
+inline void launch_pass(const double* P0, double* state0, typename O::T* out0, const double* P1, double* state1,
+                        typename O::T* out1, int64_t n, int64_t nt, bool first, bool last, hipStream_t stream) {
   const int64_t blocks = (n + CB - 1) / CB;
-  hipLaunchKernelGGL((pass_kernel<O>), dim3(static_cast<unsigned>(blocks)), dim3(THREADS2), 0, stream, P, n, nt,
-                     state, first ? 1 : 0, last ? 1 : 0, out);
+  PassArrays<O> arr{{P0, P1}, {state0, state1}, {out0, out1}};
+  hipLaunchKernelGGL((pass_kernel<O>), dim3(static_cast<unsigned>(blocks), out1 ? 2u : 1u), dim3(THREADS2), 0, stream,
+                     arr, n, nt, first ? 1 : 0, last ? 1 : 0);
 }
 
 }  // namespace colsum

@@ -513,8 +513,13 @@ hipError_t launch_params(const void* dy, const void* x, const double* mean, cons
       hipLaunchKernelGGL((param_tile_kernel<E, false>), g1, b1, 0, stream, static_cast<const T*>(dy),
                          static_cast<const T*>(x), mean, rstd, rows, h, t0, nt, static_cast<int>(ncb), Pg, Pb);
     const bool first = ch == 0, last = ch == ck.nch - 1;
-    if (dgamma) colsum::launch_pass<O>(Pg, h, nt, Sg, first, last, static_cast<typename O::T*>(dgamma), stream);
-    if (dbeta) colsum::launch_pass<O>(Pb, h, nt, Sb, first, last, static_cast<typename O::T*>(dbeta), stream);
+    // dgamma and dbeta in one launch (their ordered passes run side by side)
+    auto* og = static_cast<typename O::T*>(dgamma);
+    auto* ob = static_cast<typename O::T*>(dbeta);
+    if (og)
+      colsum::launch_pass<O>(Pg, Sg, og, ob ? Pb : nullptr, ob ? Sb : nullptr, ob, h, nt, first, last, stream);
+    else
+      colsum::launch_pass<O>(Pb, Sb, ob, nullptr, nullptr, nullptr, h, nt, first, last, stream);
   }
   return hipGetLastError();
 }
