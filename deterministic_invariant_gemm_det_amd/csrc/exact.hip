@@ -495,6 +495,144 @@ __global__ void __launch_bounds__(THREADS) exact_mfma_kernel(GemmArgs args) {
     }
 }
 
+// ---- skinny path -------------------------------------------------------------
+//
+// For few output rows (decode-sized batches) the blocked kernels leave most of
+// the GPU idle: a handful of blocks each walk every tile in turn. The tile
+// partials p_t of the different (row, column) outputs are independent of one
+// another, and only the Neumaier combine is ordered, so this path computes
+// all partials in parallel -- one wave per (tile, 64 columns), every row --
+// into the stream's workspace, then combines them per output in tile order.
+// The arithmetic is the definition above step for step, so the bits are those
+// of the other kernels.
+//   1. partials: P[t][row][col] = fma chain over the tile's indices from +0;
+//      the wave upcasts its tile of A (rows x 32) into LDS once, and every
+//      lane then reads those values as broadcasts;
+//   2. combine: (s, c) <- Neumaier(s, c, P[t]) for t ascending; s + c, the
+//      bias, one rounding.
+constexpr int SK_ROWS = 32;   // row counts up to this take the skinny path (also the LDS row chunk)
+constexpr int SK_ILP = 4;     // rows whose chains advance side by side
+
+// One wave per (tile t, 64 columns): lane = column; the tile's 32 B values
+// are loaded once, and SK_ILP rows' chains advance together.
+template <typename E, bool A_RC, bool B_RC>
+__global__ void __launch_bounds__(64) skinny_partial_kernel(const typename E::T* __restrict__ A, int64_t lda,
+                                                            const typename E::T* __restrict__ B, int64_t ldb,
+                                                            int64_t rows, int64_t cols, int64_t red, int64_t ncb,
+                                                            double* __restrict__ P) {
+  __shared__ double As[SK_ROWS * KT];
+  const int lane = threadIdx.x;
+  const int64_t t = blockIdx.x / ncb, cb = blockIdx.x - t * ncb;
+  const int64_t c = cb * 64 + lane;
+  const bool ok = c < cols;
+  const int64_t cc = ok ? c : cols - 1;   // clamped column: loads stay inside B, nothing is stored
+  const int64_t l0 = t * KT;
+  const int cnt = static_cast<int>(red - l0 < KT ? red - l0 : KT);
+  double b[KT];
+#pragma unroll
+  for (int j = 0; j < KT; ++j) {
+    const int64_t l = l0 + (j < cnt ? j : cnt - 1);
+    b[j] = E::up(B_RC ? B[cc * ldb + l] : B[l * ldb + cc]);
+  }
+  for (int64_t r0 = 0; r0 < rows; r0 += SK_ROWS) {
+    const int nr = static_cast<int>(rows - r0 < SK_ROWS ? rows - r0 : SK_ROWS);
+    __syncthreads();   // the previous chunk's reads are done (one wave: orders LDS only)
+    // all of the chunk's loads are issued before any is used
+    constexpr int PER = SK_ROWS * KT / 64;
+    typename E::T av[PER];
+#pragma unroll
+    for (int u = 0; u < PER; ++u) {
+      const int i = lane + 64 * u;
+      const int r = i / KT < nr ? i / KT : nr - 1, j = i % KT;
+      const int64_t l = l0 + (j < cnt ? j : cnt - 1);
+      av[u] = A_RC ? A[(r0 + r) * lda + l] : A[l * lda + r0 + r];
+    }
+#pragma unroll
+    for (int u = 0; u < PER; ++u)
+      if (lane + 64 * u < nr * KT) As[lane + 64 * u] = E::up(av[u]);
+    __syncthreads();
+    int r = 0;
+    for (; r + SK_ILP <= nr; r += SK_ILP) {
+      double p[SK_ILP];
+#pragma unroll
+      for (int q = 0; q < SK_ILP; ++q) p[q] = 0.0;
+      if (cnt == KT) {
+#pragma unroll
+        for (int j = 0; j < KT; ++j)
+#pragma unroll
+          for (int q = 0; q < SK_ILP; ++q) p[q] = __builtin_fma(As[(r + q) * KT + j], b[j], p[q]);
+      } else {
+        for (int j = 0; j < cnt; ++j)
+#pragma unroll
+          for (int q = 0; q < SK_ILP; ++q) p[q] = __builtin_fma(As[(r + q) * KT + j], b[j], p[q]);
+      }
+      if (ok) {
+#pragma unroll
+        for (int q = 0; q < SK_ILP; ++q) P[(t * rows + r0 + r + q) * cols + c] = p[q];
+      }
+    }
+    for (; r < nr; ++r) {
+      double p = 0.0;
+      if (cnt == KT) {
+#pragma unroll
+        for (int j = 0; j < KT; ++j) p = __builtin_fma(As[r * KT + j], b[j], p);
+      } else {
+        for (int j = 0; j < cnt; ++j) p = __builtin_fma(As[r * KT + j], b[j], p);
+      }
+      if (ok) P[(t * rows + r0 + r) * cols + c] = p;
+    }
+  }
+}
+
+template <typename E, typename O>
+__global__ void __launch_bounds__(256) skinny_combine_kernel(const double* __restrict__ P, int64_t T, int64_t rows,
+                                                             int64_t cols, const typename E::T* __restrict__ bias,
+                                                             typename O::T* __restrict__ Y) {
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;   // row * cols + col
+  if (i >= rows * cols) return;
+  const int64_t stride = rows * cols;
+  double s = 0.0, c = 0.0;
+  int64_t t = 0;
+  for (; t + 32 <= T; t += 32) {   // 32 partials in flight at a time
+    double v[32];
+#pragma unroll
+    for (int j = 0; j < 32; ++j) v[j] = P[(t + j) * stride + i];
+#pragma unroll
+    for (int j = 0; j < 32; ++j) kbn_add(s, c, v[j]);
+  }
+  if (t < T) {   // the rest (fewer than 32) likewise, loads first
+    double v[32];
+#pragma unroll
+    for (int j = 0; j < 32; ++j) v[j] = t + j < T ? P[(t + j) * stride + i] : 0.0;
+#pragma unroll
+    for (int j = 0; j < 32; ++j)
+      if (t + j < T) kbn_add(s, c, v[j]);
+  }
+  double v = s + c;
+  if (bias) v = v + E::up(bias[i % cols]);
+  Y[i] = round_from_f64<O>(v);
+}
+
+template <typename E, bool AC, bool BC, typename O>
+hipError_t launch_skinny(const GemmArgs& a, hipStream_t stream) {
+  const int64_t T = (a.red + KT - 1) / KT;
+  const int64_t ncb = (a.cols + 63) / 64;
+  const int64_t n_p = T * a.rows * a.cols;
+  if (T * ncb > 0x7fffffff || (a.rows * a.cols + 255) / 256 > 0x7fffffff) return hipErrorInvalidConfiguration;
+  void* ws = nullptr;
+  hipError_t e = stream_workspace(stream, sizeof(double) * static_cast<size_t>(n_p), &ws);
+  if (e != hipSuccess) return e;
+  double* P = static_cast<double*>(ws);
+  using T_ = typename E::T;
+  hipLaunchKernelGGL((skinny_partial_kernel<E, AC, BC>), dim3(static_cast<unsigned>(T * ncb)), dim3(64), 0, stream,
+                     static_cast<const T_*>(a.A), a.lda, static_cast<const T_*>(a.B), a.ldb, a.rows, a.cols, a.red,
+                     ncb, P);
+  hipLaunchKernelGGL((skinny_combine_kernel<E, O>), dim3(static_cast<unsigned>((a.rows * a.cols + 255) / 256)),
+                     dim3(256), 0, stream, P, T, a.rows, a.cols, static_cast<const T_*>(a.bias),
+                     static_cast<typename O::T*>(a.out));
+  return hipGetLastError();
+}
+
 // ---- launch -----------------------------------------------------------------
 
 // Launch balance of the default kernel: every block of one grid does the same
@@ -511,7 +649,8 @@ bool use_48_rows(const GemmArgs& a) {
 
 template <typename E, bool AC, bool BC, typename O = E>
 hipError_t launch_typed(const GemmArgs& a, int variant, hipStream_t stream) {
-  if (variant < 0) variant = use_48_rows(a) ? 4 : 0;
+  if (variant < 0) variant = a.rows <= SK_ROWS ? 5 : use_48_rows(a) ? 4 : 0;
+  if (variant == 5) return launch_skinny<E, AC, BC, O>(a, stream);
   // f32 output: the default kernel in its two row-block forms (identical bits)
   if constexpr (!std::is_same<O, E>::value) {
     if (variant != 4) variant = 0;

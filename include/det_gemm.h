@@ -50,8 +50,12 @@
  *
  * Ownership and execution
  *   The caller owns every buffer. The library keeps no reference to any of them
- *   and allocates no device memory per call, with two exceptions: the fast
- *   tier's split dW (above) needs S * k * n * 4 bytes of f32 partials, and
+ *   and allocates no device memory per call, with these exceptions: the fast
+ *   tier's split dW (above) needs S * k * n * 4 bytes of f32 partials; the
+ *   exact tier with at most 32 output rows (fwd and dX with m <= 32, dW with
+ *   k <= 32) computes every tile partial in parallel and needs
+ *   8 * rows * cols * ceil(red / 32) bytes (rows x cols the output, red the
+ *   reduction length); and
  *   det_gemm_db needs the float64 tile partials of up to max(2^23, 128 * n)
  *   values (m / 32 * n of them when that is less) plus 2 * n, and
  *   det_layernorm_bwd twice that for its two parameter gradients; the
@@ -227,8 +231,10 @@ det_status_t det_gemm_debug_force_family(int family);
  * (-1 automatic, 0 = 4x4x4 float64 matrix-core kernel with 64-row blocks,
  * 1 = 16x16x4 float64 matrix-core kernel, 2 = float64 vector-ALU kernel,
  * 3 = the 4x4x4 kernel with a double-buffered LDS stage, 4 = the 4x4x4 kernel
- * with 48-row blocks). All produce the same bits (the oracle's), so this
- * changes speed only. Returns DET_EINVAL for other values.
+ * with 48-row blocks, 5 = the few-rows path: tile partials of every output in
+ * parallel, then the ordered combine, through the stream's workspace). All
+ * produce the same bits (the oracle's), so this changes speed only. Returns
+ * DET_EINVAL for other values.
  */
 det_status_t det_gemm_debug_force_exact_kernel(int variant);
 

@@ -38,7 +38,7 @@ def _auto_variant():
     dg.det_gemm_debug_force_exact_kernel(-1)
 
 
-@pytest.mark.parametrize("variant", [0, 1, 2, 3, 4], ids=["mfma4", "mfma16", "valu", "mfma4db", "mfma4r48"])
+@pytest.mark.parametrize("variant", [0, 1, 2, 3, 4, 5], ids=["mfma4", "mfma16", "valu", "mfma4db", "mfma4r48", "skinny"])
 @pytest.mark.parametrize("dt", DTS)
 @pytest.mark.parametrize("op", ["fwd", "dx", "dw"])
 def test_ragged_shapes(op, dt, variant):
