@@ -201,21 +201,77 @@ int fast_dw_split(int64_t m, int64_t k, int64_t n, int* chunk_stages) {
   return static_cast<int>((nst + c - 1) / c);
 }
 
+hipError_t launch_fast16_w_dw_bt(Dt dt, const GemmArgs& a, hipStream_t stream);   // fast16w.hip
+
+// out[c * R + r] = in[r * C + c]: an R x C matrix of 16-bit elements transposed
+// through LDS in 64 x 64 tiles (row reads and column writes both coalesced).
+__global__ void __launch_bounds__(256) transpose16_kernel(const uint16_t* __restrict__ in, int64_t R, int64_t C,
+                                                          uint16_t* __restrict__ out) {
+  __shared__ uint16_t t[64][66];
+  const int64_t r0 = static_cast<int64_t>(blockIdx.y) * 64, c0 = static_cast<int64_t>(blockIdx.x) * 64;
+  const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
+#pragma unroll
+  for (int i = ty; i < 64; i += 4) {
+    const int64_t r = r0 + i, c = c0 + tx;
+    if (r < R && c < C) t[i][tx] = in[r * C + c];
+  }
+  __syncthreads();
+#pragma unroll
+  for (int i = ty; i < 64; i += 4) {
+    const int64_t c = c0 + i, r = r0 + tx;
+    if (c < C && r < R) out[c * R + r] = t[tx][i];
+  }
+}
+
 hipError_t launch_fast(Op op, Dt dt, const GemmArgs& a, int family, hipStream_t stream) {
   if (op == OP_DW && dt != DT_F32 && a.partial == nullptr) {
     int chunk = 0;
     const int split = fast_dw_split(a.red, a.rows, a.cols, &chunk);
     if (split > 1) {
       // chunk partials into the stream's workspace, then the ordered combine
-      void* ws = nullptr;
       const size_t count = static_cast<size_t>(a.rows) * static_cast<size_t>(a.cols);
-      hipError_t e = stream_workspace(stream, count * sizeof(float) * static_cast<size_t>(split), &ws);
+      const size_t pbytes = (count * sizeof(float) * static_cast<size_t>(split) + 255) / 256 * 256;
+      // The default family takes the smaller operand (x or dY, both reduction-
+      // major) copied transposed: the kernel then stages that one straight into
+      // LDS, as the forward's x, and only the other through registers. Same
+      // values in the same instruction order, so the same bits.
+      const bool base = family == 0 && a.red % 64 == 0 && a.red <= int64_t(64) * 65535;
+      const bool tr = base && a.rows <= a.cols && a.vec_b && a.off32_b && a.rows * a.red * 2 < (int64_t(1) << 31);
+      const bool trb = base && !tr && a.vec_a && a.off32_a && a.cols * a.red * 2 < (int64_t(1) << 31);
+      const size_t tbytes = tr ? static_cast<size_t>(a.rows) * static_cast<size_t>(a.red) * 2
+                          : trb ? static_cast<size_t>(a.cols) * static_cast<size_t>(a.red) * 2 : 0;
+      void* ws = nullptr;
+      hipError_t e = stream_workspace(stream, pbytes + tbytes, &ws);
       if (e != hipSuccess) return e;
       GemmArgs p = a;
       p.partial = static_cast<float*>(ws);
       p.split = split;
       p.chunk_stages = chunk;
-      e = launch_fast(op, dt, p, family, stream);
+      if (tr) {
+        uint16_t* xt = reinterpret_cast<uint16_t*>(static_cast<char*>(ws) + pbytes);
+        const dim3 grid(static_cast<unsigned>((a.rows + 63) / 64), static_cast<unsigned>((a.red + 63) / 64));
+        hipLaunchKernelGGL(transpose16_kernel, grid, dim3(256), 0, stream, static_cast<const uint16_t*>(a.A), a.red,
+                           a.rows, xt);
+        p.A = xt;
+        p.lda = a.red;
+        p.vec_a = true;
+        p.off32_a = true;
+        p.a_bytes = static_cast<int64_t>(tbytes);
+        e = launch_fast16_w(OP_FWD, dt, p, 0, stream);   // x rows now contiguous along the reduction
+      } else if (trb) {
+        uint16_t* yt = reinterpret_cast<uint16_t*>(static_cast<char*>(ws) + pbytes);
+        const dim3 grid(static_cast<unsigned>((a.cols + 63) / 64), static_cast<unsigned>((a.red + 63) / 64));
+        hipLaunchKernelGGL(transpose16_kernel, grid, dim3(256), 0, stream, static_cast<const uint16_t*>(a.B), a.red,
+                           a.cols, yt);
+        p.B = yt;
+        p.ldb = a.red;
+        p.vec_b = true;
+        p.off32_b = true;
+        p.b_bytes = static_cast<int64_t>(tbytes);
+        e = launch_fast16_w_dw_bt(dt, p, stream);   // dY columns now contiguous along the reduction
+      } else {
+        e = launch_fast(op, dt, p, family, stream);
+      }
       if (e != hipSuccess) return e;
       return launch_combine(dt, a.out_f32, p.partial, split, static_cast<int64_t>(count), a.out, stream);
     }

@@ -660,6 +660,14 @@ bool fast16_w_ok(const GemmArgs& a) {
 // stages of 64 otherwise). Chosen from the column count only.
 int fast16_w_shape(int64_t cols) { return cols >= 1536 ? 0 : 4; }
 
+// dW with dY supplied transposed ([n][m], contiguous along the reduction) and x
+// as given (reduction-major): 256 x 192 tiles.
+hipError_t launch_fast16_w_dw_bt(Dt dt, const GemmArgs& a, hipStream_t stream) {
+  if (dt == DT_BF16) return w8::launch_typed<BF16, false, true, 256, 192, 4, 2, 2>(a, stream);
+  if (dt == DT_F16) return w8::launch_typed<F16, false, true, 256, 192, 4, 2, 2>(a, stream);
+  return hipErrorInvalidValue;
+}
+
 hipError_t launch_fast16_w(Op op, Dt dt, const GemmArgs& a, int shape, hipStream_t stream) {
   if (dt == DT_BF16) return w8::launch_op<BF16>(op, a, shape, stream);
   if (dt == DT_F16) return w8::launch_op<F16>(op, a, shape, stream);
