@@ -51,7 +51,8 @@
  * Ownership and execution
  *   The caller owns every buffer. The library keeps no reference to any of them
  *   and allocates no device memory per call, with these exceptions: the fast
- *   tier's split dW (above) needs S * k * n * 4 bytes of f32 partials; the
+ *   tier's split dW (above) needs S * k * n * 4 bytes of f32 partials plus a
+ *   transposed copy of its smaller operand (2 * m * min(k, n) bytes); the
  *   exact tier with at most 32 output rows (fwd and dX with m <= 32, dW with
  *   k <= 32) computes every tile partial in parallel and needs
  *   8 * rows * cols * ceil(red / 32) bytes (rows x cols the output, red the
