@@ -51,6 +51,8 @@ def parse():
     p.add_argument("--no-skinny", action="store_true", help="skip the skinny-M bandwidth measurements")
     p.add_argument("--no-vendor", action="store_true", help="skip the vendor-BLAS context timings")
     p.add_argument("--no-peak", action="store_true", help="skip the measured-peak microkernels")
+    p.add_argument("--shapes", action="store_true",
+                   help="instead of the step: fwd/dX/dW in both tiers on the other workloads' shapes (one JSON line)")
     p.add_argument("--no-next", action="store_true",
                    help="skip the bias-gradient, f32-dW and LayerNorm measurements")
     p.add_argument("--only", default=None,
@@ -319,6 +321,46 @@ def host_cpu():
     return model, os.cpu_count()
 
 
+SWEEP = (("gpt2_qkv", "bf16", 8192, 768, 2304), ("gpt2_attn_proj", "bf16", 8192, 768, 768),
+         ("gpt2_c_fc", "bf16", 8192, 768, 3072), ("gpt2_c_proj", "bf16", 8192, 3072, 768),
+         ("f32_4096", "f32", 4096, 4096, 4096), ("bf16_up", "bf16", 4096, 4096, 11008),
+         ("bf16_down", "bf16", 4096, 11008, 4096))
+PEAKS = {("exact", "bf16"): PEAK_FP64, ("exact", "f32"): PEAK_FP64, ("fast", "bf16"): PEAK_BF16,
+         ("fast", "f32"): 157.3}
+
+
+def shape_sweep(dev):
+    """fwd, dX and dW in both tiers on the other workloads' shapes (M x K x N): mean microseconds
+    per launch (HIP events around back-to-back calls on the current stream), TFLOP/s and the
+    fraction of the tier's peak for the dtype (FP64 for the exact tier; bf16 or FP32 matrix
+    peak for the fast tier)."""
+    import torch
+    import deterministic_invariant_gemm_det_amd as dg
+    stream = torch.cuda.current_stream(dev)
+    out = {}
+    for name, dt, m, k, n in SWEEP:
+        tdt = torch.bfloat16 if dt == "bf16" else torch.float32
+        g0 = torch.Generator(device=dev)
+        g0.manual_seed(42)
+        x = torch.randn(m, k, device=dev, generator=g0).to(tdt)
+        w = (torch.randn(k, n, device=dev, generator=g0) * 0.02).to(tdt)
+        g = torch.randn(m, n, device=dev, generator=g0).to(tdt)
+        y, gx, gw = (torch.empty(m, n, device=dev, dtype=tdt), torch.empty(m, k, device=dev, dtype=tdt),
+                     torch.empty(k, n, device=dev, dtype=tdt))
+        fl = 2.0 * m * k * n
+        for tier in ("exact", "fast"):
+            for op, f in (("fwd", lambda: dg.fwd(x, w, None, tier, out=y)), ("dx", lambda: dg.dx(g, w, tier, out=gx)),
+                          ("dw", lambda: dg.dw(x, g, tier, out=gw))):
+                reps = 3 if tier == "exact" else 20
+                us = _time_calls(f, stream, reps=reps, warmup=1)
+                tf = fl / (us * 1e-6) / 1e12
+                out[f"{name}.{tier}.{op}"] = {"mkn": [m, k, n], "dtype": dt, "us": round(us, 1), "tflops": round(tf, 1),
+                                              "frac_of_peak": round(tf / PEAKS[(tier, dt)], 4)}
+                print(f"{name} {tier} {op}: {us:.1f} us {tf:.1f} TFLOP/s", file=sys.stderr, flush=True)
+        del x, w, g, y, gx, gw
+    return out
+
+
 def vendor_context(data, dev, fast_per):
     """Context only, not the product path: the vendor BLAS behind torch.matmul (hipBLASLt)
     on the step's own bf16 tensors in their natural layouts (X @ W, dY @ W^T, X^T @ dY, the
@@ -387,6 +429,9 @@ def main():
     dev = torch.device("cuda:0")
     if args.copy_mib:
         copy_calibration(dev, args.copy_mib, args.steps, args.warmup)
+        return
+    if args.shapes:
+        print(json.dumps({"shape_sweep": shape_sweep(dev)}))
         return
     data = make_inputs(dev)
     steps = launches(data, args.only)

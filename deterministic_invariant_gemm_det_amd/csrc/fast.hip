@@ -193,7 +193,7 @@ int fast_dw_split(int64_t m, int64_t k, int64_t n, int* chunk_stages) {
   const int64_t nst = (m + 63) / 64;
   const int64_t tiles = ((k + 255) / 256) * ((n + 191) / 192);
   int64_t s = tiles < 128 ? 256 / tiles : 1;
-  if (s > 8) s = 8;
+  if (s > 16) s = 16;
   if (s > nst / 8) s = nst / 8;
   if (s < 1) s = 1;
   const int64_t c = (nst + s - 1) / s;
