@@ -17,6 +17,8 @@
 //   * The two families (large: 128x128 outputs per workgroup, small: 64x64)
 //     differ only in how outputs are grouped into workgroups.
 
+#include <type_traits>
+
 #include "common.hpp"
 
 namespace detgemm {
@@ -165,8 +167,162 @@ hipError_t launch_op(Op op, const GemmArgs& a, hipStream_t stream) {
   return hipErrorInvalidValue;
 }
 
+// f32 inputs, large tiles: the same instruction sequence per output as
+// fast_kernel (V_MFMA_F32_16X16X4_F32 over 4-index steps from index 0, from a
+// zero accumulator; bias in f32; one rounding), staged for speed: 128 x 128
+// outputs per workgroup, 32 reduction indices per stage, both operands kept in
+// LDS as [l][x] (row stride 144 floats: the four reduction rows one fragment
+// read touches fall 16 banks apart), double buffered, the next stage's global
+// loads (16 bytes where the operand allows) in registers during the current
+// stage's matrix work, one barrier per stage.
+constexpr int F32_BM = 128, F32_LDX = F32_BM + 16;
+
+// Four consecutive elements along the operand's contiguous dimension starting
+// at (x, l) -- along l when RC, along x otherwise -- zero outside the operand.
+template <bool RC>
+__device__ inline void load4_f32(const float* __restrict__ src, int64_t ld, int64_t x, int64_t l, int64_t xlen,
+                                 int64_t llen, bool vec, float (&v)[4]) {
+  const int64_t first = RC ? l : x, lim = RC ? llen : xlen;
+  const bool in = RC ? (x < xlen) : (l < llen);
+  const float* p = RC ? src + x * ld + l : src + l * ld + x;
+  if (in && vec && first + 4 <= lim) {
+    const float4 q = *reinterpret_cast<const float4*>(p);
+    v[0] = q.x; v[1] = q.y; v[2] = q.z; v[3] = q.w;
+    return;
+  }
+#pragma unroll
+  for (int e = 0; e < 4; ++e) v[e] = (in && first + e < lim) ? p[e] : 0.0f;
+}
+
+template <bool A_RC, bool B_RC>
+__global__ void __launch_bounds__(THREADS) fast_f32_kernel(GemmArgs args) {
+  constexpr int BM = F32_BM, BN = F32_BM, LDX = F32_LDX;
+  constexpr int NI = 4, NJ = 4;                 // 16 x 16 blocks per wave (64 x 64 outputs)
+  constexpr int Q = BM * KS / 4 / THREADS;      // float4 pieces per thread per operand and stage
+  __shared__ __attribute__((aligned(16))) float As[2][KS * LDX];
+  __shared__ __attribute__((aligned(16))) float Bs[2][KS * LDX];
+  const float* __restrict__ A = static_cast<const float*>(args.A);
+  const float* __restrict__ B = static_cast<const float*>(args.B);
+  const int64_t tiles_n = (args.cols + BN - 1) / BN;
+  const int64_t row0 = (static_cast<int64_t>(blockIdx.x) / tiles_n) * BM;
+  const int64_t col0 = (static_cast<int64_t>(blockIdx.x) % tiles_n) * BN;
+  const int t = threadIdx.x, wave = t >> 6, lane = t & 63;
+  const int wm = (wave >> 1) * 64, wn = (wave & 1) * 64;
+  const int lx = lane & 15, lk = lane >> 4;
+  const bool va = args.vec_a, vb = args.vec_b;
+
+  // piece q of this thread: RC -- x = idx % 128, l = 4 (idx / 128); otherwise
+  // l = idx / 32, x = 4 (idx % 32) (idx = t + 256 q), so that consecutive
+  // lanes write consecutive LDS addresses.
+  float ra[Q][4], rb[Q][4];
+  auto load = [&](int64_t l0) {
+#pragma unroll
+    for (int q = 0; q < Q; ++q) {
+      const int idx = t + THREADS * q;
+      const int xa = A_RC ? idx % BM : 4 * (idx % (BM / 4)), la = A_RC ? 4 * (idx / BM) : idx / (BM / 4);
+      const int xb = B_RC ? idx % BN : 4 * (idx % (BN / 4)), lb = B_RC ? 4 * (idx / BN) : idx / (BN / 4);
+      load4_f32<A_RC>(A, args.lda, row0 + xa, l0 + la, args.rows, args.red, va, ra[q]);
+      load4_f32<B_RC>(B, args.ldb, col0 + xb, l0 + lb, args.cols, args.red, vb, rb[q]);
+    }
+  };
+  auto store = [&](int buf) {
+#pragma unroll
+    for (int q = 0; q < Q; ++q) {
+      const int idx = t + THREADS * q;
+      if (A_RC) {
+        const int x = idx % BM, l = 4 * (idx / BM);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) As[buf][(l + e) * LDX + x] = ra[q][e];
+      } else {
+        const int x = 4 * (idx % (BM / 4)), l = idx / (BM / 4);
+        *reinterpret_cast<float4*>(&As[buf][l * LDX + x]) = make_float4(ra[q][0], ra[q][1], ra[q][2], ra[q][3]);
+      }
+      if (B_RC) {
+        const int x = idx % BN, l = 4 * (idx / BN);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) Bs[buf][(l + e) * LDX + x] = rb[q][e];
+      } else {
+        const int x = 4 * (idx % (BN / 4)), l = idx / (BN / 4);
+        *reinterpret_cast<float4*>(&Bs[buf][l * LDX + x]) = make_float4(rb[q][0], rb[q][1], rb[q][2], rb[q][3]);
+      }
+    }
+  };
+
+  v4f acc[NI][NJ];
+#pragma unroll
+  for (int i = 0; i < NI; ++i)
+#pragma unroll
+    for (int j = 0; j < NJ; ++j)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) acc[i][j][e] = 0.0f;
+
+  const int64_t nst = (args.red + KS - 1) / KS;
+  load(0);
+  store(0);
+  __syncthreads();
+  for (int64_t st = 0; st < nst; ++st) {
+    const int buf = static_cast<int>(st & 1);
+    const bool more = st + 1 < nst;
+    if (more) load((st + 1) * KS);
+    const float* as = As[buf];
+    const float* bs = Bs[buf];
+#pragma unroll
+    for (int d = 0; d < KS; d += 4) {
+      float a[NI], b[NJ];
+#pragma unroll
+      for (int i = 0; i < NI; ++i) a[i] = as[(d + lk) * LDX + wm + 16 * i + lx];
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) b[j] = bs[(d + lk) * LDX + wn + 16 * j + lx];
+#pragma unroll
+      for (int i = 0; i < NI; ++i)
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[i], b[j], acc[i][j], 0, 0, 0);
+    }
+    if (more) store(buf ^ 1);
+    __syncthreads();
+  }
+
+  float* __restrict__ Y = static_cast<float*>(args.out);
+  const float* __restrict__ bias = static_cast<const float*>(args.bias);
+#pragma unroll
+  for (int i = 0; i < NI; ++i)
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) {
+      const int64_t col = col0 + wn + 16 * j + lx;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int64_t row = row0 + wm + 16 * i + 4 * lk + e;
+        if (row < args.rows && col < args.cols) {
+          float r = acc[i][j][e];
+          if (bias) r = r + bias[col];
+          Y[row * args.cols + col] = r;
+        }
+      }
+    }
+}
+
+template <bool AC, bool BC>
+hipError_t launch_f32_large(const GemmArgs& a, hipStream_t stream) {
+  const int64_t blocks = ((a.cols + F32_BM - 1) / F32_BM) * ((a.rows + F32_BM - 1) / F32_BM);
+  if (blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
+  hipLaunchKernelGGL((fast_f32_kernel<AC, BC>), dim3(static_cast<unsigned>(blocks)), dim3(THREADS), 0, stream, a);
+  return hipGetLastError();
+}
+
 template <typename E>
 hipError_t launch_family(Op op, int family, const GemmArgs& a, hipStream_t stream) {
+  if constexpr (std::is_same<E, F32>::value) {
+    // f32: family 0 is the staged large-tile kernel, family 1 the plain one (same bits)
+    if (family == 0) {
+      switch (op) {
+        case OP_FWD: return launch_f32_large<true, false>(a, stream);
+        case OP_DX:  return launch_f32_large<true, true>(a, stream);
+        case OP_DW:  return launch_f32_large<false, false>(a, stream);
+      }
+      return hipErrorInvalidValue;
+    }
+    return launch_op<E, 64, 64>(op, a, stream);
+  }
   return family == 0 ? launch_op<E, 128, 128>(op, a, stream) : launch_op<E, 64, 64>(op, a, stream);
 }
 
@@ -174,11 +330,13 @@ hipError_t launch_family(Op op, int family, const GemmArgs& a, hipStream_t strea
 
 // Shape-only choice of the tile family: never reads the row count of fwd/dx.
 // Family choice from the call's shape alone (the families give identical
-// bits, so this only affects speed). f32: wide outputs take the large tiles.
+// bits, so this only affects speed). f32: the staged 128 x 128 kernel unless
+// the output is narrow or the reduction short, where the 64 x 64 tiles of the
+// plain kernel keep more of the chip busy.
 // 16-bit: the large direct-to-LDS tiles pay off on long reductions outside dW;
 // short reductions and dW run faster on the smaller register-staged tiles.
 int fast_auto_family(Op op, Dt dt, int64_t cols, int64_t red) {
-  if (dt == DT_F32) return cols >= 1024 ? 0 : 1;
+  if (dt == DT_F32) return (cols >= 512 && red >= 512) ? 0 : 1;
   (void)red;
   return (op == OP_DW || cols >= 256) ? 0 : 1;
 }
