@@ -20,6 +20,7 @@
 #include <type_traits>
 
 #include "common.hpp"
+#include "transpose.hpp"
 
 namespace detgemm {
 namespace {
@@ -361,26 +362,6 @@ int fast_dw_split(int64_t m, int64_t k, int64_t n, int* chunk_stages) {
 
 hipError_t launch_fast16_w_dw_bt(Dt dt, const GemmArgs& a, hipStream_t stream);   // fast16w.hip
 
-// out[c * R + r] = in[r * C + c]: an R x C matrix of 16-bit elements transposed
-// through LDS in 64 x 64 tiles (row reads and column writes both coalesced).
-__global__ void __launch_bounds__(256) transpose16_kernel(const uint16_t* __restrict__ in, int64_t R, int64_t C,
-                                                          uint16_t* __restrict__ out) {
-  __shared__ uint16_t t[64][66];
-  const int64_t r0 = static_cast<int64_t>(blockIdx.y) * 64, c0 = static_cast<int64_t>(blockIdx.x) * 64;
-  const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
-#pragma unroll
-  for (int i = ty; i < 64; i += 4) {
-    const int64_t r = r0 + i, c = c0 + tx;
-    if (r < R && c < C) t[i][tx] = in[r * C + c];
-  }
-  __syncthreads();
-#pragma unroll
-  for (int i = ty; i < 64; i += 4) {
-    const int64_t c = c0 + i, r = r0 + tx;
-    if (c < C && r < R) out[c * R + r] = t[tx][i];
-  }
-}
-
 hipError_t launch_fast(Op op, Dt dt, const GemmArgs& a, int family, hipStream_t stream) {
   if (op == OP_DW && dt != DT_F32 && a.partial == nullptr) {
     int chunk = 0;
@@ -407,9 +388,8 @@ hipError_t launch_fast(Op op, Dt dt, const GemmArgs& a, int family, hipStream_t 
       p.chunk_stages = chunk;
       if (tr) {
         uint16_t* xt = reinterpret_cast<uint16_t*>(static_cast<char*>(ws) + pbytes);
-        const dim3 grid(static_cast<unsigned>((a.rows + 63) / 64), static_cast<unsigned>((a.red + 63) / 64));
-        hipLaunchKernelGGL(transpose16_kernel, grid, dim3(256), 0, stream, static_cast<const uint16_t*>(a.A), a.red,
-                           a.rows, xt);
+        e = launch_transpose<uint16_t>(a.A, a.red, a.rows, xt, stream);
+        if (e != hipSuccess) return e;
         p.A = xt;
         p.lda = a.red;
         p.vec_a = true;
@@ -418,9 +398,8 @@ hipError_t launch_fast(Op op, Dt dt, const GemmArgs& a, int family, hipStream_t 
         e = launch_fast16_w(OP_FWD, dt, p, 0, stream);   // x rows now contiguous along the reduction
       } else if (trb) {
         uint16_t* yt = reinterpret_cast<uint16_t*>(static_cast<char*>(ws) + pbytes);
-        const dim3 grid(static_cast<unsigned>((a.cols + 63) / 64), static_cast<unsigned>((a.red + 63) / 64));
-        hipLaunchKernelGGL(transpose16_kernel, grid, dim3(256), 0, stream, static_cast<const uint16_t*>(a.B), a.red,
-                           a.cols, yt);
+        e = launch_transpose<uint16_t>(a.B, a.red, a.cols, yt, stream);
+        if (e != hipSuccess) return e;
         p.B = yt;
         p.ldb = a.red;
         p.vec_b = true;
