@@ -360,30 +360,38 @@ int fast_dw_split(int64_t m, int64_t k, int64_t n, int* chunk_stages) {
   return static_cast<int>((nst + c - 1) / c);
 }
 
-hipError_t launch_fast16_w_dw_bt(Dt dt, const GemmArgs& a, hipStream_t stream);   // fast16w.hip
+hipError_t launch_fast16_w_dw_bt(Dt dt, const GemmArgs& a, int shape, hipStream_t stream);   // fast16w.hip
 
 hipError_t launch_fast(Op op, Dt dt, const GemmArgs& a, int family, hipStream_t stream) {
   if (op == OP_DW && dt != DT_F32 && a.partial == nullptr) {
     int chunk = 0;
     const int split = fast_dw_split(a.red, a.rows, a.cols, &chunk);
-    if (split > 1) {
-      // chunk partials into the stream's workspace, then the ordered combine
+    // The default family may take the smaller operand (x or dY, both
+    // reduction-major) copied transposed: the kernel then stages that one
+    // straight into LDS, as the forward's x, and only the other through
+    // registers. Tile shape and copy by measured speed: without a split, four
+    // fat waves (128 x 96 each) with the copy; split into long chunks, eight
+    // waves (64 x 96 each) with the copy; split into short chunks (at most 20
+    // stages), four fat waves without it. Same values in the same instruction
+    // order in every form, so the same bits.
+    const bool base = family == 0 && a.red % 64 == 0 && a.red <= int64_t(64) * 65535;
+    const bool tr0 = base && a.rows <= a.cols && a.vec_b && a.off32_b && a.rows * a.red * 2 < (int64_t(1) << 31);
+    const bool trb0 = base && !tr0 && a.vec_a && a.off32_a && a.cols * a.red * 2 < (int64_t(1) << 31);
+    const bool copy = (tr0 || trb0) && (split == 1 || chunk > 20);
+    const bool tr = copy && tr0, trb = copy && trb0;
+    const int shape = split > 1 && copy ? 0 : 5;
+    if (split > 1 || copy) {
+      // chunk partials (when split) and the transposed copy in the stream's
+      // workspace; with a split, the ordered combine writes the output
       const size_t count = static_cast<size_t>(a.rows) * static_cast<size_t>(a.cols);
-      const size_t pbytes = (count * sizeof(float) * static_cast<size_t>(split) + 255) / 256 * 256;
-      // The default family takes the smaller operand (x or dY, both reduction-
-      // major) copied transposed: the kernel then stages that one straight into
-      // LDS, as the forward's x, and only the other through registers. Same
-      // values in the same instruction order, so the same bits.
-      const bool base = family == 0 && a.red % 64 == 0 && a.red <= int64_t(64) * 65535;
-      const bool tr = base && a.rows <= a.cols && a.vec_b && a.off32_b && a.rows * a.red * 2 < (int64_t(1) << 31);
-      const bool trb = base && !tr && a.vec_a && a.off32_a && a.cols * a.red * 2 < (int64_t(1) << 31);
+      const size_t pbytes = split > 1 ? (count * sizeof(float) * static_cast<size_t>(split) + 255) / 256 * 256 : 0;
       const size_t tbytes = tr ? static_cast<size_t>(a.rows) * static_cast<size_t>(a.red) * 2
                           : trb ? static_cast<size_t>(a.cols) * static_cast<size_t>(a.red) * 2 : 0;
       void* ws = nullptr;
       hipError_t e = stream_workspace(stream, pbytes + tbytes, &ws);
       if (e != hipSuccess) return e;
       GemmArgs p = a;
-      p.partial = static_cast<float*>(ws);
+      p.partial = split > 1 ? static_cast<float*>(ws) : nullptr;
       p.split = split;
       p.chunk_stages = chunk;
       if (tr) {
@@ -395,7 +403,7 @@ hipError_t launch_fast(Op op, Dt dt, const GemmArgs& a, int family, hipStream_t 
         p.vec_a = true;
         p.off32_a = true;
         p.a_bytes = static_cast<int64_t>(tbytes);
-        e = launch_fast16_w(OP_FWD, dt, p, 0, stream);   // x rows now contiguous along the reduction
+        e = launch_fast16_w(OP_FWD, dt, p, shape, stream);   // x rows now contiguous along the reduction
       } else if (trb) {
         uint16_t* yt = reinterpret_cast<uint16_t*>(static_cast<char*>(ws) + pbytes);
         e = launch_transpose<uint16_t>(a.B, a.red, a.cols, yt, stream);
@@ -405,13 +413,15 @@ hipError_t launch_fast(Op op, Dt dt, const GemmArgs& a, int family, hipStream_t 
         p.vec_b = true;
         p.off32_b = true;
         p.b_bytes = static_cast<int64_t>(tbytes);
-        e = launch_fast16_w_dw_bt(dt, p, stream);   // dY columns now contiguous along the reduction
+        e = launch_fast16_w_dw_bt(dt, p, shape, stream);   // dY columns now contiguous along the reduction
       } else {
-        e = launch_fast(op, dt, p, family, stream);
+        e = launch_fast(op, dt, p, family == 0 ? 15 : family, stream);
       }
       if (e != hipSuccess) return e;
+      if (split == 1) return hipSuccess;
       return launch_combine(dt, a.out_f32, p.partial, split, static_cast<int64_t>(count), a.out, stream);
     }
+    if (family == 0) family = 15;   // no split, no copy: four fat waves
   }
   switch (dt) {
     case DT_F32: return launch_family<F32>(op, family == 1 ? 1 : 0, a, stream);

@@ -270,8 +270,8 @@ __device__ inline void tile_origin(const GemmArgs& a, uint32_t t, int64_t& row0,
 // Epilogue: acc + bias, one rounding, written through LDS (the stage slots are
 // free by then) as a row-major tile, then copied out with 16-byte stores
 // along whole tile rows.
-template <typename E, bool A_RC, bool B_RC, int BM, int BN, int WR, int WC, int NS, int BK>
-__global__ void __launch_bounds__(64 * WR * WC, 8 / (WR * WC)) fast16w_kernel(GemmArgs args) {
+template <typename E, bool A_RC, bool B_RC, int BM, int BN, int WR, int WC, int NS, int BK, int WPE>
+__global__ void __launch_bounds__(64 * WR * WC, WPE) fast16w_kernel(GemmArgs args) {
   using T = typename E::T;
   constexpr int WAVES = WR * WC, THREADS = 64 * WAVES;
   constexpr int WM = BM / WR, WN = BN / WC, NI = WM / 32, NJ = WN / 32;
@@ -281,7 +281,8 @@ __global__ void __launch_bounds__(64 * WR * WC, 8 / (WR * WC)) fast16w_kernel(Ge
   constexpr int A_BYTES = BM * BK * 2, B_BYTES = BN * BK * 2, SLOT = A_BYTES + B_BYTES;
   constexpr int RS = BN * 2 + 16;   // LDS row stride of the output tile (bytes)
   static_assert(BM * RS <= NS * SLOT, "output tile must fit the stage slots");
-  static_assert(NS >= 2 && NS * SLOT * (8 / WAVES) <= 160 * 1024, "LDS (8 waves per compute unit)");
+  constexpr int WG_PER_CU = WPE * 4 / WAVES < 1 ? 1 : WPE * 4 / WAVES;
+  static_assert(NS >= 2 && NS * SLOT * WG_PER_CU <= 160 * 1024, "LDS of the resident workgroups");
   // direct-to-LDS loads per wave per stage (the ones vmcnt must account for)
   constexpr int DL = (A_RC ? RcOperand<BM, WAVES, BK>::LOADS : 0) + (B_RC ? RcOperand<BN, WAVES, BK>::LOADS : 0);
   static_assert((NS - 2) * DL <= 63 && NS <= 4, "vmcnt range; the stage wait below handles up to four stages");
@@ -547,7 +548,7 @@ __global__ void __launch_bounds__(64 * WR * WC, 8 / (WR * WC)) fast16w_kernel(Ge
   }
 }
 
-template <typename E, bool AC, bool BC, int BM, int BN, int WR, int WC, int NS, int BK = 64>
+template <typename E, bool AC, bool BC, int BM, int BN, int WR, int WC, int NS, int BK = 64, int WPE = 8 / (WR * WC)>
 hipError_t launch_typed(const GemmArgs& a, hipStream_t stream) {
   // a split reduction counts its chunks in stages of 64
   if (a.red % BK != 0 || (a.partial && BK != 64)) return hipErrorInvalidValue;
@@ -557,7 +558,7 @@ hipError_t launch_typed(const GemmArgs& a, hipStream_t stream) {
   const int64_t grid = tiles * (a.partial ? a.split : 1);
   // the kernel counts tiles and (tile, stage) pairs in 32 bits
   if (grid > 0x7fffffff || a.red / BK > 0x7fffffff) return hipErrorInvalidConfiguration;
-  hipLaunchKernelGGL((fast16w_kernel<E, AC, BC, BM, BN, WR, WC, NS, BK>), dim3(static_cast<unsigned>(grid)), dim3(64 * WR * WC),
+  hipLaunchKernelGGL((fast16w_kernel<E, AC, BC, BM, BN, WR, WC, NS, BK, WPE>), dim3(static_cast<unsigned>(grid)), dim3(64 * WR * WC),
                      0, stream, a);
   return hipGetLastError();
 }
@@ -573,6 +574,7 @@ hipError_t launch_shape(const GemmArgs& a, int shape, hipStream_t stream) {
     case 1: return launch_typed<E, AC, BC, 128, 192, 4, 2, 2>(a, stream);
     case 2: return launch_typed<E, AC, BC, 128, 192, 2, 2, 2>(a, stream);   // four waves, two workgroups per CU
     case 3: return launch_typed<E, AC, BC, 64, 192, 2, 2, 2>(a, stream);    // four waves, two workgroups per CU
+    case 5: return launch_typed<E, AC, BC, 256, 192, 2, 2, 2, 64, 1>(a, stream);   // four waves of 128 x 96, one per SIMD
     default:   // stages of 128 (half the barriers) where the reduction allows it
       if (a.red % 128 != 0 || a.partial) return launch_typed<E, AC, BC, 128, 192, 4, 2, 2>(a, stream);
       return launch_typed<E, AC, BC, 128, 192, 4, 2, 2, 128>(a, stream);
@@ -662,7 +664,12 @@ int fast16_w_shape(int64_t cols) { return cols >= 1536 ? 0 : 4; }
 
 // dW with dY supplied transposed ([n][m], contiguous along the reduction) and x
 // as given (reduction-major): 256 x 192 tiles.
-hipError_t launch_fast16_w_dw_bt(Dt dt, const GemmArgs& a, hipStream_t stream) {
+hipError_t launch_fast16_w_dw_bt(Dt dt, const GemmArgs& a, int shape, hipStream_t stream) {
+  if (shape == 5) {
+    if (dt == DT_BF16) return w8::launch_typed<BF16, false, true, 256, 192, 2, 2, 2, 64, 1>(a, stream);
+    if (dt == DT_F16) return w8::launch_typed<F16, false, true, 256, 192, 2, 2, 2, 64, 1>(a, stream);
+    return hipErrorInvalidValue;
+  }
   if (dt == DT_BF16) return w8::launch_typed<BF16, false, true, 256, 192, 4, 2, 2>(a, stream);
   if (dt == DT_F16) return w8::launch_typed<F16, false, true, 256, 192, 4, 2, 2>(a, stream);
   return hipErrorInvalidValue;

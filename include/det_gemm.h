@@ -51,8 +51,9 @@
  * Ownership and execution
  *   The caller owns every buffer. The library keeps no reference to any of them
  *   and allocates no device memory per call, with these exceptions: the fast
- *   tier's split dW (above) needs S * k * n * 4 bytes of f32 partials plus a
- *   transposed copy of its smaller operand (2 * m * min(k, n) bytes); the
+ *   tier's dW of bf16/f16 inputs may take a transposed copy of its smaller
+ *   operand (2 * m * min(k, n) bytes) and, when split (above), needs
+ *   S * k * n * 4 bytes of f32 partials; the
  *   exact tier with at most 32 output rows (fwd and dX with m <= 32, dW with
  *   k <= 32) computes every tile partial in parallel and needs
  *   8 * rows * cols * ceil(red / 32) bytes (rows x cols the output, red the
@@ -221,7 +222,8 @@ int det_gemm_version(void);
  * (-1 automatic, 0 = the large family, 1 = the small family, 10 + s = tile
  * shape s of the large family's kernel where it applies: 10 = 256 x 192,
  * 11 = 128 x 192, 12 = 128 x 192 in two four-wave workgroups per compute
- * unit, 13 = 64 x 192 likewise, 14 = 128 x 192 in stages of 128). All
+ * unit, 13 = 64 x 192 likewise, 14 = 128 x 192 in stages of 128, 15 =
+ * 256 x 192 in four waves of 128 x 96, one per SIMD). All
  * families produce identical bits, so this changes speed only. Returns
  * DET_EINVAL for other values.
  */

@@ -37,8 +37,11 @@ def test_static_strings_and_version():
 
 
 def test_force_family_validation():
-    with pytest.raises(dg.DetGemmError):
-        dg.det_gemm_debug_force_family(2)
+    for bad in (-2, 2, 9, 16):
+        with pytest.raises(dg.DetGemmError):
+            dg.det_gemm_debug_force_family(bad)
+    for good in (-1, 0, 1, 10, 15):
+        dg.det_gemm_debug_force_family(good)
     dg.det_gemm_debug_force_family(-1)
 
 

@@ -14,7 +14,7 @@ pytestmark = pytest.mark.gpu
 
 M = 8192
 LAYERS = [("c_fc", 768, 3072), ("c_proj", 3072, 768)]
-FAMILIES = (0, 1, 10, 11, 12, 13, 14)
+FAMILIES = (0, 1, 10, 11, 12, 13, 14, 15)
 ROWS = np.array([0, 1, 31, 32, 255, 256, 1000, 4095, 4096, 8190, 8191])
 
 

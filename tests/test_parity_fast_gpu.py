@@ -38,7 +38,7 @@ def test_tolerance_and_families(op, dt):
         y = gpu_op(op, dt, A, B, bias, tier="fast")
         assert_within_tolerance(y, r, S, dt, f"fast {op} {dt} {(m, k, n)}")
         assert_bits_equal(gpu_op(op, dt, A, B, bias, tier="fast"), y, "rerun")
-        for fam in (0, 1, 10, 12, 14):
+        for fam in (0, 1, 10, 12, 14, 15):
             dg.det_gemm_debug_force_family(fam)
             assert_bits_equal(gpu_op(op, dt, A, B, bias, tier="fast"), y, f"family {fam}")
         dg.det_gemm_debug_force_family(-1)
@@ -73,7 +73,7 @@ def test_dw_split(dt):
         y = gpu_op("dw", dt, A, B, tier="fast")
         assert_within_tolerance(y, r, S, dt, f"fast dw {dt} {(m, k, n)}")
         assert_bits_equal(gpu_op("dw", dt, A, B, tier="fast"), y, "rerun")
-        for fam in (0, 1, 10, 11, 12, 13, 14):
+        for fam in (0, 1, 10, 11, 12, 13, 14, 15):
             dg.det_gemm_debug_force_family(fam)
             assert_bits_equal(gpu_op("dw", dt, A, B, tier="fast"), y, f"family {fam}")
         dg.det_gemm_debug_force_family(-1)
