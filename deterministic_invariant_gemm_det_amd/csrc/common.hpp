@@ -93,7 +93,7 @@ hipError_t launch_exact(Op op, Dt dt, const GemmArgs& a, int variant, hipStream_
 hipError_t launch_fast(Op op, Dt dt, const GemmArgs& a, int family, hipStream_t stream);
 hipError_t launch_fast16(Op op, Dt dt, const GemmArgs& a, int family, hipStream_t stream);
 bool fast16_w_ok(const GemmArgs& a);
-int fast16_w_shape(int64_t cols);
+int fast16_w_shape(int64_t cols, int64_t red);
 hipError_t launch_fast16_w(Op op, Dt dt, const GemmArgs& a, int shape, hipStream_t stream);
 int fast_auto_family(Op op, Dt dt, int64_t cols, int64_t red);
 

@@ -431,7 +431,7 @@ hipError_t launch_fast(Op op, Dt dt, const GemmArgs& a, int family, hipStream_t 
       // a given tile shape s of that kernel); otherwise, and family 1, the
       // four-wave register-staged kernel. Identical bits.
       if (family == 0 && fast16_w_ok(a))
-        return launch_fast16_w(op, dt, a, op == OP_DW ? 0 : fast16_w_shape(a.cols), stream);
+        return launch_fast16_w(op, dt, a, op == OP_DW ? 0 : fast16_w_shape(a.cols, a.red), stream);
       if (family >= 10 && fast16_w_ok(a)) return launch_fast16_w(op, dt, a, family - 10, stream);
       return launch_fast16(op, dt, a, family == 1 ? 1 : 0, stream);
   }

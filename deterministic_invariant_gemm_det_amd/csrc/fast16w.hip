@@ -657,10 +657,16 @@ bool fast16_w_ok(const GemmArgs& a) {
          reinterpret_cast<uintptr_t>(a.bias) % 16 == 0;
 }
 
-// Wide outputs: 256 x 192 tiles; narrow ones: 128 x 192 tiles with stages of
-// 128 reduction indices where the reduction allows it (shape 4 falls back to
-// stages of 64 otherwise). Chosen from the column count only.
-int fast16_w_shape(int64_t cols) { return cols >= 1536 ? 0 : 4; }
+// Wide outputs: 256 x 192 tiles, except long reductions (4096 indices or
+// more) into at most 4096 columns, which measured faster as 128 x 192 tiles
+// in two four-wave workgroups per compute unit; narrow outputs: 128 x 192
+// tiles with stages of 128 reduction indices where the reduction allows it
+// (shape 4 falls back to stages of 64 otherwise). Chosen from the column count
+// and the reduction length only, never the row count.
+int fast16_w_shape(int64_t cols, int64_t red) {
+  if (cols < 1536) return 4;
+  return (red >= 4096 && cols <= 4096) ? 2 : 0;
+}
 
 // dW with dY supplied transposed ([n][m], contiguous along the reduction) and x
 // as given (reduction-major): 256 x 192 tiles.
