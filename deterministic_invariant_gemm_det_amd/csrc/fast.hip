@@ -14,8 +14,10 @@
 //     its own column of B and the reduction length: not the row count, the tile
 //     family or the position of its tile. Padding rows and reduction indices
 //     are zeros, which add nothing.
-//   * The two families (large: 128x128 outputs per workgroup, small: 64x64)
-//     differ only in how outputs are grouped into workgroups.
+//   * The tile families -- for f32 inputs the staged 128x128 kernel and the
+//     plain 64x64 one here; for 16-bit inputs the tile shapes of fast16w.hip
+//     and fast16.hip -- differ only in how outputs are grouped into
+//     workgroups and how operands reach the matrix cores.
 
 #include <type_traits>
 
