@@ -28,8 +28,11 @@
  *     matrix-core products with f32 accumulation over a fixed ascending walk of
  *     the reduction, no split of the reduction for fwd and dx, one rounding to
  *     `dt` after the bias add. Identical bits on every run; for fwd and dx the
- *     bits of a row do not depend on m. Two tile families give identical bits;
- *     the family is chosen from the shape without reading m. dW of bf16/f16
+ *     bits of a row do not depend on m. Every tile family and operand layout
+ *     gives identical bits; the family is chosen from the shape without
+ *     reading m (only whether a long-reduction forward with m >= 4096 first
+ *     copies the weight transposed, 2 * k * n bytes of the stream's
+ *     workspace, looks at m: speed alone). dW of bf16/f16
  *     inputs (its reduction is over m, so batch invariance does not apply):
  *     when k x n gives few output tiles, the m rows are split into S chunks
  *     of whole 64-row stages, each accumulated from 0 in f32, and the chunk
@@ -51,7 +54,9 @@
  * Ownership and execution
  *   The caller owns every buffer. The library keeps no reference to any of them
  *   and allocates no device memory per call, with these exceptions: the fast
- *   tier's dW of bf16/f16 inputs may take a transposed copy of its smaller
+ *   tier's forward of bf16/f16 inputs with k >= 3072 and m >= 4096 takes a
+ *   transposed copy of the weight (2 * k * n bytes); its dW of bf16/f16 inputs
+ *   may take a transposed copy of its smaller
  *   operand (2 * m * min(k, n) bytes) and, when split (above), needs
  *   S * k * n * 4 bytes of f32 partials; the
  *   exact tier with at most 32 output rows (fwd and dX with m <= 32, dW with

@@ -41,3 +41,23 @@ def test_m_sweep(dt, tier):
         assert_bits_equal(full_y[rows], oracle.fwd(dt, X, W, rows=rows)[0], "fwd vs oracle")
         assert_bits_equal(full_yb[rows], oracle.fwd(dt, X, W, b, rows=rows)[0], "fwd+bias vs oracle")
         assert_bits_equal(full_dx[rows], oracle.dx(dt, G, W, rows=rows)[0], "dx vs oracle")
+
+
+@pytest.mark.parametrize("dt", ["bf16", "f16"])
+def test_m_sweep_long_reduction_fast(dt):
+    """K = 3072, N = 768 (GPT-2 c_proj): from m = 4096 on, the fast forward
+    first copies the weight transposed; rows must not change across that
+    switch (nor anywhere else in the sweep), with and without the bias."""
+    import deterministic_invariant_gemm_det_amd as dg
+    k, n = 3072, 768
+    X = syn.normal(43, syn.TID_X, (8192, k), dt=dt)
+    W = syn.normal(43, syn.TID_W, (k, n), sigma=0.02, dt=dt)
+    b = syn.normal(43, syn.TID_B, (n,), sigma=0.1, dt=dt)
+    w, bb = to_dev(W, dt), to_dev(b, dt)
+    full = to_host(dg.fwd(to_dev(X, dt), w, bb, "fast"), dt)
+    full_nb = to_host(dg.fwd(to_dev(X, dt), w, None, "fast"), dt)
+    for M in (1, 17, 2048, 4095, 4096, 6000):
+        print(f"long-reduction sweep {dt} M={M}", flush=True)
+        x = to_dev(np.ascontiguousarray(X[:M]), dt)
+        assert_bits_equal(to_host(dg.fwd(x, w, bb, "fast"), dt), full[:M], f"fwd+bias M={M}")
+        assert_bits_equal(to_host(dg.fwd(x, w, None, "fast"), dt), full_nb[:M], f"fwd M={M}")
