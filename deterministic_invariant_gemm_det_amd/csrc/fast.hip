@@ -436,16 +436,20 @@ hipError_t launch_fast(Op op, Dt dt, const GemmArgs& a, int family, hipStream_t 
       a.red % 8 == 0 && a.cols % 8 == 0 && a.red <= int64_t(64) * 65535 && a.cols * a.red * 2 < (int64_t(1) << 31)) {
     void* ws = nullptr;
     hipError_t e = stream_workspace(stream, static_cast<size_t>(a.cols) * static_cast<size_t>(a.red) * 2, &ws);
-    if (e != hipSuccess) return e;
-    e = launch_transpose<uint16_t>(a.B, a.red, a.cols, ws, stream);
-    if (e != hipSuccess) return e;
-    GemmArgs p = a;
-    p.B = ws;
-    p.ldb = a.red;
-    p.vec_b = true;
-    p.off32_b = true;
-    p.b_bytes = a.cols * a.red * 2;
-    return launch_fast16_w(OP_DX, dt, p, fast16_w_shape(a.cols, a.red), stream);   // both operands along rows
+    if (e == hipErrorOutOfMemory) {
+      (void)hipGetLastError();   // no room for the copy: the plain form below, same bits
+    } else {
+      if (e != hipSuccess) return e;
+      e = launch_transpose<uint16_t>(a.B, a.red, a.cols, ws, stream);
+      if (e != hipSuccess) return e;
+      GemmArgs p = a;
+      p.B = ws;
+      p.ldb = a.red;
+      p.vec_b = true;
+      p.off32_b = true;
+      p.b_bytes = a.cols * a.red * 2;
+      return launch_fast16_w(OP_DX, dt, p, fast16_w_shape(a.cols, a.red), stream);   // both operands along rows
+    }
   }
   switch (dt) {
     case DT_F32: return launch_family<F32>(op, family == 1 ? 1 : 0, a, stream);
