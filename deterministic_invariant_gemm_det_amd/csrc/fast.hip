@@ -331,13 +331,13 @@ hipError_t launch_family(Op op, int family, const GemmArgs& a, hipStream_t strea
 
 }  // namespace
 
-// Shape-only choice of the tile family: never reads the row count of fwd/dx.
-// Family choice from the call's shape alone (the families give identical
-// bits, so this only affects speed). f32: the staged 128 x 128 kernel unless
-// the output is narrow or the reduction short, where the 64 x 64 tiles of the
-// plain kernel keep more of the chip busy.
-// 16-bit: the large direct-to-LDS tiles pay off on long reductions outside dW;
-// short reductions and dW run faster on the smaller register-staged tiles.
+// First family choice from the output width and the reduction length (the
+// families give identical bits, so this only affects speed; launch_fast
+// refines family 0 with the row count). f32: the staged 128 x 128 kernel
+// unless the output is narrow or the reduction short, where the 64 x 64 tiles
+// of the plain kernel keep more of the chip busy. 16-bit: the large
+// direct-to-LDS tiles for outputs of 256 columns or more and for dW, the small
+// register-staged tiles otherwise.
 int fast_auto_family(Op op, Dt dt, int64_t cols, int64_t red) {
   if (dt == DT_F32) return (cols >= 512 && red >= 512) ? 0 : 1;
   (void)red;
@@ -435,7 +435,7 @@ hipError_t launch_fast(Op op, Dt dt, const GemmArgs& a, int family, hipStream_t 
   // in the same instruction order, so the same bits. Measured: GPT-2 c_proj
   // (k = 3072) 53.9 -> 49.8 us and 4096 x 11008 x 4096 915 -> 849 us at
   // m = 8192; slower for k = 768 (c_fc 51.4 -> 52.7 us) and, the copy being
-  // 2 k n bytes each way, on few rows -- the one use of m here (speed only).
+  // 2 k n bytes each way, on few rows.
   if (op == OP_FWD && dt != DT_F32 && family == 0 && fast16_w_ok(a) && a.rows >= 4096 && a.red >= 3072 &&
       a.red % 8 == 0 && a.cols % 8 == 0 && a.red <= int64_t(64) * 65535 && a.cols * a.red * 2 < (int64_t(1) << 31)) {
     void* ws = nullptr;
@@ -462,8 +462,18 @@ hipError_t launch_fast(Op op, Dt dt, const GemmArgs& a, int family, hipStream_t 
       // family 0: eight-wave large tiles where the shape allows it (10 + s:
       // a given tile shape s of that kernel); otherwise, and family 1, the
       // four-wave register-staged kernel. Identical bits.
-      if (family == 0 && fast16_w_ok(a))
-        return launch_fast16_w(op, dt, a, op == OP_DW ? 0 : fast16_w_shape(a.cols, a.red), stream);
+      if (family == 0 && fast16_w_ok(a)) {
+        const int sh = op == OP_DW ? 0 : fast16_w_shape(a.cols, a.red);
+        // Fewer tiles than compute units (few rows): smaller tiles for speed,
+        // the same bits -- fwd on fast16's 128 x 64 tiles, dX on 64 x 192
+        // tiles two per compute unit (measured at m = 256 .. 2048: fwd
+        // 768 -> 3072 at m = 256 20.2 -> 10.0 us, dX into 768 columns at
+        // m = 1024 34.1 -> 26.7 us).
+        const int64_t bm = sh == 0 ? 256 : 128;
+        if (op != OP_DW && ((a.rows + bm - 1) / bm) * ((a.cols + 191) / 192) < 256)
+          return op == OP_FWD ? launch_fast16(op, dt, a, 1, stream) : launch_fast16_w(op, dt, a, 3, stream);
+        return launch_fast16_w(op, dt, a, sh, stream);
+      }
       if (family >= 10 && fast16_w_ok(a)) return launch_fast16_w(op, dt, a, family - 10, stream);
       return launch_fast16(op, dt, a, family == 1 ? 1 : 0, stream);
   }

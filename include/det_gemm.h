@@ -29,10 +29,11 @@
  *     the reduction, no split of the reduction for fwd and dx, one rounding to
  *     `dt` after the bias add. Identical bits on every run; for fwd and dx the
  *     bits of a row do not depend on m. Every tile family and operand layout
- *     gives identical bits; the family is chosen from the shape without
- *     reading m (only whether a long-reduction forward with m >= 4096 first
- *     copies the weight transposed, 2 * k * n bytes of the stream's
- *     workspace, looks at m: speed alone). dW of bf16/f16
+ *     gives identical bits, so the library picks them for speed from the
+ *     shape, m included (smaller tiles for few rows; a long-reduction
+ *     forward with m >= 4096 first copies the weight transposed, 2 * k * n
+ *     bytes of the stream's workspace); the bits never depend on that
+ *     choice. dW of bf16/f16
  *     inputs (its reduction is over m, so batch invariance does not apply):
  *     when k x n gives few output tiles, the m rows are split into S chunks
  *     of whole 64-row stages, each accumulated from 0 in f32, and the chunk
