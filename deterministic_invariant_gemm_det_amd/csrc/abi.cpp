@@ -127,9 +127,7 @@ det_status_t run(detgemm::Op op, void* out, const void* A, const void* B, const 
   } else if (tier == DET_TIER_CR) {
     err = detgemm::launch_cr(op, d, a, g_force_cr_fallback.load(std::memory_order_relaxed), stream);
   } else {
-    int fam = g_force_family.load(std::memory_order_relaxed);
-    if (fam < 0) fam = detgemm::fast_auto_family(op, d, a.cols, a.red);
-    err = detgemm::launch_fast(op, d, a, fam, stream);
+    err = detgemm::launch_fast(op, d, a, g_force_family.load(std::memory_order_relaxed), stream);   // -1: automatic
   }
   if (err != hipSuccess) return fail(DET_ELAUNCH, "det_gemm: kernel launch failed: %s", hipGetErrorString(err));
   return DET_OK;

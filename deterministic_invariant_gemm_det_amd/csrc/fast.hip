@@ -365,6 +365,10 @@ int fast_dw_split(int64_t m, int64_t k, int64_t n, int* chunk_stages) {
 hipError_t launch_fast16_w_dw_bt(Dt dt, const GemmArgs& a, int shape, hipStream_t stream);   // fast16w.hip
 
 hipError_t launch_fast(Op op, Dt dt, const GemmArgs& a, int family, hipStream_t stream) {
+  // family < 0: automatic (a forced family runs its own kernels, so that the
+  // tests can compare every family on every shape)
+  const bool automatic = family < 0;
+  if (automatic) family = fast_auto_family(op, dt, a.cols, a.red);
   if (op == OP_DW && dt != DT_F32 && a.partial == nullptr) {
     int chunk = 0;
     const int split = fast_dw_split(a.red, a.rows, a.cols, &chunk);
@@ -464,13 +468,17 @@ hipError_t launch_fast(Op op, Dt dt, const GemmArgs& a, int family, hipStream_t 
       // four-wave register-staged kernel. Identical bits.
       if (family == 0 && fast16_w_ok(a)) {
         const int sh = op == OP_DW ? 0 : fast16_w_shape(a.cols, a.red);
-        // Fewer tiles than compute units (few rows): smaller tiles for speed,
-        // the same bits -- fwd on fast16's 128 x 64 tiles, dX on 64 x 192
-        // tiles two per compute unit (measured at m = 256 .. 2048: fwd
-        // 768 -> 3072 at m = 256 20.2 -> 10.0 us, dX into 768 columns at
-        // m = 1024 34.1 -> 26.7 us).
+        // Automatic choice, fewer tiles than compute units and rows that fill
+        // the smaller tiles exactly (ragged ones measured slower: m = 200,
+        // 27.9 against 19.9 us): smaller tiles for speed, the same bits -- fwd on fast16's
+        // 128 x 64 tiles, dX on 64 x 192 tiles two per compute unit
+        // (measured at m = 256 .. 2048: fwd 768 -> 3072 at m = 256 20.2 ->
+        // 10.0 us, at m = 128 19.5 -> 9.7 us, dX into 768 columns at m = 1024
+        // 34.1 -> 26.7 us; from m = 1 to 64 the large tiles stay faster,
+        // 19.2 against 22 - 27 us).
         const int64_t bm = sh == 0 ? 256 : 128;
-        if (op != OP_DW && ((a.rows + bm - 1) / bm) * ((a.cols + 191) / 192) < 256)
+        if (automatic && op != OP_DW && a.rows % (op == OP_FWD ? 128 : 64) == 0 &&
+            ((a.rows + bm - 1) / bm) * ((a.cols + 191) / 192) < 256)
           return op == OP_FWD ? launch_fast16(op, dt, a, 1, stream) : launch_fast16_w(op, dt, a, 3, stream);
         return launch_fast16_w(op, dt, a, sh, stream);
       }
