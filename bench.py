@@ -500,10 +500,10 @@ def main():
     }
     result["output_sha256"] = output_hashes(data, steps)
     if not args.no_peak:
-        import deterministic_invariant_gemm_det_amd as dg
-        peaks = {"fp64_mfma_4x4x4": round(dg.measure_peak(0, 4000), 2), "fp64_fma_valu": round(dg.measure_peak(1, 4000), 2),
-                 "bf16_mfma_32x32x16": round(dg.measure_peak(2, 2000), 2), "unit": "TFLOP/s",
-                 "note": "the library's peak-rate microkernels at the box's running clock (no memory traffic)"}
+        from deterministic_invariant_gemm_det_amd import peak as dpeak
+        peaks = {"fp64_mfma_4x4x4": round(dpeak.measure(0, 4000), 2), "fp64_fma_valu": round(dpeak.measure(1, 4000), 2),
+                 "bf16_mfma_32x32x16": round(dpeak.measure(2, 2000), 2), "unit": "TFLOP/s",
+                 "note": "peak-rate microkernels (libdetpeak.so) at the box's running clock (no memory traffic)"}
         result["measured_peak"] = peaks
         result["tiers"]["exact"]["pct_of_measured_peak"] = round(100 * result["tiers"]["exact"]["tflops"] / peaks["fp64_mfma_4x4x4"], 2)
         result["tiers"]["fast"]["pct_of_measured_peak"] = round(100 * result["tiers"]["fast"]["tflops"] / peaks["bf16_mfma_32x32x16"], 2)

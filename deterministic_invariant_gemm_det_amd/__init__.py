@@ -14,7 +14,7 @@ import os
 __all__ = [
     "det_gemm_fwd", "det_gemm_dx", "det_gemm_dw", "det_gemm_dw_out", "det_gemm_db", "det_gemm_strerror",
     "det_gemm_last_error", "det_gemm_version", "det_gemm_debug_force_family", "det_gemm_debug_force_exact_kernel",
-    "det_gemm_debug_force_db_chunk", "det_gemm_debug_force_cr_fallback", "det_gemm_measure_peak", "measure_peak",
+    "det_gemm_debug_force_db_chunk", "det_gemm_debug_force_cr_fallback", "det_gemm_debug_force_arch",
     "DetGemmError", "LIB_PATH", "fwd", "dx", "dw", "db", "deterministic_linear", "Linear", "DTYPES", "TIERS",
     "det_layernorm_fwd", "det_layernorm_bwd", "layer_norm", "layer_norm_backward", "deterministic_layer_norm",
 ]
@@ -75,8 +75,8 @@ def lib():
         L.det_gemm_debug_force_db_chunk.restype = ci
         L.det_gemm_debug_force_cr_fallback.argtypes = [ci]
         L.det_gemm_debug_force_cr_fallback.restype = ci
-        L.det_gemm_measure_peak.argtypes = [ci, ci, vp, i64, ctypes.POINTER(ctypes.c_double), vp]
-        L.det_gemm_measure_peak.restype = ci
+        L.det_gemm_debug_force_arch.argtypes = [ctypes.c_char_p]
+        L.det_gemm_debug_force_arch.restype = ci
         _lib = L
     return _lib
 
@@ -167,31 +167,9 @@ def det_gemm_debug_force_cr_fallback(on):
     _check(lib().det_gemm_debug_force_cr_fallback(int(bool(on))))
 
 
-def det_gemm_measure_peak(kind, iters, out, out_len, stream):
-    """One peak-rate microkernel launch (measurement aid); returns the flops it performs."""
-    fl = ctypes.c_double(0.0)
-    _check(lib().det_gemm_measure_peak(kind, iters, _p(out), out_len, ctypes.byref(fl), stream))
-    return fl.value
-
-
-def measure_peak(kind, iters, reps=5, device=None):
-    """Sustained TFLOP/s of peak-rate microkernel `kind` (0: float64 4x4x4 MFMA, 1: float64
-    vector fma, 2: bf16 32x32x16 MFMA) on the current stream: one warm-up launch, then `reps`
-    launches between two events."""
-    import torch
-    dev = torch.device("cuda", torch.cuda.current_device()) if device is None else torch.device(device)
-    cus = torch.cuda.get_device_properties(dev).multi_processor_count
-    out = torch.empty(cus * 512, dtype=torch.float64, device=dev)
-    stream = torch.cuda.current_stream(dev)
-    det_gemm_measure_peak(kind, iters, out, out.numel(), stream.cuda_stream)
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record(stream)
-    flops = 0.0
-    for _ in range(reps):
-        flops += det_gemm_measure_peak(kind, iters, out, out.numel(), stream.cuda_stream)
-    e1.record(stream)
-    torch.cuda.synchronize(dev)
-    return flops / (e0.elapsed_time(e1) * 1e-3) / 1e12
+def det_gemm_debug_force_arch(arch):
+    """Test hook: check `arch` (a string) instead of the device's architecture; None restores it."""
+    _check(lib().det_gemm_debug_force_arch(None if arch is None else arch.encode()))
 
 
 # ---------------------------------------------------------------- torch layer
@@ -224,28 +202,39 @@ def _prep(*ts):
     return out, torch.cuda.current_stream(dev).cuda_stream
 
 
+def _out(out, shape, dtype, device):
+    """The output tensor: a new one, or the caller's `out` after checking that the kernels may
+    write exactly shape x dtype into it (contiguous, on the operands' device); a mismatch raises
+    ValueError before anything is launched."""
+    import torch
+    if out is None:
+        return torch.empty(shape, dtype=dtype, device=device)
+    if out.dtype != dtype or tuple(out.shape) != tuple(shape) or not out.is_contiguous() or out.device != device:
+        raise ValueError(f"out must be a contiguous {tuple(shape)} tensor of {dtype} on {device}; got "
+                         f"{tuple(out.shape)} {out.dtype} on {out.device} (contiguous={out.is_contiguous()})")
+    return out
+
+
 def fwd(x, w, bias=None, tier="exact", out=None):
     """y[m,n] = x[m,k] @ w[k,n] (+ bias[n]) on the current stream."""
-    import torch
     (x, w, bias), stream = _prep(x, w, bias)
     m, k = x.shape
     k2, n = w.shape
     if k2 != k or (bias is not None and tuple(bias.shape) != (n,)):
         raise ValueError("shape mismatch")
-    y = out if out is not None else torch.empty((m, n), dtype=x.dtype, device=x.device)
+    y = _out(out, (m, n), x.dtype, x.device)
     det_gemm_fwd(y, x, w, bias, m, k, n, _torch_dtype_name(x), tier, stream)
     return y
 
 
 def dx(dy, w, tier="exact", out=None):
     """dx[m,k] = dy[m,n] @ w[k,n]^T on the current stream."""
-    import torch
     (dy, w), stream = _prep(dy, w)
     m, n = dy.shape
     k, n2 = w.shape
     if n2 != n:
         raise ValueError("shape mismatch")
-    g = out if out is not None else torch.empty((m, k), dtype=dy.dtype, device=dy.device)
+    g = _out(out, (m, k), dy.dtype, dy.device)
     det_gemm_dx(g, dy, w, m, k, n, _torch_dtype_name(dy), tier, stream)
     return g
 
@@ -260,9 +249,7 @@ def dw(x, dy, tier="exact", out=None, out_dtype=None):
     if m2 != m:
         raise ValueError("shape mismatch")
     odt = out_dtype or x.dtype
-    g = out if out is not None else torch.empty((k, n), dtype=odt, device=x.device)
-    if g.dtype != odt or not g.is_contiguous() or tuple(g.shape) != (k, n):
-        raise ValueError("out must be a contiguous (k, n) tensor of the output dtype")
+    g = _out(out, (k, n), odt, x.device)
     if odt == x.dtype:
         det_gemm_dw(g, x, dy, m, k, n, _torch_dtype_name(x), tier, stream)
     else:
@@ -277,9 +264,7 @@ def db(dy, tier="exact", out=None, out_dtype=None):
     (dy,), stream = _prep(dy)
     m, n = dy.shape
     odt = out_dtype or dy.dtype
-    g = out if out is not None else torch.empty((n,), dtype=odt, device=dy.device)
-    if g.dtype != odt or not g.is_contiguous() or g.numel() != n:
-        raise ValueError("out must be a contiguous tensor of n elements of the output dtype")
+    g = _out(out, (n,), odt, dy.device)
     det_gemm_db(g, _torch_dtype_name(g), dy, m, n, _torch_dtype_name(dy), tier, stream)
     return g
 
@@ -293,9 +278,7 @@ def layer_norm(x, gamma=None, beta=None, eps=1e-5, out=None):
     for v in (gamma, beta):
         if v is not None and tuple(v.shape) != (h,):
             raise ValueError("gamma and beta must have h elements")
-    y = out if out is not None else torch.empty_like(x)
-    if y.dtype != x.dtype or not y.is_contiguous() or tuple(y.shape) != (rows, h):
-        raise ValueError("out must be a contiguous tensor like x")
+    y = _out(out, (rows, h), x.dtype, x.device)
     mean = torch.empty(rows, dtype=torch.float64, device=x.device)
     rstd = torch.empty(rows, dtype=torch.float64, device=x.device)
     det_layernorm_fwd(y, mean, rstd, x, gamma, beta, rows, h, eps, _torch_dtype_name(x), stream)

@@ -1,4 +1,5 @@
-"""Build libdetgemm.so (the C-ABI HIP library) for gfx950 with hipcc.
+"""Build libdetgemm.so (the C-ABI HIP library) and libdetpeak.so (the
+benchmark's peak-rate microkernels, a separate library) for gfx950 with hipcc.
 
 Every source under csrc/ is compiled ahead of time for gfx950 only. Floating
 point contraction is off (the exact tier's float64 operations are written out
@@ -12,8 +13,9 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 ROOT = os.path.dirname(HERE)
 LIB = os.path.join(HERE, "libdetgemm.so")
-SOURCES = ["abi.cpp", "exact.hip", "fast.hip", "fast16.hip", "fast16w.hip", "colsum.hip", "layernorm.hip", "cr.hip",
-           "peak.hip"]
+PEAK_LIB = os.path.join(HERE, "libdetpeak.so")
+SOURCES = ["abi.cpp", "exact.hip", "fast.hip", "fast16.hip", "fast16w.hip", "colsum.hip", "layernorm.hip", "cr.hip"]
+PEAK_SOURCES = ["peak.hip"]
 # Per-source extra flags. The exact tier keeps matrix-core results in ordinary
 # VGPRs: the Neumaier update reads every partial on the vector ALU, and the
 # accumulator-register form would add a copy per partial.
@@ -38,17 +40,22 @@ def _compile(src, build_dir):
     return obj
 
 
-def build(out=LIB, jobs=4):
-    build_dir = os.path.join(HERE, "_build")
-    os.makedirs(build_dir, exist_ok=True)
-    with cf.ThreadPoolExecutor(max_workers=jobs) as ex:
-        objs = list(ex.map(lambda s: _compile(s, build_dir), SOURCES))
+def _link(objs, out):
     tmp = out + ".tmp"
     r = subprocess.run([HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", tmp],
                        capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stdout}\n{r.stderr}")
     os.replace(tmp, out)
+
+
+def build(out=LIB, jobs=4, peak_out=PEAK_LIB):
+    build_dir = os.path.join(HERE, "_build")
+    os.makedirs(build_dir, exist_ok=True)
+    with cf.ThreadPoolExecutor(max_workers=jobs) as ex:
+        objs = list(ex.map(lambda s: _compile(s, build_dir), SOURCES + PEAK_SOURCES))
+    _link(objs[:len(SOURCES)], out)
+    _link(objs[len(SOURCES):], peak_out)
     return out
 
 

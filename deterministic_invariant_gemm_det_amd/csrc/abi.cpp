@@ -10,17 +10,9 @@
 #include <map>
 #include <mutex>
 #include <utility>
+#include <vector>
 
 #include "common.hpp"
-
-namespace detgemm {
-// Peak-rate microkernels (measurement only, peak.hip): threads launched for
-// num_cu compute units, and the launch of kind 0 (float64 4x4x4 MFMA), 1
-// (float64 vector fma) or 2 (bf16 32x32x16 MFMA); *flops receives the flops
-// the launch performs.
-int64_t peak_threads(int num_cu);
-hipError_t launch_peak(int kind, int num_cu, int iters, double* out, double* flops, hipStream_t stream);
-}  // namespace detgemm
 
 namespace {
 
@@ -43,6 +35,13 @@ det_status_t fail(det_status_t st, const char* fmt, const char* detail = "") {
   return st;
 }
 
+// Test hook: an architecture name that replaces the device's own in the check
+// below (empty: none). Guarded by a mutex; the flag keeps the common path free
+// of the lock.
+std::atomic<bool> g_arch_override_on{false};
+std::mutex g_arch_override_mu;
+char g_arch_override[64] = "";
+
 det_status_t check_device(int* cus) {
   int dev = -1;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0) {
@@ -50,6 +49,15 @@ det_status_t check_device(int* cus) {
     return fail(DET_EDEVICE, "det_gemm: no current HIP device%s");
   }
   if (dev >= kMaxDevices) return fail(DET_EDEVICE, "det_gemm: device index out of range%s");
+  if (g_arch_override_on.load(std::memory_order_acquire)) {
+    char arch[64];
+    {
+      std::lock_guard<std::mutex> lock(g_arch_override_mu);
+      std::memcpy(arch, g_arch_override, sizeof(arch));
+    }
+    if (arch[0] != '\0' && std::strncmp(arch, "gfx950", 6) != 0)
+      return fail(DET_EDEVICE, "det_gemm: device architecture %s is not gfx950 (MI355X); refusing to run", arch);
+  }
   int state = g_device_ok[dev].load(std::memory_order_acquire);
   if (state == 0) {
     hipDeviceProp_t prop;
@@ -120,6 +128,7 @@ det_status_t run(detgemm::Op op, void* out, const void* A, const void* B, const 
   a.a_bytes = a_elems * esz;
   a.b_bytes = b_elems * esz;
   const detgemm::Dt d = static_cast<detgemm::Dt>(dt);
+  detgemm::StreamCallLock call_lock(stream);
   hipError_t err;
   if (tier == DET_TIER_EXACT) {
     const int v = g_force_exact.load(std::memory_order_relaxed);
@@ -137,36 +146,103 @@ det_status_t run(detgemm::Op op, void* out, const void* A, const void* B, const 
 
 namespace detgemm {
 
-// Per (device, stream) workspace. Calls on one stream are ordered by the
-// stream, so they may share it; calls on different streams get different
-// ones. Growing waits for the stream's earlier work before freeing the old
-// allocation.
+namespace {
+
+// Per (device, stream) state: the call lock and the workspace.
+struct StreamSlot {
+  std::mutex call;          // held by a call from its first workspace request to its last launch
+  void* buf = nullptr;      // current workspace
+  size_t bytes = 0;
+  std::vector<void*> retired;   // outgrown buffers: still possibly in use by enqueued work, never freed
+};
+
+std::mutex g_slots_mu;
+std::map<std::pair<int, hipStream_t>, StreamSlot*> g_slots;
+
+StreamSlot* slot_of(int dev, hipStream_t stream) {
+  std::lock_guard<std::mutex> lock(g_slots_mu);
+  StreamSlot*& s = g_slots[{dev, stream}];
+  if (!s) s = new StreamSlot();   // kept until the process ends
+  return s;
+}
+
+// A fixed device buffer that replaces the stream workspace for the calls of
+// one thread (the entry point that allocates nothing sets it for the duration
+// of its call).
+struct FixedWorkspace {
+  void* ptr;
+  size_t cap;
+  size_t wanted;   // largest request seen, for the error message
+};
+thread_local FixedWorkspace* t_fixed = nullptr;
+
+}  // namespace
+
+// Holds the calling stream's lock for the duration of one entry point's
+// enqueueing, so that the launches of concurrent calls on one stream do not
+// interleave (each call's kernels meet its workspace in stream order).
+StreamCallLock::StreamCallLock(hipStream_t stream) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) {
+    (void)hipGetLastError();
+    dev = -1;
+  }
+  mu_ = &slot_of(dev, stream)->call;
+  mu_->lock();
+}
+StreamCallLock::~StreamCallLock() { mu_->unlock(); }
+
+// Workspace of at least `bytes` for (current device, stream). Calls on one
+// stream are ordered by the stream (and by StreamCallLock between threads), so
+// they share it; calls on different streams get different ones. Growth takes
+// a new allocation of at least twice the old size and retires the old one
+// without freeing it (work already enqueued may still use it), so a call
+// never synchronises. Under a FixedWorkspace the fixed buffer is returned, or
+// hipErrorOutOfMemory when it is too small (nothing is allocated).
 hipError_t stream_workspace(hipStream_t stream, size_t bytes, void** ptr) {
-  static std::mutex mu;
-  static std::map<std::pair<int, hipStream_t>, std::pair<void*, size_t>> cache;
+  if (t_fixed) {
+    if (bytes > t_fixed->wanted) t_fixed->wanted = bytes;
+    if (bytes > t_fixed->cap) return hipErrorOutOfMemory;
+    *ptr = t_fixed->ptr;
+    return hipSuccess;
+  }
   int dev = -1;
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return e;
-  std::lock_guard<std::mutex> lock(mu);
-  auto& slot = cache[{dev, stream}];
-  if (slot.second >= bytes) {
-    *ptr = slot.first;
+  StreamSlot* slot = slot_of(dev, stream);   // the caller holds slot->call
+  if (slot->bytes >= bytes) {
+    *ptr = slot->buf;
     return hipSuccess;
   }
-  if (slot.first) {
-    e = hipStreamSynchronize(stream);
-    if (e != hipSuccess) return e;
-    (void)hipFree(slot.first);
-    slot = {nullptr, 0};
-  }
   const size_t grain = size_t(1) << 24;
-  const size_t want = (bytes + grain - 1) / grain * grain;
+  size_t want = (bytes + grain - 1) / grain * grain;
+  if (want < 2 * slot->bytes) want = 2 * slot->bytes;
   void* p = nullptr;
   e = hipMalloc(&p, want);
+  if (e != hipSuccess && want > bytes) {   // the doubling did not fit: the request itself
+    (void)hipGetLastError();
+    want = (bytes + grain - 1) / grain * grain;
+    e = hipMalloc(&p, want);
+  }
   if (e != hipSuccess) return e;
-  slot = {p, want};
+  if (slot->buf) slot->retired.push_back(slot->buf);
+  slot->buf = p;
+  slot->bytes = want;
   *ptr = p;
   return hipSuccess;
+}
+
+// Runs `fn` with `ptr` (cap bytes, device memory) in place of the stream
+// workspace for every request it makes on this thread; *wanted receives the
+// largest request (0 if none).
+hipError_t with_fixed_workspace(void* ptr, size_t cap, size_t* wanted, hipError_t (*fn)(void*), void* ctx) {
+  FixedWorkspace fw{ptr, cap, 0};
+  FixedWorkspace* prev = t_fixed;
+  t_fixed = &fw;
+  const hipError_t e = fn(ctx);
+  t_fixed = prev;
+  *wanted = fw.wanted;
+  return e;
 }
 
 }  // namespace detgemm
@@ -218,6 +294,7 @@ det_status_t det_gemm_db(void* db, det_dtype_t db_dt, const void* dy, int64_t m,
   int cus = 0;
   const det_status_t dev = check_device(&cus);
   if (dev != DET_OK) return dev;
+  detgemm::StreamCallLock call_lock(stream);
   if (tier == DET_TIER_CR) {   // the correctly rounded column sum: dW of a column of ones
     detgemm::GemmArgs a;
     std::memset(&a, 0, sizeof(a));
@@ -276,6 +353,7 @@ det_status_t det_layernorm_bwd(void* dx, void* dgamma, void* dbeta, det_dtype_t 
   int cus = 0;
   const det_status_t dev = check_device(&cus);
   if (dev != DET_OK) return dev;
+  detgemm::StreamCallLock call_lock(stream);
   const hipError_t err = detgemm::launch_layernorm_bwd(static_cast<detgemm::Dt>(dt), param_dt == DET_F32 && dt != DET_F32,
                                                        dy, x, mean, rstd, gamma, rows, h, dx, dgamma, dbeta, stream);
   if (err != hipSuccess) return fail(DET_ELAUNCH, "det_layernorm: kernel launch failed: %s", hipGetErrorString(err));
@@ -317,26 +395,23 @@ det_status_t det_gemm_debug_force_cr_fallback(int on) {
   return DET_OK;
 }
 
-det_status_t det_gemm_debug_force_db_chunk(int64_t tiles) {
-  if (tiles < 0) return fail(DET_EINVAL, "det_gemm: db chunk must be >= 0%s");
-  g_force_db_chunk.store(tiles, std::memory_order_relaxed);
+det_status_t det_gemm_debug_force_arch(const char* arch) {
+  if (arch != nullptr && std::strlen(arch) >= sizeof(g_arch_override))
+    return fail(DET_EINVAL, "det_gemm: architecture name longer than 63 characters%s");
+  std::lock_guard<std::mutex> lock(g_arch_override_mu);
+  if (arch == nullptr || arch[0] == '\0') {
+    g_arch_override[0] = '\0';
+    g_arch_override_on.store(false, std::memory_order_release);
+  } else {
+    std::snprintf(g_arch_override, sizeof(g_arch_override), "%s", arch);
+    g_arch_override_on.store(true, std::memory_order_release);
+  }
   return DET_OK;
 }
 
-det_status_t det_gemm_measure_peak(int kind, int iters, double* out, int64_t out_len, double* flops,
-                                   hipStream_t stream) {
-  if (kind < 0 || kind > 2) return fail(DET_EINVAL, "det_gemm_measure_peak: kind must be 0, 1 or 2%s");
-  if (iters < 1 || out == nullptr || flops == nullptr)
-    return fail(DET_EINVAL, "det_gemm_measure_peak: iters >= 1 and non-null out and flops required%s");
-  int cus = 0;
-  const det_status_t st = check_device(&cus);
-  if (st != DET_OK) return st;
-  if (out_len < detgemm::peak_threads(cus))
-    return fail(DET_EINVAL, "det_gemm_measure_peak: out must hold one double per thread (compute units x 512)%s");
-  if (detgemm::launch_peak(kind, cus, iters, out, flops, stream) != hipSuccess) {
-    (void)hipGetLastError();
-    return fail(DET_ELAUNCH, "det_gemm_measure_peak: kernel launch failed%s");
-  }
+det_status_t det_gemm_debug_force_db_chunk(int64_t tiles) {
+  if (tiles < 0) return fail(DET_EINVAL, "det_gemm: db chunk must be >= 0%s");
+  g_force_db_chunk.store(tiles, std::memory_order_relaxed);
   return DET_OK;
 }
 

@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <mutex>
+
 namespace detgemm {
 
 enum Op { OP_FWD = 0, OP_DX = 1, OP_DW = 2 };
@@ -107,8 +109,6 @@ hipError_t launch_combine(Dt dt, bool out_f32, const float* partial, int split, 
 // chunk_tiles > 0 forces the tiles per chunk of the column sum (bits unchanged)
 hipError_t launch_db(Dt dt, bool out_f32, const void* dy, int64_t m, int64_t n, void* db, int64_t chunk_tiles,
                      hipStream_t stream);
-// A device workspace of at least `bytes` owned by the library for (current device, stream);
-// grown on demand, kept for later calls on the same stream.
 // LayerNorm over rows of h elements (h <= 65536), float64 statistics.
 hipError_t launch_layernorm_fwd(Dt dt, const void* x, const void* gamma, const void* beta, int64_t rows, int64_t h,
                                 double eps, void* y, double* mean, double* rstd, hipStream_t stream);
@@ -117,6 +117,21 @@ hipError_t launch_layernorm_bwd(Dt dt, bool param_f32, const void* dy, const voi
                                 void* dgamma, void* dbeta, hipStream_t stream);
 // Correctly rounded tier; a null A stands for a column of ones.
 hipError_t launch_cr(Op op, Dt dt, const GemmArgs& a, int force_fallback, hipStream_t stream);
+// A device workspace of at least `bytes` for (current device, stream), owned
+// by the library; the caller holds that stream's StreamCallLock.
 hipError_t stream_workspace(hipStream_t stream, size_t bytes, void** ptr);
+// Held by every entry point while it requests workspace and enqueues its
+// kernels: one lock per (device, stream).
+class StreamCallLock {
+ public:
+  explicit StreamCallLock(hipStream_t stream);
+  ~StreamCallLock();
+  StreamCallLock(const StreamCallLock&) = delete;
+  StreamCallLock& operator=(const StreamCallLock&) = delete;
+
+ private:
+  std::mutex* mu_;
+};
+hipError_t with_fixed_workspace(void* ptr, size_t cap, size_t* wanted, hipError_t (*fn)(void*), void* ctx);
 
 }  // namespace detgemm

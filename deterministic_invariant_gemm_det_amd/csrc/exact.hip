@@ -660,10 +660,29 @@ bool use_mfma16(const GemmArgs& a) {
   return ((a.cols + BN - 1) / BN) * ((a.rows + BM - 1) / BM) <= 2 * units;
 }
 
+// The few-rows path keeps every tile partial: 8 * rows * cols * ceil(red / 32)
+// bytes. It is taken automatically only up to this size (a dW with few output
+// rows has a reduction over the batch, whose tile count has no bound), and the
+// blocked kernels, which need no workspace and give the same bits, run when
+// the workspace cannot be had.
+constexpr int64_t SK_MAX_BYTES = int64_t(64) << 20;
+
+bool use_skinny(const GemmArgs& a) {
+  if (a.rows > SK_ROWS) return false;
+  const int64_t T = (a.red + KT - 1) / KT;
+  return T <= SK_MAX_BYTES / 8 / (a.rows * a.cols);   // 8 T rows cols <= SK_MAX_BYTES without overflow
+}
+
 template <typename E, bool AC, bool BC, typename O = E>
 hipError_t launch_typed(const GemmArgs& a, int variant, hipStream_t stream) {
-  if (variant < 0) variant = a.rows <= SK_ROWS ? 5 : use_48_rows(a) ? 4 : use_mfma16(a) ? 1 : 0;
-  if (variant == 5) return launch_skinny<E, AC, BC, O>(a, stream);
+  const bool automatic = variant < 0;
+  if (automatic) variant = use_skinny(a) ? 5 : use_48_rows(a) ? 4 : use_mfma16(a) ? 1 : 0;
+  if (variant == 5) {
+    const hipError_t e = launch_skinny<E, AC, BC, O>(a, stream);
+    if (!(automatic && e == hipErrorOutOfMemory)) return e;
+    (void)hipGetLastError();   // nothing was enqueued: the blocked kernels below, same bits
+    variant = use_48_rows(a) ? 4 : use_mfma16(a) ? 1 : 0;
+  }
   // f32 output: the default kernel in its two row-block forms (identical bits)
   if constexpr (!std::is_same<O, E>::value) {
     if (variant != 4) variant = 0;

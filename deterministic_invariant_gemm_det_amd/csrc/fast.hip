@@ -19,8 +19,6 @@
 //     and fast16.hip -- differ only in how outputs are grouped into
 //     workgroups and how operands reach the matrix cores.
 
-#include <type_traits>
-
 #include "common.hpp"
 #include "transpose.hpp"
 
@@ -31,33 +29,9 @@ constexpr int THREADS = 256;  // 4 waves, 2x2
 constexpr int KS = 32;        // reduction depth staged in LDS per step
 
 typedef float v4f __attribute__((ext_vector_type(4)));
-typedef float v16f __attribute__((ext_vector_type(16)));
-typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
-typedef _Float16 v8h __attribute__((ext_vector_type(8)));
-typedef uint16_t v8u16 __attribute__((ext_vector_type(8)));
 
 template <typename E> struct Mfma;
 
-// 32x32 outputs per instruction, depth 16; lane l holds A[l%32][8*(l/32)+j],
-// B[8*(l/32)+j][l%32]; accumulator i of lane l is D[8*(i/4)+4*(l/32)+i%4][l%32].
-template <> struct Mfma<BF16> {
-  static constexpr int BLK = 32, DEPTH = 16, PER = 8, ACC = 16;
-  using Acc = v16f;
-  __device__ static inline Acc step(const uint16_t* a, const uint16_t* b, Acc c) {
-    const v8u16 av = *reinterpret_cast<const v8u16*>(a);
-    const v8u16 bv = *reinterpret_cast<const v8u16*>(b);
-    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(v8bf, av), __builtin_bit_cast(v8bf, bv), c, 0, 0, 0);
-  }
-  __device__ static inline int row(int lane, int i) { return 8 * (i / 4) + 4 * (lane / 32) + (i % 4); }
-};
-template <> struct Mfma<F16> {
-  static constexpr int BLK = 32, DEPTH = 16, PER = 8, ACC = 16;
-  using Acc = v16f;
-  __device__ static inline Acc step(const _Float16* a, const _Float16* b, Acc c) {
-    return __builtin_amdgcn_mfma_f32_32x32x16_f16(*reinterpret_cast<const v8h*>(a), *reinterpret_cast<const v8h*>(b), c, 0, 0, 0);
-  }
-  __device__ static inline int row(int lane, int i) { return 8 * (i / 4) + 4 * (lane / 32) + (i % 4); }
-};
 // 16x16 outputs per instruction, depth 4; lane l holds A[l%16][l/16],
 // B[l/16][l%16]; accumulator i of lane l is D[4*(l/16)+i][l%16].
 template <> struct Mfma<F32> {
@@ -312,21 +286,18 @@ hipError_t launch_f32_large(const GemmArgs& a, hipStream_t stream) {
   return hipGetLastError();
 }
 
-template <typename E>
-hipError_t launch_family(Op op, int family, const GemmArgs& a, hipStream_t stream) {
-  if constexpr (std::is_same<E, F32>::value) {
-    // f32: family 0 is the staged large-tile kernel, family 1 the plain one (same bits)
-    if (family == 0) {
-      switch (op) {
-        case OP_FWD: return launch_f32_large<true, false>(a, stream);
-        case OP_DX:  return launch_f32_large<true, true>(a, stream);
-        case OP_DW:  return launch_f32_large<false, false>(a, stream);
-      }
-      return hipErrorInvalidValue;
+// f32 inputs: family 0 is the staged 128 x 128 kernel, family 1 the plain
+// 64 x 64 one (the same instruction sequence per output, so the same bits).
+hipError_t launch_family_f32(Op op, int family, const GemmArgs& a, hipStream_t stream) {
+  if (family == 0) {
+    switch (op) {
+      case OP_FWD: return launch_f32_large<true, false>(a, stream);
+      case OP_DX:  return launch_f32_large<true, true>(a, stream);
+      case OP_DW:  return launch_f32_large<false, false>(a, stream);
     }
-    return launch_op<E, 64, 64>(op, a, stream);
+    return hipErrorInvalidValue;
   }
-  return family == 0 ? launch_op<E, 128, 128>(op, a, stream) : launch_op<E, 64, 64>(op, a, stream);
+  return launch_op<F32, 64, 64>(op, a, stream);
 }
 
 }  // namespace
@@ -460,7 +431,7 @@ hipError_t launch_fast(Op op, Dt dt, const GemmArgs& a, int family, hipStream_t 
     }
   }
   switch (dt) {
-    case DT_F32: return launch_family<F32>(op, family == 1 ? 1 : 0, a, stream);
+    case DT_F32: return launch_family_f32(op, family == 1 ? 1 : 0, a, stream);
     case DT_BF16:
     case DT_F16:
       // family 0: eight-wave large tiles where the shape allows it (10 + s:

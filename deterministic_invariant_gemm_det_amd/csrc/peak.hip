@@ -14,6 +14,9 @@
 // thread writes one float64 (a sum of its accumulators) to out[global thread
 // index], so that nothing is optimised away; the values carry no meaning.
 
+#include <cstring>
+
+#include "../../include/det_peak.h"
 #include "common.hpp"
 
 namespace detgemm {
@@ -74,8 +77,6 @@ __global__ void __launch_bounds__(256) peak_kernel(double* __restrict__ out, int
 
 }  // namespace
 
-int64_t peak_threads(int num_cu) { return static_cast<int64_t>(num_cu) * 2 * 256; }
-
 hipError_t launch_peak(int kind, int num_cu, int iters, double* out, double* flops, hipStream_t stream) {
   const int blocks = num_cu * 2;
   const double waves = 4.0 * blocks;
@@ -99,3 +100,21 @@ hipError_t launch_peak(int kind, int num_cu, int iters, double* out, double* flo
 }
 
 }  // namespace detgemm
+
+extern "C" int det_peak_run(int kind, int iters, double* out, int64_t out_len, double* flops, hipStream_t stream) {
+  if (kind < 0 || kind > 2 || iters < 1 || out == nullptr || flops == nullptr) return -1;
+  int dev = -1;
+  hipDeviceProp_t prop;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || hipGetDeviceProperties(&prop, dev) != hipSuccess) {
+    (void)hipGetLastError();
+    return -4;
+  }
+  if (std::strncmp(prop.gcnArchName, "gfx950", 6) != 0) return -4;
+  const int cus = prop.multiProcessorCount > 0 ? prop.multiProcessorCount : 1;
+  if (out_len < static_cast<int64_t>(cus) * 2 * 256) return -1;
+  if (detgemm::launch_peak(kind, cus, iters, out, flops, stream) != hipSuccess) {
+    (void)hipGetLastError();
+    return -5;
+  }
+  return 0;
+}

@@ -53,29 +53,38 @@
  *     output tile, times 3).
  *
  * Ownership and execution
- *   The caller owns every buffer. The library keeps no reference to any of them
- *   and allocates no device memory per call, with these exceptions: the fast
- *   tier's forward of bf16/f16 inputs with k >= 3072 and m >= 4096 takes a
- *   transposed copy of the weight (2 * k * n bytes); its dW of bf16/f16 inputs
- *   may take a transposed copy of its smaller
- *   operand (2 * m * min(k, n) bytes) and, when split (above), needs
- *   S * k * n * 4 bytes of f32 partials; the
- *   exact tier with at most 32 output rows (fwd and dX with m <= 32, dW with
- *   k <= 32) computes every tile partial in parallel and needs
- *   8 * rows * cols * ceil(red / 32) bytes (rows x cols the output, red the
- *   reduction length); and
- *   det_gemm_db needs the float64 tile partials of up to max(2^23, 128 * n)
- *   values (m / 32 * n of them when that is less) plus 2 * n, and
- *   det_layernorm_bwd twice that for its two parameter gradients; the
- *   library keeps one such workspace per (device, stream), allocated on first
- *   need and grown (after synchronising that stream) when a larger one is
- *   needed, and never frees it. Calls on one stream share it in stream order,
- *   calls on different streams use different ones. Work is enqueued on `stream`
- *   (0 = the null stream) and the call returns once it is enqueued; the caller
- *   keeps the buffers alive until the stream has finished. Outputs must not
- *   alias inputs. Faults during execution surface at the caller's next
- *   synchronisation. The library is re-entrant; it never aborts, never prints
- *   and never changes the current device.
+ *   The caller owns every buffer. The library keeps no reference to any of
+ *   them. Some calls need device memory beyond their inputs and outputs (a
+ *   workspace); the library keeps one per (device, stream):
+ *     - fast tier, bf16/f16 forward with k >= 3072 and m >= 4096: a transposed
+ *       copy of the weight, 2 * k * n bytes (when it cannot be had, the call
+ *       runs without the copy: same bits);
+ *     - fast tier, bf16/f16 dW: possibly a transposed copy of its smaller
+ *       operand (2 * m * min(k, n) bytes) and, when the reduction is split
+ *       (above), S * k * n * 4 bytes of f32 partials;
+ *     - exact tier with at most 32 output rows (fwd and dx with m <= 32, dw
+ *       with k <= 32) when 8 * rows * cols * ceil(red / 32) bytes (rows x cols
+ *       the output, red the reduction length) is at most 64 MiB: every tile
+ *       partial, computed in parallel (otherwise, or when the memory cannot be
+ *       had, the blocked kernels run: same bits);
+ *     - det_gemm_db: the float64 tile partials of up to max(2^23, 128 * n)
+ *       values (m / 32 * n of them when that is less) plus 2 * n, and
+ *       det_layernorm_bwd twice that for its two parameter gradients;
+ *     - the correctly rounded tier: its statistics and slices (see "Tiers").
+ *   The workspace is allocated (hipMalloc) on a stream's first need and
+ *   replaced by a larger one when a call needs more; a replaced workspace is
+ *   kept, not freed (work already enqueued may still use it), until the
+ *   process ends. Those two moments allocate device memory, so they must not
+ *   happen under stream capture; no call synchronises the stream or the
+ *   device. Calls on one stream share its workspace in stream order; a call
+ *   holds a lock of its stream from its first workspace use to its last
+ *   launch, so calls from several threads on one stream do not interleave
+ *   their kernels. Work is enqueued on `stream` (0 = the null stream) and
+ *   the call returns once it is enqueued; the caller keeps the buffers alive
+ *   until the stream has finished. Outputs must not alias inputs. Faults
+ *   during execution surface at the caller's next synchronisation. The
+ *   library is re-entrant; it never aborts, never prints and never changes
+ *   the current device.
  *
  * Errors
  *   Every entry point returns DET_OK or a negative det_status_t; on error
@@ -264,22 +273,16 @@ det_status_t det_gemm_debug_force_db_chunk(int64_t tiles);
 det_status_t det_gemm_debug_force_cr_fallback(int on);
 
 /*
- * Measurement aid, not an operation of the method: runs one peak-rate
- * microkernel on `stream`, so that a tier's rate can be compared with what the
- * device sustains at its running clock as well as with the datasheet peak.
- *   kind 0: V_MFMA_F64_4X4X4_4B_F64 back to back (the exact tier's chains);
- *   kind 1: float64 vector fma (the exact tier's other float64 work);
- *   kind 2: V_MFMA_F32_32X32X16_BF16 back to back (the fast tier).
- * Two workgroups of 256 threads per compute unit, `iters` (>= 1) iterations
- * each, no memory traffic. out: device buffer of out_len doubles, at least
- * (compute units x 512); every thread writes one meaningless value (so the
- * arithmetic is not optimised away). *flops (host) receives the flops the
- * launch performs; time it with events on `stream`. DET_EINVAL for a bad
- * kind, iters < 1, null pointers or a short buffer; DET_EDEVICE off gfx950;
- * DET_ELAUNCH if the launch fails. The library allocates nothing.
+ * Test hook: the device check of every later call, from any thread, compares
+ * `arch` instead of the current device's gcnArchName (NULL or "" restores the
+ * device's own name). With any name other than gfx950 every entry point that
+ * checks the device returns DET_EDEVICE, with det_gemm_last_error() naming
+ * `arch`, and enqueues nothing -- so that the refusal a non-gfx950 device
+ * gets (sgemm-bi 0.1.2 PyPI page, introduction: unsupported platforms are
+ * refused with a clear message) can be exercised where the device is
+ * supported. The name is copied; DET_EINVAL if it is 64 characters or longer.
  */
-det_status_t det_gemm_measure_peak(int kind, int iters, double* out, int64_t out_len, double* flops,
-                                   hipStream_t stream);
+det_status_t det_gemm_debug_force_arch(const char* arch);
 
 #ifdef __cplusplus
 }

@@ -12,6 +12,7 @@ import pytest
 import deterministic_invariant_gemm_det_amd as dg
 
 HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "det_gemm.h")
+PEAK_HEADER = os.path.join(os.path.dirname(HEADER), "det_peak.h")
 
 
 def declared_functions():
@@ -116,12 +117,45 @@ def test_cr_tier_checks():
     assert dg.lib().det_gemm_debug_force_cr_fallback(0) == 0
 
 
-def test_measure_peak_argument_checks():
-    L = dg.lib()
+def test_peak_library_is_separate_and_checks_arguments():
+    """The peak-rate microkernels live in libdetpeak.so (include/det_peak.h), not in the GEMM library."""
+    from deterministic_invariant_gemm_det_amd import peak
+    L = peak.lib()
+    text = re.sub(r"/\*.*?\*/", "", open(PEAK_HEADER).read(), flags=re.S)
+    names = sorted(set(re.findall(r"\b(det_peak_\w+)\s*\(", text)))
+    assert names == ["det_peak_run"]
+    for name in names:
+        assert hasattr(L, name)
+    assert not hasattr(ctypes.CDLL(dg.LIB_PATH), "det_gemm_measure_peak")
     fl = ctypes.c_double(0.0)
-    p = 0x1000  # never dereferenced: rejected before any launch
-    assert L.det_gemm_measure_peak(3, 10, p, 1 << 20, ctypes.byref(fl), None) == -1
-    assert L.det_gemm_measure_peak(-1, 10, p, 1 << 20, ctypes.byref(fl), None) == -1
-    assert L.det_gemm_measure_peak(0, 0, p, 1 << 20, ctypes.byref(fl), None) == -1
-    assert L.det_gemm_measure_peak(0, 10, None, 1 << 20, ctypes.byref(fl), None) == -1
-    assert L.det_gemm_measure_peak(0, 10, p, 1 << 20, None, None) == -1
+    p = 0x1000  # never dereferenced: rejected before any device call
+    assert L.det_peak_run(3, 10, p, 1 << 20, ctypes.byref(fl), None) == -1
+    assert L.det_peak_run(-1, 10, p, 1 << 20, ctypes.byref(fl), None) == -1
+    assert L.det_peak_run(0, 0, p, 1 << 20, ctypes.byref(fl), None) == -1
+    assert L.det_peak_run(0, 10, None, 1 << 20, ctypes.byref(fl), None) == -1
+    assert L.det_peak_run(0, 10, p, 1 << 20, None, None) == -1
+
+
+def test_force_arch_validation():
+    assert dg.lib().det_gemm_debug_force_arch(b"x" * 64) == -1
+    dg.det_gemm_debug_force_arch("gfx942")
+    dg.det_gemm_debug_force_arch(None)
+    dg.det_gemm_debug_force_arch("")
+
+
+def test_out_tensor_checks_before_launch():
+    """A caller-supplied out of the wrong shape, dtype, layout or device is refused before any
+    launch (the kernels would write shape x dtype bytes into it)."""
+    import torch
+    cpu = torch.device("cpu")
+    good = torch.empty((4, 6), dtype=torch.bfloat16)
+    assert dg._out(good, (4, 6), torch.bfloat16, cpu) is good
+    assert dg._out(None, (4, 6), torch.float32, cpu).shape == (4, 6)
+    for bad in (torch.empty((4, 5), dtype=torch.bfloat16),            # too small
+                torch.empty((6, 4), dtype=torch.bfloat16),            # transposed shape
+                torch.empty((4, 6), dtype=torch.float16),             # narrower or other dtype
+                torch.empty((4, 6), dtype=torch.float32),             # wider dtype
+                torch.empty((6, 4), dtype=torch.bfloat16).t(),        # non-contiguous view
+                torch.empty((4, 6), dtype=torch.bfloat16, device="meta")):   # another device
+        with pytest.raises(ValueError):
+            dg._out(bad, (4, 6), torch.bfloat16, cpu)

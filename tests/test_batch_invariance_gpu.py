@@ -61,3 +61,33 @@ def test_m_sweep_long_reduction_fast(dt):
         x = to_dev(np.ascontiguousarray(X[:M]), dt)
         assert_bits_equal(to_host(dg.fwd(x, w, bb, "fast"), dt), full[:M], f"fwd+bias M={M}")
         assert_bits_equal(to_host(dg.fwd(x, w, None, "fast"), dt), full_nb[:M], f"fwd M={M}")
+
+
+# Row counts on both sides of every point where the fast tier's choice of kernel changes
+# with m for K = 768, N = 3072 (each choice gives the same bits; the rows must not change):
+#   fwd: 128 x 64 tiles when m is a multiple of 128 and 256 x 192 tiles would number fewer
+#        than 256 (m <= 3840), else 256 x 192 tiles -- m = 127/128/129, 3840/3841/3968;
+#   dX (768 columns): 64 x 192 tiles when m is a multiple of 64 and 128 x 192 tiles would
+#        number fewer than 256 (m <= 8064), else 128 x 192 -- m = 63/64/65, 8064/8065/8128;
+#   plus the few-rows limit of the exact tier (m = 32/33).
+SWITCH_MS = (32, 33, 63, 64, 65, 127, 128, 129, 3840, 3841, 3968, 4095, 4096, 8064, 8065, 8128)
+
+
+@pytest.mark.parametrize("tier", ["fast", "exact"])
+@pytest.mark.parametrize("dt", ["bf16", "f16"])
+def test_m_sweep_switch_points(dt, tier):
+    import deterministic_invariant_gemm_det_amd as dg
+    X = syn.normal(44, syn.TID_X, (8192, K), dt=dt)
+    W = syn.normal(44, syn.TID_W, (K, N), sigma=0.02, dt=dt)
+    b = syn.normal(44, syn.TID_B, (N,), sigma=0.1, dt=dt)
+    G = syn.normal(44, syn.TID_DY, (8192, N), dt=dt)
+    w, bb = to_dev(W, dt), to_dev(b, dt)
+    full_yb = to_host(dg.fwd(to_dev(X, dt), w, bb, tier), dt)
+    full_dx = to_host(dg.dx(to_dev(G, dt), w, tier), dt)
+    Ms = SWITCH_MS if tier == "fast" else (32, 33, 63, 64, 65)
+    for M in Ms:
+        print(f"switch sweep {dt} {tier} M={M}", flush=True)
+        x = to_dev(np.ascontiguousarray(X[:M]), dt)
+        g = to_dev(np.ascontiguousarray(G[:M]), dt)
+        assert_bits_equal(to_host(dg.fwd(x, w, bb, tier), dt), full_yb[:M], f"fwd+bias M={M}")
+        assert_bits_equal(to_host(dg.dx(g, w, tier), dt), full_dx[:M], f"dx M={M}")

@@ -25,6 +25,24 @@ MUTANTS = {
     "ties_down": ("else code = (lo % 2 == 0) ? lo : hi;", "else code = lo;"),
     "bias_dropped": ("v = v + bj;", "v = v + 0.0 * bj;"),
     "compensation_dropped_at_end": ("return s + c;\n}", "return s;\n}"),
+    # ways a four-deep matrix instruction could order its products: each
+    # group of four indices (from the tile start) summed pairwise, or as a
+    # chain from 0 and only then added to the running partial, or exactly
+    # (in long double) with the running partial and rounded once
+    "pairwise_in_groups_of_four": (
+        "p = std::fma(a[k], b[k], p);",
+        "if ((k - t0) % 4 == 0) { double v[4] = {0.0, 0.0, 0.0, 0.0}; "
+        "for (int64_t q = k; q < std::min(k + 4, t1); ++q) v[q - k] = a[q] * b[q]; "
+        "p = p + ((v[0] + v[1]) + (v[2] + v[3])); }"),
+    "group_chain_then_added": (
+        "p = std::fma(a[k], b[k], p);",
+        "if ((k - t0) % 4 == 0) { double g = 0.0; "
+        "for (int64_t q = k; q < std::min(k + 4, t1); ++q) g = std::fma(a[q], b[q], g); p = p + g; }"),
+    "group_fused_with_partial": (
+        "p = std::fma(a[k], b[k], p);",
+        "if ((k - t0) % 4 == 0) { long double g = p; "
+        "for (int64_t q = k; q < std::min(k + 4, t1); ++q) g += (long double)a[q] * (long double)b[q]; "
+        "p = (double)g; }"),
 }
 
 

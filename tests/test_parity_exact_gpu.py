@@ -65,7 +65,15 @@ def test_integer_inputs_exact(dt):
             assert_bits_equal(gpu_op(op, dt, A, B), want, f"int {op} {dt} {(m, k, n)}")
 
 
-def test_golden_witnesses():
+VARIANTS = [0, 1, 2, 3, 4, 5]
+VARIANT_IDS = ["mfma4", "mfma16", "valu", "mfma4db", "mfma4r48", "skinny"]
+
+
+@pytest.mark.parametrize("variant", VARIANTS, ids=VARIANT_IDS)
+def test_golden_witnesses(variant):
+    """Every hand-derived witness as a single output, through each exact kernel."""
+    import deterministic_invariant_gemm_det_amd as dg
+    dg.det_gemm_debug_force_exact_kernel(variant)
     for case in pins.golden()["cases"] + pins.golden()["downcast"]:
         dts = [case["dt"]] if "dt" in case else DTS
         for op in ("fwd", "dx", "dw"):
@@ -73,7 +81,73 @@ def test_golden_witnesses():
                 A, B, m, k, n = pins._witness_operands(op, dt, case["L"], pins._golden_terms(case))
                 want, r, _ = oracle.gemm(op, dt, A, B, m, k, n, want_r=True)
                 assert r[0, 0] == float.fromhex(case["r"])
-                assert_bits_equal(gpu_op(op, dt, A, B), want, f"{case['name']} {op} {dt}")
+                assert_bits_equal(gpu_op(op, dt, A, B), want, f"{case['name']} {op} {dt} variant {variant}")
+
+
+# Output positions of the embedded witnesses: first, middle and last rows and
+# columns of 64-, 48- and 16-wide blocks and of the lanes' 4 x 4 sub-blocks.
+EMB_ROWS = [0, 5, 14, 31, 33, 47, 48, 63, 64, 70, 81, 95]
+EMB_COLS = [0, 3, 16, 31, 32, 47, 50, 63, 64, 66, 75, 79]
+
+
+def _embedded(op, dt, seed):
+    """All witness cases of the golden file inside one 96 x 80 output over a reduction of 128, the
+    rest of the operands random: witness q sits at output (EMB_ROWS[q], EMB_COLS[q]), its row of
+    the first operand zero except its terms, its column of the second holding the term values."""
+    cases = pins.golden()["cases"]
+    assert len(cases) <= len(EMB_ROWS)
+    L, R, C = 128, 96, 80
+    m, k, n = {"fwd": (R, L, C), "dx": (R, C, L), "dw": (L, R, C)}[op]
+    sa, sb = operand_shapes(op, m, k, n)
+    A = syn.from_storage(syn.normal(seed, 0, sa, dt=dt), dt).copy()
+    B = syn.from_storage(syn.normal(seed, 1, sb, sigma=0.5, dt=dt), dt).copy()
+    for case, i, j in zip(cases, EMB_ROWS, EMB_COLS):
+        assert case["L"] <= L
+        if op == "dw":
+            A[:, i] = 0.0
+        else:
+            A[i, :] = 0.0
+        for idx, xv, wv in pins._golden_terms(case):
+            if op == "fwd":
+                A[i, idx], B[idx, j] = xv, wv
+            elif op == "dx":
+                A[i, idx], B[j, idx] = xv, wv
+            else:
+                A[idx, i], B[idx, j] = xv, wv
+    return cases, pins.stor(A, dt), pins.stor(B, dt), m, k, n
+
+
+@pytest.mark.parametrize("variant", VARIANTS, ids=VARIANT_IDS)
+@pytest.mark.parametrize("op", ["fwd", "dx", "dw"])
+def test_witnesses_inside_blocks(op, variant):
+    """The order witnesses (a sequential fma chain inside each four-index matrix-instruction group,
+    the running partial entering each group first, ties to even, tiles anchored at 0, Neumaier
+    across tiles) at many positions of full blocks of every exact kernel, random data around them:
+    the oracle's float64 value at each witness is the hand-derived one, and the whole output is
+    the oracle's bit for bit."""
+    import deterministic_invariant_gemm_det_amd as dg
+    dg.det_gemm_debug_force_exact_kernel(variant)
+    for dt in DTS:
+        print(f"embedded witnesses {op} {dt} variant {variant}", flush=True)
+        cases, A, B, m, k, n = _embedded(op, dt, 1200 + DTS.index(dt))
+        want, r, _ = oracle.gemm(op, dt, A, B, m, k, n, want_r=True)
+        for case, i, j in zip(cases, EMB_ROWS, EMB_COLS):
+            assert r[i, j] == float.fromhex(case["r"]) and not np.signbit(r[i, j]), (case["name"], op, dt)
+        assert_bits_equal(gpu_op(op, dt, A, B), want, f"embedded {op} {dt} variant {variant}")
+        if op == "dw" and dt != "f32" and variant in (0, 4):
+            # the f32-output dW (the default kernel in its two row-block forms)
+            want32 = oracle.round_to("f32", r)
+            got32 = _dw_f32(dt, A, B)
+            assert_bits_equal(got32, want32, f"embedded dw->f32 {dt} variant {variant}")
+
+
+def _dw_f32(dt, A, B):
+    import torch
+    import deterministic_invariant_gemm_det_amd as dg
+    from tests.gpu_util import to_dev
+    out = dg.dw(to_dev(A, dt), to_dev(B, dt), "exact", out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    return out.cpu().numpy()
 
 
 @pytest.mark.parametrize("dt,scale_x,scale_w", [
