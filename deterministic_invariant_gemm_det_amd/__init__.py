@@ -12,7 +12,8 @@ import ctypes
 import os
 
 __all__ = [
-    "det_gemm_fwd", "det_gemm_dx", "det_gemm_dw", "det_gemm_dw_out", "det_gemm_db", "det_gemm_strerror",
+    "det_gemm_fwd", "det_gemm_dx", "det_gemm_dw", "det_gemm_dw_out", "det_gemm_dw_noalloc", "det_gemm_db",
+    "det_gemm_strerror",
     "det_gemm_last_error", "det_gemm_version", "det_gemm_debug_force_family", "det_gemm_debug_force_exact_kernel",
     "det_gemm_debug_force_db_chunk", "det_gemm_debug_force_cr_fallback", "det_gemm_debug_force_arch",
     "DetGemmError", "LIB_PATH", "fwd", "dx", "dw", "db", "deterministic_linear", "Linear", "DTYPES", "TIERS",
@@ -56,10 +57,11 @@ def lib():
         L.det_gemm_dx.argtypes = [vp, vp, vp, i64, i64, i64, ci, ci, vp]
         L.det_gemm_dw.argtypes = [vp, vp, vp, i64, i64, i64, ci, ci, vp]
         L.det_gemm_dw_out.argtypes = [vp, ci, vp, vp, i64, i64, i64, ci, ci, vp]
+        L.det_gemm_dw_noalloc.argtypes = [vp, ci, vp, vp, i64, i64, i64, ci, ci, vp]
         L.det_gemm_db.argtypes = [vp, ci, vp, i64, i64, ci, ci, vp]
         L.det_layernorm_fwd.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, ctypes.c_double, ci, vp]
         L.det_layernorm_bwd.argtypes = [vp, vp, vp, ci, vp, vp, vp, vp, vp, i64, i64, ci, vp]
-        for f in (L.det_gemm_fwd, L.det_gemm_dx, L.det_gemm_dw, L.det_gemm_dw_out, L.det_gemm_db,
+        for f in (L.det_gemm_fwd, L.det_gemm_dx, L.det_gemm_dw, L.det_gemm_dw_out, L.det_gemm_dw_noalloc, L.det_gemm_db,
                   L.det_layernorm_fwd, L.det_layernorm_bwd):
             f.restype = ci
         L.det_gemm_strerror.argtypes = [ci]
@@ -122,6 +124,11 @@ def det_gemm_dw(dw_, x, dy, m, k, n, dtype, tier, stream=0):
 def det_gemm_dw_out(dw_, dw_dtype, x, dy, m, k, n, dtype, tier, stream=0):
     _check(lib().det_gemm_dw_out(_p(dw_), _code(DTYPES, dw_dtype, "dtype"), _p(x), _p(dy), m, k, n,
                                  _code(DTYPES, dtype, "dtype"), _code(TIERS, tier, "tier"), _p(stream)))
+
+
+def det_gemm_dw_noalloc(dw_, dw_dtype, x, dy, m, k, n, dtype, tier, stream=0):
+    _check(lib().det_gemm_dw_noalloc(_p(dw_), _code(DTYPES, dw_dtype, "dtype"), _p(x), _p(dy), m, k, n,
+                                     _code(DTYPES, dtype, "dtype"), _code(TIERS, tier, "tier"), _p(stream)))
 
 
 def det_gemm_db(db_, db_dtype, dy, m, n, dtype, tier, stream=0):

@@ -9,6 +9,7 @@
 #include <cstring>
 #include <map>
 #include <mutex>
+#include <optional>
 #include <utility>
 #include <vector>
 
@@ -128,7 +129,10 @@ det_status_t run(detgemm::Op op, void* out, const void* A, const void* B, const 
   a.a_bytes = a_elems * esz;
   a.b_bytes = b_elems * esz;
   const detgemm::Dt d = static_cast<detgemm::Dt>(dt);
-  detgemm::StreamCallLock call_lock(stream);
+  // the stream lock guards the stream workspace; a call on a fixed buffer
+  // (the entry point that allocates nothing) takes neither
+  std::optional<detgemm::StreamCallLock> call_lock;
+  if (!detgemm::fixed_workspace_active()) call_lock.emplace(stream);
   hipError_t err;
   if (tier == DET_TIER_EXACT) {
     const int v = g_force_exact.load(std::memory_order_relaxed);
@@ -138,13 +142,49 @@ det_status_t run(detgemm::Op op, void* out, const void* A, const void* B, const 
   } else {
     err = detgemm::launch_fast(op, d, a, g_force_family.load(std::memory_order_relaxed), stream);   // -1: automatic
   }
-  if (err != hipSuccess) return fail(DET_ELAUNCH, "det_gemm: kernel launch failed: %s", hipGetErrorString(err));
+  if (err != hipSuccess) {
+    size_t wanted = 0, cap = 0;
+    if (err == hipErrorOutOfMemory && detgemm::fixed_workspace_overflow(&wanted, &cap)) {
+      (void)hipGetLastError();
+      std::snprintf(g_last_error, sizeof(g_last_error),
+                    "det_gemm: this call needs %zu bytes of scratch; the fixed scratch holds %zu", wanted, cap);
+      return DET_EINVAL;
+    }
+    return fail(DET_ELAUNCH, "det_gemm: kernel launch failed: %s", hipGetErrorString(err));
+  }
   return DET_OK;
 }
 
 }  // namespace
 
 namespace detgemm {
+
+// det_gemm_dw_out on a fixed device buffer instead of the stream workspace:
+// the arguments and the device are checked first, then `scratch` gives the
+// current device's buffer (its address and size) or an error.
+det_status_t dw_out_on_scratch(hipError_t (*scratch)(void** ptr, size_t* cap), void* dw, det_dtype_t dw_dt,
+                               const void* x, const void* dy, int64_t m, int64_t k, int64_t n, det_dtype_t dt,
+                               det_tier_t tier, hipStream_t stream) {
+  g_last_error[0] = '\0';
+  if (dw_dt != dt && dw_dt != DET_F32)
+    return fail(DET_EDTYPE, "det_gemm_dw_noalloc: the output dtype must be the input dtype or DET_F32%s");
+  if (dt != DET_F32 && dt != DET_BF16 && dt != DET_F16) return fail(DET_EDTYPE, "det_gemm: unknown dtype%s");
+  if (tier != DET_TIER_EXACT && tier != DET_TIER_FAST && tier != DET_TIER_CR)
+    return fail(DET_ETIER, "det_gemm: unknown tier%s");
+  int cus = 0;
+  const det_status_t dev = check_device(&cus);
+  if (dev != DET_OK) return dev;
+  void* ptr = nullptr;
+  size_t cap = 0;
+  const hipError_t e = scratch(&ptr, &cap);
+  if (e != hipSuccess) {
+    (void)hipGetLastError();
+    return fail(DET_ELAUNCH, "det_gemm_dw_noalloc: the scratch buffer's address is not available: %s",
+                hipGetErrorString(e));
+  }
+  FixedWorkspaceScope scope(ptr, cap);
+  return run(OP_DW, dw, x, dy, nullptr, m, k, n, dt, tier, stream, dw_dt == DET_F32);
+}
 
 namespace {
 
@@ -232,17 +272,23 @@ hipError_t stream_workspace(hipStream_t stream, size_t bytes, void** ptr) {
   return hipSuccess;
 }
 
-// Runs `fn` with `ptr` (cap bytes, device memory) in place of the stream
-// workspace for every request it makes on this thread; *wanted receives the
-// largest request (0 if none).
-hipError_t with_fixed_workspace(void* ptr, size_t cap, size_t* wanted, hipError_t (*fn)(void*), void* ctx) {
-  FixedWorkspace fw{ptr, cap, 0};
-  FixedWorkspace* prev = t_fixed;
-  t_fixed = &fw;
-  const hipError_t e = fn(ctx);
-  t_fixed = prev;
-  *wanted = fw.wanted;
-  return e;
+FixedWorkspaceScope::FixedWorkspaceScope(void* ptr, size_t cap) : prev_(t_fixed) {
+  static_assert(sizeof(FixedWorkspace) <= sizeof(storage_), "scope storage");
+  FixedWorkspace* fw = reinterpret_cast<FixedWorkspace*>(storage_);
+  fw->ptr = ptr;
+  fw->cap = cap;
+  fw->wanted = 0;
+  t_fixed = fw;
+}
+FixedWorkspaceScope::~FixedWorkspaceScope() { t_fixed = static_cast<FixedWorkspace*>(prev_); }
+
+bool fixed_workspace_active() { return t_fixed != nullptr; }
+
+bool fixed_workspace_overflow(size_t* wanted, size_t* cap) {
+  if (!t_fixed || t_fixed->wanted <= t_fixed->cap) return false;
+  *wanted = t_fixed->wanted;
+  *cap = t_fixed->cap;
+  return true;
 }
 
 }  // namespace detgemm

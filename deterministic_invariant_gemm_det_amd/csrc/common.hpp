@@ -132,6 +132,23 @@ class StreamCallLock {
  private:
   std::mutex* mu_;
 };
-hipError_t with_fixed_workspace(void* ptr, size_t cap, size_t* wanted, hipError_t (*fn)(void*), void* ctx);
+// While one lives on a thread, every workspace request of that thread's calls
+// gets `ptr` (cap bytes of device memory) instead of the stream workspace, or
+// hipErrorOutOfMemory when it asks for more; nothing is allocated.
+class FixedWorkspaceScope {
+ public:
+  FixedWorkspaceScope(void* ptr, size_t cap);
+  ~FixedWorkspaceScope();
+  FixedWorkspaceScope(const FixedWorkspaceScope&) = delete;
+  FixedWorkspaceScope& operator=(const FixedWorkspaceScope&) = delete;
+
+ private:
+  void* prev_;
+  alignas(8) unsigned char storage_[32];
+};
+bool fixed_workspace_active();
+// true when a request of the current scope exceeded its buffer (the largest
+// request and the buffer's size are returned)
+bool fixed_workspace_overflow(size_t* wanted, size_t* cap);
 
 }  // namespace detgemm

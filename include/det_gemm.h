@@ -166,6 +166,31 @@ det_status_t det_gemm_dw_out(void* dw, det_dtype_t dw_dt, const void* x, const v
                              int64_t m, int64_t k, int64_t n,
                              det_dtype_t dt, det_tier_t tier, hipStream_t stream);
 
+/* Size of the fixed scratch array behind det_gemm_dw_noalloc (bytes). */
+#define DET_GEMM_NOALLOC_SCRATCH_BYTES (64u << 20)
+
+/*
+ * det_gemm_dw_out for callers that cannot allocate device memory (code under
+ * stream capture, tight serving loops, harnesses that forbid hipMalloc): the
+ * same computation and bits as det_gemm_dw_out with the same arguments, but
+ * every workspace the call needs (see "Ownership and execution") is taken from
+ * one array of DET_GEMM_NOALLOC_SCRATCH_BYTES that the library holds on each
+ * device (a static device allocation, kept until the process ends), and the
+ * call allocates nothing. A call whose workspace would be larger returns
+ * DET_EINVAL, enqueues nothing, and det_gemm_last_error() states both sizes
+ * (the GPT-2-sized dW of 8192 tokens into 768 x 3072, 3072 x 768 or 768 x 2304
+ * outputs fits in both tiers; a split fast-tier dW needs S * k * n * 4 bytes
+ * plus 2 * m * min(k, n)). The array keeps whatever the last call left in it;
+ * every kernel that reads it writes it first in the same call. All calls on one
+ * device share the array, so calls that may run at the same time on one device
+ * (on different streams, or from different threads without ordering) race on
+ * it: order them. The call takes no stream lock. Errors as for det_gemm_dw_out;
+ * DET_ELAUNCH also when the array's device address cannot be looked up.
+ */
+det_status_t det_gemm_dw_noalloc(void* dw, det_dtype_t dw_dt, const void* x, const void* dy,
+                                 int64_t m, int64_t k, int64_t n,
+                                 det_dtype_t dt, det_tier_t tier, hipStream_t stream);
+
 /*
  * Bias gradient: db[n] = sum over i < m of dy[i, n] (sgemm-bi 0.1.2 PyPI page,
  * note after "Determinism contracts": a column sum of dY, which that engine
