@@ -14,15 +14,19 @@
 // slots: while stage s is multiplied out of one slot, stage s + 1 is written
 // into the other.
 //
-// LDS layout of an operand slot (the same for both source orientations): row
-// x holds the stage's 64 reduction indices of output row (A) or column (B) x,
-// as eight 16-byte pieces. Rows are paired: pair y = x / 2 occupies 256 bytes
-// (all 64 banks once), and piece p of row x sits in 16-byte slot
-// (8 (x mod 2) + p) XOR h(y) of the pair, with
-// h(y) = ((y XOR y / 8) mod 8) + 8 ((y / 4) mod 2). A fragment read (lanes
-// 0..31 rows xb..xb+31 at one piece, lanes 32..63 the next piece) then touches
-// 16 distinct slots in every group of 16 lanes, and so does the transposing
-// write below; both are conflict-free.
+// LDS layout of an operand slot: row x holds the stage's 64 reduction indices
+// of output row (A) or column (B) x, as eight 16-byte pieces, swizzled so that
+// fragment reads (lanes 0..31 rows xb..xb+31 at one piece, lanes 32..63 the
+// next piece) spread over the banks. Where one operand is register-transposed
+// (the forward weight, dW), rows are paired: pair y = x / 2 occupies 256
+// bytes and piece p of row x sits in 16-byte slot (8 (x mod 2) + p) XOR h(y),
+// h(y) = ((y XOR y / 8) mod 8) + 8 ((y / 4) mod 2), which also keeps the
+// transposing writes apart. Where both operands arrive by direct loads, row x
+// occupies 128 bytes with piece p in slot p XOR s(x), s(x) = ((x / 2) mod 8)
+// XOR ((x / 8) mod 2): measured on gfx950 with the fragment-read pattern,
+// 240 B/clk/CU against 180 for the paired layout, and s has period 32, so a
+// lane's fragments of one step are one address plus constants. The slots of
+// all stages hold their A regions first, then their B regions.
 //
 // Filling a slot:
 //   * reduction-contiguous source (A of fwd and dX, B of dX): buffer loads that
@@ -90,6 +94,19 @@ template <> struct Lay<64> {
   }
 };
 
+// BK = 64, rows of 128 bytes (used where both operands are staged by direct
+// loads): piece p of row x at slot p XOR s(x), s(x) = ((x / 2) mod 8) XOR
+// ((x / 8) mod 2). s has period 32 in x, so the fragments of rows x and x + 32
+// sit exactly 4096 bytes apart.
+struct Lay64r {
+  __host__ __device__ static constexpr int sw(int x) { return ((x >> 1) & 7) ^ ((x >> 3) & 1); }
+  __host__ __device__ static constexpr uint32_t off(int x, int p) { return static_cast<uint32_t>(x * 128 + 16 * (p ^ sw(x))); }
+  __device__ static inline void direct(int gi, int lane, int& x, int& p) {
+    x = 8 * gi + (lane >> 3);
+    p = (lane & 7) ^ sw(x);
+  }
+};
+
 // BK = 128: row x occupies 256 bytes and piece p sits in slot p XOR f(x),
 // f(x) = (x XOR x / 8) mod 16.
 template <> struct Lay<128> {
@@ -110,7 +127,7 @@ __device__ inline v4u buffer_rsrc(const void* src, int64_t bytes) {
 
 // Reduction-contiguous operand: element (x, l) at src[x * ld + l]; X rows per
 // tile, WAVES waves per workgroup.
-template <int X, int WAVES, int BK>
+template <int X, int WAVES, int BK, typename LAY = Lay<BK>>
 struct RcOperand {
   static constexpr int NQ = X * BK * 2 / 1024 / WAVES;   // 1 KB wave instructions per wave per stage
   static_assert(NQ * 1024 * WAVES == X * BK * 2, "tile extent must fill whole wave instructions");
@@ -127,7 +144,7 @@ struct RcOperand {
 #pragma unroll
     for (int q = 0; q < NQ; ++q) {
       int x, p;
-      Lay<BK>::direct(wave * NQ + q, lane, x, p);
+      LAY::direct(wave * NQ + q, lane, x, p);
       voff[q] = static_cast<uint32_t>((x * ld + 8 * p) * 2);
     }
   }
@@ -309,34 +326,61 @@ __global__ void __launch_bounds__(64 * WR * WC, WPE) fast16w_kernel(GemmArgs arg
   const int wm = (wave / WC) * WM;
   const int wn = (wave % WC) * WN;
 
-  typename OperandOf<BM, WAVES, BK, A_RC>::type oa;
-  typename OperandOf<BN, WAVES, BK, B_RC>::type ob;
+  // both operands staged by direct loads in stages of 64: the periodic layout,
+  // whose fragment offsets are a per-lane value per step plus constants
+  constexpr bool RR = A_RC && B_RC && BK == 64;
+  std::conditional_t<RR, RcOperand<BM, WAVES, BK, Lay64r>, typename OperandOf<BM, WAVES, BK, A_RC>::type> oa;
+  std::conditional_t<RR, RcOperand<BN, WAVES, BK, Lay64r>, typename OperandOf<BN, WAVES, BK, B_RC>::type> ob;
   oa.init(args.A, args.lda, args.a_bytes);
   ob.init(args.B, args.ldb, args.b_bytes);
   const bool has_bias = args.bias != nullptr;
 
+  // LDS: the A regions of the NS stage slots, then their B regions (a
+  // slot's base is then a constant offset of each fragment read)
+  auto region_a = [&](int sl) { return lds + sl * A_BYTES; };
+  auto region_b = [&](int sl) { return lds + NS * A_BYTES + sl * B_BYTES; };
   // Everything stage st needs from global memory: the register-staged
   // operand first, then the direct-to-LDS ones (so that waiting for the
   // latter covers the former).
   auto request = [&](int st) {
     if constexpr (!A_RC) { if (oa.active()) oa.load(row0, s0 + st); }
     if constexpr (!B_RC) { if (ob.active()) ob.load(col0, s0 + st); }
-    char* sl = lds + (st % NS) * SLOT;
-    if constexpr (A_RC) oa.issue(sl, row0, s0 + st);
-    if constexpr (B_RC) ob.issue(sl + A_BYTES, col0, s0 + st);
+    if constexpr (A_RC) oa.issue(region_a(st % NS), row0, s0 + st);
+    if constexpr (B_RC) ob.issue(region_b(st % NS), col0, s0 + st);
   };
   auto write_km = [&](int st) {
-    char* sl = lds + (st % NS) * SLOT;
-    if constexpr (!A_RC) { if (oa.active()) oa.store(sl); }
-    if constexpr (!B_RC) { if (ob.active()) ob.store(sl + A_BYTES); }
+    if constexpr (!A_RC) { if (oa.active()) oa.store(region_a(st % NS)); }
+    if constexpr (!B_RC) { if (ob.active()) ob.store(region_b(st % NS)); }
   };
-  auto read_step = [&](v4u (&af)[NI], v4u (&bf)[NJ], int st, int ks) {
-    const char* As = lds + (st % NS) * SLOT;
-    const char* Bs = As + A_BYTES;
+  // per-lane fragment offsets of each step of a stage (periodic layout: the
+  // fragments 32 rows further sit 4096 bytes further)
+  constexpr bool PRE = RR;
+  uint32_t fa[PRE ? KS : 1], fb[PRE ? KS : 1];
+  if constexpr (PRE) {
 #pragma unroll
-    for (int i = 0; i < NI; ++i) af[i] = frag<BK>(As, wm + 32 * i, ks);
+    for (int ks = 0; ks < KS; ++ks) {
+      fa[ks] = Lay64r::off(wm + (lane & 31), 2 * ks + (lane >> 5));
+      fb[ks] = Lay64r::off(wn + (lane & 31), 2 * ks + (lane >> 5));
+    }
+  }
+  // fragments of step ks of the stage in slot sl
+  auto read_step = [&](v4u (&af)[NI], v4u (&bf)[NJ], int sl, int ks) {
+    const char* As = lds + sl * A_BYTES;
+    const char* Bs = lds + NS * A_BYTES + sl * B_BYTES;
+    if constexpr (PRE) {
+      // one address per operand and step; the fragments 32 rows apart at immediate offsets
+      const char* pa = As + fa[ks];
+      const char* pb = Bs + fb[ks];
 #pragma unroll
-    for (int j = 0; j < NJ; ++j) bf[j] = frag<BK>(Bs, wn + 32 * j, ks);
+      for (int i = 0; i < NI; ++i) af[i] = *reinterpret_cast<const v4u*>(pa + 4096 * i);
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) bf[j] = *reinterpret_cast<const v4u*>(pb + 4096 * j);
+    } else {
+#pragma unroll
+      for (int i = 0; i < NI; ++i) af[i] = frag<BK>(As, wm + 32 * i, ks);
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) bf[j] = frag<BK>(Bs, wn + 32 * j, ks);
+    }
   };
 
   // Prologue: stages 0 .. NS - 1 requested and stage 0 published; the last
@@ -389,7 +433,7 @@ __global__ void __launch_bounds__(64 * WR * WC, WPE) fast16w_kernel(GemmArgs arg
   // The tile's bias slice goes into the LDS slot that stage nst - 2 used
   // (free from the start of the last stage on; an unused slot when nst < NS)
   // by one direct load at the start of the last stage.
-  char* const bias_lds = lds + ((nst + NS - 2) % NS) * SLOT;
+  char* const bias_lds = region_a((nst + NS - 2) % NS);
   static_assert(BN * 2 <= 1024, "bias slice must fit one wave instruction");
   auto load_bias = [&]() {
     if (wave == 0 && lane < BN * 2 / 16) {
@@ -404,6 +448,7 @@ __global__ void __launch_bounds__(64 * WR * WC, WPE) fast16w_kernel(GemmArgs arg
   };
   auto stage = [&](int g, auto last_tag) {
     constexpr bool LAST = decltype(last_tag)::value;
+    const int SL = g % NS, SLN = (g + 1) % NS;
     if constexpr (LAST) { if (has_bias) load_bias(); }
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
@@ -436,14 +481,12 @@ __global__ void __launch_bounds__(64 * WR * WC, WPE) fast16w_kernel(GemmArgs arg
         }
       }
       // fragments of step 4 g + ks + 2
-      if (ks < KS - 2) read_step(af[(ks + 2) & 3], bf[(ks + 2) & 3], g, ks + 2);
-      else if (!LAST) read_step(af[(ks + 2) & 3], bf[(ks + 2) & 3], g + 1, ks + 2 - KS);
-      __builtin_amdgcn_sched_barrier(0);
+      if (ks < KS - 2) read_step(af[(ks + 2) & 3], bf[(ks + 2) & 3], SL, ks + 2);
+      else if (!LAST) read_step(af[(ks + 2) & 3], bf[(ks + 2) & 3], SLN, ks + 2 - KS);
 #pragma unroll
       for (int i = 0; i < NI; ++i)
 #pragma unroll
         for (int j = 0; j < NJ; ++j) acc[i][j] = mfma_step<E>(bf[ks & 3][j], af[ks & 3][i], acc[i][j]);
-      __builtin_amdgcn_sched_barrier(0);
     }
   };
   for (int g = 0; g + 1 < nst; ++g) stage(g, std::false_type{});
