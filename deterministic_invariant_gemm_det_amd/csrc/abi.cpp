@@ -423,8 +423,8 @@ const char* det_gemm_last_error(void) { return g_last_error; }
 int det_gemm_version(void) { return 200; }
 
 det_status_t det_gemm_debug_force_family(int family) {
-  if (family < -1 || (family > 1 && family < 10) || family > 15)
-    return fail(DET_EINVAL, "det_gemm: family must be -1, 0, 1 or 10 .. 15%s");
+  if (family < -1 || (family > 1 && family < 10) || family > 16)
+    return fail(DET_EINVAL, "det_gemm: family must be -1, 0, 1 or 10 .. 16%s");
   g_force_family.store(family, std::memory_order_relaxed);
   return DET_OK;
 }

@@ -98,6 +98,10 @@ bool fast16_w_ok(const GemmArgs& a);
 int fast16_w_shape(int64_t cols, int64_t red);
 hipError_t launch_fast16_w(Op op, Dt dt, const GemmArgs& a, int shape, hipStream_t stream);
 int fast_auto_family(Op op, Dt dt, int64_t cols, int64_t red);
+// Forward of 16-bit inputs with at most 32 rows: one 32-column block per
+// workgroup streaming the weight (skinny.hip); same bits as the tiled kernels.
+bool fast16_skinny_ok(const GemmArgs& a);
+hipError_t launch_fast16_skinny(Dt dt, const GemmArgs& a, hipStream_t stream);
 
 // Split of the fast tier's dW reduction (16-bit inputs), from the shape only:
 // returns the chunk count S >= 1 and sets *chunk_stages.

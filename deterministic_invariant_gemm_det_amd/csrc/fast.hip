@@ -404,6 +404,14 @@ hipError_t launch_fast(Op op, Dt dt, const GemmArgs& a, int family, hipStream_t 
     }
     if (family == 0) family = 15;   // no split, no copy: four fat waves
   }
+  // Forward of 16-bit inputs with at most 32 rows (decode-sized batches): the
+  // work is a stream of the weight, which the tiled kernels read through a
+  // handful of tiles; the few-rows kernel gives every 32 output columns a
+  // workgroup of its own. Same instruction sequence per output, so the same
+  // bits. Family 16 forces it (where it applies).
+  if (op == OP_FWD && dt != DT_F32 && (automatic || family == 16) && fast16_skinny_ok(a))
+    return launch_fast16_skinny(dt, a, stream);
+  if (family == 16) family = 0;
   // Forward of 16-bit inputs with many rows and a long reduction: the weight
   // copied transposed first ([n][k], contiguous along the reduction), so that
   // the kernel stages both operands straight into LDS, as for dX. Same values

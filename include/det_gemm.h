@@ -263,7 +263,9 @@ int det_gemm_version(void);
  * shape s of the large family's kernel where it applies: 10 = 256 x 192,
  * 11 = 128 x 192, 12 = 128 x 192 in two four-wave workgroups per compute
  * unit, 13 = 64 x 192 likewise, 14 = 128 x 192 in stages of 128, 15 =
- * 256 x 192 in four waves of 128 x 96, one per SIMD). All
+ * 256 x 192 in four waves of 128 x 96, one per SIMD; 16 = the forward for
+ * at most 32 rows of 16-bit inputs, one 32-column block per workgroup,
+ * where it applies, else as 0). All
  * families produce identical bits, so this changes speed only. Returns
  * DET_EINVAL for other values.
  */

@@ -38,10 +38,10 @@ def test_static_strings_and_version():
 
 
 def test_force_family_validation():
-    for bad in (-2, 2, 9, 16):
+    for bad in (-2, 2, 9, 17):
         with pytest.raises(dg.DetGemmError):
             dg.det_gemm_debug_force_family(bad)
-    for good in (-1, 0, 1, 10, 15):
+    for good in (-1, 0, 1, 10, 15, 16):
         dg.det_gemm_debug_force_family(good)
     dg.det_gemm_debug_force_family(-1)
 

@@ -77,3 +77,30 @@ def test_dw_split(dt):
             dg.det_gemm_debug_force_family(fam)
             assert_bits_equal(gpu_op("dw", dt, A, B, tier="fast"), y, f"family {fam}")
         dg.det_gemm_debug_force_family(-1)
+
+
+# The forward for at most 32 rows (one 32-column block per workgroup, the weight streamed
+# through LDS): bit-identical to the tiled kernels; k a multiple of 8 (other k take the tiled
+# kernels); ragged n, k past the last 128-index chunk, with and without the bias.
+SKINNY = [(1, 768, 3072), (3, 768, 3072), (17, 3072, 768), (32, 72, 1000), (31, 8, 5), (2, 200, 40), (9, 1032, 136),
+          (1, 11008, 64)]
+
+
+@pytest.mark.parametrize("dt", ["bf16", "f16"])
+def test_skinny_forward_matches_tiled(dt):
+    import deterministic_invariant_gemm_det_amd as dg
+    for si, (m, k, n) in enumerate(SKINNY):
+        print(f"skinny fwd {dt} {(m, k, n)}", flush=True)
+        X = syn.normal(1500 + si, 0, (m, k), dt=dt)
+        W = syn.normal(1500 + si, 1, (k, n), sigma=0.1, dt=dt)
+        b = syn.normal(1500 + si, 2, (n,), sigma=0.1, dt=dt)
+        _, r, S = oracle.fwd(dt, X, W, b, want_r=True, want_S=True)
+        for bias in (b, None):
+            dg.det_gemm_debug_force_family(16)
+            y16 = gpu_op("fwd", dt, X, W, bias, tier="fast")
+            dg.det_gemm_debug_force_family(0)
+            y0 = gpu_op("fwd", dt, X, W, bias, tier="fast")
+            dg.det_gemm_debug_force_family(-1)
+            assert_bits_equal(y16, y0, f"skinny vs tiled {dt} {(m, k, n)} bias={bias is not None}")
+            assert_bits_equal(gpu_op("fwd", dt, X, W, bias, tier="fast"), y0, "automatic")
+        assert_within_tolerance(gpu_op("fwd", dt, X, W, b, tier="fast"), r, S, dt, f"skinny {dt} {(m, k, n)}")
