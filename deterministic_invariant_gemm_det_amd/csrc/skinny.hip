@@ -9,8 +9,8 @@
 //
 // With few rows the work is a stream of the weight: all m rows fit one 32-row
 // matrix block, so each 32 columns of output are one chain of dependent
-// matrix instructions, and the time goes to reading w. One workgroup of five
-// waves owns 32 columns. Waves 1 .. 4 move the weight's 128-row chunks
+// matrix instructions, and the time goes to reading w. One workgroup of nine
+// waves owns 32 columns. Waves 1 .. 8 move the weight's 128-row chunks
 // ([k][32], 64-byte rows) and the x rows below m of the matching 32 x 128
 // piece through registers (plain 16-byte loads, D chunks in flight per wave)
 // into a ring of R LDS slots; wave 0 runs the chain one chunk behind its
@@ -40,7 +40,8 @@ constexpr int X_BYTES = 32 * CK * 2;    // x chunk: 32 rows x 128 indices, 256-b
 constexpr int SLOT = W_BYTES + X_BYTES;
 constexpr int R = 4;                    // LDS ring slots
 constexpr int D = 6;                    // chunks each loader wave holds in flight in registers
-constexpr int LOADERS = 4;              // waves 1 .. 4 move the operands; wave 0 runs the chain
+constexpr int LOADERS = 8;              // waves 1 .. LOADERS move the operands; wave 0 runs the chain
+constexpr int BPW = 8 / LOADERS;        // 1 KB blocks of each chunk (weight, and x) per loader wave
 constexpr int THREADS = 64 * (LOADERS + 1);
 constexpr uint32_t OUTSIDE = 0x80000000u;   // a byte offset past every buffer this path takes
 
@@ -92,6 +93,17 @@ __device__ inline void run_chain(v16f& acc, const v4u (&fa)[8], const v4u (&fb)[
   for (int s = 0; s < N; ++s) acc = mfma_step<E>(fa[s], fb[s], acc);
 }
 
+// The next chunk's 24 LDS reads are placed 3 after each matrix instruction of
+// the current chain, so that they issue while each instruction waits for the
+// previous one's result.
+__device__ inline void interleave_reads() {
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one matrix instruction
+    __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);   // three LDS reads
+  }
+}
+
 // wave 0's side of barrier c: its reads of chunk c - 1 are complete (so the
 // loaders may refill that slot after the barrier), and chunk c is in LDS after it
 __device__ inline void sync_chunk() {
@@ -113,18 +125,18 @@ __global__ void __launch_bounds__(THREADS, 1) skinny_fwd_kernel(GemmArgs a) {
   const int nch = (nsteps + 7) / 8;
 
   if (wave != 0) {
-    // loader wave w, blocks gi = 2 (w - 1) + q, q = 0, 1 of each chunk:
+    // loader wave w, blocks gi = BPW (w - 1) + q, q < BPW of each chunk:
     // weight rows 16 gi + lane / 4, columns 8 (lane mod 4) .. + 7, to LDS byte
     // 1024 gi + 16 lane; x row 4 gi + lane / 16, piece (lane mod 16) XOR f(row),
     // to x byte 1024 gi + 16 lane. x rows >= m are never loaded: their LDS
     // bytes are cleared once and stay zero.
     const auto wr = __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(a.B), 0, static_cast<int>(a.b_bytes), 0x00020000);
     const auto xr = __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(a.A), 0, static_cast<int>(a.a_bytes), 0x00020000);
-    uint32_t w_off[2], x_off[2], x_k[2];
-    bool x_live[2];
-    int lds_at[2];
-    for (int q = 0; q < 2; ++q) {
-      const int gi = 2 * (wave - 1) + q;
+    uint32_t w_off[BPW], x_off[BPW], x_k[BPW];
+    bool x_live[BPW];
+    int lds_at[BPW];
+    for (int q = 0; q < BPW; ++q) {
+      const int gi = BPW * (wave - 1) + q;
       w_off[q] = static_cast<uint32_t>(((16 * gi + (lane >> 2)) * N + col0 + 8 * (lane & 3)) * 2);
       const int xrow = 4 * gi + (lane >> 4);
       const int p = (lane & 15) ^ xf(xrow);
@@ -134,16 +146,16 @@ __global__ void __launch_bounds__(THREADS, 1) skinny_fwd_kernel(GemmArgs a) {
       lds_at[q] = 1024 * gi + 16 * lane;
     }
     for (int sl = 0; sl < R; ++sl)
-      for (int q = 0; q < 2; ++q)
+      for (int q = 0; q < BPW; ++q)
         if (!x_live[q]) *reinterpret_cast<v4u*>(lds + sl * SLOT + W_BYTES + lds_at[q]) = v4u{0, 0, 0, 0};
-    v4u wv[D][2], xv[D][2];
+    v4u wv[D][BPW], xv[D][BPW];
     // loads are unconditional (dead x lanes and chunks past the end read from
     // outside the buffers), so that the counts the compiler waits on stay exact
-    auto load = [&](int c, v4u (&w)[2], v4u (&x)[2]) {
+    auto load = [&](int c, v4u (&w)[BPW], v4u (&x)[BPW]) {
       const uint32_t k0 = static_cast<uint32_t>(c * CK);
       const bool in = c < nch;
 #pragma unroll
-      for (int q = 0; q < 2; ++q) {
+      for (int q = 0; q < BPW; ++q) {
         w[q] = __builtin_bit_cast(v4u, __builtin_amdgcn_raw_buffer_load_b128(
             wr, in ? w_off[q] + k0 * static_cast<uint32_t>(N) * 2u : OUTSIDE, 0, 0));
         x[q] = __builtin_bit_cast(v4u, __builtin_amdgcn_raw_buffer_load_b128(
@@ -152,10 +164,10 @@ __global__ void __launch_bounds__(THREADS, 1) skinny_fwd_kernel(GemmArgs a) {
     };
     // chunk c to its slot (free: wave 0 finished reading chunk c - R before
     // barrier c - R + 1), the registers refilled with chunk c + D, then barrier c
-    auto put = [&](int c, v4u (&w)[2], v4u (&x)[2]) {
+    auto put = [&](int c, v4u (&w)[BPW], v4u (&x)[BPW]) {
       char* slot = lds + (c % R) * SLOT;
 #pragma unroll
-      for (int q = 0; q < 2; ++q) {
+      for (int q = 0; q < BPW; ++q) {
         *reinterpret_cast<v4u*>(slot + lds_at[q]) = w[q];
         if (x_live[q]) *reinterpret_cast<v4u*>(slot + W_BYTES + lds_at[q]) = x[q];
       }
@@ -196,14 +208,17 @@ __global__ void __launch_bounds__(THREADS, 1) skinny_fwd_kernel(GemmArgs a) {
     sync_chunk();
     read_chunk(a1, b1, slot(c), xrow, xpiece, wfrag);
     run_chain<E, 8>(acc, a0, b0);
+    interleave_reads();
     sync_chunk();
     read_chunk(a0, b0, slot(c + 1), xrow, xpiece, wfrag);
     run_chain<E, 8>(acc, a1, b1);
+    interleave_reads();
   }
   if (c == nch - 1) {
     sync_chunk();
     read_chunk(a1, b1, slot(c), xrow, xpiece, wfrag);
     run_chain<E, 8>(acc, a0, b0);
+    interleave_reads();
     __builtin_amdgcn_s_waitcnt(WAIT_LGKM0);
     if (last_full) run_chain<E, 8>(acc, a1, b1);
     else run_chain<E, 4>(acc, a1, b1);
