@@ -9,6 +9,7 @@
 #include <cstring>
 #include <map>
 #include <mutex>
+#include <new>
 #include <optional>
 #include <utility>
 #include <vector>
@@ -197,12 +198,18 @@ struct StreamSlot {
 };
 
 std::mutex g_slots_mu;
-std::map<std::pair<int, hipStream_t>, StreamSlot*> g_slots;
+// The slots and their workspaces are kept until the process ends: the map
+// itself is never destroyed, so that no call racing with static destruction
+// at exit finds it gone, and its buffers stay reachable.
+std::map<std::pair<int, hipStream_t>, StreamSlot*>& slots() {
+  static auto* m = new std::map<std::pair<int, hipStream_t>, StreamSlot*>();
+  return *m;
+}
 
 StreamSlot* slot_of(int dev, hipStream_t stream) {
   std::lock_guard<std::mutex> lock(g_slots_mu);
-  StreamSlot*& s = g_slots[{dev, stream}];
-  if (!s) s = new StreamSlot();   // kept until the process ends
+  StreamSlot*& s = slots()[{dev, stream}];
+  if (!s) s = new StreamSlot();
   return s;
 }
 
@@ -273,12 +280,8 @@ hipError_t stream_workspace(hipStream_t stream, size_t bytes, void** ptr) {
 }
 
 FixedWorkspaceScope::FixedWorkspaceScope(void* ptr, size_t cap) : prev_(t_fixed) {
-  static_assert(sizeof(FixedWorkspace) <= sizeof(storage_), "scope storage");
-  FixedWorkspace* fw = reinterpret_cast<FixedWorkspace*>(storage_);
-  fw->ptr = ptr;
-  fw->cap = cap;
-  fw->wanted = 0;
-  t_fixed = fw;
+  static_assert(sizeof(FixedWorkspace) <= sizeof(storage_) && alignof(FixedWorkspace) <= 8, "scope storage");
+  t_fixed = new (storage_) FixedWorkspace{ptr, cap, 0};
 }
 FixedWorkspaceScope::~FixedWorkspaceScope() { t_fixed = static_cast<FixedWorkspace*>(prev_); }
 

@@ -101,16 +101,23 @@
 extern "C" {
 #endif
 
+/* The *_RANGE_MIN_ and *_RANGE_MAX_ members name no dtype or tier: they make
+ * every int a value of the type, so that an unknown value from a caller is a
+ * defined value that the library refuses (DET_EDTYPE, DET_ETIER). */
 typedef enum {
   DET_F32 = 0,   /* IEEE binary32 */
   DET_BF16 = 1,  /* bfloat16 */
-  DET_F16 = 2    /* IEEE binary16 */
+  DET_F16 = 2,   /* IEEE binary16 */
+  DET_DTYPE_RANGE_MIN_ = -2147483647 - 1,
+  DET_DTYPE_RANGE_MAX_ = 2147483647
 } det_dtype_t;
 
 typedef enum {
   DET_TIER_EXACT = 0, /* float64 tiles + Neumaier compensation, oracle bits */
   DET_TIER_FAST = 1,  /* matrix cores, f32 accumulate, within tolerance */
-  DET_TIER_CR = 2     /* the exact value rounded once: correctly rounded, order-free */
+  DET_TIER_CR = 2,    /* the exact value rounded once: correctly rounded, order-free */
+  DET_TIER_RANGE_MIN_ = -2147483647 - 1,
+  DET_TIER_RANGE_MAX_ = 2147483647
 } det_tier_t;
 
 typedef enum {
