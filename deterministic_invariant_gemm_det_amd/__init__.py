@@ -16,7 +16,7 @@ __all__ = [
     "det_gemm_strerror",
     "det_gemm_last_error", "det_gemm_version", "det_gemm_debug_force_family", "det_gemm_debug_force_exact_kernel",
     "det_gemm_debug_force_db_chunk", "det_gemm_debug_force_cr_fallback", "det_gemm_debug_force_arch",
-    "DetGemmError", "LIB_PATH", "fwd", "dx", "dw", "db", "deterministic_linear", "Linear", "DTYPES", "TIERS",
+    "det_gemm_debug_round_f32", "det_gemm_debug_round_f64", "DetGemmError", "LIB_PATH", "fwd", "dx", "dw", "db", "deterministic_linear", "Linear", "DTYPES", "TIERS",
     "det_layernorm_fwd", "det_layernorm_bwd", "layer_norm", "layer_norm_backward", "deterministic_layer_norm",
 ]
 
@@ -79,6 +79,10 @@ def lib():
         L.det_gemm_debug_force_cr_fallback.restype = ci
         L.det_gemm_debug_force_arch.argtypes = [ctypes.c_char_p]
         L.det_gemm_debug_force_arch.restype = ci
+        L.det_gemm_debug_round_f32.argtypes = [vp, ctypes.c_uint32, i64, ci, vp]
+        L.det_gemm_debug_round_f32.restype = ci
+        L.det_gemm_debug_round_f64.argtypes = [vp, vp, i64, ci, vp]
+        L.det_gemm_debug_round_f64.restype = ci
         _lib = L
     return _lib
 
@@ -177,6 +181,31 @@ def det_gemm_debug_force_cr_fallback(on):
 def det_gemm_debug_force_arch(arch):
     """Test hook: check `arch` (a string) instead of the device's architecture; None restores it."""
     _check(lib().det_gemm_debug_force_arch(None if arch is None else arch.encode()))
+
+
+def det_gemm_debug_round_f32(first, count, dt, device="cuda:0"):
+    """Test hook: the fast tier's output rounding of the f32 values with bits
+    first .. first + count - 1 (mod 2^32), on the device; returns a uint16 (bf16,
+    f16) or float32 (f32) tensor of raw output bits."""
+    import torch
+    storage = torch.float32 if dt == "f32" else torch.int16
+    out = torch.empty(count, dtype=storage, device=device)
+    stream = torch.cuda.current_stream(out.device).cuda_stream
+    _check(lib().det_gemm_debug_round_f32(_p(out), first & 0xffffffff, count, DTYPES[dt], stream))
+    return out
+
+
+def det_gemm_debug_round_f64(values, dt):
+    """Test hook: the exact tier's output rounding of a float64 device tensor, on
+    the device; returns raw output bits as int16 (bf16, f16) or float32 (f32)."""
+    import torch
+    if values.dtype != torch.float64 or not values.is_cuda or not values.is_contiguous():
+        raise ValueError("values must be a contiguous float64 device tensor")
+    storage = torch.float32 if dt == "f32" else torch.int16
+    out = torch.empty(values.numel(), dtype=storage, device=values.device)
+    stream = torch.cuda.current_stream(values.device).cuda_stream
+    _check(lib().det_gemm_debug_round_f64(_p(out), _p(values), values.numel(), DTYPES[dt], stream))
+    return out
 
 
 # ---------------------------------------------------------------- torch layer

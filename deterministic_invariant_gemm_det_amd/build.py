@@ -15,7 +15,7 @@ ROOT = os.path.dirname(HERE)
 LIB = os.path.join(HERE, "libdetgemm.so")
 PEAK_LIB = os.path.join(HERE, "libdetpeak.so")
 SOURCES = ["abi.cpp", "exact.hip", "fast.hip", "fast16.hip", "fast16w.hip", "colsum.hip", "layernorm.hip", "cr.hip",
-           "noalloc.hip", "skinny.hip"]
+           "noalloc.hip", "skinny.hip", "debug_round.hip"]
 PEAK_SOURCES = ["peak.hip"]
 # Per-source extra flags. The exact tier keeps matrix-core results in ordinary
 # VGPRs: the Neumaier update reads every partial on the vector ALU, and the

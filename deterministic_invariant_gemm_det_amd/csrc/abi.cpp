@@ -458,6 +458,34 @@ det_status_t det_gemm_debug_force_arch(const char* arch) {
   return DET_OK;
 }
 
+det_status_t det_gemm_debug_round_f32(void* out, uint32_t first, int64_t count, det_dtype_t dt,
+                                      hipStream_t stream) {
+  g_last_error[0] = '\0';
+  if (dt != DET_F32 && dt != DET_BF16 && dt != DET_F16) return fail(DET_EDTYPE, "det_gemm: unknown dtype%s");
+  if (count < 0 || count > (int64_t(1) << 32)) return fail(DET_EINVAL, "det_gemm_debug_round_f32: count must be in 0 .. 2^32%s");
+  if (count > 0 && !out) return fail(DET_EINVAL, "det_gemm: null %s pointer", "output");
+  int cus = 0;
+  const det_status_t dev = check_device(&cus);
+  if (dev != DET_OK) return dev;
+  const hipError_t e = detgemm::launch_round_f32(static_cast<detgemm::Dt>(dt), out, first, count, stream);
+  if (e != hipSuccess) return fail(DET_ELAUNCH, "det_gemm: kernel launch failed: %s", hipGetErrorString(e));
+  return DET_OK;
+}
+
+det_status_t det_gemm_debug_round_f64(void* out, const double* in, int64_t count, det_dtype_t dt,
+                                      hipStream_t stream) {
+  g_last_error[0] = '\0';
+  if (dt != DET_F32 && dt != DET_BF16 && dt != DET_F16) return fail(DET_EDTYPE, "det_gemm: unknown dtype%s");
+  if (count < 0) return fail(DET_EINVAL, "det_gemm_debug_round_f64: count must be >= 0%s");
+  if (count > 0 && (!out || !in)) return fail(DET_EINVAL, "det_gemm: null %s pointer", !out ? "output" : "input");
+  int cus = 0;
+  const det_status_t dev = check_device(&cus);
+  if (dev != DET_OK) return dev;
+  const hipError_t e = detgemm::launch_round_f64(static_cast<detgemm::Dt>(dt), out, in, count, stream);
+  if (e != hipSuccess) return fail(DET_ELAUNCH, "det_gemm: kernel launch failed: %s", hipGetErrorString(e));
+  return DET_OK;
+}
+
 det_status_t det_gemm_debug_force_db_chunk(int64_t tiles) {
   if (tiles < 0) return fail(DET_EINVAL, "det_gemm: db chunk must be >= 0%s");
   g_force_db_chunk.store(tiles, std::memory_order_relaxed);

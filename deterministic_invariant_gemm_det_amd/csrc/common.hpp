@@ -119,6 +119,10 @@ hipError_t launch_layernorm_fwd(Dt dt, const void* x, const void* gamma, const v
 hipError_t launch_layernorm_bwd(Dt dt, bool param_f32, const void* dy, const void* x, const double* mean,
                                 const double* rstd, const void* gamma, int64_t rows, int64_t h, void* dx,
                                 void* dgamma, void* dbeta, hipStream_t stream);
+// Test hooks: round_from_f32 on the f32 values with bits first, first + 1, ...
+// (count of them, wrapping at 2^32) and round_from_f64 on in[0 .. count - 1].
+hipError_t launch_round_f32(Dt dt, void* out, uint32_t first, int64_t count, hipStream_t stream);
+hipError_t launch_round_f64(Dt dt, void* out, const double* in, int64_t count, hipStream_t stream);
 // Correctly rounded tier; a null A stands for a column of ones.
 hipError_t launch_cr(Op op, Dt dt, const GemmArgs& a, int force_fallback, hipStream_t stream);
 // A device workspace of at least `bytes` for (current device, stream), owned

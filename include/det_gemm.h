@@ -318,6 +318,30 @@ det_status_t det_gemm_debug_force_cr_fallback(int on);
  */
 det_status_t det_gemm_debug_force_arch(const char* arch);
 
+/*
+ * Test hooks: the output roundings of the tiers, on the device, with the same
+ * functions their epilogues call (sgemm-bi 0.1.2 PyPI page, "Determinism
+ * contracts": the round-to-nearest-even downcast), so that the last step of
+ * every output can be compared with a reference over chosen inputs.
+ *
+ * det_gemm_debug_round_f32: out[i] = the fast tier's rounding of the f32 value
+ * whose bits are first + i (mod 2^32), i = 0 .. count - 1, to dt (f32: the
+ * value itself). out holds count elements of dt (device memory, caller-owned).
+ * DET_EINVAL if count < 0 or count > 2^32 or out is NULL with count > 0.
+ *
+ * det_gemm_debug_round_f64: out[i] = the exact tier's rounding of in[i]
+ * (float64, device memory) to dt: round to odd at f32, then round to nearest
+ * even, which equals one rounding of in[i] to dt. DET_EINVAL if count < 0 or
+ * a pointer is NULL with count > 0.
+ *
+ * Both: asynchronous on `stream`; DET_EDTYPE for an unknown dt; the device
+ * check and DET_ELAUNCH as for the GEMMs.
+ */
+det_status_t det_gemm_debug_round_f32(void* out, uint32_t first, int64_t count, det_dtype_t dt,
+                                      hipStream_t stream);
+det_status_t det_gemm_debug_round_f64(void* out, const double* in, int64_t count, det_dtype_t dt,
+                                      hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -116,6 +116,24 @@ void refusals() {
   expect(det_gemm_debug_force_arch(long_name.c_str()), DET_EINVAL, "arch name of 64 characters");
 }
 
+void rounding_hooks() {
+  for (int dt = 0; dt < 3; ++dt) {
+    Buf out(1000 * esz(static_cast<det_dtype_t>(dt))), in(1000 * 8);
+    expect(det_gemm_debug_round_f32(out.p, 0xfffffff0u, 1000, static_cast<det_dtype_t>(dt), stream_a), DET_OK,
+           "round f32");
+    expect(det_gemm_debug_round_f64(out.p, static_cast<const double*>(in.p), 1000, static_cast<det_dtype_t>(dt),
+                                    stream_a), DET_OK, "round f64");
+  }
+  expect(det_gemm_debug_round_f32(nullptr, 0, 0, DET_BF16, stream_a), DET_OK, "round f32, nothing");
+  expect(det_gemm_debug_round_f32(nullptr, 0, 5, DET_BF16, stream_a), DET_EINVAL, "round f32, null out");
+  expect(det_gemm_debug_round_f32(nullptr, 0, (int64_t(1) << 32) + 1, DET_BF16, stream_a), DET_EINVAL,
+         "round f32, count > 2^32");
+  expect(det_gemm_debug_round_f64(nullptr, nullptr, -1, DET_F16, stream_a), DET_EINVAL, "round f64, count < 0");
+  expect(det_gemm_debug_round_f64(nullptr, nullptr, 3, DET_F16, stream_a), DET_EINVAL, "round f64, null");
+  expect(det_gemm_debug_round_f64(nullptr, nullptr, 0, static_cast<det_dtype_t>(-9), stream_a), DET_EDTYPE,
+         "round f64, bad dtype");
+}
+
 void devices() {
   Buf x(64), w(64), y(64);
   expect(det_gemm_debug_force_arch("gfx942"), DET_OK, "force arch");
@@ -207,6 +225,7 @@ int main() {
     layernorm_calls(37, 300, static_cast<det_dtype_t>(dt), stream_b);
   }
   refusals();
+  rounding_hooks();
   devices();
   fixed_scratch();
   failed_allocation();
