@@ -48,6 +48,8 @@ def parse():
     p.add_argument("--warmup", type=int, default=3)
     p.add_argument("--cpu-seconds", type=float, default=12.0, help="budget of the CPU-oracle sample")
     p.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline")
+    p.add_argument("--cpu-full", action="store_true",
+                   help="time the oracle on configs 1-4 in full (several minutes) instead of the bounded sample")
     p.add_argument("--no-skinny", action="store_true", help="skip the skinny-M bandwidth measurements")
     p.add_argument("--no-vendor", action="store_true", help="skip the vendor-BLAS context timings")
     p.add_argument("--no-peak", action="store_true", help="skip the measured-peak microkernels")
@@ -409,39 +411,105 @@ def vendor_context(data, dev, fast_per):
     return out
 
 
-def cpu_baseline(data, budget_s):
-    """The oracle, as it stands, on a bounded sample of the step's exact-tier GEMMs (one core)."""
+CONFIG4 = (("qkv", 768, 2304), ("attn_proj", 768, 768), ("c_fc", 768, 3072), ("c_proj", 3072, 768))
+
+
+def cpu_baseline(budget_s, full=False):
+    """The oracle, as it stands, single-threaded on this host, on the workloads' own inputs.
+
+    Bounded (default, about budget_s seconds): config 1 (f32 256 x 512 x 512 fwd, dX, dW) and
+    one training step of config 3 (the f32 MLP) in full, config 2's forward at M = 1, 3, 17 in
+    full (f32 and bf16), and output rows of config 4's twelve bf16 GEMMs (the four GPT-2 linears
+    at 8192 tokens, fwd/dX/dW) for equal shares of the rest of the budget. full=True times
+    configs 1 to 4 in full instead: all 50 MLP steps, every M prefix of config 2, every output
+    of config 4 (several minutes; progress on stderr). `value` is config 4's useful rate
+    (2*M*N*K flops per second over the rows done)."""
     import numpy as np
     import oracle
-    flops = 0.0
-    t0 = time.perf_counter()
-    per_op = budget_s / 6.0
-    pieces = []
-    for name, k, n in LAYERS:
-        d = data[name]
+    import synthetic as syn
+    from oracle import mlp
+
+    per = {}
+
+    def record(key, flops, secs, note=None):
+        per[key] = {"gflop": round(flops / 1e9, 4), "s": round(secs, 3), "gflops": round(flops / secs / 1e9, 3)}
+        if note:
+            per[key]["rows"] = note
+        if full:
+            print(f"cpu_baseline {key}: {secs:.1f} s", file=sys.stderr, flush=True)
+
+    def timed(f):
+        t0 = time.perf_counter()
+        f()
+        return time.perf_counter() - t0
+
+    t_all = time.perf_counter()
+    # config 1: f32, M=256, K=512, N=512, seed 42
+    m, k, n = 256, 512, 512
+    X = syn.normal(42, syn.TID_X, (m, k))
+    W = syn.normal(42, syn.TID_W, (k, n))
+    b = syn.normal(42, syn.TID_B, (n,), sigma=0.1)
+    G = syn.normal(42, syn.TID_DY, (m, n))
+    record("cfg1.fwd", 2.0 * m * k * n, timed(lambda: oracle.fwd("f32", X, W, b)))
+    record("cfg1.dx", 2.0 * m * k * n, timed(lambda: oracle.dx("f32", G, W)))
+    record("cfg1.dw", 2.0 * m * k * n, timed(lambda: oracle.dw("f32", X, G)))
+
+    # config 3: the f32 MLP (seed 42), one step or all 50
+    widths, batch = syn.MLP_WIDTHS, syn.MLP_BATCH
+    layers = list(zip(widths[:-1], widths[1:]))
+    step_flops = sum(2.0 * batch * i * o * 2 + 2.0 * batch * o for i, o in layers)   # fwd, dW, db
+    step_flops += sum(2.0 * batch * i * o for i, o in layers[1:])                      # dX below layer 1
+    steps = 50 if full else 1
+
+    def train():
+        params = syn.mlp_init(42)
+        for s_ in range(steps):
+            Xs, Ts = syn.mlp_batch(42, s_)
+            params, _ = mlp.step(params, Xs, Ts)
+    record("cfg3.mlp_steps", step_flops * steps, timed(train), note=f"{steps} of 50 steps")
+
+    # config 2: forward of the M prefixes of an 8192-row X, K=768, N=3072, f32 and bf16
+    for dt in ("f32", "bf16"):
+        X8 = syn.normal(42, syn.TID_X, (8192, 768), dt=dt)
+        W2 = syn.normal(42, syn.TID_W, (768, 3072), sigma=0.02, dt=dt)
+        for M in (1, 3, 17, 64, 127, 512, 2048, 8192):
+            if full or M <= 17:
+                record(f"cfg2.{dt}.M{M}", 2.0 * M * 768 * 3072, timed(lambda: oracle.fwd(dt, X8[:M], W2)))
+
+    # config 4: GPT-2 linears at 8192 tokens, bf16, seed 42
+    spent = time.perf_counter() - t_all
+    share = max(0.2, (budget_s - spent) / 12.0)
+    flops4, secs4 = 0.0, 0.0
+    for name, k, n in CONFIG4:
+        m = TOKENS
+        X = syn.normal(42, syn.TID_X, (m, k), dt="bf16")
+        W = syn.normal(42, syn.TID_W, (k, n), sigma=0.02, dt="bf16")
+        G = syn.normal(42, syn.TID_DY, (m, n), dt="bf16")
         for op in OPS:
-            rows_done = 0
-            t_op = time.perf_counter()
-            chunk = 8 if op != "dw" else 2
-            while time.perf_counter() - t_op < per_op:
-                rows = np.arange(rows_done, rows_done + chunk)
-                if op == "fwd":
-                    oracle.fwd("bf16", d["X"], d["W"], rows=rows)
-                    flops += 2.0 * chunk * k * n
-                elif op == "dx":
-                    oracle.dx("bf16", d["G"], d["W"], rows=rows)
-                    flops += 2.0 * chunk * n * k
-                else:
-                    oracle.dw("bf16", d["X"], d["G"], rows=rows)
-                    flops += 2.0 * chunk * TOKENS * n
-                rows_done += chunk
-            pieces.append(f"{name}.{op}:{rows_done} rows")
-    secs = time.perf_counter() - t0
+            A, B = {"fwd": (X, W), "dx": (G, W), "dw": (X, G)}[op]
+            out_rows = k if op == "dw" else m
+            row_flops = 2.0 * m * k * n / out_rows
+            if full:
+                secs = timed(lambda: oracle.gemm(op, "bf16", A, B, m, k, n))
+                done = out_rows
+            else:
+                # one call, as in the full run (the oracle upcasts the other operand once per
+                # call), with as many rows as fill the share at about 1.5 GFLOP/s
+                done = int(max(1, min(out_rows, share * 1.5e9 / row_flops)))
+                rows = np.arange(done, dtype=np.int64)
+                secs = timed(lambda: oracle.gemm(op, "bf16", A, B, m, k, n, rows=rows))
+            record(f"cfg4.{name}.{op}", row_flops * done, secs, note=f"{done} of {out_rows}")
+            flops4 += row_flops * done
+            secs4 += secs
+    total = time.perf_counter() - t_all
     model, ncpu = host_cpu()
-    return {"value": flops / secs / 1e12, "unit": "TFLOP/s", "cores": 1, "kind": "oracle",
+    what = ("configs 1-4 in full" if full else
+            "config 1 and one config-3 step in full, config 2 at M=1,3,17 in full, output rows of config 4's "
+            "twelve GEMMs")
+    return {"value": flops4 / secs4 / 1e12, "unit": "TFLOP/s", "cores": 1, "kind": "oracle",
             "host_cpu": model, "host_logical_cpus": ncpu,
-            "sample": "exact-tier output rows of the step's six GEMMs (" + ", ".join(pieces) +
-                      f"), {secs:.1f} s single-threaded, useful 2*M*N*K flops per row"}
+            "sample": f"{what}; single-threaded, {total:.1f} s; value = config 4's useful 2*M*N*K flops per second",
+            "per_workload": per}
 
 
 def main():
@@ -538,7 +606,7 @@ def main():
     if not args.no_vendor:
         result["vendor_blas_context"] = vendor_context(data, dev, per)
     if not args.no_cpu:
-        result["cpu_baseline"] = cpu_baseline(data, args.cpu_seconds)
+        result["cpu_baseline"] = cpu_baseline(args.cpu_seconds, full=args.cpu_full)
     print(json.dumps(result))
 
 
