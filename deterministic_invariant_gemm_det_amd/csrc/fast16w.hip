@@ -277,7 +277,8 @@ __device__ inline void tile_origin(const GemmArgs& a, uint32_t t, int64_t& row0,
 //
 // Reduction steps (16 indices each, four per stage) run in one sequence; the
 // fragments of step t + 2 are read from LDS while step t's MFMAs run (four
-// fragment buffers, step t in buffer t mod 4). Stage g + 1 must therefore be
+// fragment buffers, step t in buffer t mod 4; one read placed after each
+// matrix instruction). Stage g + 1 must therefore be
 // visible before step 4 g + 2 reads it: between steps 4 g + 1 and 4 g + 2 each
 // wave writes its register-staged part of the last requested stage, waits for
 // its own loads of stage g + 1, and meets the others at a barrier. After the
@@ -487,6 +488,13 @@ __global__ void __launch_bounds__(64 * WR * WC, WPE) fast16w_kernel(GemmArgs arg
       for (int i = 0; i < NI; ++i)
 #pragma unroll
         for (int j = 0; j < NJ; ++j) acc[i][j] = mfma_step<E>(bf[ks & 3][j], af[ks & 3][i], acc[i][j]);
+      // one fragment read of step ks + 2 after each matrix instruction of step ks
+#pragma unroll
+      for (int t = 0; t < NI + NJ && t < NI * NJ; ++t) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      }
+      if constexpr (NI * NJ > NI + NJ) __builtin_amdgcn_sched_group_barrier(0x008, NI * NJ - (NI + NJ), 0);
     }
   };
   for (int g = 0; g + 1 < nst; ++g) stage(g, std::false_type{});
