@@ -51,6 +51,9 @@ def parse():
     p.add_argument("--cpu-full", action="store_true",
                    help="time the oracle on configs 1-4 in full (several minutes) instead of the bounded sample")
     p.add_argument("--no-skinny", action="store_true", help="skip the skinny-M bandwidth measurements")
+    p.add_argument("--skinny-only", action="store_true",
+                   help="profiling aid: only the skinny-M measurements (one JSON line)")
+    p.add_argument("--skinny-light", action="store_true", help="a tenth of the skinny-M calls (for runs under a profiler)")
     p.add_argument("--no-vendor", action="store_true", help="skip the vendor-BLAS context timings")
     p.add_argument("--no-peak", action="store_true", help="skip the measured-peak microkernels")
     p.add_argument("--shapes", action="store_true",
@@ -180,7 +183,7 @@ def copy_calibration(dev, mib, n_steps, warmup):
                       "GB_per_s": round(2 * n / (ms * 1e-3) / 1e9, 1)}))
 
 
-def skinny(data, dev):
+def skinny(data, dev, light=False):
     """Skinny-M forward, both tiers: M = 1, 3, 17 (the first rows of the c_fc
     input, k=768, n=3072) and M = 1 on c_proj (k=3072, n=768). Achieved GB/s of
     algorithmic bytes (x, w and y once each):
@@ -189,7 +192,8 @@ def skinny(data, dev):
       eager: 200 back-to-back calls through the Python binding (host-paced
              when the kernel is shorter than the call);
       cold:  one call after a 512 MiB buffer is written, so the weight comes
-             from HBM (median of 20)."""
+             from HBM (median of 20).
+    light: a tenth of the calls (for runs under a profiler)."""
     import torch
     import deterministic_invariant_gemm_det_amd as dg
     flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
@@ -203,6 +207,7 @@ def skinny(data, dev):
         algo_bytes = 2 * (m * k + k * n + m * n)
         for tier in ("exact", "fast"):
             f = lambda: dg.fwd(x, d["w"], None, tier, out=y)
+            n_eager, n_graph, n_replay, n_cold = (20, 10, 2, 5) if light else (200, 50, 4, 20)
             side = torch.cuda.Stream(dev)
             side.wait_stream(torch.cuda.current_stream(dev))
             with torch.cuda.stream(side):
@@ -211,25 +216,25 @@ def skinny(data, dev):
                 side.synchronize()
                 e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
                 e0.record(side)
-                for _ in range(200):
+                for _ in range(n_eager):
                     f()
                 e1.record(side)
                 side.synchronize()
-                eager_us = e0.elapsed_time(e1) * 1e3 / 200
+                eager_us = e0.elapsed_time(e1) * 1e3 / n_eager
                 g = torch.cuda.CUDAGraph()
                 with torch.cuda.graph(g, stream=side):
-                    for _ in range(50):
+                    for _ in range(n_graph):
                         f()
                 g.replay()
                 side.synchronize()
                 e0.record(side)
-                for _ in range(4):
+                for _ in range(n_replay):
                     g.replay()
                 e1.record(side)
                 side.synchronize()
-                warm_us = e0.elapsed_time(e1) * 1e3 / 200
+                warm_us = e0.elapsed_time(e1) * 1e3 / (n_graph * n_replay)
                 cold = []
-                for _ in range(20):
+                for _ in range(n_cold):
                     flush.fill_(7)
                     a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
                     a.record(side)
@@ -526,6 +531,9 @@ def main():
         print(json.dumps({"shape_sweep": shape_sweep(dev)}))
         return
     data = make_inputs(dev)
+    if args.skinny_only:
+        print(json.dumps({"skinny_fwd_bf16": skinny(data, dev, light=args.skinny_light)}))
+        return
     steps = launches(data, args.only)
     stream = torch.cuda.current_stream(dev)
     total_ms, per_launch_ms = time_launches(steps, args.steps, args.warmup, stream)
@@ -600,7 +608,7 @@ def main():
         result["tiers"]["exact"]["pct_of_measured_peak"] = round(100 * result["tiers"]["exact"]["tflops"] / peaks["fp64_mfma_4x4x4"], 2)
         result["tiers"]["fast"]["pct_of_measured_peak"] = round(100 * result["tiers"]["fast"]["tflops"] / peaks["bf16_mfma_32x32x16"], 2)
     if not args.no_skinny:
-        result["skinny_fwd_bf16"] = skinny(data, dev)
+        result["skinny_fwd_bf16"] = skinny(data, dev, light=args.skinny_light)
     if not args.no_next:
         result["next_rows"] = next_rows(data, dev)
     if not args.no_vendor:
