@@ -16,7 +16,7 @@ __all__ = [
     "det_gemm_strerror",
     "det_gemm_last_error", "det_gemm_version", "det_gemm_debug_force_family", "det_gemm_debug_force_exact_kernel",
     "det_gemm_debug_force_db_chunk", "det_gemm_debug_force_cr_fallback", "det_gemm_debug_force_arch",
-    "det_gemm_debug_round_f32", "det_gemm_debug_round_f64", "DetGemmError", "LIB_PATH", "fwd", "dx", "dw", "db", "deterministic_linear", "Linear", "DTYPES", "TIERS",
+    "det_gemm_debug_round_f32", "det_gemm_debug_round_f64", "det_gemm_debug_round_f64_grouped", "DetGemmError", "LIB_PATH", "fwd", "dx", "dw", "db", "deterministic_linear", "Linear", "DTYPES", "TIERS",
     "det_layernorm_fwd", "det_layernorm_bwd", "layer_norm", "layer_norm_backward", "deterministic_layer_norm",
 ]
 
@@ -83,6 +83,8 @@ def lib():
         L.det_gemm_debug_round_f32.restype = ci
         L.det_gemm_debug_round_f64.argtypes = [vp, vp, i64, ci, vp]
         L.det_gemm_debug_round_f64.restype = ci
+        L.det_gemm_debug_round_f64_grouped.argtypes = [vp, vp, i64, ci, vp]
+        L.det_gemm_debug_round_f64_grouped.restype = ci
         _lib = L
     return _lib
 
@@ -195,17 +197,27 @@ def det_gemm_debug_round_f32(first, count, dt, device="cuda:0"):
     return out
 
 
-def det_gemm_debug_round_f64(values, dt):
-    """Test hook: the exact tier's output rounding of a float64 device tensor, on
-    the device; returns raw output bits as int16 (bf16, f16) or float32 (f32)."""
+def _debug_round_f64(fn, values, dt):
     import torch
     if values.dtype != torch.float64 or not values.is_cuda or not values.is_contiguous():
         raise ValueError("values must be a contiguous float64 device tensor")
     storage = torch.float32 if dt == "f32" else torch.int16
     out = torch.empty(values.numel(), dtype=storage, device=values.device)
     stream = torch.cuda.current_stream(values.device).cuda_stream
-    _check(lib().det_gemm_debug_round_f64(_p(out), _p(values), values.numel(), DTYPES[dt], stream))
+    _check(fn(_p(out), _p(values), values.numel(), DTYPES[dt], stream))
     return out
+
+
+def det_gemm_debug_round_f64(values, dt):
+    """Test hook: the exact tier's output rounding of a float64 device tensor, on
+    the device; returns raw output bits as int16 (bf16, f16) or float32 (f32)."""
+    return _debug_round_f64(lib().det_gemm_debug_round_f64, values, dt)
+
+
+def det_gemm_debug_round_f64_grouped(values, dt):
+    """Test hook: the LayerNorm forward's grouped rounding of the same values
+    (eight per lane); the bits must equal det_gemm_debug_round_f64's."""
+    return _debug_round_f64(lib().det_gemm_debug_round_f64_grouped, values, dt)
 
 
 # ---------------------------------------------------------------- torch layer

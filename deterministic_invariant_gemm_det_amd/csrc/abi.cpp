@@ -472,8 +472,8 @@ det_status_t det_gemm_debug_round_f32(void* out, uint32_t first, int64_t count, 
   return DET_OK;
 }
 
-det_status_t det_gemm_debug_round_f64(void* out, const double* in, int64_t count, det_dtype_t dt,
-                                      hipStream_t stream) {
+static det_status_t debug_round_f64(bool grouped, void* out, const double* in, int64_t count, det_dtype_t dt,
+                                    hipStream_t stream) {
   g_last_error[0] = '\0';
   if (dt != DET_F32 && dt != DET_BF16 && dt != DET_F16) return fail(DET_EDTYPE, "det_gemm: unknown dtype%s");
   if (count < 0) return fail(DET_EINVAL, "det_gemm_debug_round_f64: count must be >= 0%s");
@@ -481,9 +481,21 @@ det_status_t det_gemm_debug_round_f64(void* out, const double* in, int64_t count
   int cus = 0;
   const det_status_t dev = check_device(&cus);
   if (dev != DET_OK) return dev;
-  const hipError_t e = detgemm::launch_round_f64(static_cast<detgemm::Dt>(dt), out, in, count, stream);
+  const detgemm::Dt d = static_cast<detgemm::Dt>(dt);
+  const hipError_t e = grouped ? detgemm::launch_round_f64_grouped(d, out, in, count, stream)
+                               : detgemm::launch_round_f64(d, out, in, count, stream);
   if (e != hipSuccess) return fail(DET_ELAUNCH, "det_gemm: kernel launch failed: %s", hipGetErrorString(e));
   return DET_OK;
+}
+
+det_status_t det_gemm_debug_round_f64(void* out, const double* in, int64_t count, det_dtype_t dt,
+                                      hipStream_t stream) {
+  return debug_round_f64(false, out, in, count, dt, stream);
+}
+
+det_status_t det_gemm_debug_round_f64_grouped(void* out, const double* in, int64_t count, det_dtype_t dt,
+                                              hipStream_t stream) {
+  return debug_round_f64(true, out, in, count, dt, stream);
 }
 
 det_status_t det_gemm_debug_force_db_chunk(int64_t tiles) {

@@ -2,6 +2,7 @@
 #pragma once
 
 #include <hip/hip_runtime.h>
+#include <type_traits>
 #include <stdint.h>
 
 #include <mutex>
@@ -82,6 +83,36 @@ template <> __device__ inline uint16_t round_from_f64<BF16>(double r) {
 }
 template <> __device__ inline _Float16 round_from_f64<F16>(double r) { return static_cast<_Float16>(f64_to_f32_odd(r)); }
 
+// N float64 values each rounded once, as round_from_f64 does, with fewer
+// float64 operations for bf16: round to nearest even at float32, then the
+// hardware conversion. Rounding to nearest is monotone and every midpoint
+// between neighbouring bf16 values is a float32 value, so the two roundings
+// equal one unless the float32 result is such a midpoint (its low 16 bits are
+// 0x8000). If any lane of the wave meets that case, the whole group takes the
+// round-to-odd path (one branch for the wave, rarely taken). f16 and f32 use
+// round_from_f64 as it stands.
+template <typename E, int N>
+__device__ inline void round_group(const double (&u)[N], typename E::T (&out)[N]) {
+  if constexpr (std::is_same<E, BF16>::value) {
+    float f[N];
+    bool tie = false;
+#pragma unroll
+    for (int e = 0; e < N; ++e) {
+      f[e] = static_cast<float>(u[e]);
+      tie |= (__float_as_uint(f[e]) & 0xffffu) == 0x8000u;
+    }
+    if (__builtin_amdgcn_ballot_w64(tie) != 0) {
+#pragma unroll
+      for (int e = 0; e < N; ++e) f[e] = f64_to_f32_odd(u[e]);
+    }
+#pragma unroll
+    for (int e = 0; e < N; ++e) out[e] = __builtin_bit_cast(uint16_t, static_cast<__bf16>(f[e]));
+  } else {
+#pragma unroll
+    for (int e = 0; e < N; ++e) out[e] = round_from_f64<E>(u[e]);
+  }
+}
+
 // Round-to-nearest-even of an f32 accumulator to the output type.
 template <typename E> __device__ inline typename E::T round_from_f32(float r);
 template <> __device__ inline float round_from_f32<F32>(float r) { return r; }
@@ -123,6 +154,7 @@ hipError_t launch_layernorm_bwd(Dt dt, bool param_f32, const void* dy, const voi
 // (count of them, wrapping at 2^32) and round_from_f64 on in[0 .. count - 1].
 hipError_t launch_round_f32(Dt dt, void* out, uint32_t first, int64_t count, hipStream_t stream);
 hipError_t launch_round_f64(Dt dt, void* out, const double* in, int64_t count, hipStream_t stream);
+hipError_t launch_round_f64_grouped(Dt dt, void* out, const double* in, int64_t count, hipStream_t stream);
 // Correctly rounded tier; a null A stands for a column of ones.
 hipError_t launch_cr(Op op, Dt dt, const GemmArgs& a, int force_fallback, hipStream_t stream);
 // A device workspace of at least `bytes` for (current device, stream), owned

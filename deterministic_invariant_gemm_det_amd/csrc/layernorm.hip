@@ -15,14 +15,17 @@
 // Every float64 operation is IEEE-rounded (division and square root included),
 // so the results are the same bits on any device that follows the order.
 //
-// Row kernels (at least four waves per SIMD, at most 128 registers, except the
-// backward with more than one tile per lane): a row belongs to G = min(T, 64)
-// lanes of one wave (T = tiles
-// per row); lane g owns tiles g, g + G, ... and keeps their values in
-// registers (up to TPL tiles, else it reads them again from memory). Each pass
-// writes the lane's tile partials to LDS; one lane per row runs the Neumaier
-// pass over them in tile order and shares the result through LDS. 64 / G rows
-// share a wave (two rows of 24 tiles for H = 768).
+// Forward with whole tiles and aligned operands (fwd_staged_kernel): an
+// eight-wave workgroup copies up to 64 rows through LDS in 16-byte pieces,
+// one thread per tile, and one lane per row runs that row's Neumaier passes.
+// Other row kernels (at least four waves per SIMD, at most 128 registers,
+// except the backward with more than one tile per lane): a row belongs to
+// G = min(T, 64) lanes of one wave (T = tiles per row); lane g owns tiles
+// g, g + G, ... and keeps their values in registers (up to TPL tiles, else it
+// reads them again from memory). Each pass writes the lane's tile partials to
+// LDS; one lane per row runs the Neumaier pass over them in tile order and
+// shares the result through LDS. 64 / G rows share a wave (two rows of 24
+// tiles for H = 768).
 
 #include <type_traits>
 
@@ -310,6 +313,130 @@ __global__ void __launch_bounds__(256, 4) fwd_kernel(const typename E::T* __rest
   });
 }
 
+// Forward for rows whose length is a multiple of the tile width, with
+// 16-byte aligned operands (STAGE_WAVES waves, SRW = min(64, 64 STAGE_WAVES / T)
+// rows per workgroup: 21 rows of 24 tiles for H = 768). The workgroup's rows
+// are one contiguous block of SRW T tiles. The block, gamma and beta move
+// between memory and LDS in 16-byte pieces, consecutive lanes on consecutive
+// pieces; in LDS piece q of tile f sits in slot f PPT + (q XOR ((f / (16 / PPT))
+// mod PPT)), PPT = pieces per tile, which keeps the copies and the per-tile
+// reads free of bank conflicts. Thread i takes tile i (row i / T, tile i mod T)
+// into float64 registers: x after pass 1, x - mean after pass 2. The outputs
+// go back through the tile's own slots. Thread r < SRW runs row r's two
+// Neumaier passes, so one instruction stream serves all the rows.
+constexpr int STAGE_WAVES = 8;
+constexpr size_t STAGE_LDS_MAX = 81920;   // two workgroups per compute unit
+
+template <typename E>
+__global__ void __launch_bounds__(64 * STAGE_WAVES) fwd_staged_kernel(
+    const typename E::T* __restrict__ x, const typename E::T* __restrict__ gamma,
+    const typename E::T* __restrict__ beta, int64_t rows, int h, int T, int SRW, double eps,
+    typename E::T* __restrict__ y, double* __restrict__ mean_out, double* __restrict__ rstd_out) {
+  using TT = typename E::T;
+  constexpr int PER = 16 / sizeof(TT);   // elements per piece
+  constexpr int PPT = KT / PER;          // pieces per tile
+  constexpr int TPG = 16 / PPT;          // tiles per 256 bytes (all 64 banks)
+  constexpr int NTH = 64 * STAGE_WAVES;
+  extern __shared__ uint4 smem[];
+  uint4* X = smem;                                       // SRW T tiles of x, then of y
+  uint4* G = X + SRW * T * PPT;                          // T tiles of gamma
+  uint4* B = G + T * PPT;                                // T tiles of beta
+  double* P = reinterpret_cast<double*>(B + T * PPT);    // tile partials
+  double* stat = P + NTH;                                // [r] mean, [64 + r] rstd
+  const auto slot = [](int f, int q) { return f * PPT + (q ^ ((f / TPG) % PPT)); };
+  const int tid = threadIdx.x;
+  const int64_t row0 = static_cast<int64_t>(blockIdx.x) * SRW;
+  const int nr = rows - row0 < SRW ? static_cast<int>(rows - row0) : SRW;
+  const int ntile = nr * T;
+
+  const uint4* xs = reinterpret_cast<const uint4*>(x + row0 * h);
+  for (int i = tid; i < ntile * PPT; i += NTH) X[slot(i / PPT, i % PPT)] = xs[i];
+  if (gamma) {
+    const uint4* gs = reinterpret_cast<const uint4*>(gamma);
+    for (int i = tid; i < T * PPT; i += NTH) G[slot(i / PPT, i % PPT)] = gs[i];
+  }
+  if (beta) {
+    const uint4* bs = reinterpret_cast<const uint4*>(beta);
+    for (int i = tid; i < T * PPT; i += NTH) B[slot(i / PPT, i % PPT)] = bs[i];
+  }
+  __syncthreads();
+
+  const bool own = tid < ntile;
+  const int r = tid / T, t = tid - r * T;
+  double v[KT];
+#pragma unroll
+  for (int q = 0; q < PPT; ++q) {
+    TT e8[PER];
+    if (own) {
+      const uint4 w = X[slot(tid, q)];
+      __builtin_memcpy(e8, &w, 16);
+    } else {
+      __builtin_memset(e8, 0, 16);
+    }
+#pragma unroll
+    for (int e = 0; e < PER; ++e) v[q * PER + e] = static_cast<double>(E::to_f32(e8[e]));
+  }
+
+  // pass 1: tile sums of x
+  {
+    double p = 0.0;
+#pragma unroll
+    for (int e = 0; e < KT; ++e) p = p + v[e];
+    if (own) P[tid] = p;
+  }
+  __syncthreads();
+  const bool lead = tid < nr;
+  if (lead) stat[tid] = ordered_sum(P + tid * T, T) / static_cast<double>(h);
+  __syncthreads();
+
+  // pass 2: d = x - mean kept in place; tile sums of d * d
+  {
+    const double mu = stat[own ? r : 0];
+    double p = 0.0;
+#pragma unroll
+    for (int e = 0; e < KT; ++e) {
+      const double d = v[e] - mu;
+      v[e] = d;
+      p = __builtin_fma(d, d, p);
+    }
+    if (own) P[tid] = p;
+  }
+  __syncthreads();
+  if (lead) {
+    const double var = ordered_sum(P + tid * T, T) / static_cast<double>(h);
+    const double rs = 1.0 / __builtin_sqrt(var + eps);
+    stat[64 + tid] = rs;
+    if (mean_out) mean_out[row0 + tid] = stat[tid];
+    if (rstd_out) rstd_out[row0 + tid] = rs;
+  }
+  __syncthreads();
+
+  // pass 3: y = (d * rstd) * gamma + beta, one rounding, into the tile's own slots
+  if (own) {
+    const double rs = stat[64 + r];
+#pragma unroll
+    for (int q = 0; q < PPT; ++q) {
+      TT gv[PER], bv[PER], out[PER];
+      if (gamma) { const uint4 w = G[slot(t, q)]; __builtin_memcpy(gv, &w, 16); }
+      if (beta) { const uint4 w = B[slot(t, q)]; __builtin_memcpy(bv, &w, 16); }
+      double u[PER];
+#pragma unroll
+      for (int e = 0; e < PER; ++e) {
+        u[e] = v[q * PER + e] * rs;
+        if (gamma) u[e] = u[e] * static_cast<double>(E::to_f32(gv[e]));
+        if (beta) u[e] = u[e] + static_cast<double>(E::to_f32(bv[e]));
+      }
+      round_group<E>(u, out);
+      uint4 w;
+      __builtin_memcpy(&w, out, 16);
+      X[slot(tid, q)] = w;
+    }
+  }
+  __syncthreads();
+  uint4* ys = reinterpret_cast<uint4*>(y + row0 * h);
+  for (int i = tid; i < ntile * PPT; i += NTH) ys[i] = X[slot(i / PPT, i % PPT)];
+}
+
 template <typename E, int TPL, bool VEC>
 __global__ void __launch_bounds__(256, TPL == 1 ? 4 : 2) bwd_dx_kernel(const typename E::T* __restrict__ dy,
                                                      const typename E::T* __restrict__ x,
@@ -457,6 +584,21 @@ hipError_t launch_fwd_e(const void* x, const void* gamma, const void* beta, int6
                         void* y, double* mean, double* rstd, hipStream_t stream) {
   using T = typename E::T;
   const Geom gm = geom(h);
+  {
+    // the staged kernel: whole tiles, 16-byte aligned operands, and its LDS within STAGE_LDS_MAX
+    const int srw = 64 * STAGE_WAVES / gm.T < 64 ? 64 * STAGE_WAVES / gm.T : 64;
+    const size_t lds = static_cast<size_t>(srw + 2) * h * sizeof(T) + sizeof(double) * (64 * STAGE_WAVES + 128);
+    const bool aligned = reinterpret_cast<uintptr_t>(x) % 16 == 0 && reinterpret_cast<uintptr_t>(y) % 16 == 0 &&
+                         reinterpret_cast<uintptr_t>(gamma) % 16 == 0 && reinterpret_cast<uintptr_t>(beta) % 16 == 0;
+    if (h % KT == 0 && aligned && srw >= 1 && lds <= STAGE_LDS_MAX) {
+      const int64_t blocks = (rows + srw - 1) / srw;
+      if (blocks > INT_MAX) return hipErrorInvalidConfiguration;
+      hipLaunchKernelGGL((fwd_staged_kernel<E>), dim3(static_cast<unsigned>(blocks)), dim3(64 * STAGE_WAVES), lds,
+                         stream, static_cast<const T*>(x), static_cast<const T*>(gamma), static_cast<const T*>(beta),
+                         rows, static_cast<int>(h), gm.T, srw, eps, static_cast<T*>(y), mean, rstd);
+      return hipGetLastError();
+    }
+  }
   const int64_t per_wg = gm.NW * gm.RW;
   const int64_t blocks = (rows + per_wg - 1) / per_wg;
   if (blocks > INT_MAX) return hipErrorInvalidConfiguration;

@@ -334,13 +334,21 @@ det_status_t det_gemm_debug_force_arch(const char* arch);
  * even, which equals one rounding of in[i] to dt. DET_EINVAL if count < 0 or
  * a pointer is NULL with count > 0.
  *
- * Both: asynchronous on `stream`; DET_EDTYPE for an unknown dt; the device
+ * det_gemm_debug_round_f64_grouped: the same values through the LayerNorm
+ * forward's rounding of eight values per lane (for bf16: round to nearest
+ * even at f32 unless a lane of the wave meets an f32 result halfway between
+ * two bf16 values, then round to odd at f32 for the whole group); the result
+ * must equal det_gemm_debug_round_f64's. Same arguments and errors.
+ *
+ * All three: asynchronous on `stream`; DET_EDTYPE for an unknown dt; the device
  * check and DET_ELAUNCH as for the GEMMs.
  */
 det_status_t det_gemm_debug_round_f32(void* out, uint32_t first, int64_t count, det_dtype_t dt,
                                       hipStream_t stream);
 det_status_t det_gemm_debug_round_f64(void* out, const double* in, int64_t count, det_dtype_t dt,
                                       hipStream_t stream);
+det_status_t det_gemm_debug_round_f64_grouped(void* out, const double* in, int64_t count, det_dtype_t dt,
+                                              hipStream_t stream);
 
 #ifdef __cplusplus
 }

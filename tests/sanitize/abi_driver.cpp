@@ -123,6 +123,8 @@ void rounding_hooks() {
            "round f32");
     expect(det_gemm_debug_round_f64(out.p, static_cast<const double*>(in.p), 1000, static_cast<det_dtype_t>(dt),
                                     stream_a), DET_OK, "round f64");
+    expect(det_gemm_debug_round_f64_grouped(out.p, static_cast<const double*>(in.p), 1000,
+                                            static_cast<det_dtype_t>(dt), stream_a), DET_OK, "round f64 grouped");
   }
   expect(det_gemm_debug_round_f32(nullptr, 0, 0, DET_BF16, stream_a), DET_OK, "round f32, nothing");
   expect(det_gemm_debug_round_f32(nullptr, 0, 5, DET_BF16, stream_a), DET_EINVAL, "round f32, null out");
@@ -130,6 +132,8 @@ void rounding_hooks() {
          "round f32, count > 2^32");
   expect(det_gemm_debug_round_f64(nullptr, nullptr, -1, DET_F16, stream_a), DET_EINVAL, "round f64, count < 0");
   expect(det_gemm_debug_round_f64(nullptr, nullptr, 3, DET_F16, stream_a), DET_EINVAL, "round f64, null");
+  expect(det_gemm_debug_round_f64_grouped(nullptr, nullptr, 3, DET_BF16, stream_a), DET_EINVAL,
+         "round f64 grouped, null");
   expect(det_gemm_debug_round_f64(nullptr, nullptr, 0, static_cast<det_dtype_t>(-9), stream_a), DET_EDTYPE,
          "round f64, bad dtype");
 }

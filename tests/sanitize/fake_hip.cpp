@@ -166,4 +166,8 @@ hipError_t launch_round_f64(Dt dt, void* out, const double* in, int64_t count, h
   return hipSuccess;
 }
 
+hipError_t launch_round_f64_grouped(Dt dt, void* out, const double* in, int64_t count, hipStream_t stream) {
+  return launch_round_f64(dt, out, in, count, stream);
+}
+
 }  // namespace detgemm

@@ -11,7 +11,11 @@ odd at f32, then the hardware's round to nearest even) on float64 values chosen
 where a double rounding would go wrong -- each midpoint between neighbouring
 outputs, and values a hair above or below it that round to the midpoint at f32
 -- together with the neighbours of every output value, the overflow and
-subnormal edges, specials and random values, to bf16, f16 and f32."""
+subnormal edges, specials and random values, to bf16, f16 and f32. The same
+values go through round_group, the LayerNorm forward's rounding of eight values
+per lane (for bf16 a plain rounding at f32 unless the wave meets a bf16
+midpoint): every value above that rounds to a midpoint at f32 takes its slow
+path, and its neighbours in the same wave are checked with it."""
 import concurrent.futures as cf
 import os
 
@@ -115,13 +119,15 @@ def _hard_cases(dt):
     return np.concatenate([cases, -cases])
 
 
+@pytest.mark.parametrize("grouped", [False, True])
 @pytest.mark.parametrize("dt", ["bf16", "f16", "f32"])
-def test_exact_tier_rounding_of_hard_float64_values(dt):
+def test_exact_tier_rounding_of_hard_float64_values(dt, grouped):
     import deterministic_invariant_gemm_det_amd as dg
     import torch
     x = _hard_cases(dt)
-    print(f"{dt}: {x.size} float64 values", flush=True)
-    got = dg.det_gemm_debug_round_f64(torch.from_numpy(x).to("cuda:0"), dt).cpu().numpy()
+    print(f"{dt} grouped={grouped}: {x.size} float64 values", flush=True)
+    hook = dg.det_gemm_debug_round_f64_grouped if grouped else dg.det_gemm_debug_round_f64
+    got = hook(torch.from_numpy(x).to("cuda:0"), dt).cpu().numpy()
     with np.errstate(invalid="ignore"):
         want = oracle.round_to(dt, x)
     if dt == "f32":
