@@ -437,6 +437,115 @@ __global__ void __launch_bounds__(64 * STAGE_WAVES) fwd_staged_kernel(
   for (int i = tid; i < ntile * PPT; i += NTH) ys[i] = X[slot(i / PPT, i % PPT)];
 }
 
+// Backward dx for rows of whole tiles with 16-byte aligned operands, laid out
+// as the staged forward: a workgroup of BWD_WAVES waves copies its rows of x
+// and dy and all of gamma through LDS in 16-byte pieces; thread i keeps
+// g = dy gamma and xhat of tile i in float64 registers across the two
+// passes, and its dx goes back through the tile's slots of x.
+#ifndef LN_BWD_WAVES
+#define LN_BWD_WAVES 4
+#endif
+constexpr int BWD_WAVES = LN_BWD_WAVES;
+
+template <typename E>
+__global__ void __launch_bounds__(64 * BWD_WAVES) bwd_staged_kernel(
+    const typename E::T* __restrict__ dy, const typename E::T* __restrict__ x, const double* __restrict__ mean,
+    const double* __restrict__ rstd, const typename E::T* __restrict__ gamma, int64_t rows, int h, int T, int SRW,
+    typename E::T* __restrict__ dx) {
+  using TT = typename E::T;
+  constexpr int PER = 16 / sizeof(TT);
+  constexpr int PPT = KT / PER;
+  constexpr int TPG = 16 / PPT;
+  constexpr int NTH = 64 * BWD_WAVES;
+  extern __shared__ uint4 smem[];
+  uint4* X = smem;                                       // SRW T tiles of x, then of dx
+  uint4* D = X + SRW * T * PPT;                          // SRW T tiles of dy
+  uint4* G = D + SRW * T * PPT;                          // T tiles of gamma
+  double* Pa = reinterpret_cast<double*>(G + T * PPT);   // tile partials of g and of g xhat
+  double* Pb = Pa + NTH;
+  double* stat = Pb + NTH;                               // [r] a, [64 + r] b
+  const auto slot = [](int f, int q) { return f * PPT + (q ^ ((f / TPG) % PPT)); };
+  const int tid = threadIdx.x;
+  const int64_t row0 = static_cast<int64_t>(blockIdx.x) * SRW;
+  const int nr = rows - row0 < SRW ? static_cast<int>(rows - row0) : SRW;
+  const int ntile = nr * T;
+
+  const uint4* xs = reinterpret_cast<const uint4*>(x + row0 * h);
+  const uint4* ds = reinterpret_cast<const uint4*>(dy + row0 * h);
+  for (int i = tid; i < ntile * PPT; i += NTH) {
+    X[slot(i / PPT, i % PPT)] = xs[i];
+    D[slot(i / PPT, i % PPT)] = ds[i];
+  }
+  if (gamma) {
+    const uint4* gs = reinterpret_cast<const uint4*>(gamma);
+    for (int i = tid; i < T * PPT; i += NTH) G[slot(i / PPT, i % PPT)] = gs[i];
+  }
+  const bool own = tid < ntile;
+  const int r = tid / T, t = tid - r * T;
+  const double mu = own ? mean[row0 + r] : 0.0, rs = own ? rstd[row0 + r] : 0.0;
+  __syncthreads();
+
+  double gv[KT], xh[KT];
+#pragma unroll
+  for (int q = 0; q < PPT; ++q) {
+    TT ex[PER], ed[PER], eg[PER];
+    if (own) {
+      const uint4 wx = X[slot(tid, q)], wd = D[slot(tid, q)];
+      __builtin_memcpy(ex, &wx, 16);
+      __builtin_memcpy(ed, &wd, 16);
+    } else {
+      __builtin_memset(ex, 0, 16);
+      __builtin_memset(ed, 0, 16);
+    }
+    if (gamma) { const uint4 wg = G[slot(t, q)]; __builtin_memcpy(eg, &wg, 16); }
+#pragma unroll
+    for (int e = 0; e < PER; ++e) {
+      const double d = static_cast<double>(E::to_f32(ed[e]));
+      gv[q * PER + e] = gamma ? d * static_cast<double>(E::to_f32(eg[e])) : d;
+      xh[q * PER + e] = (static_cast<double>(E::to_f32(ex[e])) - mu) * rs;
+    }
+  }
+
+  // tile sums of g and of g * xhat
+  {
+    double pa = 0.0, pb = 0.0;
+#pragma unroll
+    for (int e = 0; e < KT; ++e) {
+      pa = pa + gv[e];
+      pb = __builtin_fma(gv[e], xh[e], pb);
+    }
+    if (own) {
+      Pa[tid] = pa;
+      Pb[tid] = pb;
+    }
+  }
+  __syncthreads();
+  if (tid < nr) {
+    stat[tid] = ordered_sum(Pa + tid * T, T) / static_cast<double>(h);
+    stat[64 + tid] = ordered_sum(Pb + tid * T, T) / static_cast<double>(h);
+  }
+  __syncthreads();
+
+  // dx = rstd ((g - a) - xhat b), one rounding, into the tile's slots of x
+  if (own) {
+    const double a = stat[r], b = stat[64 + r];
+#pragma unroll
+    for (int q = 0; q < PPT; ++q) {
+      double u[PER];
+      TT out[PER];
+#pragma unroll
+      for (int e = 0; e < PER; ++e) u[e] = rs * ((gv[q * PER + e] - a) - xh[q * PER + e] * b);
+      round_group<E>(u, out);
+      uint4 w;
+      __builtin_memcpy(&w, out, 16);
+      X[slot(tid, q)] = w;
+    }
+  }
+  __syncthreads();
+  uint4* os = reinterpret_cast<uint4*>(dx + row0 * h);
+  for (int i = tid; i < ntile * PPT; i += NTH) os[i] = X[slot(i / PPT, i % PPT)];
+}
+
 template <typename E, int TPL, bool VEC>
 __global__ void __launch_bounds__(256, TPL == 1 ? 4 : 2) bwd_dx_kernel(const typename E::T* __restrict__ dy,
                                                      const typename E::T* __restrict__ x,
@@ -671,7 +780,26 @@ hipError_t launch_bwd_e(bool pf32, const void* dy, const void* x, const double* 
                         const void* gamma, int64_t rows, int64_t h, void* dx, void* dgamma, void* dbeta,
                         hipStream_t stream) {
   using T = typename E::T;
+  bool dx_done = false;
   if (dx) {
+    // the staged kernel: whole tiles, 16-byte aligned operands, and its LDS within STAGE_LDS_MAX
+    const int Tt = static_cast<int>((h + KT - 1) / KT);
+    const int srw = 64 * BWD_WAVES / Tt < 64 ? 64 * BWD_WAVES / Tt : 64;
+    const size_t lds = static_cast<size_t>(2 * srw + 1) * h * sizeof(T) + sizeof(double) * (2 * 64 * BWD_WAVES + 128);
+    const bool aligned = reinterpret_cast<uintptr_t>(x) % 16 == 0 && reinterpret_cast<uintptr_t>(dy) % 16 == 0 &&
+                         reinterpret_cast<uintptr_t>(dx) % 16 == 0 && reinterpret_cast<uintptr_t>(gamma) % 16 == 0;
+    if (h % KT == 0 && aligned && srw >= 1 && lds <= STAGE_LDS_MAX) {
+      const int64_t blocks = (rows + srw - 1) / srw;
+      if (blocks > INT_MAX) return hipErrorInvalidConfiguration;
+      hipLaunchKernelGGL((bwd_staged_kernel<E>), dim3(static_cast<unsigned>(blocks)), dim3(64 * BWD_WAVES), lds, stream,
+                         static_cast<const T*>(dy), static_cast<const T*>(x), mean, rstd, static_cast<const T*>(gamma),
+                         rows, static_cast<int>(h), Tt, srw, static_cast<T*>(dx));
+      const hipError_t e = hipGetLastError();
+      if (e != hipSuccess) return e;
+      dx_done = true;
+    }
+  }
+  if (dx && !dx_done) {
     const Geom gm = geom(h);
     const int64_t per_wg = gm.NW * gm.RW;
     const int64_t blocks = (rows + per_wg - 1) / per_wg;
