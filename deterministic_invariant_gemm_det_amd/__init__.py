@@ -177,7 +177,7 @@ def det_gemm_debug_force_db_chunk(tiles):
 
 
 def det_gemm_debug_force_cr_fallback(on):
-    _check(lib().det_gemm_debug_force_cr_fallback(int(bool(on))))
+    _check(lib().det_gemm_debug_force_cr_fallback(int(on)))
 
 
 def det_gemm_debug_force_arch(arch):

@@ -439,7 +439,7 @@ det_status_t det_gemm_debug_force_exact_kernel(int variant) {
 }
 
 det_status_t det_gemm_debug_force_cr_fallback(int on) {
-  if (on != 0 && on != 1) return fail(DET_EINVAL, "det_gemm: cr fallback switch must be 0 or 1%s");
+  if (on < 0 || on > 2) return fail(DET_EINVAL, "det_gemm: cr path switch must be 0, 1 or 2%s");
   g_force_cr_fallback.store(on, std::memory_order_relaxed);
   return DET_OK;
 }

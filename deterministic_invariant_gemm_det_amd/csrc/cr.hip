@@ -32,6 +32,10 @@
 //     least two bits narrower is one correct rounding (Boldo and Melquiond,
 //     IEEE TC 2008).
 //
+// For 16-bit inputs a faster form of 2 runs first (2b below): 8-bit slices on
+// the bf16 matrix instructions, exact in float32 over 256 reduction indices;
+// the tiles it cannot take (wider spans, non-finite values) go on to 2.
+//
 // A null A operand stands for a column of ones (the bias gradient as the
 // correctly rounded column sum of dY).
 //
@@ -301,12 +305,13 @@ constexpr int SUBS = 4;   // 32-index stages per exact block (128 indices: 128 p
 template <typename O>
 __global__ void __launch_bounds__(256) sliced_kernel(GemmArgs g, Stats st, int tiles_c, int force_fallback,
                                                      const float* __restrict__ SA, const float* __restrict__ SB,
-                                                     int64_t npa, int64_t npb, int64_t ktp) {
+                                                     int64_t npa, int64_t npb, int64_t ktp, int after8) {
   __shared__ double As[KB][LSD];
   __shared__ double Bs[KB][LSD];
   __shared__ int red_s[4];
   const int tid = threadIdx.x;
   const int tile = blockIdx.x;
+  if (after8 && !st.flag[tile]) return;   // finished by the 8-bit path (uniform over the workgroup)
   const int64_t r0 = static_cast<int64_t>(tile / tiles_c) * TILE, c0 = static_cast<int64_t>(tile % tiles_c) * TILE;
 
   // the tile's slice counts and non-finite flag
@@ -454,6 +459,255 @@ __global__ void __launch_bounds__(256) sliced_kernel(GemmArgs g, Stats st, int t
     }
 }
 
+// ---- 2b. 8-bit slices on the bf16 matrix instructions (16-bit inputs) --------
+//
+// The same exact value from narrower slices on a 32x faster pipe. A value of
+// row r is cut into 8-bit slices below top_r: slice j holds the bits with
+// weights 2^(top_r - 8 j - 7) .. 2^(top_r - 8 j) as a signed integer of
+// magnitude below 2^8, which bf16 holds exactly. For one slice pair (s, t) the
+// products are integers below 2^16 and V_MFMA_F32_32X32X16_BF16 sums them in
+// float32; over 256 reduction indices every partial sum stays below
+// 256 * 255^2 < 2^24, so the sum is exact whatever order the instruction adds
+// in. Each 256-index sum is added to a float64 per weight class q = s + t (an
+// integer below 2^53 for any reduction this tier takes); at the end of a class
+// the float64 goes into the int128 at 8 (qmax - q) bits up, and the int128 is
+// rounded as in 2. A tile is taken here when its rows and columns need at most
+// S8MAX slices (spans of at most 40 bits) and all its values are finite; the
+// others are flagged for path 2.
+constexpr int S8 = 8;           // bits per slice
+constexpr int S8MAX = 5;        // slices per value on this path
+constexpr int K8 = 64;          // reduction indices per stage
+constexpr int CH8 = 4;          // stages per exact float32 sum (256 indices)
+
+__device__ inline int slices8_of(int t, int lo) { return t == NOBITS ? 0 : (t - lo + S8) / S8; }
+
+// Slice j of a value whose row or column has top bit `top`, as a signed integer.
+__device__ inline int slice8(const Parts& p, int top, int j) {
+  if (p.sig == 0) return 0;
+  const int low = top - S8 * j - (S8 - 1);
+  const int sh = p.lsb - low;
+  uint32_t part;
+  if (sh >= 0)
+    part = sh >= S8 ? 0u : ((p.sig << sh) & 0xffu);
+  else
+    part = -sh >= 32 ? 0u : ((p.sig >> (-sh)) & 0xffu);
+  return p.neg ? -static_cast<int>(part) : static_cast<int>(part);
+}
+
+// bf16 bits of a small integer (exact: at most 8 significant bits)
+__device__ inline uint16_t bf16_of_int(int v) {
+  return static_cast<uint16_t>(__float_as_uint(static_cast<float>(v)) >> 16);
+}
+
+// S[j][x][l] (bf16 bits) for j < S8MAX, x < np, l < kp: slice j of the operand
+// value (x, l) (A row x or B column x, reduction index l; the bias index as in
+// path 2), zero past the operand. A workgroup converts a 64 x 64 block, read
+// along the source's contiguous dimension through LDS and written along l.
+template <typename E, bool IS_A, bool RC>
+__global__ void __launch_bounds__(256) slice8_prep_kernel(GemmArgs g, const int* __restrict__ top, int64_t n,
+                                                          int64_t np, int64_t kp, uint16_t* __restrict__ S) {
+  __shared__ uint16_t raw[64][65];
+  using T = typename E::T;
+  const int tid = threadIdx.x;
+  const int64_t lb = kp / 64;
+  const int64_t x0 = static_cast<int64_t>(blockIdx.x / lb) * 64, l0 = static_cast<int64_t>(blockIdx.x % lb) * 64;
+  const int64_t kt = g.red + (g.bias ? 1 : 0);
+  const T* X = static_cast<const T*>(IS_A ? g.A : g.B);
+  const int64_t ld = IS_A ? g.lda : g.ldb;
+  // element (x, l) of the operand sits at x * ld + l (RC) or l * ld + x; the bias
+  // index and an absent A are not read from memory (a_at / b_at below)
+  for (int i = tid; i < 64 * 64; i += 256) {
+    const int fast = i % 64, slow = i / 64;
+    const int x = RC ? slow : fast, l = RC ? fast : slow;
+    const int64_t gx = x0 + x, gl = l0 + l;
+    uint16_t v = 0;
+    if (gx < n && gl < g.red && X) {
+      const T e = RC ? X[gx * ld + gl] : X[gl * ld + gx];
+      __builtin_memcpy(&v, &e, 2);
+    }
+    raw[x][l] = v;
+  }
+  __syncthreads();
+  for (int i = tid; i < 64 * 64; i += 256) {
+    const int x = i / 64, l = i % 64;
+    const int64_t gx = x0 + x, gl = l0 + l;
+    int v[S8MAX];
+#pragma unroll
+    for (int j = 0; j < S8MAX; ++j) v[j] = 0;
+    if (gx < n && gl < kt) {
+      Parts p;
+      if (gl == g.red || (IS_A && !X)) {
+        p = IS_A ? a_at<E, RC>(g, gx, gl) : b_at<E, RC>(g, gl, gx);
+      } else {
+        T e;
+        const uint16_t bits = raw[x][l];
+        __builtin_memcpy(&e, &bits, 2);
+        p = parts<E>(e);
+      }
+      if (p.finite && p.sig) {
+        const int t = top[gx];
+#pragma unroll
+        for (int j = 0; j < S8MAX; ++j) v[j] = slice8(p, t, j);
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < S8MAX; ++j) S[(j * np + gx) * kp + gl] = bf16_of_int(v[j]);
+  }
+}
+
+typedef __bf16 v8bf_t __attribute__((ext_vector_type(8)));
+typedef float v16f_t __attribute__((ext_vector_type(16)));
+typedef uint32_t v4u_t __attribute__((ext_vector_type(4)));
+
+// LDS stage of one operand: 64 rows (or columns) x 64 reduction indices, row x
+// in 128 bytes with 16-byte piece p in slot p XOR sw(x), so that the fragment
+// reads of 32 rows at one piece spread over the banks.
+__device__ inline int sw8(int x) { return ((x >> 1) & 7) ^ ((x >> 3) & 1); }
+
+template <typename O>
+__global__ void __launch_bounds__(256) sliced8_kernel(GemmArgs g, Stats st, int tiles_c,
+                                                      const uint16_t* __restrict__ SA, const uint16_t* __restrict__ SB,
+                                                      int64_t npa, int64_t npb, int64_t kp) {
+  __shared__ __attribute__((aligned(16))) uint16_t Ls[2][2][64 * 64];   // [buffer][A, B][row * 64 + index]
+  __shared__ int red_s[4];
+  const int tid = threadIdx.x;
+  const int tile = blockIdx.x;
+  const int64_t r0 = static_cast<int64_t>(tile / tiles_c) * TILE, c0 = static_cast<int64_t>(tile % tiles_c) * TILE;
+  if (tid < 4) red_s[tid] = 0;
+  __syncthreads();
+  {
+    const int i = tid & 63;
+    if (tid < 64 && r0 + i < g.rows) {
+      atomicMax(&red_s[0], slices8_of(st.topA[r0 + i], st.lowA[r0 + i]));
+      if (st.badA[r0 + i]) atomicOr(&red_s[2], 1);
+    } else if (tid >= 64 && tid < 128 && c0 + i < g.cols) {
+      atomicMax(&red_s[1], slices8_of(st.topB[c0 + i], st.lowB[c0 + i]));
+      if (st.badB[c0 + i]) atomicOr(&red_s[2], 1);
+    }
+  }
+  __syncthreads();
+  const int LA = red_s[0], LB = red_s[1];
+  const bool elsewhere = red_s[2] || LA > S8MAX || LB > S8MAX;
+  if (tid == 0) st.flag[tile] = elsewhere ? 1 : 0;
+  if (elsewhere) return;   // uniform over the workgroup
+
+  // a wave owns 32 x 32 outputs; acc = MFMA(B fragment, A fragment, acc): the
+  // lane holds row lane % 32 and, in accumulator 4 q + e, column 8 q + 4 (lane / 32) + e
+  const int wave = tid >> 6, lane = tid & 63;
+  const int wm = (wave >> 1) * 32, wn = (wave & 1) * 32;
+  const int fr = lane & 31, fh = lane >> 5;
+
+  __int128 Z[16];
+  double C[16];
+  v16f_t acc;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) { Z[i] = 0; C[i] = 0.0; acc[i] = 0.0f; }
+
+  const int nks = static_cast<int>(kp / K8);
+  const int qmax = LA + LB - 2;
+  const int64_t nsteps = LA > 0 && LB > 0 ? static_cast<int64_t>(LA) * LB * nks : 0;
+  // step state: class q, slice s of A (t = q - s of B), stage ks
+  auto smin = [&](int q) { return q - (LB - 1) > 0 ? q - (LB - 1) : 0; };
+  auto smax = [&](int q) { return q < LA - 1 ? q : LA - 1; };
+  // the thread's two 16-byte pieces of each operand per stage: rows x0, x1 = x0 + 32, piece pc
+  const int x0 = tid >> 3, x1 = x0 + 32, pc0 = tid & 7;
+  const int la0 = x0 * 64 + 8 * (pc0 ^ sw8(x0)), la1 = x1 * 64 + 8 * (pc0 ^ sw8(x1));
+  const uint16_t* ga = SA + (r0 + x0) * kp + 8 * pc0;   // slice 0, stage 0
+  const uint16_t* gb = SB + (c0 + x0) * kp + 8 * pc0;
+  const int64_t sa_step = npa * kp, sb_step = npb * kp, half = 32 * kp;
+  uint4 ra0 = {}, ra1 = {}, rb0 = {}, rb1 = {};
+  // fragment reads: row (column) wm + fr (wn + fr), piece 2 k16 + fh of the stage
+  const int xa = wm + fr, xb = wn + fr;
+
+  int q = 0, s = 0, ks = 0;
+  if (nsteps > 0) {
+    const uint16_t* pa = ga;
+    const uint16_t* pb = gb + static_cast<int64_t>(q - s) * sb_step;
+    ra0 = *reinterpret_cast<const uint4*>(pa);
+    ra1 = *reinterpret_cast<const uint4*>(pa + half);
+    rb0 = *reinterpret_cast<const uint4*>(pb);
+    rb1 = *reinterpret_cast<const uint4*>(pb + half);
+    *reinterpret_cast<uint4*>(&Ls[0][0][la0]) = ra0;
+    *reinterpret_cast<uint4*>(&Ls[0][0][la1]) = ra1;
+    *reinterpret_cast<uint4*>(&Ls[0][1][la0]) = rb0;
+    *reinterpret_cast<uint4*>(&Ls[0][1][la1]) = rb1;
+  }
+  __syncthreads();
+  for (int64_t n = 0; n < nsteps; ++n) {
+    const int buf = static_cast<int>(n & 1);
+    // the next step's (class, slice, stage)
+    int nq = q, ns = s, nk = ks + 1;
+    if (nk == nks) {
+      nk = 0;
+      ++ns;
+      if (ns > smax(nq)) {
+        ++nq;
+        ns = smin(nq);
+      }
+    }
+    const bool more = n + 1 < nsteps;
+    if (more) {
+      const uint16_t* pa = ga + ns * sa_step + static_cast<int64_t>(nk) * K8;
+      const uint16_t* pb = gb + (nq - ns) * sb_step + static_cast<int64_t>(nk) * K8;
+      ra0 = *reinterpret_cast<const uint4*>(pa);
+      ra1 = *reinterpret_cast<const uint4*>(pa + half);
+      rb0 = *reinterpret_cast<const uint4*>(pb);
+      rb1 = *reinterpret_cast<const uint4*>(pb + half);
+    }
+    const uint16_t* la = &Ls[buf][0][0];
+    const uint16_t* lb = &Ls[buf][1][0];
+#pragma unroll
+    for (int k16 = 0; k16 < K8 / 16; ++k16) {
+      const int pc = 2 * k16 + fh;
+      const v4u_t af = *reinterpret_cast<const v4u_t*>(la + xa * 64 + 8 * (pc ^ sw8(xa)));
+      const v4u_t bf = *reinterpret_cast<const v4u_t*>(lb + xb * 64 + 8 * (pc ^ sw8(xb)));
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(v8bf_t, bf), __builtin_bit_cast(v8bf_t, af), acc,
+                                                    0, 0, 0);
+    }
+    const bool pair_end = ks == nks - 1;
+    if (pair_end || ks % CH8 == CH8 - 1) {   // an exact 256-index sum (or the pair's last, shorter one)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        C[i] = C[i] + static_cast<double>(acc[i]);
+        acc[i] = 0.0f;
+      }
+      if (pair_end && s == smax(q)) {   // the class is complete
+        const int sh = S8 * (qmax - q);
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          Z[i] += static_cast<__int128>(static_cast<int64_t>(C[i])) << sh;
+          C[i] = 0.0;
+        }
+      }
+    }
+    if (more) {
+      *reinterpret_cast<uint4*>(&Ls[buf ^ 1][0][la0]) = ra0;
+      *reinterpret_cast<uint4*>(&Ls[buf ^ 1][0][la1]) = ra1;
+      *reinterpret_cast<uint4*>(&Ls[buf ^ 1][1][la0]) = rb0;
+      *reinterpret_cast<uint4*>(&Ls[buf ^ 1][1][la1]) = rb1;
+    }
+    __syncthreads();
+    q = nq;
+    s = ns;
+    ks = nk;
+  }
+
+  using OT = typename O::T;
+  OT* out = static_cast<OT*>(g.out);
+  const int64_t r = r0 + wm + fr;
+#pragma unroll
+  for (int qq = 0; qq < 4; ++qq)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int64_t c = c0 + wn + 8 * qq + 4 * fh + e;
+      if (r < g.rows && c < g.cols) {
+        const __int128 z = Z[4 * qq + e];
+        const double v = z == 0 ? 0.0 : round_odd53(z, st.topA[r] + st.topB[c] - 2 * (S8 - 1) - S8 * qmax);
+        out[r * g.cols + c] = round_from_f64<O>(v);
+      }
+    }
+}
+
 // ---- 3. fallback ---------------------------------------------------------------
 
 // Adds the finite float64 term v to the chunks (each chunk counts 32 bits;
@@ -570,16 +824,25 @@ hipError_t launch_typed(const GemmArgs& a, int force_fallback, hipStream_t strea
   const int64_t kt = a.red + (a.bias ? 1 : 0);
   const int64_t ktp = (kt + KB - 1) / KB * KB;
   const int64_t npa = tiles_r * TILE, npb = tiles_c * TILE;
-  // workspace: int stats and flags, then (256-byte aligned) the float slices of A and B
+  // the 8-bit path for 16-bit inputs (force_fallback: 1 the superaccumulator for
+  // every tile, 2 path 2 for every tile)
+  const bool use8 = sizeof(T) == 2 && force_fallback == 0;
+  const int64_t kp8 = (kt + K8 - 1) / K8 * K8;
+  // workspace: int stats and flags, then (256-byte aligned) the float slices of A
+  // and B, then the bf16 slices of A and B
   const size_t ints = static_cast<size_t>(3 * a.rows + 3 * a.cols + tiles);
   const size_t off_slices = (ints * sizeof(int) + 255) / 256 * 256;
   const size_t sa_floats = static_cast<size_t>(2 * ktp * npa), sb_floats = static_cast<size_t>(2 * ktp * npb);
+  const size_t off8 = off_slices + ((sa_floats + sb_floats) * sizeof(float) + 255) / 256 * 256;
+  const size_t s8a = use8 ? static_cast<size_t>(S8MAX * npa * kp8) : 0, s8b = use8 ? static_cast<size_t>(S8MAX * npb * kp8) : 0;
   void* ws = nullptr;
-  hipError_t e = stream_workspace(stream, off_slices + (sa_floats + sb_floats) * sizeof(float), &ws);
+  hipError_t e = stream_workspace(stream, off8 + (s8a + s8b) * sizeof(uint16_t), &ws);
   if (e != hipSuccess) return e;
   int* p = static_cast<int*>(ws);
   float* SA = reinterpret_cast<float*>(static_cast<char*>(ws) + off_slices);
   float* SB = SA + sa_floats;
+  uint16_t* SA8 = reinterpret_cast<uint16_t*>(static_cast<char*>(ws) + off8);
+  uint16_t* SB8 = SA8 + s8a;
   Stats st;
   int* topA = p;
   int* lowA = topA + a.rows;
@@ -610,12 +873,20 @@ hipError_t launch_typed(const GemmArgs& a, int force_fallback, hipStream_t strea
   };
   if (a.A) stats(a.A, A_RC, a.rows, a.red, a.lda, topA, lowA, badA);
   stats(a.B, B_RC, a.cols, a.red, a.ldb, topB, lowB, badB);
+  if (use8) {
+    hipLaunchKernelGGL((slice8_prep_kernel<E, true, A_RC>), dim3(static_cast<unsigned>(npa / 64 * (kp8 / 64))),
+                       dim3(256), 0, stream, a, topA, a.rows, npa, kp8, SA8);
+    hipLaunchKernelGGL((slice8_prep_kernel<E, false, B_RC>), dim3(static_cast<unsigned>(npb / 64 * (kp8 / 64))),
+                       dim3(256), 0, stream, a, topB, a.cols, npb, kp8, SB8);
+    hipLaunchKernelGGL((sliced8_kernel<O>), dim3(static_cast<unsigned>(tiles)), dim3(256), 0, stream, a, st,
+                       static_cast<int>(tiles_c), SA8, SB8, npa, npb, kp8);
+  }
   hipLaunchKernelGGL((slice_prep_kernel<E, true, A_RC>), dim3(static_cast<unsigned>((ktp * npa + 255) / 256)),
                      dim3(256), 0, stream, a, topA, a.rows, npa, ktp, SA);
   hipLaunchKernelGGL((slice_prep_kernel<E, false, B_RC>), dim3(static_cast<unsigned>((ktp * npb + 255) / 256)),
                      dim3(256), 0, stream, a, topB, a.cols, npb, ktp, SB);
   hipLaunchKernelGGL((sliced_kernel<O>), dim3(static_cast<unsigned>(tiles)), dim3(256), 0, stream, a, st,
-                     static_cast<int>(tiles_c), force_fallback, SA, SB, npa, npb, ktp);
+                     static_cast<int>(tiles_c), force_fallback == 1 ? 1 : 0, SA, SB, npa, npb, ktp, use8 ? 1 : 0);
   hipLaunchKernelGGL((fallback_kernel<E, O, A_RC, B_RC>), dim3(static_cast<unsigned>(tiles)), dim3(256), 0, stream, a,
                      st, static_cast<int>(tiles_c));
   return hipGetLastError();

@@ -299,10 +299,13 @@ det_status_t det_gemm_debug_force_exact_kernel(int variant);
 det_status_t det_gemm_debug_force_db_chunk(int64_t tiles);
 
 /*
- * Test hook: 1 sends every output tile of the correctly rounded tier to its
- * per-output superaccumulator path, 0 restores the shape-and-data choice. Both
- * paths compute the exact value, so this changes speed only. DET_EINVAL for
- * other values.
+ * Test hook: the correctly rounded tier's path for every later call. 0: the
+ * shape-and-data choice (16-bit inputs: 8-bit slices on the bf16 matrix
+ * instructions where a tile's rows and columns span at most 40 bits, else the
+ * next path); 2: 23-bit slices on the float64 matrix instructions where they
+ * span at most 46 bits, else the superaccumulator; 1: the per-output
+ * superaccumulator for every tile. Every path computes the exact value, so
+ * this changes speed only. DET_EINVAL for other values.
  */
 det_status_t det_gemm_debug_force_cr_fallback(int on);
 

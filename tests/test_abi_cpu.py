@@ -113,7 +113,8 @@ def test_cr_tier_checks():
     assert L.det_gemm_dw(p, p, p, 1 << 27, 4, 4, BF16, CR, None) == -1
     assert L.det_gemm_db(p, BF16, p, 1 << 27, 4, BF16, CR, None) == -1
     assert L.det_gemm_fwd(p, p, p, None, 4, 4, 4, BF16, 3, None) == -3
-    assert dg.lib().det_gemm_debug_force_cr_fallback(2) == -1
+    assert dg.lib().det_gemm_debug_force_cr_fallback(3) == -1
+    assert dg.lib().det_gemm_debug_force_cr_fallback(-1) == -1
     assert dg.lib().det_gemm_debug_force_cr_fallback(0) == 0
 
 

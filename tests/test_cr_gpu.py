@@ -1,6 +1,7 @@
 """Correctly rounded tier on the GPU against the oracle, bit for bit: every op and dtype
-on ragged multi-tile shapes (the sliced path), the same forced through the per-output
-superaccumulator path, wide exponent ranges and non-finite values (which take that path
+on ragged multi-tile shapes (16-bit inputs: the 8-bit slices on the bf16 matrix
+instructions, and the same forced through the 23-bit float64 slices; f32: the 23-bit
+slices), the same forced through the per-output superaccumulator path, wide exponent ranges and non-finite values (which take that path
 by themselves), cancellation witnesses, permutation invariance, the column sum and f32
 outputs, and sampled rows of the GPT-2 c_fc forward."""
 import numpy as np
@@ -64,10 +65,11 @@ def test_cr_parity(op, dt):
             want = oracle.gemm_cr(op, dt, A, B, m, k, n, bias=bias)
             got = _gpu(op, dt, A, B, bias)
             assert_bits_equal(got, want, f"cr {op} {dt} {(m, k, n)} wide={wide}")
-            dg.det_gemm_debug_force_cr_fallback(1)
-            got2 = _gpu(op, dt, A, B, bias)
-            dg.det_gemm_debug_force_cr_fallback(0)
-            assert_bits_equal(got2, want, f"cr fallback {op} {dt} {(m, k, n)} wide={wide}")
+            for path in ((1, 2) if dt != "f32" else (1,)):
+                dg.det_gemm_debug_force_cr_fallback(path)
+                got2 = _gpu(op, dt, A, B, bias)
+                dg.det_gemm_debug_force_cr_fallback(0)
+                assert_bits_equal(got2, want, f"cr path {path} {op} {dt} {(m, k, n)} wide={wide}")
 
 
 def test_cr_nonfinite():
@@ -159,3 +161,34 @@ def test_cr_two_slices(dt):
     dg.det_gemm_debug_force_cr_fallback(1)
     assert_bits_equal(_gpu("fwd", dt, A, B, bias), want, f"two slices {dt}, superaccumulator")
     dg.det_gemm_debug_force_cr_fallback(0)
+
+
+@pytest.mark.parametrize("dt", ["bf16", "f16"])
+def test_cr_eight_bit_slices(dt):
+    """16-bit inputs on the 8-bit slice path: row blocks of A spanning three to five slices (one small
+    value per row), columns of B spanning more (one small row of B), a reduction of several 256-index
+    exact sums with the bias index, and in the same call a row block whose span exceeds five slices and
+    an all-zero row block, which take the other paths; bits against the oracle and against paths 1 and 2."""
+    import deterministic_invariant_gemm_det_amd as dg
+    m, k, n = 270, 1100, 150
+    Av = vals(syn.normal(1600, 0, (m, k), dt=dt), dt)
+    Bv = vals(syn.normal(1600, 1, (k, n), sigma=0.5, dt=dt), dt)
+    small = (2.0 ** -20, 2.0 ** -30, 2.0 ** -60) if dt == "bf16" else (2.0 ** -12, 2.0 ** -18, 2.0 ** -24)
+    Av[0:64, 5] = 1.5 * small[0]
+    Av[64:128, 9] = -1.25 * small[1]
+    if dt == "bf16":
+        Av[128:192, 3] = small[2]   # beyond five slices: the 23-bit path or the superaccumulator
+    Av[192:256, :] = 0.0
+    Bv[7, :] = -1.75 * small[0]
+    A, B = stor(Av, dt), stor(Bv, dt)
+    bias = syn.normal(1600, 2, (n,), sigma=0.3, dt=dt)
+    want = oracle.gemm_cr("fwd", dt, A, B, m, k, n, bias=bias)
+    assert_bits_equal(_gpu("fwd", dt, A, B, bias), want, f"8-bit slices {dt}")
+    for path in (2, 1):
+        dg.det_gemm_debug_force_cr_fallback(path)
+        assert_bits_equal(_gpu("fwd", dt, A, B, bias), want, f"8-bit slices {dt}, path {path}")
+        dg.det_gemm_debug_force_cr_fallback(0)
+    # the weight gradient of the same operands (reduction over 270 rows, reduction-major operands)
+    G = stor(vals(syn.normal(1601, 3, (m, n), dt=dt), dt), dt)
+    want = oracle.gemm_cr("dw", dt, A, G, m, k, n)
+    assert_bits_equal(_gpu("dw", dt, A, G), want, f"8-bit slices dw {dt}")
