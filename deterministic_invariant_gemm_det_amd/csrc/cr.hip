@@ -32,9 +32,10 @@
 //     least two bits narrower is one correct rounding (Boldo and Melquiond,
 //     IEEE TC 2008).
 //
-// For 16-bit inputs a faster form of 2 runs first (2b below): 8-bit slices on
-// the bf16 matrix instructions, exact in float32 over 256 reduction indices;
-// the tiles it cannot take (wider spans, non-finite values) go on to 2.
+// For 16-bit inputs faster forms of 2 run first (2b, 2c below): 7-bit slices
+// on the int8 matrix instructions (exact int32 sums), then 8-bit slices on the
+// bf16 ones (exact float32 sums over 256 reduction indices); the tiles they
+// cannot take (wider spans, non-finite values) go on to 2.
 //
 // A null A operand stands for a column of ones (the bias gradient as the
 // correctly rounded column sum of dY).
@@ -459,9 +460,261 @@ __global__ void __launch_bounds__(256) sliced_kernel(GemmArgs g, Stats st, int t
     }
 }
 
-// ---- 2b. 8-bit slices on the bf16 matrix instructions (16-bit inputs) --------
+// ---- 2b. 7-bit slices on the int8 matrix instructions (16-bit inputs) --------
 //
-// The same exact value from narrower slices on a 32x faster pipe. A value of
+// The same exact value from narrow slices on the integer matrix pipe. A value
+// of row r is cut into 7-bit slices below top_r: slice j holds the bits with
+// weights 2^(top_r - 7 j - 6) .. 2^(top_r - 7 j) as a signed integer of
+// magnitude below 2^7 (an int8). V_MFMA_I32_32X32X32_I8 multiplies and sums
+// them exactly in int32; all pairs (s, t) of one weight class q = s + t (at
+// most S7MAX of them) share one accumulator, whose sums stay below
+// 4 * 16384 * 127^2 < 2^31 over 16384 reduction indices, after which (and at
+// the end) each class goes into the int128 at 7 (qmax - q) bits up; the int128
+// is rounded as in 2. Per stage of 128 reduction indices the workgroup stages
+// every slice of its 64 rows and 64 columns once (direct-to-LDS loads) and runs
+// every slice pair from registers. A tile is taken here when its rows and
+// columns need at most S7MAX slices (spans of at most 28 bits) and all its
+// values are finite; the others are flagged for 2c.
+constexpr int S7 = 7;                // bits per slice
+constexpr int S7MAX = 5;             // slices per value on this path
+constexpr int NQ7 = 2 * S7MAX - 1;   // weight classes
+constexpr int K7 = 128;              // reduction indices per stage (128 bytes of int8 per row)
+constexpr int FL7 = 16384 / K7;      // stages per exact int32 sum
+
+__device__ inline int slices7_of(int t, int lo) { return t == NOBITS ? 0 : (t - lo + S7) / S7; }
+
+// Slice j of a value whose row or column has top bit `top`, as a signed integer.
+__device__ inline int slice7(const Parts& p, int top, int j) {
+  if (p.sig == 0) return 0;
+  const int low = top - S7 * j - (S7 - 1);
+  const int sh = p.lsb - low;
+  uint32_t part;
+  if (sh >= 0)
+    part = sh >= S7 ? 0u : ((p.sig << sh) & 0x7fu);
+  else
+    part = -sh >= 32 ? 0u : ((p.sig >> (-sh)) & 0x7fu);
+  return p.neg ? -static_cast<int>(part) : static_cast<int>(part);
+}
+
+// S[j][x][l] (int8) for j < S7MAX, x < np, l < kp: slice j of the operand value
+// (x, l) (A row x or B column x, reduction index l; the bias index as in path
+// 2), zero past the operand. A workgroup converts a 64 x 64 block, read along
+// the source's contiguous dimension through LDS and written along l.
+template <typename E, bool IS_A, bool RC>
+__global__ void __launch_bounds__(256) slice7_prep_kernel(GemmArgs g, const int* __restrict__ top, int64_t n,
+                                                          int64_t np, int64_t kp, int8_t* __restrict__ S) {
+  __shared__ uint16_t raw[64][65];
+  using T = typename E::T;
+  const int tid = threadIdx.x;
+  const int64_t lb = kp / 64;
+  const int64_t x0 = static_cast<int64_t>(blockIdx.x / lb) * 64, l0 = static_cast<int64_t>(blockIdx.x % lb) * 64;
+  const int64_t kt = g.red + (g.bias ? 1 : 0);
+  const T* X = static_cast<const T*>(IS_A ? g.A : g.B);
+  const int64_t ld = IS_A ? g.lda : g.ldb;
+  for (int i = tid; i < 64 * 64; i += 256) {
+    const int fast = i % 64, slow = i / 64;
+    const int x = RC ? slow : fast, l = RC ? fast : slow;
+    const int64_t gx = x0 + x, gl = l0 + l;
+    uint16_t v = 0;
+    if (gx < n && gl < g.red && X) {
+      const T e = RC ? X[gx * ld + gl] : X[gl * ld + gx];
+      __builtin_memcpy(&v, &e, 2);
+    }
+    raw[x][l] = v;
+  }
+  __syncthreads();
+  for (int i = tid; i < 64 * 64; i += 256) {
+    const int x = i / 64, l = i % 64;
+    const int64_t gx = x0 + x, gl = l0 + l;
+    int v[S7MAX];
+#pragma unroll
+    for (int j = 0; j < S7MAX; ++j) v[j] = 0;
+    if (gx < n && gl < kt) {
+      Parts p;
+      if (gl == g.red || (IS_A && !X)) {
+        p = IS_A ? a_at<E, RC>(g, gx, gl) : b_at<E, RC>(g, gl, gx);
+      } else {
+        T e;
+        const uint16_t bits = raw[x][l];
+        __builtin_memcpy(&e, &bits, 2);
+        p = parts<E>(e);
+      }
+      if (p.finite && p.sig) {
+        const int t = top[gx];
+#pragma unroll
+        for (int j = 0; j < S7MAX; ++j) v[j] = slice7(p, t, j);
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < S7MAX; ++j) S[(j * np + gx) * kp + gl] = static_cast<int8_t>(v[j]);
+  }
+}
+
+typedef int v4i_t __attribute__((ext_vector_type(4)));
+typedef int v16i_t __attribute__((ext_vector_type(16)));
+typedef uint32_t v4u_rs __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void lds_void_t;
+
+// buffer resource: base address, stride 0, size in bytes (reads past it return zeros)
+__device__ inline v4u_rs rsrc_of(const void* src, int64_t bytes) {
+  const uint64_t base = reinterpret_cast<uint64_t>(src);
+  return v4u_rs{static_cast<uint32_t>(base), static_cast<uint32_t>(base >> 32) & 0xffffu, static_cast<uint32_t>(bytes),
+                0x00020000u};
+}
+
+// LDS stage of one slice: 64 rows (or columns) x 128 reduction indices, row x
+// in 128 bytes with 16-byte piece p in slot p XOR sw7(x), so that the fragment
+// reads of 32 rows at one piece spread over the banks.
+__device__ inline int sw7(int x) { return ((x >> 1) & 7) ^ ((x >> 3) & 1); }
+
+template <typename O>
+__global__ void __launch_bounds__(256, 2) sliced7_kernel(GemmArgs g, Stats st, int tiles_c,
+                                                         const int8_t* __restrict__ SA, const int8_t* __restrict__ SB,
+                                                         int64_t npa, int64_t npb, int64_t kp, int64_t sa_bytes,
+                                                         int64_t sb_bytes, int enabled) {
+  // two stages (double buffered) of A slices, then B slices; the tile's slice
+  // counts are gathered in the second stage's space before any staging
+  __shared__ __attribute__((aligned(16))) int8_t Ls[2][2 * S7MAX][64 * K7];
+  int* red_s = reinterpret_cast<int*>(&Ls[1][0][0]);
+  const int tid = threadIdx.x;
+  const int tile = blockIdx.x;
+  const int64_t r0 = static_cast<int64_t>(tile / tiles_c) * TILE, c0 = static_cast<int64_t>(tile % tiles_c) * TILE;
+  if (tid < 4) red_s[tid] = 0;
+  __syncthreads();
+  {
+    const int i = tid & 63;
+    if (tid < 64 && r0 + i < g.rows) {
+      atomicMax(&red_s[0], slices7_of(st.topA[r0 + i], st.lowA[r0 + i]));
+      if (st.badA[r0 + i]) atomicOr(&red_s[2], 1);
+    } else if (tid >= 64 && tid < 128 && c0 + i < g.cols) {
+      atomicMax(&red_s[1], slices7_of(st.topB[c0 + i], st.lowB[c0 + i]));
+      if (st.badB[c0 + i]) atomicOr(&red_s[2], 1);
+    }
+  }
+  __syncthreads();
+  const int LA = red_s[0], LB = red_s[1];
+  const bool elsewhere = !enabled || red_s[2] || LA > S7MAX || LB > S7MAX;
+  if (tid == 0) st.flag[tile] = elsewhere ? 1 : 0;
+  if (elsewhere) return;   // uniform over the workgroup
+
+  // a wave owns 32 x 32 outputs; acc = MFMA(B fragment, A fragment, acc): the
+  // lane holds row lane % 32 and, in accumulator 4 q + e, column 8 q + 4 (lane / 32) + e
+  const int wave = tid >> 6, lane = tid & 63;
+  const int wm = (wave >> 1) * 32, wn = (wave & 1) * 32;
+  const int fr = lane & 31, fh = lane >> 5;
+  const int xa = wm + fr, xb = wn + fr;
+
+  __int128 Z[16];
+  v16i_t acc[NQ7];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) Z[i] = 0;
+#pragma unroll
+  for (int q = 0; q < NQ7; ++q)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) acc[q][i] = 0;
+
+  const int nks = (LA > 0 && LB > 0) ? static_cast<int>(kp / K7) : 0;
+  const int qmax = LA + LB - 2;
+  // Staging by direct-to-LDS buffer loads: a slice's 64 x 128 stage is eight 1 KB
+  // wave instructions; instruction gi puts rows 8 gi .. 8 gi + 7 in place, lane l
+  // fetching the piece that belongs at byte 16 l (row 8 gi + l / 8, slot l % 8).
+  // The (LA + LB) x 8 instructions of a stage go round the four waves.
+  const v4u_rs rsa = rsrc_of(SA, sa_bytes), rsb = rsrc_of(SB, sb_bytes);
+  const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+  const int nins = (LA + LB) * 8;
+  const uint32_t lds0 = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_void_t*)&Ls[0][0]));
+
+  // request stage ks of every slice into buffer b
+  auto request = [&](int ks, int b) {
+    for (int gf = wave_u; gf < nins; gf += 4) {
+      const int si = gf >> 3, gi = gf & 7;
+      const bool is_a = si < LA;
+      const int sl = is_a ? si : si - LA;                       // slice of A or of B
+      const int slot = is_a ? sl : S7MAX + sl;                  // its LDS stage
+      const int x = 8 * gi + (lane >> 3);
+      const int pc = (lane & 7) ^ sw7(x);
+      const int64_t byte = (sl * (is_a ? npa : npb) + (is_a ? r0 : c0) + x) * kp + static_cast<int64_t>(ks) * K7 + 16 * pc;
+      const uint32_t off = static_cast<uint32_t>(byte);
+      const uint32_t m0 = lds0 + static_cast<uint32_t>(b * 2 * S7MAX + slot) * (64 * K7) + 1024u * static_cast<uint32_t>(gi);
+      if (is_a)
+        __asm__ volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+                         :
+                         : "s"(m0), "v"(off), "s"(rsa)
+                         : "memory", "m0");
+      else
+        __asm__ volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+                         :
+                         : "s"(m0), "v"(off), "s"(rsb)
+                         : "memory", "m0");
+    }
+  };
+
+  __syncthreads();   // every wave has read the slice counts (their space is the second buffer)
+  if (nks > 0) request(0, 0);
+  __builtin_amdgcn_s_waitcnt(0);   // this wave's loads are in LDS
+  __asm__ volatile("" ::: "memory");
+  __syncthreads();
+  for (int ks = 0; ks < nks; ++ks) {
+    const int buf = ks & 1;
+    // the next stage goes into the other buffer, read last in the previous stage
+    if (ks + 1 < nks) request(ks + 1, buf ^ 1);
+    const int8_t* lsb = &Ls[buf][0][0];
+#pragma unroll
+    for (int k32 = 0; k32 < K7 / 32; ++k32) {
+      // A and B use the same (lane, byte) -> reduction index map, so the products pair up
+      const int pc = 2 * k32 + fh;
+      const int oa = xa * K7 + 16 * (pc ^ sw7(xa)), ob = xb * K7 + 16 * (pc ^ sw7(xb));
+      v4i_t af[S7MAX];
+#pragma unroll
+      for (int s = 0; s < S7MAX; ++s)
+        if (s < LA) af[s] = *reinterpret_cast<const v4i_t*>(lsb + s * (64 * K7) + oa);
+#pragma unroll
+      for (int t = 0; t < S7MAX; ++t) {
+        if (t < LB) {
+          const v4i_t bf = *reinterpret_cast<const v4i_t*>(lsb + (S7MAX + t) * (64 * K7) + ob);
+#pragma unroll
+          for (int s = 0; s < S7MAX; ++s)
+            if (s < LA) acc[s + t] = __builtin_amdgcn_mfma_i32_32x32x32_i8(bf, af[s], acc[s + t], 0, 0, 0);
+        }
+      }
+    }
+    if (ks % FL7 == FL7 - 1 || ks == nks - 1) {   // the exact int32 sums of every class
+#pragma unroll
+      for (int q = 0; q < NQ7; ++q) {
+        if (q <= qmax) {
+          const int sh = S7 * (qmax - q);
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            Z[i] += static_cast<__int128>(acc[q][i]) << sh;
+            acc[q][i] = 0;
+          }
+        }
+      }
+    }
+    __builtin_amdgcn_s_waitcnt(0);   // this wave's requests for the next stage are in LDS
+    __asm__ volatile("" ::: "memory");
+    __syncthreads();                 // and everyone's; every wave is done reading this stage
+  }
+
+  using OT = typename O::T;
+  OT* out = static_cast<OT*>(g.out);
+  const int64_t r = r0 + wm + fr;
+#pragma unroll
+  for (int qq = 0; qq < 4; ++qq)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int64_t c = c0 + wn + 8 * qq + 4 * fh + e;
+      if (r < g.rows && c < g.cols) {
+        const __int128 z = Z[4 * qq + e];
+        const double v = z == 0 ? 0.0 : round_odd53(z, st.topA[r] + st.topB[c] - 2 * (S7 - 1) - S7 * qmax);
+        out[r * g.cols + c] = round_from_f64<O>(v);
+      }
+    }
+}
+
+// ---- 2c. 8-bit slices, one pair at a time (16-bit inputs) --------------------
+//
+// The tiles that 2b leaves, from 8-bit slices on the bf16 pipe. A value of
 // row r is cut into 8-bit slices below top_r: slice j holds the bits with
 // weights 2^(top_r - 8 j - 7) .. 2^(top_r - 8 j) as a signed integer of
 // magnitude below 2^8, which bf16 holds exactly. For one slice pair (s, t) the
@@ -471,9 +724,9 @@ __global__ void __launch_bounds__(256) sliced_kernel(GemmArgs g, Stats st, int t
 // in. Each 256-index sum is added to a float64 per weight class q = s + t (an
 // integer below 2^53 for any reduction this tier takes); at the end of a class
 // the float64 goes into the int128 at 8 (qmax - q) bits up, and the int128 is
-// rounded as in 2. A tile is taken here when its rows and columns need at most
-// S8MAX slices (spans of at most 40 bits) and all its values are finite; the
-// others are flagged for path 2.
+// rounded as in 2. A tile flagged by 2b is taken here when its rows and columns
+// need at most S8MAX slices (spans of at most 40 bits) and all its values are
+// finite; the others stay flagged for path 2.
 constexpr int S8 = 8;           // bits per slice
 constexpr int S8MAX = 5;        // slices per value on this path
 constexpr int K8 = 64;          // reduction indices per stage
@@ -572,6 +825,7 @@ __global__ void __launch_bounds__(256) sliced8_kernel(GemmArgs g, Stats st, int 
   __shared__ int red_s[4];
   const int tid = threadIdx.x;
   const int tile = blockIdx.x;
+  if (!st.flag[tile]) return;   // finished by 2b (uniform over the workgroup)
   const int64_t r0 = static_cast<int64_t>(tile / tiles_c) * TILE, c0 = static_cast<int64_t>(tile % tiles_c) * TILE;
   if (tid < 4) red_s[tid] = 0;
   __syncthreads();
@@ -828,6 +1082,7 @@ hipError_t launch_typed(const GemmArgs& a, int force_fallback, hipStream_t strea
   // every tile, 2 path 2 for every tile)
   const bool use8 = sizeof(T) == 2 && force_fallback == 0;
   const int64_t kp8 = (kt + K8 - 1) / K8 * K8;
+  const int64_t kp7 = (kt + K7 - 1) / K7 * K7;
   // workspace: int stats and flags, then (256-byte aligned) the float slices of A
   // and B, then the bf16 slices of A and B
   const size_t ints = static_cast<size_t>(3 * a.rows + 3 * a.cols + tiles);
@@ -835,14 +1090,18 @@ hipError_t launch_typed(const GemmArgs& a, int force_fallback, hipStream_t strea
   const size_t sa_floats = static_cast<size_t>(2 * ktp * npa), sb_floats = static_cast<size_t>(2 * ktp * npb);
   const size_t off8 = off_slices + ((sa_floats + sb_floats) * sizeof(float) + 255) / 256 * 256;
   const size_t s8a = use8 ? static_cast<size_t>(S8MAX * npa * kp8) : 0, s8b = use8 ? static_cast<size_t>(S8MAX * npb * kp8) : 0;
+  const size_t off7 = off8 + ((s8a + s8b) * sizeof(uint16_t) + 255) / 256 * 256;
+  const size_t s7a = use8 ? static_cast<size_t>(S7MAX * npa * kp7) : 0, s7b = use8 ? static_cast<size_t>(S7MAX * npb * kp7) : 0;
   void* ws = nullptr;
-  hipError_t e = stream_workspace(stream, off8 + (s8a + s8b) * sizeof(uint16_t), &ws);
+  hipError_t e = stream_workspace(stream, off7 + s7a + s7b, &ws);
   if (e != hipSuccess) return e;
   int* p = static_cast<int*>(ws);
   float* SA = reinterpret_cast<float*>(static_cast<char*>(ws) + off_slices);
   float* SB = SA + sa_floats;
   uint16_t* SA8 = reinterpret_cast<uint16_t*>(static_cast<char*>(ws) + off8);
   uint16_t* SB8 = SA8 + s8a;
+  int8_t* SA7 = reinterpret_cast<int8_t*>(static_cast<char*>(ws) + off7);
+  int8_t* SB7 = SA7 + s7a;
   Stats st;
   int* topA = p;
   int* lowA = topA + a.rows;
@@ -874,6 +1133,15 @@ hipError_t launch_typed(const GemmArgs& a, int force_fallback, hipStream_t strea
   if (a.A) stats(a.A, A_RC, a.rows, a.red, a.lda, topA, lowA, badA);
   stats(a.B, B_RC, a.cols, a.red, a.ldb, topB, lowB, badB);
   if (use8) {
+    // 2b: the direct loads address the slices with 32-bit byte offsets
+    const int on7 = s7a < (size_t(1) << 31) && s7b < (size_t(1) << 31) ? 1 : 0;
+    hipLaunchKernelGGL((slice7_prep_kernel<E, true, A_RC>), dim3(static_cast<unsigned>(npa / 64 * (kp7 / 64))),
+                       dim3(256), 0, stream, a, topA, a.rows, npa, kp7, SA7);
+    hipLaunchKernelGGL((slice7_prep_kernel<E, false, B_RC>), dim3(static_cast<unsigned>(npb / 64 * (kp7 / 64))),
+                       dim3(256), 0, stream, a, topB, a.cols, npb, kp7, SB7);
+    hipLaunchKernelGGL((sliced7_kernel<O>), dim3(static_cast<unsigned>(tiles)), dim3(256), 0, stream, a, st,
+                       static_cast<int>(tiles_c), SA7, SB7, npa, npb, kp7, static_cast<int64_t>(s7a),
+                       static_cast<int64_t>(s7b), on7);
     hipLaunchKernelGGL((slice8_prep_kernel<E, true, A_RC>), dim3(static_cast<unsigned>(npa / 64 * (kp8 / 64))),
                        dim3(256), 0, stream, a, topA, a.rows, npa, kp8, SA8);
     hipLaunchKernelGGL((slice8_prep_kernel<E, false, B_RC>), dim3(static_cast<unsigned>(npb / 64 * (kp8 / 64))),
