@@ -568,7 +568,7 @@ __device__ inline v4u_rs rsrc_of(const void* src, int64_t bytes) {
 __device__ inline int sw7(int x) { return ((x >> 1) & 7) ^ ((x >> 3) & 1); }
 
 template <typename O>
-__global__ void __launch_bounds__(256, 2) sliced7_kernel(GemmArgs g, Stats st, int tiles_c,
+__global__ void __launch_bounds__(512, 2) sliced7_kernel(GemmArgs g, Stats st, int tiles_c,
                                                          const int8_t* __restrict__ SA, const int8_t* __restrict__ SB,
                                                          int64_t npa, int64_t npb, int64_t kp, int64_t sa_bytes,
                                                          int64_t sb_bytes, int enabled) {
@@ -597,36 +597,38 @@ __global__ void __launch_bounds__(256, 2) sliced7_kernel(GemmArgs g, Stats st, i
   if (tid == 0) st.flag[tile] = elsewhere ? 1 : 0;
   if (elsewhere) return;   // uniform over the workgroup
 
-  // a wave owns 32 x 32 outputs; acc = MFMA(B fragment, A fragment, acc): the
-  // lane holds row lane % 32 and, in accumulator 4 q + e, column 8 q + 4 (lane / 32) + e
+  // Eight waves in a 4 x 2 grid, 16 x 32 outputs each as two 16 x 16 blocks.
+  // acc = MFMA(B fragment, A fragment, acc) with V_MFMA_I32_16X16X64_I8: the lane
+  // holds row lane % 16 and, in accumulator e of block b, column 16 b + 4 (lane / 16) + e.
+  // Fragments: lane l holds 16 bytes of its row (column) at reduction indices
+  // 64 k64 + 16 (l / 16) .. + 15, the same map for A and B, so the products pair up.
   const int wave = tid >> 6, lane = tid & 63;
-  const int wm = (wave >> 1) * 32, wn = (wave & 1) * 32;
-  const int fr = lane & 31, fh = lane >> 5;
-  const int xa = wm + fr, xb = wn + fr;
+  const int wm = (wave >> 1) * 16, wn = (wave & 1) * 32;
+  const int fr = lane & 15, fq = lane >> 4;
+  const int xa = wm + fr, xb0 = wn + fr, xb1 = wn + 16 + fr;
 
-  __int128 Z[16];
-  v16i_t acc[NQ7];
+  __int128 Z[8];
+  v4i_t acc[NQ7][2];
 #pragma unroll
-  for (int i = 0; i < 16; ++i) Z[i] = 0;
+  for (int i = 0; i < 8; ++i) Z[i] = 0;
 #pragma unroll
   for (int q = 0; q < NQ7; ++q)
 #pragma unroll
-    for (int i = 0; i < 16; ++i) acc[q][i] = 0;
+    for (int b = 0; b < 2; ++b) acc[q][b] = v4i_t{0, 0, 0, 0};
 
   const int nks = (LA > 0 && LB > 0) ? static_cast<int>(kp / K7) : 0;
   const int qmax = LA + LB - 2;
   // Staging by direct-to-LDS buffer loads: a slice's 64 x 128 stage is eight 1 KB
   // wave instructions; instruction gi puts rows 8 gi .. 8 gi + 7 in place, lane l
   // fetching the piece that belongs at byte 16 l (row 8 gi + l / 8, slot l % 8).
-  // The (LA + LB) x 8 instructions of a stage go round the four waves.
+  // The (LA + LB) x 8 instructions of a stage go round the eight waves.
   const v4u_rs rsa = rsrc_of(SA, sa_bytes), rsb = rsrc_of(SB, sb_bytes);
   const int wave_u = __builtin_amdgcn_readfirstlane(wave);
   const int nins = (LA + LB) * 8;
   const uint32_t lds0 = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_void_t*)&Ls[0][0]));
-
   // request stage ks of every slice into buffer b
   auto request = [&](int ks, int b) {
-    for (int gf = wave_u; gf < nins; gf += 4) {
+    for (int gf = wave_u; gf < nins; gf += 8) {
       const int si = gf >> 3, gi = gf & 7;
       const bool is_a = si < LA;
       const int sl = is_a ? si : si - LA;                       // slice of A or of B
@@ -660,10 +662,10 @@ __global__ void __launch_bounds__(256, 2) sliced7_kernel(GemmArgs g, Stats st, i
     if (ks + 1 < nks) request(ks + 1, buf ^ 1);
     const int8_t* lsb = &Ls[buf][0][0];
 #pragma unroll
-    for (int k32 = 0; k32 < K7 / 32; ++k32) {
-      // A and B use the same (lane, byte) -> reduction index map, so the products pair up
-      const int pc = 2 * k32 + fh;
-      const int oa = xa * K7 + 16 * (pc ^ sw7(xa)), ob = xb * K7 + 16 * (pc ^ sw7(xb));
+    for (int k64 = 0; k64 < K7 / 64; ++k64) {
+      const int pc = 4 * k64 + fq;
+      const int oa = xa * K7 + 16 * (pc ^ sw7(xa));
+      const int ob0 = xb0 * K7 + 16 * (pc ^ sw7(xb0)), ob1 = xb1 * K7 + 16 * (pc ^ sw7(xb1));
       v4i_t af[S7MAX];
 #pragma unroll
       for (int s = 0; s < S7MAX; ++s)
@@ -671,10 +673,15 @@ __global__ void __launch_bounds__(256, 2) sliced7_kernel(GemmArgs g, Stats st, i
 #pragma unroll
       for (int t = 0; t < S7MAX; ++t) {
         if (t < LB) {
-          const v4i_t bf = *reinterpret_cast<const v4i_t*>(lsb + (S7MAX + t) * (64 * K7) + ob);
+          const int8_t* bt = lsb + (S7MAX + t) * (64 * K7);
+          const v4i_t bf0 = *reinterpret_cast<const v4i_t*>(bt + ob0);
+          const v4i_t bf1 = *reinterpret_cast<const v4i_t*>(bt + ob1);
 #pragma unroll
           for (int s = 0; s < S7MAX; ++s)
-            if (s < LA) acc[s + t] = __builtin_amdgcn_mfma_i32_32x32x32_i8(bf, af[s], acc[s + t], 0, 0, 0);
+            if (s < LA) {
+              acc[s + t][0] = __builtin_amdgcn_mfma_i32_16x16x64_i8(bf0, af[s], acc[s + t][0], 0, 0, 0);
+              acc[s + t][1] = __builtin_amdgcn_mfma_i32_16x16x64_i8(bf1, af[s], acc[s + t][1], 0, 0, 0);
+            }
         }
       }
     }
@@ -684,10 +691,12 @@ __global__ void __launch_bounds__(256, 2) sliced7_kernel(GemmArgs g, Stats st, i
         if (q <= qmax) {
           const int sh = S7 * (qmax - q);
 #pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            Z[i] += static_cast<__int128>(acc[q][i]) << sh;
-            acc[q][i] = 0;
-          }
+          for (int b = 0; b < 2; ++b)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              Z[4 * b + e] += static_cast<__int128>(acc[q][b][e]) << sh;
+              acc[q][b][e] = 0;
+            }
         }
       }
     }
@@ -700,12 +709,12 @@ __global__ void __launch_bounds__(256, 2) sliced7_kernel(GemmArgs g, Stats st, i
   OT* out = static_cast<OT*>(g.out);
   const int64_t r = r0 + wm + fr;
 #pragma unroll
-  for (int qq = 0; qq < 4; ++qq)
+  for (int b = 0; b < 2; ++b)
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      const int64_t c = c0 + wn + 8 * qq + 4 * fh + e;
+      const int64_t c = c0 + wn + 16 * b + 4 * fq + e;
       if (r < g.rows && c < g.cols) {
-        const __int128 z = Z[4 * qq + e];
+        const __int128 z = Z[4 * b + e];
         const double v = z == 0 ? 0.0 : round_odd53(z, st.topA[r] + st.topB[c] - 2 * (S7 - 1) - S7 * qmax);
         out[r * g.cols + c] = round_from_f64<O>(v);
       }
@@ -1139,7 +1148,7 @@ hipError_t launch_typed(const GemmArgs& a, int force_fallback, hipStream_t strea
                        dim3(256), 0, stream, a, topA, a.rows, npa, kp7, SA7);
     hipLaunchKernelGGL((slice7_prep_kernel<E, false, B_RC>), dim3(static_cast<unsigned>(npb / 64 * (kp7 / 64))),
                        dim3(256), 0, stream, a, topB, a.cols, npb, kp7, SB7);
-    hipLaunchKernelGGL((sliced7_kernel<O>), dim3(static_cast<unsigned>(tiles)), dim3(256), 0, stream, a, st,
+    hipLaunchKernelGGL((sliced7_kernel<O>), dim3(static_cast<unsigned>(tiles)), dim3(512), 0, stream, a, st,
                        static_cast<int>(tiles_c), SA7, SB7, npa, npb, kp7, static_cast<int64_t>(s7a),
                        static_cast<int64_t>(s7b), on7);
     hipLaunchKernelGGL((slice8_prep_kernel<E, true, A_RC>), dim3(static_cast<unsigned>(npa / 64 * (kp8 / 64))),
