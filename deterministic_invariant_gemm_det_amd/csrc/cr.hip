@@ -216,8 +216,10 @@ __global__ void __launch_bounds__(256) stats_init_kernel(int64_t rows, int64_t c
                                                          int* __restrict__ lowA, int* __restrict__ badA,
                                                          int* __restrict__ topB, int* __restrict__ lowB,
                                                          int* __restrict__ badB,
-                                                         const typename E::T* __restrict__ bias, int ones_a) {
+                                                         const typename E::T* __restrict__ bias, int ones_a,
+                                                         int* __restrict__ left) {
   const int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (i < 2) left[i] = 0;
   if (i < rows) {
     topA[i] = (bias || ones_a) ? 0 : NOBITS;   // the value 1 at the bias index, or A all ones
     lowA[i] = (bias || ones_a) ? 0 : NOLOW;
@@ -268,7 +270,8 @@ __device__ inline Parts b_at(const GemmArgs& g, int64_t l, int64_t c) {
 
 struct Stats {
   const int *topA, *lowA, *badA, *topB, *lowB, *badB;
-  int* flag;   // per tile: 1 when the fallback must finish it
+  int* flag;   // per tile: 1 when the next path must finish it
+  int* left;   // tiles left by the int8 path [0] and by the bf16 path [1]
 };
 
 // ---- 2. sliced tiles ---------------------------------------------------------
@@ -281,7 +284,9 @@ struct Stats {
 // the fallback, so two suffice here.
 template <typename E, bool IS_A, bool RC>
 __global__ void __launch_bounds__(256) slice_prep_kernel(GemmArgs g, const int* __restrict__ top, int64_t n,
-                                                         int64_t np, int64_t ktp, float* __restrict__ S) {
+                                                         int64_t np, int64_t ktp, float* __restrict__ S,
+                                                         const int* __restrict__ need) {
+  if (need && *need == 0) return;   // the 16-bit paths left no tile (uniform over the grid)
   const int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
   if (i >= ktp * np) return;
   const int64_t l = i / np, x = i % np;
@@ -594,7 +599,10 @@ __global__ void __launch_bounds__(512, 2) sliced7_kernel(GemmArgs g, Stats st, i
   __syncthreads();
   const int LA = red_s[0], LB = red_s[1];
   const bool elsewhere = !enabled || red_s[2] || LA > S7MAX || LB > S7MAX;
-  if (tid == 0) st.flag[tile] = elsewhere ? 1 : 0;
+  if (tid == 0) {
+    st.flag[tile] = elsewhere ? 1 : 0;
+    if (elsewhere) atomicAdd(&st.left[0], 1);
+  }
   if (elsewhere) return;   // uniform over the workgroup
 
   // Eight waves in a 4 x 2 grid, 16 x 32 outputs each as two 16 x 16 blocks.
@@ -767,8 +775,10 @@ __device__ inline uint16_t bf16_of_int(int v) {
 // along the source's contiguous dimension through LDS and written along l.
 template <typename E, bool IS_A, bool RC>
 __global__ void __launch_bounds__(256) slice8_prep_kernel(GemmArgs g, const int* __restrict__ top, int64_t n,
-                                                          int64_t np, int64_t kp, uint16_t* __restrict__ S) {
+                                                          int64_t np, int64_t kp, uint16_t* __restrict__ S,
+                                                          const int* __restrict__ need) {
   __shared__ uint16_t raw[64][65];
+  if (*need == 0) return;   // the int8 path left no tile (uniform over the grid)
   using T = typename E::T;
   const int tid = threadIdx.x;
   const int64_t lb = kp / 64;
@@ -851,7 +861,10 @@ __global__ void __launch_bounds__(256) sliced8_kernel(GemmArgs g, Stats st, int 
   __syncthreads();
   const int LA = red_s[0], LB = red_s[1];
   const bool elsewhere = red_s[2] || LA > S8MAX || LB > S8MAX;
-  if (tid == 0) st.flag[tile] = elsewhere ? 1 : 0;
+  if (tid == 0) {
+    st.flag[tile] = elsewhere ? 1 : 0;
+    if (elsewhere) atomicAdd(&st.left[1], 1);
+  }
   if (elsewhere) return;   // uniform over the workgroup
 
   // a wave owns 32 x 32 outputs; acc = MFMA(B fragment, A fragment, acc): the
@@ -1094,7 +1107,7 @@ hipError_t launch_typed(const GemmArgs& a, int force_fallback, hipStream_t strea
   const int64_t kp7 = (kt + K7 - 1) / K7 * K7;
   // workspace: int stats and flags, then (256-byte aligned) the float slices of A
   // and B, then the bf16 slices of A and B
-  const size_t ints = static_cast<size_t>(3 * a.rows + 3 * a.cols + tiles);
+  const size_t ints = static_cast<size_t>(3 * a.rows + 3 * a.cols + tiles + 2);
   const size_t off_slices = (ints * sizeof(int) + 255) / 256 * 256;
   const size_t sa_floats = static_cast<size_t>(2 * ktp * npa), sb_floats = static_cast<size_t>(2 * ktp * npb);
   const size_t off8 = off_slices + ((sa_floats + sb_floats) * sizeof(float) + 255) / 256 * 256;
@@ -1119,14 +1132,16 @@ hipError_t launch_typed(const GemmArgs& a, int force_fallback, hipStream_t strea
   int* lowB = topB + a.cols;
   int* badB = lowB + a.cols;
   int* flag = badB + a.cols;
+  int* left = flag + tiles;
   st.topA = topA; st.lowA = lowA; st.badA = badA;
   st.topB = topB; st.lowB = lowB; st.badB = badB;
   st.flag = flag;
+  st.left = left;
   const int64_t nmax = a.rows > a.cols ? a.rows : a.cols;
   hipLaunchKernelGGL((stats_init_kernel<E>), dim3(static_cast<unsigned>((nmax + 255) / 256)), dim3(256), 0, stream,
                      a.rows, a.cols, topA, lowA, badA, topB, lowB, badB, static_cast<const T*>(a.bias),
-                     a.A ? 0 : 1);
-  const int64_t strip = 256;
+                     a.A ? 0 : 1, left);
+  const int64_t strip = 256, strip_cols = 32;   // more strips for per-column stats (one thread each)
   auto stats = [&](const void* X, bool rc, int64_t n_idx, int64_t red, int64_t ld, int* top, int* low, int* bad) {
     // the array is [n_idx][ld] (rc) or [red][ld] (!rc); ld is its contiguous length
     if (rc) {
@@ -1134,9 +1149,9 @@ hipError_t launch_typed(const GemmArgs& a, int force_fallback, hipStream_t strea
       hipLaunchKernelGGL((stats_kernel<E, true>), dim3(static_cast<unsigned>((waves * 64 + 255) / 256)), dim3(256), 0,
                          stream, static_cast<const T*>(X), n_idx, ld, strip, top, low, bad);
     } else {
-      const int64_t threads = ld * ((red + strip - 1) / strip);
+      const int64_t threads = ld * ((red + strip_cols - 1) / strip_cols);
       hipLaunchKernelGGL((stats_kernel<E, false>), dim3(static_cast<unsigned>((threads + 255) / 256)), dim3(256), 0,
-                         stream, static_cast<const T*>(X), red, ld, strip, top, low, bad);
+                         stream, static_cast<const T*>(X), red, ld, strip_cols, top, low, bad);
     }
   };
   if (a.A) stats(a.A, A_RC, a.rows, a.red, a.lda, topA, lowA, badA);
@@ -1152,16 +1167,16 @@ hipError_t launch_typed(const GemmArgs& a, int force_fallback, hipStream_t strea
                        static_cast<int>(tiles_c), SA7, SB7, npa, npb, kp7, static_cast<int64_t>(s7a),
                        static_cast<int64_t>(s7b), on7);
     hipLaunchKernelGGL((slice8_prep_kernel<E, true, A_RC>), dim3(static_cast<unsigned>(npa / 64 * (kp8 / 64))),
-                       dim3(256), 0, stream, a, topA, a.rows, npa, kp8, SA8);
+                       dim3(256), 0, stream, a, topA, a.rows, npa, kp8, SA8, left);
     hipLaunchKernelGGL((slice8_prep_kernel<E, false, B_RC>), dim3(static_cast<unsigned>(npb / 64 * (kp8 / 64))),
-                       dim3(256), 0, stream, a, topB, a.cols, npb, kp8, SB8);
+                       dim3(256), 0, stream, a, topB, a.cols, npb, kp8, SB8, left);
     hipLaunchKernelGGL((sliced8_kernel<O>), dim3(static_cast<unsigned>(tiles)), dim3(256), 0, stream, a, st,
                        static_cast<int>(tiles_c), SA8, SB8, npa, npb, kp8);
   }
   hipLaunchKernelGGL((slice_prep_kernel<E, true, A_RC>), dim3(static_cast<unsigned>((ktp * npa + 255) / 256)),
-                     dim3(256), 0, stream, a, topA, a.rows, npa, ktp, SA);
+                     dim3(256), 0, stream, a, topA, a.rows, npa, ktp, SA, use8 ? left + 1 : nullptr);
   hipLaunchKernelGGL((slice_prep_kernel<E, false, B_RC>), dim3(static_cast<unsigned>((ktp * npb + 255) / 256)),
-                     dim3(256), 0, stream, a, topB, a.cols, npb, ktp, SB);
+                     dim3(256), 0, stream, a, topB, a.cols, npb, ktp, SB, use8 ? left + 1 : nullptr);
   hipLaunchKernelGGL((sliced_kernel<O>), dim3(static_cast<unsigned>(tiles)), dim3(256), 0, stream, a, st,
                      static_cast<int>(tiles_c), force_fallback == 1 ? 1 : 0, SA, SB, npa, npb, ktp, use8 ? 1 : 0);
   hipLaunchKernelGGL((fallback_kernel<E, O, A_RC, B_RC>), dim3(static_cast<unsigned>(tiles)), dim3(256), 0, stream, a,
