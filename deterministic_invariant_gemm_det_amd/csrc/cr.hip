@@ -572,6 +572,176 @@ __device__ inline v4u_rs rsrc_of(const void* src, int64_t bytes) {
 // reads of 32 rows at one piece spread over the banks.
 __device__ inline int sw7(int x) { return ((x >> 1) & 7) ^ ((x >> 3) & 1); }
 
+typedef int8_t Ls7_t[2][2 * S7MAX][64 * K7];
+
+// One tile whose rows need LA and columns LB slices (both at least 1), with
+// the counts fixed at compile time so that the fragment reads and the LA x LB
+// matrix instructions of a step are one straight block the compiler can
+// schedule freely. Eight waves in a 4 x 2 grid, 16 x 32 outputs each as two
+// 16 x 16 blocks: acc = MFMA(B fragment, A fragment, acc) with
+// V_MFMA_I32_16X16X64_I8, the lane holding row lane % 16 and, in accumulator e
+// of block b, column 16 b + 4 (lane / 16) + e. Fragments: lane l holds 16 bytes
+// of its row (column) at reduction indices 64 k64 + 16 (l / 16) .. + 15, the
+// same map for A and B, so the products pair up.
+template <typename O, int LA, int LB>
+__device__ __forceinline__ void sliced7_tile(const GemmArgs& g, const Stats& st, Ls7_t& Ls, int64_t r0, int64_t c0,
+                                             const int8_t* SA, const int8_t* SB, int64_t npa, int64_t npb, int64_t kp,
+                                             int64_t sa_bytes, int64_t sb_bytes) {
+  constexpr int NQ = LA + LB - 1;   // weight classes q = s + t
+  constexpr int QMAX = NQ - 1;
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6, lane = tid & 63;
+  const int wm = (wave >> 1) * 16, wn = (wave & 1) * 32;
+  const int fr = lane & 15, fq = lane >> 4;
+  const int xa = wm + fr, xb0 = wn + fr, xb1 = wn + 16 + fr;
+  // the output scales' top bits, fetched now so that their latency hides behind the loop
+  const int64_t ro = r0 + wm + fr;
+  const int ta = ro < g.rows ? st.topA[ro] : 0;
+  int tb[2][4];
+#pragma unroll
+  for (int b = 0; b < 2; ++b)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int64_t c = c0 + wn + 16 * b + 4 * fq + e;
+      tb[b][e] = c < g.cols ? st.topB[c] : 0;
+    }
+
+  __int128 Z[8];
+  v4i_t acc[NQ][2];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) Z[i] = 0;
+#pragma unroll
+  for (int q = 0; q < NQ; ++q)
+#pragma unroll
+    for (int b = 0; b < 2; ++b) acc[q][b] = v4i_t{0, 0, 0, 0};
+  const int nks = static_cast<int>(kp / K7);
+
+  // Staging by direct-to-LDS buffer loads: a slice's 64 x 128 stage is eight 1 KB
+  // wave instructions, instruction gi putting rows 8 gi .. 8 gi + 7 in place, lane
+  // l fetching the piece that belongs at byte 16 l (row 8 gi + l / 8, slot l % 8).
+  // The lane's byte offset depends on gi only; the slice and the stage go into
+  // the scalar offset.
+  const v4u_rs rsa = rsrc_of(SA, sa_bytes), rsb = rsrc_of(SB, sb_bytes);
+  const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+  const uint32_t sla = static_cast<uint32_t>(npa * kp), slb = static_cast<uint32_t>(npb * kp);
+  const uint32_t lds0 = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_void_t*)&Ls[0][0][0]));
+  auto voff = [&](int64_t base, int gi) {
+    const int x = 8 * gi + (lane >> 3);
+    return static_cast<uint32_t>((base + x) * kp + 16 * ((lane & 7) ^ sw7(x)));
+  };
+  // instruction gi of slice j (A slices, then B slices) of stage ks into buffer b
+  auto issue = [&](int j, int gi, uint32_t va, uint32_t vb, int ks, int b) {
+    const bool is_a = j < LA;
+    const int sl = is_a ? j : j - LA;
+    const uint32_t so = static_cast<uint32_t>(sl) * (is_a ? sla : slb) + static_cast<uint32_t>(ks) * K7;
+    const uint32_t m0 =
+        lds0 + static_cast<uint32_t>(b * 2 * S7MAX + (is_a ? sl : S7MAX + sl)) * (64 * K7) + 1024u * static_cast<uint32_t>(gi);
+    if (is_a)
+      __asm__ volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
+                       :
+                       : "s"(m0), "v"(va), "s"(rsa), "s"(so)
+                       : "memory", "m0");
+    else
+      __asm__ volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
+                       :
+                       : "s"(m0), "v"(vb), "s"(rsb), "s"(so)
+                       : "memory", "m0");
+  };
+  // The first stage: wave w issues instruction w of every slice. The later ones:
+  // waves 0 .. 3 (one on each SIMD) issue instructions 2 w and 2 w + 1 of every
+  // slice of stage ks + 1 at the start of stage ks, while the other wave on
+  // their SIMD goes straight to the matrix work.
+  const bool loader = wave_u < 4;
+  const uint32_t va0 = voff(r0, 2 * wave_u), va1 = voff(r0, 2 * wave_u + 1);
+  const uint32_t vb0 = voff(c0, 2 * wave_u), vb1 = voff(c0, 2 * wave_u + 1);
+
+  __syncthreads();   // every wave has read the slice counts (their space is the second buffer)
+  if (nks > 0) {
+    const uint32_t va = voff(r0, wave_u), vb = voff(c0, wave_u);
+#pragma unroll
+    for (int j = 0; j < LA + LB; ++j) issue(j, wave_u, va, vb, 0, 0);
+  }
+  __builtin_amdgcn_s_waitcnt(0);   // this wave's loads are in LDS
+  __asm__ volatile("" ::: "memory");
+  __syncthreads();
+  for (int ks = 0; ks < nks; ++ks) {
+    const int buf = ks & 1;
+    // the next stage goes into the other buffer, read last in the previous stage
+    if (loader && ks + 1 < nks) {
+#pragma unroll
+      for (int j = 0; j < LA + LB; ++j) {
+        issue(j, 2 * wave_u, va0, vb0, ks + 1, buf ^ 1);
+        issue(j, 2 * wave_u + 1, va1, vb1, ks + 1, buf ^ 1);
+      }
+    }
+    const int8_t* lsb = &Ls[buf][0][0];
+#pragma unroll
+    for (int k64 = 0; k64 < K7 / 64; ++k64) {
+      const int pc = 4 * k64 + fq;
+      const int oa = xa * K7 + 16 * (pc ^ sw7(xa));
+      const int ob0 = xb0 * K7 + 16 * (pc ^ sw7(xb0)), ob1 = xb1 * K7 + 16 * (pc ^ sw7(xb1));
+      v4i_t af[LA], bf[LB][2];
+#pragma unroll
+      for (int s = 0; s < LA; ++s) af[s] = *reinterpret_cast<const v4i_t*>(lsb + s * (64 * K7) + oa);
+#pragma unroll
+      for (int t = 0; t < LB; ++t) {
+        const int8_t* bt = lsb + (S7MAX + t) * (64 * K7);
+        bf[t][0] = *reinterpret_cast<const v4i_t*>(bt + ob0);
+        bf[t][1] = *reinterpret_cast<const v4i_t*>(bt + ob1);
+      }
+#pragma unroll
+      for (int t = 0; t < LB; ++t)
+#pragma unroll
+        for (int s = 0; s < LA; ++s) {
+          acc[s + t][0] = __builtin_amdgcn_mfma_i32_16x16x64_i8(bf[t][0], af[s], acc[s + t][0], 0, 0, 0);
+          acc[s + t][1] = __builtin_amdgcn_mfma_i32_16x16x64_i8(bf[t][1], af[s], acc[s + t][1], 0, 0, 0);
+        }
+    }
+    if (ks % FL7 == FL7 - 1 || ks == nks - 1) {
+      // The exact int32 sums of every class, weighted 2^(7 (QMAX - q)): the five
+      // lowest weights (up to 2^28) sum in an int64 below 2^60, the four highest
+      // (2^35 up) in an int64 below 2^53 counted in units of 2^35; one int128 add.
+      int64_t lo[8], hi[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) lo[i] = hi[i] = 0;
+#pragma unroll
+      for (int q = 0; q < NQ; ++q) {
+        const int sh = S7 * (QMAX - q);
+#pragma unroll
+        for (int b = 0; b < 2; ++b)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int64_t v = acc[q][b][e];
+            if (sh < 5 * S7)
+              lo[4 * b + e] += v << sh;
+            else
+              hi[4 * b + e] += v << (sh - 5 * S7);
+            acc[q][b][e] = 0;
+          }
+      }
+#pragma unroll
+      for (int i = 0; i < 8; ++i) Z[i] += (static_cast<__int128>(hi[i]) << (5 * S7)) + lo[i];
+    }
+    __builtin_amdgcn_s_waitcnt(0);   // this wave's requests for the next stage are in LDS
+    __asm__ volatile("" ::: "memory");
+    __syncthreads();                 // and everyone's; every wave is done reading this stage
+  }
+
+  using OT = typename O::T;
+  OT* out = static_cast<OT*>(g.out);
+#pragma unroll
+  for (int b = 0; b < 2; ++b)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int64_t c = c0 + wn + 16 * b + 4 * fq + e;
+      if (ro < g.rows && c < g.cols) {
+        const __int128 z = Z[4 * b + e];
+        const double v = z == 0 ? 0.0 : round_odd53(z, ta + tb[b][e] - 2 * (S7 - 1) - S7 * QMAX);
+        out[ro * g.cols + c] = round_from_f64<O>(v);
+      }
+    }
+}
+
 template <typename O>
 __global__ void __launch_bounds__(512, 2) sliced7_kernel(GemmArgs g, Stats st, int tiles_c,
                                                          const int8_t* __restrict__ SA, const int8_t* __restrict__ SB,
@@ -579,7 +749,7 @@ __global__ void __launch_bounds__(512, 2) sliced7_kernel(GemmArgs g, Stats st, i
                                                          int64_t sb_bytes, int enabled) {
   // two stages (double buffered) of A slices, then B slices; the tile's slice
   // counts are gathered in the second stage's space before any staging
-  __shared__ __attribute__((aligned(16))) int8_t Ls[2][2 * S7MAX][64 * K7];
+  __shared__ __attribute__((aligned(16))) Ls7_t Ls;
   int* red_s = reinterpret_cast<int*>(&Ls[1][0][0]);
   const int tid = threadIdx.x;
   const int tile = blockIdx.x;
@@ -597,136 +767,35 @@ __global__ void __launch_bounds__(512, 2) sliced7_kernel(GemmArgs g, Stats st, i
     }
   }
   __syncthreads();
-  const int LA = red_s[0], LB = red_s[1];
+  const int LA = __builtin_amdgcn_readfirstlane(red_s[0]), LB = __builtin_amdgcn_readfirstlane(red_s[1]);
   const bool elsewhere = !enabled || red_s[2] || LA > S7MAX || LB > S7MAX;
   if (tid == 0) {
     st.flag[tile] = elsewhere ? 1 : 0;
     if (elsewhere) atomicAdd(&st.left[0], 1);
   }
   if (elsewhere) return;   // uniform over the workgroup
-
-  // Eight waves in a 4 x 2 grid, 16 x 32 outputs each as two 16 x 16 blocks.
-  // acc = MFMA(B fragment, A fragment, acc) with V_MFMA_I32_16X16X64_I8: the lane
-  // holds row lane % 16 and, in accumulator e of block b, column 16 b + 4 (lane / 16) + e.
-  // Fragments: lane l holds 16 bytes of its row (column) at reduction indices
-  // 64 k64 + 16 (l / 16) .. + 15, the same map for A and B, so the products pair up.
-  const int wave = tid >> 6, lane = tid & 63;
-  const int wm = (wave >> 1) * 16, wn = (wave & 1) * 32;
-  const int fr = lane & 15, fq = lane >> 4;
-  const int xa = wm + fr, xb0 = wn + fr, xb1 = wn + 16 + fr;
-
-  __int128 Z[8];
-  v4i_t acc[NQ7][2];
-#pragma unroll
-  for (int i = 0; i < 8; ++i) Z[i] = 0;
-#pragma unroll
-  for (int q = 0; q < NQ7; ++q)
-#pragma unroll
-    for (int b = 0; b < 2; ++b) acc[q][b] = v4i_t{0, 0, 0, 0};
-
-  const int nks = (LA > 0 && LB > 0) ? static_cast<int>(kp / K7) : 0;
-  const int qmax = LA + LB - 2;
-  // Staging by direct-to-LDS buffer loads: a slice's 64 x 128 stage is eight 1 KB
-  // wave instructions; instruction gi puts rows 8 gi .. 8 gi + 7 in place, lane l
-  // fetching the piece that belongs at byte 16 l (row 8 gi + l / 8, slot l % 8).
-  // The (LA + LB) x 8 instructions of a stage go round the eight waves.
-  const v4u_rs rsa = rsrc_of(SA, sa_bytes), rsb = rsrc_of(SB, sb_bytes);
-  const int wave_u = __builtin_amdgcn_readfirstlane(wave);
-  const int nins = (LA + LB) * 8;
-  const uint32_t lds0 = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_void_t*)&Ls[0][0]));
-  // request stage ks of every slice into buffer b
-  auto request = [&](int ks, int b) {
-    for (int gf = wave_u; gf < nins; gf += 8) {
-      const int si = gf >> 3, gi = gf & 7;
-      const bool is_a = si < LA;
-      const int sl = is_a ? si : si - LA;                       // slice of A or of B
-      const int slot = is_a ? sl : S7MAX + sl;                  // its LDS stage
-      const int x = 8 * gi + (lane >> 3);
-      const int pc = (lane & 7) ^ sw7(x);
-      const int64_t byte = (sl * (is_a ? npa : npb) + (is_a ? r0 : c0) + x) * kp + static_cast<int64_t>(ks) * K7 + 16 * pc;
-      const uint32_t off = static_cast<uint32_t>(byte);
-      const uint32_t m0 = lds0 + static_cast<uint32_t>(b * 2 * S7MAX + slot) * (64 * K7) + 1024u * static_cast<uint32_t>(gi);
-      if (is_a)
-        __asm__ volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
-                         :
-                         : "s"(m0), "v"(off), "s"(rsa)
-                         : "memory", "m0");
-      else
-        __asm__ volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
-                         :
-                         : "s"(m0), "v"(off), "s"(rsb)
-                         : "memory", "m0");
+  if (LA == 0 || LB == 0) {   // an all-zero row or column block: every product is zero
+    using OT = typename O::T;
+    OT* out = static_cast<OT*>(g.out);
+    for (int i = tid; i < TILE * TILE; i += 512) {
+      const int64_t r = r0 + i / TILE, c = c0 + i % TILE;
+      if (r < g.rows && c < g.cols) out[r * g.cols + c] = round_from_f64<O>(0.0);
     }
-  };
-
-  __syncthreads();   // every wave has read the slice counts (their space is the second buffer)
-  if (nks > 0) request(0, 0);
-  __builtin_amdgcn_s_waitcnt(0);   // this wave's loads are in LDS
-  __asm__ volatile("" ::: "memory");
-  __syncthreads();
-  for (int ks = 0; ks < nks; ++ks) {
-    const int buf = ks & 1;
-    // the next stage goes into the other buffer, read last in the previous stage
-    if (ks + 1 < nks) request(ks + 1, buf ^ 1);
-    const int8_t* lsb = &Ls[buf][0][0];
-#pragma unroll
-    for (int k64 = 0; k64 < K7 / 64; ++k64) {
-      const int pc = 4 * k64 + fq;
-      const int oa = xa * K7 + 16 * (pc ^ sw7(xa));
-      const int ob0 = xb0 * K7 + 16 * (pc ^ sw7(xb0)), ob1 = xb1 * K7 + 16 * (pc ^ sw7(xb1));
-      v4i_t af[S7MAX];
-#pragma unroll
-      for (int s = 0; s < S7MAX; ++s)
-        if (s < LA) af[s] = *reinterpret_cast<const v4i_t*>(lsb + s * (64 * K7) + oa);
-#pragma unroll
-      for (int t = 0; t < S7MAX; ++t) {
-        if (t < LB) {
-          const int8_t* bt = lsb + (S7MAX + t) * (64 * K7);
-          const v4i_t bf0 = *reinterpret_cast<const v4i_t*>(bt + ob0);
-          const v4i_t bf1 = *reinterpret_cast<const v4i_t*>(bt + ob1);
-#pragma unroll
-          for (int s = 0; s < S7MAX; ++s)
-            if (s < LA) {
-              acc[s + t][0] = __builtin_amdgcn_mfma_i32_16x16x64_i8(bf0, af[s], acc[s + t][0], 0, 0, 0);
-              acc[s + t][1] = __builtin_amdgcn_mfma_i32_16x16x64_i8(bf1, af[s], acc[s + t][1], 0, 0, 0);
-            }
-        }
-      }
-    }
-    if (ks % FL7 == FL7 - 1 || ks == nks - 1) {   // the exact int32 sums of every class
-#pragma unroll
-      for (int q = 0; q < NQ7; ++q) {
-        if (q <= qmax) {
-          const int sh = S7 * (qmax - q);
-#pragma unroll
-          for (int b = 0; b < 2; ++b)
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              Z[4 * b + e] += static_cast<__int128>(acc[q][b][e]) << sh;
-              acc[q][b][e] = 0;
-            }
-        }
-      }
-    }
-    __builtin_amdgcn_s_waitcnt(0);   // this wave's requests for the next stage are in LDS
-    __asm__ volatile("" ::: "memory");
-    __syncthreads();                 // and everyone's; every wave is done reading this stage
+    return;
   }
-
-  using OT = typename O::T;
-  OT* out = static_cast<OT*>(g.out);
-  const int64_t r = r0 + wm + fr;
-#pragma unroll
-  for (int b = 0; b < 2; ++b)
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int64_t c = c0 + wn + 16 * b + 4 * fq + e;
-      if (r < g.rows && c < g.cols) {
-        const __int128 z = Z[4 * b + e];
-        const double v = z == 0 ? 0.0 : round_odd53(z, st.topA[r] + st.topB[c] - 2 * (S7 - 1) - S7 * qmax);
-        out[r * g.cols + c] = round_from_f64<O>(v);
-      }
-    }
+  static_assert(S7MAX == 5, "one case per slice-count pair below");
+  switch (LA * 8 + LB) {
+#define DET_CR7_CASE(a, b)                                                                   \
+  case (a) * 8 + (b):                                                                        \
+    sliced7_tile<O, a, b>(g, st, Ls, r0, c0, SA, SB, npa, npb, kp, sa_bytes, sb_bytes); \
+    break;
+#define DET_CR7_ROW(a) DET_CR7_CASE(a, 1) DET_CR7_CASE(a, 2) DET_CR7_CASE(a, 3) DET_CR7_CASE(a, 4) DET_CR7_CASE(a, 5)
+    DET_CR7_ROW(1) DET_CR7_ROW(2) DET_CR7_ROW(3) DET_CR7_ROW(4) DET_CR7_ROW(5)
+#undef DET_CR7_ROW
+#undef DET_CR7_CASE
+    default:
+      break;
+  }
 }
 
 // ---- 2c. 8-bit slices, one pair at a time (16-bit inputs) --------------------

@@ -1,6 +1,7 @@
 """Correctly rounded tier on the GPU against the oracle, bit for bit: every op and dtype
-on ragged multi-tile shapes (16-bit inputs: the 8-bit slices on the bf16 matrix
-instructions, and the same forced through the 23-bit float64 slices; f32: the 23-bit
+on ragged multi-tile shapes (16-bit inputs: the 7-bit slices on the int8 and the 8-bit
+slices on the bf16 matrix instructions, every pair of 7-bit slice counts, and the same
+forced through the 23-bit float64 slices; f32: the 23-bit
 slices), the same forced through the per-output superaccumulator path, wide exponent ranges and non-finite values (which take that path
 by themselves), cancellation witnesses, permutation invariance, the column sum and f32
 outputs, and sampled rows of the GPT-2 c_fc forward."""
@@ -192,3 +193,42 @@ def test_cr_eight_bit_slices(dt):
     G = stor(vals(syn.normal(1601, 3, (m, n), dt=dt), dt), dt)
     want = oracle.gemm_cr("dw", dt, A, G, m, k, n)
     assert_bits_equal(_gpu("dw", dt, A, G), want, f"8-bit slices dw {dt}")
+
+
+@pytest.mark.parametrize("dt", ["bf16", "f16"])
+def test_cr_seven_bit_slice_counts(dt):
+    """16-bit inputs on the 7-bit slice (int8) path, every pair of slice counts in one call: row
+    block i of A (i = 0..4) spans 7 i + 6 bit positions (small odd integers times 2^-24 and one
+    value 65 * 2^(7 i - 24) per row), so it needs i + 1 slices, and column block j of B likewise
+    j + 1, with a ragged sixth column block of three; then a reduction longer than one exact int32
+    sum (16384 indices). Bits against the oracle and against the 23-bit path."""
+    import deterministic_invariant_gemm_det_amd as dg
+
+    def ints(seed, which, shape):
+        v = vals(syn.normal(seed, which, shape, dt="f32"), "f32")
+        return np.clip(np.rint(v * 40.0), -127, 127)
+
+    m, k, n = 320, 300, 330
+    ia, ib = ints(1610, 0, (m, k)), ints(1610, 1, (k, n))
+    ia[:, 1] = 3.0
+    ib[1, :] = -3.0
+    for i in range(5):
+        ia[64 * i:64 * (i + 1), 0] = 65.0 * 2.0 ** (7 * i)
+    for j in range(6):
+        ib[0, 64 * j:64 * (j + 1)] = -65.0 * 2.0 ** (7 * (j if j < 5 else 2))
+    A, B = stor(ia * 2.0 ** -24, dt), stor(ib * 2.0 ** -24, dt)
+    want = oracle.gemm_cr("fwd", dt, A, B, m, k, n)
+    assert_bits_equal(_gpu("fwd", dt, A, B), want, f"7-bit slice counts {dt}")
+    dg.det_gemm_debug_force_cr_fallback(2)
+    assert_bits_equal(_gpu("fwd", dt, A, B), want, f"7-bit slice counts {dt}, path 2")
+    dg.det_gemm_debug_force_cr_fallback(0)
+    # two exact int32 sums per class: a reduction of 16384 + 200 indices, four and five slices
+    m, k, n = 64, 16384 + 200, 96
+    ia, ib = ints(1611, 0, (m, k)), ints(1611, 1, (k, n))
+    ia[:, 1] = 1.0
+    ib[1, :] = 1.0
+    ia[:, 0] = 127.0 * 2.0 ** 21
+    ib[0, :] = -127.0 * 2.0 ** 28
+    A, B = stor(ia * 2.0 ** -24, dt), stor(ib * 2.0 ** -24, dt)
+    want = oracle.gemm_cr("fwd", dt, A, B, m, k, n)
+    assert_bits_equal(_gpu("fwd", dt, A, B), want, f"7-bit slices, long reduction {dt}")
