@@ -664,38 +664,58 @@ __device__ __forceinline__ void sliced7_tile(const GemmArgs& g, const Stats& st,
   __builtin_amdgcn_s_waitcnt(0);   // this wave's loads are in LDS
   __asm__ volatile("" ::: "memory");
   __syncthreads();
-  for (int ks = 0; ks < nks; ++ks) {
+  auto stage = [&](int ks, auto with_loads) {
+    constexpr bool WL = decltype(with_loads)::value;
     const int buf = ks & 1;
     // the next stage goes into the other buffer, read last in the previous stage
-    if (loader && ks + 1 < nks) {
+    if (WL && loader) {
 #pragma unroll
       for (int j = 0; j < LA + LB; ++j) {
         issue(j, 2 * wave_u, va0, vb0, ks + 1, buf ^ 1);
         issue(j, 2 * wave_u + 1, va1, vb1, ks + 1, buf ^ 1);
       }
     }
+    // Both 64-index steps' fragments are read up front, the second step's
+    // between the first step's matrix instructions (two per read), so that the
+    // LDS latency is paid once per stage.
     const int8_t* lsb = &Ls[buf][0][0];
+    v4i_t af[2][LA], bf[2][LB][2];
 #pragma unroll
     for (int k64 = 0; k64 < K7 / 64; ++k64) {
       const int pc = 4 * k64 + fq;
       const int oa = xa * K7 + 16 * (pc ^ sw7(xa));
       const int ob0 = xb0 * K7 + 16 * (pc ^ sw7(xb0)), ob1 = xb1 * K7 + 16 * (pc ^ sw7(xb1));
-      v4i_t af[LA], bf[LB][2];
 #pragma unroll
-      for (int s = 0; s < LA; ++s) af[s] = *reinterpret_cast<const v4i_t*>(lsb + s * (64 * K7) + oa);
+      for (int s = 0; s < LA; ++s) af[k64][s] = *reinterpret_cast<const v4i_t*>(lsb + s * (64 * K7) + oa);
 #pragma unroll
       for (int t = 0; t < LB; ++t) {
         const int8_t* bt = lsb + (S7MAX + t) * (64 * K7);
-        bf[t][0] = *reinterpret_cast<const v4i_t*>(bt + ob0);
-        bf[t][1] = *reinterpret_cast<const v4i_t*>(bt + ob1);
+        bf[k64][t][0] = *reinterpret_cast<const v4i_t*>(bt + ob0);
+        bf[k64][t][1] = *reinterpret_cast<const v4i_t*>(bt + ob1);
       }
+    }
+#pragma unroll
+    for (int k64 = 0; k64 < K7 / 64; ++k64)
 #pragma unroll
       for (int t = 0; t < LB; ++t)
 #pragma unroll
         for (int s = 0; s < LA; ++s) {
-          acc[s + t][0] = __builtin_amdgcn_mfma_i32_16x16x64_i8(bf[t][0], af[s], acc[s + t][0], 0, 0, 0);
-          acc[s + t][1] = __builtin_amdgcn_mfma_i32_16x16x64_i8(bf[t][1], af[s], acc[s + t][1], 0, 0, 0);
+          acc[s + t][0] = __builtin_amdgcn_mfma_i32_16x16x64_i8(bf[k64][t][0], af[k64][s], acc[s + t][0], 0, 0, 0);
+          acc[s + t][1] = __builtin_amdgcn_mfma_i32_16x16x64_i8(bf[k64][t][1], af[k64][s], acc[s + t][1], 0, 0, 0);
         }
+    {
+      constexpr int NR = LA + 2 * LB;    // fragment reads per step
+      constexpr int NM = 2 * LA * LB;    // matrix instructions per step
+      __builtin_amdgcn_sched_group_barrier(0x100, NR, 0);
+      constexpr int NI = NR <= NM / 2 ? NR : NM / 2;   // second-step reads placed two instructions apart
+#pragma unroll
+      for (int i = 0; i < NI; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      }
+      if constexpr (NR > NI) __builtin_amdgcn_sched_group_barrier(0x100, NR - NI, 0);
+      constexpr int REM = 2 * NM - 2 * NI;
+      __builtin_amdgcn_sched_group_barrier(0x008, REM, 0);
     }
     if (ks % FL7 == FL7 - 1 || ks == nks - 1) {
       // The exact int32 sums of every class, weighted 2^(7 (QMAX - q)): the five
@@ -725,7 +745,9 @@ __device__ __forceinline__ void sliced7_tile(const GemmArgs& g, const Stats& st,
     __builtin_amdgcn_s_waitcnt(0);   // this wave's requests for the next stage are in LDS
     __asm__ volatile("" ::: "memory");
     __syncthreads();                 // and everyone's; every wave is done reading this stage
-  }
+  };
+  for (int ks = 0; ks + 1 < nks; ++ks) stage(ks, std::true_type{});
+  if (nks > 0) stage(nks - 1, std::false_type{});
 
   using OT = typename O::T;
   OT* out = static_cast<OT*>(g.out);
