@@ -209,6 +209,53 @@ __global__ void __launch_bounds__(256) stats_kernel(const typename E::T* __restr
   if (nf) atomicOr(bad + idx, 1);
 }
 
+// The per-row stats from 16-byte pieces (V = 16 / sizeof(T) values each), for
+// arrays whose contiguous length, reduced length and base allow it.
+template <typename E>
+__device__ inline Parts parts_at(const uint4& v, int i) {
+  typename E::T x;
+  __builtin_memcpy(&x, reinterpret_cast<const char*>(&v) + i * sizeof(x), sizeof(x));
+  return parts<E>(x);
+}
+template <typename E>
+__device__ inline void fold(const Parts& p, int& t, int& lo, int& nf) {
+  if (!p.finite) nf = 1;
+  else if (p.sig) {
+    t = max(t, top_bit(p));
+    lo = min(lo, low_bit(p));
+  }
+}
+
+// per row of X[rows][ld], over its first red values: a wave per row
+template <typename E>
+__global__ void __launch_bounds__(256) stats_rows_vec_kernel(const typename E::T* __restrict__ X, int64_t rows,
+                                                             int64_t red, int64_t ld, int* __restrict__ top,
+                                                             int* __restrict__ low, int* __restrict__ bad) {
+  constexpr int V = 16 / sizeof(typename E::T);
+  const int lane = threadIdx.x & 63;
+  const int64_t row = (static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x) >> 6;
+  if (row >= rows) return;
+  const uint4* p = reinterpret_cast<const uint4*>(X + row * ld);
+  const int64_t np = red / V;
+  int t = NOBITS, lo = NOLOW, nf = 0;
+  for (int64_t q = lane; q < np; q += 64) {
+    const uint4 v = p[q];
+#pragma unroll
+    for (int i = 0; i < V; ++i) fold<E>(parts_at<E>(v, i), t, lo, nf);
+  }
+  for (int o = 32; o > 0; o >>= 1) {
+    t = max(t, __shfl_xor(t, o));
+    lo = min(lo, __shfl_xor(lo, o));
+    nf |= __shfl_xor(nf, o);
+  }
+  if (lane != 0) return;
+  if (t != NOBITS) {
+    atomicMax(top + row, t);
+    atomicMin(low + row, lo);
+  }
+  if (nf) atomicOr(bad + row, 1);
+}
+
 // Initial values of the stats, plus the extra values: 1 for every A row, the
 // bias for every B column (when `extra` is set for that side).
 template <typename E>
@@ -283,12 +330,8 @@ struct Stats {
 // unconditional read. Rows or columns that need more slices are finished by
 // the fallback, so two suffice here.
 template <typename E, bool IS_A, bool RC>
-__global__ void __launch_bounds__(256) slice_prep_kernel(GemmArgs g, const int* __restrict__ top, int64_t n,
-                                                         int64_t np, int64_t ktp, float* __restrict__ S,
-                                                         const int* __restrict__ need) {
-  if (need && *need == 0) return;   // the 16-bit paths left no tile (uniform over the grid)
-  const int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
-  if (i >= ktp * np) return;
+__device__ inline void slice_prep_one(const GemmArgs& g, const int* __restrict__ top, int64_t n, int64_t np,
+                                      int64_t ktp, float* __restrict__ S, int64_t i) {
   const int64_t l = i / np, x = i % np;
   float s0 = 0.0f, s1 = 0.0f;
   const int64_t kt = g.red + (g.bias ? 1 : 0);
@@ -302,6 +345,23 @@ __global__ void __launch_bounds__(256) slice_prep_kernel(GemmArgs g, const int* 
   }
   S[l * np + x] = s0;
   S[ktp * np + l * np + x] = s1;
+}
+
+// both operands in one grid-stride launch (A's ktp x npa elements, then B's)
+template <typename E, bool A_RC, bool B_RC>
+__global__ void __launch_bounds__(256) slice_prep_kernel(GemmArgs g, const int* __restrict__ topA,
+                                                         const int* __restrict__ topB, int64_t npa, int64_t npb,
+                                                         int64_t ktp, float* __restrict__ SA, float* __restrict__ SB,
+                                                         const int* __restrict__ need) {
+  if (need && *need == 0) return;   // the 16-bit paths left no tile (uniform over the grid)
+  const int64_t na = ktp * npa, total = na + ktp * npb;
+  for (int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < total;
+       i += static_cast<int64_t>(gridDim.x) * blockDim.x) {
+    if (i < na)
+      slice_prep_one<E, true, A_RC>(g, topA, g.rows, npa, ktp, SA, i);
+    else
+      slice_prep_one<E, false, B_RC>(g, topB, g.cols, npb, ktp, SB, i - na);
+  }
 }
 
 typedef double v4d __attribute__((ext_vector_type(4)));
@@ -470,16 +530,16 @@ __global__ void __launch_bounds__(256) sliced_kernel(GemmArgs g, Stats st, int t
 // The same exact value from narrow slices on the integer matrix pipe. A value
 // of row r is cut into 7-bit slices below top_r: slice j holds the bits with
 // weights 2^(top_r - 7 j - 6) .. 2^(top_r - 7 j) as a signed integer of
-// magnitude below 2^7 (an int8). V_MFMA_I32_32X32X32_I8 multiplies and sums
+// magnitude below 2^7 (an int8). V_MFMA_I32_16X16X64_I8 multiplies and sums
 // them exactly in int32; all pairs (s, t) of one weight class q = s + t (at
 // most S7MAX of them) share one accumulator, whose sums stay below
-// 4 * 16384 * 127^2 < 2^31 over 16384 reduction indices, after which (and at
+// 5 * 16384 * 127^2 < 2^31 over 16384 reduction indices, after which (and at
 // the end) each class goes into the int128 at 7 (qmax - q) bits up; the int128
 // is rounded as in 2. Per stage of 128 reduction indices the workgroup stages
 // every slice of its 64 rows and 64 columns once (direct-to-LDS loads) and runs
 // every slice pair from registers. A tile is taken here when its rows and
-// columns need at most S7MAX slices (spans of at most 28 bits) and all its
-// values are finite; the others are flagged for 2c.
+// columns need at most S7MAX slices (top and lowest set bit at most 34 apart)
+// and all its values are finite; the others are flagged for 2c.
 constexpr int S7 = 7;                // bits per slice
 constexpr int S7MAX = 5;             // slices per value on this path
 constexpr int NQ7 = 2 * S7MAX - 1;   // weight classes
@@ -501,58 +561,109 @@ __device__ inline int slice7(const Parts& p, int top, int j) {
   return p.neg ? -static_cast<int>(part) : static_cast<int>(part);
 }
 
-// S[j][x][l] (int8) for j < S7MAX, x < np, l < kp: slice j of the operand value
-// (x, l) (A row x or B column x, reduction index l; the bias index as in path
-// 2), zero past the operand. A workgroup converts a 64 x 64 block, read along
-// the source's contiguous dimension through LDS and written along l.
+// S[j][x][l] (int8) for x < np, l < kp and j below the slice count of x's
+// 64-row block (at most S7MAX): slice j of the operand value (x, l) (A row x or
+// B column x, reduction index l; the bias index as in path 2), zero past the
+// operand. A workgroup converts a 64 x 64 block, read along the source's
+// contiguous dimension (16-byte pieces where the operand allows) into LDS, and
+// writes each slice's 16 bytes per thread.
+typedef uint16_t Raw7_t[64][72];   // [x][l]; 144-byte rows
+
 template <typename E, bool IS_A, bool RC>
-__global__ void __launch_bounds__(256) slice7_prep_kernel(GemmArgs g, const int* __restrict__ top, int64_t n,
-                                                          int64_t np, int64_t kp, int8_t* __restrict__ S) {
-  __shared__ uint16_t raw[64][65];
+__device__ inline void slice7_prep_block(const GemmArgs& g, const int* __restrict__ top, const int* __restrict__ low,
+                                         int64_t n, int64_t np, int64_t kp, int8_t* __restrict__ S, int64_t blk,
+                                         Raw7_t& raw, int& nsl) {
   using T = typename E::T;
   const int tid = threadIdx.x;
   const int64_t lb = kp / 64;
-  const int64_t x0 = static_cast<int64_t>(blockIdx.x / lb) * 64, l0 = static_cast<int64_t>(blockIdx.x % lb) * 64;
+  const int64_t x0 = blk / lb * 64, l0 = blk % lb * 64;
   const int64_t kt = g.red + (g.bias ? 1 : 0);
   const T* X = static_cast<const T*>(IS_A ? g.A : g.B);
   const int64_t ld = IS_A ? g.lda : g.ldb;
-  for (int i = tid; i < 64 * 64; i += 256) {
-    const int fast = i % 64, slow = i / 64;
-    const int x = RC ? slow : fast, l = RC ? fast : slow;
-    const int64_t gx = x0 + x, gl = l0 + l;
-    uint16_t v = 0;
-    if (gx < n && gl < g.red && X) {
-      const T e = RC ? X[gx * ld + gl] : X[gl * ld + gx];
-      __builtin_memcpy(&v, &e, 2);
+  if (tid == 0) nsl = 0;
+  __syncthreads();
+  // the slices of this 64-row block (the tile's count on that side)
+  if (tid < 64 && x0 + tid < n) atomicMax(&nsl, slices7_of(top[x0 + tid], low[x0 + tid]));
+  if (X && (IS_A ? g.vec_a : g.vec_b) && x0 + 64 <= n && l0 + 64 <= g.red) {
+    // 16-byte pieces along the contiguous dimension
+    for (int i = tid; i < 512; i += 256) {
+      if constexpr (RC) {
+        const int x = i >> 3, pc = i & 7;
+        *reinterpret_cast<uint4*>(&raw[x][8 * pc]) = *reinterpret_cast<const uint4*>(X + (x0 + x) * ld + l0 + 8 * pc);
+      } else {
+        const int l = i >> 3, pc = i & 7;
+        const uint4 v = *reinterpret_cast<const uint4*>(X + (l0 + l) * ld + x0 + 8 * pc);
+        const uint16_t* e = reinterpret_cast<const uint16_t*>(&v);
+#pragma unroll
+        for (int q = 0; q < 8; ++q) raw[8 * pc + q][l] = e[q];
+      }
     }
-    raw[x][l] = v;
+  } else {
+    for (int i = tid; i < 64 * 64; i += 256) {
+      const int fast = i % 64, slow = i / 64;
+      const int x = RC ? slow : fast, l = RC ? fast : slow;
+      const int64_t gx = x0 + x, gl = l0 + l;
+      uint16_t v = 0;
+      if (gx < n && gl < g.red && X) {
+        const T e = RC ? X[gx * ld + gl] : X[gl * ld + gx];
+        __builtin_memcpy(&v, &e, 2);
+      }
+      raw[x][l] = v;
+    }
   }
   __syncthreads();
-  for (int i = tid; i < 64 * 64; i += 256) {
-    const int x = i / 64, l = i % 64;
-    const int64_t gx = x0 + x, gl = l0 + l;
-    int v[S7MAX];
+  // thread: row x = tid / 4, the 16 reduction indices from 16 (tid % 4); each
+  // slice's 16 bytes in one store, slices past the block's count not written
+  // (the int8 kernel reads no further)
+  const int nw = nsl < S7MAX ? nsl : S7MAX;
+  const int x = tid >> 2, lq = (tid & 3) * 16;
+  const int64_t gx = x0 + x;
+  const int t = gx < n ? top[gx] : 0;
+  uint32_t w[S7MAX][4];
 #pragma unroll
-    for (int j = 0; j < S7MAX; ++j) v[j] = 0;
+  for (int j = 0; j < S7MAX; ++j)
+#pragma unroll
+    for (int c = 0; c < 4; ++c) w[j][c] = 0;
+  uint16_t rv[16];
+  *reinterpret_cast<uint4*>(&rv[0]) = *reinterpret_cast<const uint4*>(&raw[x][lq]);
+  *reinterpret_cast<uint4*>(&rv[8]) = *reinterpret_cast<const uint4*>(&raw[x][lq + 8]);
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const int64_t gl = l0 + lq + i;
     if (gx < n && gl < kt) {
       Parts p;
       if (gl == g.red || (IS_A && !X)) {
         p = IS_A ? a_at<E, RC>(g, gx, gl) : b_at<E, RC>(g, gl, gx);
       } else {
         T e;
-        const uint16_t bits = raw[x][l];
-        __builtin_memcpy(&e, &bits, 2);
+        __builtin_memcpy(&e, &rv[i], 2);
         p = parts<E>(e);
       }
       if (p.finite && p.sig) {
-        const int t = top[gx];
 #pragma unroll
-        for (int j = 0; j < S7MAX; ++j) v[j] = slice7(p, t, j);
+        for (int j = 0; j < S7MAX; ++j)
+          w[j][i >> 2] |= static_cast<uint32_t>(static_cast<uint8_t>(static_cast<int8_t>(slice7(p, t, j)))) << (8 * (i & 3));
       }
     }
-#pragma unroll
-    for (int j = 0; j < S7MAX; ++j) S[(j * np + gx) * kp + gl] = static_cast<int8_t>(v[j]);
   }
+#pragma unroll
+  for (int j = 0; j < S7MAX; ++j)
+    if (j < nw)
+      *reinterpret_cast<uint4*>(S + (j * np + gx) * kp + l0 + lq) = uint4{w[j][0], w[j][1], w[j][2], w[j][3]};
+}
+
+// both operands in one launch: blocks below blocks_a convert A, the rest B
+template <typename E, bool A_RC, bool B_RC>
+__global__ void __launch_bounds__(256) slice7_prep_kernel(GemmArgs g, Stats st, int64_t npa, int64_t npb, int64_t kp,
+                                                          int8_t* __restrict__ SA, int8_t* __restrict__ SB,
+                                                          int64_t blocks_a) {
+  __shared__ __attribute__((aligned(16))) Raw7_t raw;
+  __shared__ int nsl;
+  const int64_t b = blockIdx.x;
+  if (b < blocks_a)
+    slice7_prep_block<E, true, A_RC>(g, st.topA, st.lowA, g.rows, npa, kp, SA, b, raw, nsl);
+  else
+    slice7_prep_block<E, false, B_RC>(g, st.topB, st.lowB, g.cols, npb, kp, SB, b - blocks_a, raw, nsl);
 }
 
 typedef int v4i_t __attribute__((ext_vector_type(4)));
@@ -864,16 +975,15 @@ __device__ inline uint16_t bf16_of_int(int v) {
 // value (x, l) (A row x or B column x, reduction index l; the bias index as in
 // path 2), zero past the operand. A workgroup converts a 64 x 64 block, read
 // along the source's contiguous dimension through LDS and written along l.
+typedef uint16_t Raw8_t[64][65];
+
 template <typename E, bool IS_A, bool RC>
-__global__ void __launch_bounds__(256) slice8_prep_kernel(GemmArgs g, const int* __restrict__ top, int64_t n,
-                                                          int64_t np, int64_t kp, uint16_t* __restrict__ S,
-                                                          const int* __restrict__ need) {
-  __shared__ uint16_t raw[64][65];
-  if (*need == 0) return;   // the int8 path left no tile (uniform over the grid)
+__device__ inline void slice8_prep_block(const GemmArgs& g, const int* __restrict__ top, int64_t n, int64_t np,
+                                         int64_t kp, uint16_t* __restrict__ S, int64_t blk, Raw8_t& raw) {
   using T = typename E::T;
   const int tid = threadIdx.x;
   const int64_t lb = kp / 64;
-  const int64_t x0 = static_cast<int64_t>(blockIdx.x / lb) * 64, l0 = static_cast<int64_t>(blockIdx.x % lb) * 64;
+  const int64_t x0 = blk / lb * 64, l0 = blk % lb * 64;
   const int64_t kt = g.red + (g.bias ? 1 : 0);
   const T* X = static_cast<const T*>(IS_A ? g.A : g.B);
   const int64_t ld = IS_A ? g.lda : g.ldb;
@@ -916,6 +1026,20 @@ __global__ void __launch_bounds__(256) slice8_prep_kernel(GemmArgs g, const int*
 #pragma unroll
     for (int j = 0; j < S8MAX; ++j) S[(j * np + gx) * kp + gl] = bf16_of_int(v[j]);
   }
+}
+
+// both operands in one launch: blocks below blocks_a convert A, the rest B
+template <typename E, bool A_RC, bool B_RC>
+__global__ void __launch_bounds__(256) slice8_prep_kernel(GemmArgs g, Stats st, int64_t npa, int64_t npb, int64_t kp,
+                                                          uint16_t* __restrict__ SA, uint16_t* __restrict__ SB,
+                                                          int64_t blocks_a) {
+  __shared__ Raw8_t raw;
+  if (st.left[0] == 0) return;   // the int8 path left no tile (uniform over the grid)
+  const int64_t b = blockIdx.x;
+  if (b < blocks_a)
+    slice8_prep_block<E, true, A_RC>(g, st.topA, g.rows, npa, kp, SA, b, raw);
+  else
+    slice8_prep_block<E, false, B_RC>(g, st.topB, g.cols, npb, kp, SB, b - blocks_a, raw);
 }
 
 typedef __bf16 v8bf_t __attribute__((ext_vector_type(8)));
@@ -1235,7 +1359,11 @@ hipError_t launch_typed(const GemmArgs& a, int force_fallback, hipStream_t strea
   const int64_t strip = 256, strip_cols = 32;   // more strips for per-column stats (one thread each)
   auto stats = [&](const void* X, bool rc, int64_t n_idx, int64_t red, int64_t ld, int* top, int* low, int* bad) {
     // the array is [n_idx][ld] (rc) or [red][ld] (!rc); ld is its contiguous length
-    if (rc) {
+    constexpr int64_t V = 16 / sizeof(T);
+    if (rc && reinterpret_cast<uintptr_t>(X) % 16 == 0 && ld % V == 0 && red % V == 0) {
+      hipLaunchKernelGGL((stats_rows_vec_kernel<E>), dim3(static_cast<unsigned>((n_idx * 64 + 255) / 256)), dim3(256), 0,
+                         stream, static_cast<const T*>(X), n_idx, red, ld, top, low, bad);
+    } else if (rc) {
       const int64_t waves = n_idx * ((red + strip - 1) / strip);
       hipLaunchKernelGGL((stats_kernel<E, true>), dim3(static_cast<unsigned>((waves * 64 + 255) / 256)), dim3(256), 0,
                          stream, static_cast<const T*>(X), n_idx, ld, strip, top, low, bad);
@@ -1250,24 +1378,21 @@ hipError_t launch_typed(const GemmArgs& a, int force_fallback, hipStream_t strea
   if (use8) {
     // 2b: the direct loads address the slices with 32-bit byte offsets
     const int on7 = s7a < (size_t(1) << 31) && s7b < (size_t(1) << 31) ? 1 : 0;
-    hipLaunchKernelGGL((slice7_prep_kernel<E, true, A_RC>), dim3(static_cast<unsigned>(npa / 64 * (kp7 / 64))),
-                       dim3(256), 0, stream, a, topA, a.rows, npa, kp7, SA7);
-    hipLaunchKernelGGL((slice7_prep_kernel<E, false, B_RC>), dim3(static_cast<unsigned>(npb / 64 * (kp7 / 64))),
-                       dim3(256), 0, stream, a, topB, a.cols, npb, kp7, SB7);
+    hipLaunchKernelGGL((slice7_prep_kernel<E, A_RC, B_RC>), dim3(static_cast<unsigned>((npa + npb) / 64 * (kp7 / 64))),
+                       dim3(256), 0, stream, a, st, npa, npb, kp7, SA7, SB7, npa / 64 * (kp7 / 64));
     hipLaunchKernelGGL((sliced7_kernel<O>), dim3(static_cast<unsigned>(tiles)), dim3(512), 0, stream, a, st,
                        static_cast<int>(tiles_c), SA7, SB7, npa, npb, kp7, static_cast<int64_t>(s7a),
                        static_cast<int64_t>(s7b), on7);
-    hipLaunchKernelGGL((slice8_prep_kernel<E, true, A_RC>), dim3(static_cast<unsigned>(npa / 64 * (kp8 / 64))),
-                       dim3(256), 0, stream, a, topA, a.rows, npa, kp8, SA8, left);
-    hipLaunchKernelGGL((slice8_prep_kernel<E, false, B_RC>), dim3(static_cast<unsigned>(npb / 64 * (kp8 / 64))),
-                       dim3(256), 0, stream, a, topB, a.cols, npb, kp8, SB8, left);
+    hipLaunchKernelGGL((slice8_prep_kernel<E, A_RC, B_RC>), dim3(static_cast<unsigned>((npa + npb) / 64 * (kp8 / 64))),
+                       dim3(256), 0, stream, a, st, npa, npb, kp8, SA8, SB8, npa / 64 * (kp8 / 64));
     hipLaunchKernelGGL((sliced8_kernel<O>), dim3(static_cast<unsigned>(tiles)), dim3(256), 0, stream, a, st,
                        static_cast<int>(tiles_c), SA8, SB8, npa, npb, kp8);
   }
-  hipLaunchKernelGGL((slice_prep_kernel<E, true, A_RC>), dim3(static_cast<unsigned>((ktp * npa + 255) / 256)),
-                     dim3(256), 0, stream, a, topA, a.rows, npa, ktp, SA, use8 ? left + 1 : nullptr);
-  hipLaunchKernelGGL((slice_prep_kernel<E, false, B_RC>), dim3(static_cast<unsigned>((ktp * npb + 255) / 256)),
-                     dim3(256), 0, stream, a, topB, a.cols, npb, ktp, SB, use8 ? left + 1 : nullptr);
+  {
+    const int64_t blocks = (ktp * (npa + npb) + 255) / 256;
+    hipLaunchKernelGGL((slice_prep_kernel<E, A_RC, B_RC>), dim3(static_cast<unsigned>(blocks < 8192 ? blocks : 8192)),
+                       dim3(256), 0, stream, a, topA, topB, npa, npb, ktp, SA, SB, use8 ? left + 1 : nullptr);
+  }
   hipLaunchKernelGGL((sliced_kernel<O>), dim3(static_cast<unsigned>(tiles)), dim3(256), 0, stream, a, st,
                      static_cast<int>(tiles_c), force_fallback == 1 ? 1 : 0, SA, SB, npa, npb, ktp, use8 ? 1 : 0);
   hipLaunchKernelGGL((fallback_kernel<E, O, A_RC, B_RC>), dim3(static_cast<unsigned>(tiles)), dim3(256), 0, stream, a,
