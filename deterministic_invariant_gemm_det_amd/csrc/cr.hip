@@ -256,6 +256,62 @@ __global__ void __launch_bounds__(256) stats_rows_vec_kernel(const typename E::T
   if (nf) atomicOr(bad + row, 1);
 }
 
+// per column of X[red][ld], columns 0 .. cols - 1: a workgroup per 64 16-byte
+// pieces of a row (64 V columns) and strip of rows, its four waves on every
+// fourth row; the waves meet in LDS and one atomic per column and workgroup
+// goes out
+template <typename E>
+__global__ void __launch_bounds__(256) stats_cols_vec_kernel(const typename E::T* __restrict__ X, int64_t red,
+                                                             int64_t cols, int64_t ld, int64_t strip,
+                                                             int* __restrict__ top, int* __restrict__ low,
+                                                             int* __restrict__ bad) {
+  constexpr int V = 16 / sizeof(typename E::T);
+  __shared__ int sh[3][4][64 * V];
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int64_t npc = cols / V, groups = (npc + 63) / 64;
+  const int64_t cg = blockIdx.x % groups;
+  const int64_t r0 = blockIdx.x / groups * strip, r1 = r0 + strip < red ? r0 + strip : red;
+  const int64_t pc = cg * 64 + lane;
+  int t[V], lo[V], nf[V];
+#pragma unroll
+  for (int i = 0; i < V; ++i) {
+    t[i] = NOBITS;
+    lo[i] = NOLOW;
+    nf[i] = 0;
+  }
+  if (pc < npc) {
+#pragma unroll 4
+    for (int64_t r = r0 + wave; r < r1; r += 4) {
+      const uint4 v = reinterpret_cast<const uint4*>(X + r * ld)[pc];
+#pragma unroll
+      for (int i = 0; i < V; ++i) fold<E>(parts_at<E>(v, i), t[i], lo[i], nf[i]);
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < V; ++i) {
+    sh[0][wave][lane * V + i] = t[i];
+    sh[1][wave][lane * V + i] = lo[i];
+    sh[2][wave][lane * V + i] = nf[i];
+  }
+  __syncthreads();
+  for (int c = threadIdx.x; c < 64 * V; c += 256) {
+    const int64_t col = cg * 64 * V + c;
+    if (col >= cols) continue;
+    int tt = NOBITS, ll = NOLOW, ff = 0;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      tt = max(tt, sh[0][w][c]);
+      ll = min(ll, sh[1][w][c]);
+      ff |= sh[2][w][c];
+    }
+    if (tt != NOBITS) {
+      atomicMax(top + col, tt);
+      atomicMin(low + col, ll);
+    }
+    if (ff) atomicOr(bad + col, 1);
+  }
+}
+
 // Initial values of the stats, plus the extra values: 1 for every A row, the
 // bias for every B column (when `extra` is set for that side).
 template <typename E>
@@ -640,9 +696,17 @@ __device__ inline void slice7_prep_block(const GemmArgs& g, const int* __restric
         p = parts<E>(e);
       }
       if (p.finite && p.sig) {
+        // the value in units of 2^(t - 7 S7MAX + 1): slice j is bits 7 (S7MAX - 1 - j) .. + 6
+        // (the same as slice7(p, t, j); bits below the last slice drop out in both)
+        const int sh = p.lsb - (t - S7 * S7MAX + 1);
+        const uint64_t m = sh >= 0 ? static_cast<uint64_t>(p.sig) << sh
+                                   : static_cast<uint64_t>(p.sig) >> (-sh < 63 ? -sh : 63);
+        const uint32_t neg = p.neg ? 0xffu : 0u;
 #pragma unroll
-        for (int j = 0; j < S7MAX; ++j)
-          w[j][i >> 2] |= static_cast<uint32_t>(static_cast<uint8_t>(static_cast<int8_t>(slice7(p, t, j)))) << (8 * (i & 3));
+        for (int j = 0; j < S7MAX; ++j) {
+          const uint32_t part = static_cast<uint32_t>(m >> (S7 * (S7MAX - 1 - j))) & 0x7fu;
+          w[j][i >> 2] |= (((part ^ neg) + (neg & 1u)) & 0xffu) << (8 * (i & 3));
+        }
       }
     }
   }
@@ -1360,9 +1424,18 @@ hipError_t launch_typed(const GemmArgs& a, int force_fallback, hipStream_t strea
   auto stats = [&](const void* X, bool rc, int64_t n_idx, int64_t red, int64_t ld, int* top, int* low, int* bad) {
     // the array is [n_idx][ld] (rc) or [red][ld] (!rc); ld is its contiguous length
     constexpr int64_t V = 16 / sizeof(T);
-    if (rc && reinterpret_cast<uintptr_t>(X) % 16 == 0 && ld % V == 0 && red % V == 0) {
+    const bool vec = reinterpret_cast<uintptr_t>(X) % 16 == 0 && ld % V == 0 && (rc ? red : n_idx) % V == 0;
+    if (vec && rc) {
       hipLaunchKernelGGL((stats_rows_vec_kernel<E>), dim3(static_cast<unsigned>((n_idx * 64 + 255) / 256)), dim3(256), 0,
                          stream, static_cast<const T*>(X), n_idx, red, ld, top, low, bad);
+    } else if (vec) {
+      const int64_t groups = (n_idx / V + 63) / 64;
+      // strips of 16 rows, longer while the grid would exceed 2048 workgroups
+      int64_t vstrip = 16;
+      while (groups * ((red + vstrip - 1) / vstrip) > 2048) vstrip *= 2;
+      hipLaunchKernelGGL((stats_cols_vec_kernel<E>),
+                         dim3(static_cast<unsigned>(groups * ((red + vstrip - 1) / vstrip))), dim3(256), 0, stream,
+                         static_cast<const T*>(X), red, n_idx, ld, vstrip, top, low, bad);
     } else if (rc) {
       const int64_t waves = n_idx * ((red + strip - 1) / strip);
       hipLaunchKernelGGL((stats_kernel<E, true>), dim3(static_cast<unsigned>((waves * 64 + 255) / 256)), dim3(256), 0,
