@@ -758,10 +758,17 @@ typedef int8_t Ls7_t[2][2 * S7MAX][64 * K7];
 // of block b, column 16 b + 4 (lane / 16) + e. Fragments: lane l holds 16 bytes
 // of its row (column) at reduction indices 64 k64 + 16 (l / 16) .. + 15, the
 // same map for A and B, so the products pair up.
+//
+// base: the LDS buffer of the tile's first stage; have0: that stage is already
+// staged (requested by the previous tile's loader waves). pf: during its last
+// stage the tile requests the first stage of the next tile (rows from nr0,
+// columns from nc0, nLA and nLB slices) into the other buffer. Returns that
+// buffer, or -1 when nothing was requested.
 template <typename O, int LA, int LB>
-__device__ __forceinline__ void sliced7_tile(const GemmArgs& g, const Stats& st, Ls7_t& Ls, int64_t r0, int64_t c0,
-                                             const int8_t* SA, const int8_t* SB, int64_t npa, int64_t npb, int64_t kp,
-                                             int64_t sa_bytes, int64_t sb_bytes) {
+__device__ __forceinline__ int sliced7_tile(const GemmArgs& g, const Stats& st, Ls7_t& Ls, int64_t r0, int64_t c0,
+                                            const int8_t* SA, const int8_t* SB, int64_t npa, int64_t npb, int64_t kp,
+                                            int64_t sa_bytes, int64_t sb_bytes, int base, bool have0, bool pf,
+                                            int64_t nr0, int64_t nc0, int nLA, int nLB) {
   constexpr int NQ = LA + LB - 1;   // weight classes q = s + t
   constexpr int QMAX = NQ - 1;
   const int tid = threadIdx.x;
@@ -804,10 +811,10 @@ __device__ __forceinline__ void sliced7_tile(const GemmArgs& g, const Stats& st,
     const int x = 8 * gi + (lane >> 3);
     return static_cast<uint32_t>((base + x) * kp + 16 * ((lane & 7) ^ sw7(x)));
   };
-  // instruction gi of slice j (A slices, then B slices) of stage ks into buffer b
-  auto issue = [&](int j, int gi, uint32_t va, uint32_t vb, int ks, int b) {
-    const bool is_a = j < LA;
-    const int sl = is_a ? j : j - LA;
+  // instruction gi of slice j (la A slices, then B slices) of stage ks into buffer b
+  auto issue = [&](int j, int la, int gi, uint32_t va, uint32_t vb, int ks, int b) {
+    const bool is_a = j < la;
+    const int sl = is_a ? j : j - la;
     const uint32_t so = static_cast<uint32_t>(sl) * (is_a ? sla : slb) + static_cast<uint32_t>(ks) * K7;
     const uint32_t m0 =
         lds0 + static_cast<uint32_t>(b * 2 * S7MAX + (is_a ? sl : S7MAX + sl)) * (64 * K7) + 1024u * static_cast<uint32_t>(gi);
@@ -830,24 +837,33 @@ __device__ __forceinline__ void sliced7_tile(const GemmArgs& g, const Stats& st,
   const uint32_t va0 = voff(r0, 2 * wave_u), va1 = voff(r0, 2 * wave_u + 1);
   const uint32_t vb0 = voff(c0, 2 * wave_u), vb1 = voff(c0, 2 * wave_u + 1);
 
-  __syncthreads();   // every wave has read the slice counts (their space is the second buffer)
-  if (nks > 0) {
+  if (!have0 && nks > 0) {
     const uint32_t va = voff(r0, wave_u), vb = voff(c0, wave_u);
 #pragma unroll
-    for (int j = 0; j < LA + LB; ++j) issue(j, wave_u, va, vb, 0, 0);
+    for (int j = 0; j < LA + LB; ++j) issue(j, LA, wave_u, va, vb, 0, base);
   }
   __builtin_amdgcn_s_waitcnt(0);   // this wave's loads are in LDS
   __asm__ volatile("" ::: "memory");
   __syncthreads();
+  const bool pf_here = pf && nks > 0;
   auto stage = [&](int ks, auto with_loads) {
     constexpr bool WL = decltype(with_loads)::value;
-    const int buf = ks & 1;
+    const int buf = (ks + base) & 1;
     // the next stage goes into the other buffer, read last in the previous stage
     if (WL && loader) {
 #pragma unroll
       for (int j = 0; j < LA + LB; ++j) {
-        issue(j, 2 * wave_u, va0, vb0, ks + 1, buf ^ 1);
-        issue(j, 2 * wave_u + 1, va1, vb1, ks + 1, buf ^ 1);
+        issue(j, LA, 2 * wave_u, va0, vb0, ks + 1, buf ^ 1);
+        issue(j, LA, 2 * wave_u + 1, va1, vb1, ks + 1, buf ^ 1);
+      }
+    }
+    // the last stage requests the next tile's first stage
+    if (!WL && pf_here && loader) {
+      const uint32_t na0 = voff(nr0, 2 * wave_u), na1 = voff(nr0, 2 * wave_u + 1);
+      const uint32_t nb0 = voff(nc0, 2 * wave_u), nb1 = voff(nc0, 2 * wave_u + 1);
+      for (int j = 0; j < nLA + nLB; ++j) {
+        issue(j, nLA, 2 * wave_u, na0, nb0, 0, buf ^ 1);
+        issue(j, nLA, 2 * wave_u + 1, na1, nb1, 0, buf ^ 1);
       }
     }
     // Both 64-index steps' fragments are read up front, the second step's
@@ -917,9 +933,13 @@ __device__ __forceinline__ void sliced7_tile(const GemmArgs& g, const Stats& st,
 #pragma unroll
       for (int i = 0; i < 8; ++i) Z[i] += (static_cast<__int128>(hi[i]) << (5 * S7)) + lo[i];
     }
-    __builtin_amdgcn_s_waitcnt(0);   // this wave's requests for the next stage are in LDS
-    __asm__ volatile("" ::: "memory");
-    __syncthreads();                 // and everyone's; every wave is done reading this stage
+    if constexpr (WL) {
+      __builtin_amdgcn_s_waitcnt(0);   // this wave's requests for the next stage are in LDS
+      __asm__ volatile("" ::: "memory");
+    }
+    // (every wave's requests are in) and every wave is done reading this stage;
+    // the next tile's first stage stays in flight through the rounding below
+    __syncthreads();
   };
   for (int ks = 0; ks + 1 < nks; ++ks) stage(ks, std::true_type{});
   if (nks > 0) stage(nks - 1, std::false_type{});
@@ -937,61 +957,89 @@ __device__ __forceinline__ void sliced7_tile(const GemmArgs& g, const Stats& st,
         out[ro * g.cols + c] = round_from_f64<O>(v);
       }
     }
+  return pf_here ? (((nks - 1 + base) & 1) ^ 1) : -1;
 }
 
+// A tile's slice counts (LA, LB) and whether it goes elsewhere (ew), from
+// every wave alike (lane i looks at row r0 + i and column c0 + i).
+__device__ inline void tile7_info(const GemmArgs& g, const Stats& st, int tile, int tiles_c, int enabled, int& LA,
+                                  int& LB, int& ew) {
+  const int lane = threadIdx.x & 63;
+  const int64_t r0 = static_cast<int64_t>(tile / tiles_c) * TILE, c0 = static_cast<int64_t>(tile % tiles_c) * TILE;
+  int la = 0, lb = 0, bad = 0;
+  if (r0 + lane < g.rows) {
+    la = slices7_of(st.topA[r0 + lane], st.lowA[r0 + lane]);
+    bad |= st.badA[r0 + lane];
+  }
+  if (c0 + lane < g.cols) {
+    lb = slices7_of(st.topB[c0 + lane], st.lowB[c0 + lane]);
+    bad |= st.badB[c0 + lane];
+  }
+  for (int o = 32; o > 0; o >>= 1) {
+    la = max(la, __shfl_xor(la, o));
+    lb = max(lb, __shfl_xor(lb, o));
+    bad |= __shfl_xor(bad, o);
+  }
+  LA = __builtin_amdgcn_readfirstlane(la);
+  LB = __builtin_amdgcn_readfirstlane(lb);
+  ew = (!enabled || __builtin_amdgcn_readfirstlane(bad) != 0 || LA > S7MAX || LB > S7MAX) ? 1 : 0;
+}
+
+// Persistent: workgroup b takes tiles b, b + G, b + 2 G, ... (G workgroups,
+// one per compute unit), each tile's first stage staged during the previous
+// tile's last stage where both take this path.
 template <typename O>
-__global__ void __launch_bounds__(512, 2) sliced7_kernel(GemmArgs g, Stats st, int tiles_c,
+__global__ void __launch_bounds__(512, 2) sliced7_kernel(GemmArgs g, Stats st, int tiles_c, int tiles,
                                                          const int8_t* __restrict__ SA, const int8_t* __restrict__ SB,
                                                          int64_t npa, int64_t npb, int64_t kp, int64_t sa_bytes,
                                                          int64_t sb_bytes, int enabled) {
-  // two stages (double buffered) of A slices, then B slices; the tile's slice
-  // counts are gathered in the second stage's space before any staging
+  // two stages (double buffered) of A slices, then B slices
   __shared__ __attribute__((aligned(16))) Ls7_t Ls;
-  int* red_s = reinterpret_cast<int*>(&Ls[1][0][0]);
   const int tid = threadIdx.x;
-  const int tile = blockIdx.x;
-  const int64_t r0 = static_cast<int64_t>(tile / tiles_c) * TILE, c0 = static_cast<int64_t>(tile % tiles_c) * TILE;
-  if (tid < 4) red_s[tid] = 0;
-  __syncthreads();
-  {
-    const int i = tid & 63;
-    if (tid < 64 && r0 + i < g.rows) {
-      atomicMax(&red_s[0], slices7_of(st.topA[r0 + i], st.lowA[r0 + i]));
-      if (st.badA[r0 + i]) atomicOr(&red_s[2], 1);
-    } else if (tid >= 64 && tid < 128 && c0 + i < g.cols) {
-      atomicMax(&red_s[1], slices7_of(st.topB[c0 + i], st.lowB[c0 + i]));
-      if (st.badB[c0 + i]) atomicOr(&red_s[2], 1);
+  int base = 0;
+  bool have0 = false;
+  int LA, LB, ew;
+  tile7_info(g, st, blockIdx.x, tiles_c, enabled, LA, LB, ew);
+  for (int tile = blockIdx.x; tile < tiles; tile += gridDim.x) {
+    if (tid == 0) {
+      st.flag[tile] = ew;
+      if (ew) atomicAdd(&st.left[0], 1);
     }
-  }
-  __syncthreads();
-  const int LA = __builtin_amdgcn_readfirstlane(red_s[0]), LB = __builtin_amdgcn_readfirstlane(red_s[1]);
-  const bool elsewhere = !enabled || red_s[2] || LA > S7MAX || LB > S7MAX;
-  if (tid == 0) {
-    st.flag[tile] = elsewhere ? 1 : 0;
-    if (elsewhere) atomicAdd(&st.left[0], 1);
-  }
-  if (elsewhere) return;   // uniform over the workgroup
-  if (LA == 0 || LB == 0) {   // an all-zero row or column block: every product is zero
-    using OT = typename O::T;
-    OT* out = static_cast<OT*>(g.out);
-    for (int i = tid; i < TILE * TILE; i += 512) {
-      const int64_t r = r0 + i / TILE, c = c0 + i % TILE;
-      if (r < g.rows && c < g.cols) out[r * g.cols + c] = round_from_f64<O>(0.0);
-    }
-    return;
-  }
-  static_assert(S7MAX == 5, "one case per slice-count pair below");
-  switch (LA * 8 + LB) {
-#define DET_CR7_CASE(a, b)                                                                   \
-  case (a) * 8 + (b):                                                                        \
-    sliced7_tile<O, a, b>(g, st, Ls, r0, c0, SA, SB, npa, npb, kp, sa_bytes, sb_bytes); \
+    const int64_t r0 = static_cast<int64_t>(tile / tiles_c) * TILE, c0 = static_cast<int64_t>(tile % tiles_c) * TILE;
+    const int nt = tile + gridDim.x;
+    int nLA = 0, nLB = 0, nEW = 1;
+    if (nt < tiles) tile7_info(g, st, nt, tiles_c, enabled, nLA, nLB, nEW);
+    const bool pf = !nEW && nLA > 0 && nLB > 0;
+    const int64_t nr0 = static_cast<int64_t>(nt / tiles_c) * TILE, nc0 = static_cast<int64_t>(nt % tiles_c) * TILE;
+    int nb = -1;
+    if (!ew && (LA == 0 || LB == 0)) {   // an all-zero row or column block: every product is zero
+      using OT = typename O::T;
+      OT* out = static_cast<OT*>(g.out);
+      for (int i = tid; i < TILE * TILE; i += 512) {
+        const int64_t r = r0 + i / TILE, c = c0 + i % TILE;
+        if (r < g.rows && c < g.cols) out[r * g.cols + c] = round_from_f64<O>(0.0);
+      }
+    } else if (!ew) {
+      static_assert(S7MAX == 5, "one case per slice-count pair below");
+      switch (LA * 8 + LB) {
+#define DET_CR7_CASE(a, b)                                                                                   \
+  case (a) * 8 + (b):                                                                                        \
+    nb = sliced7_tile<O, a, b>(g, st, Ls, r0, c0, SA, SB, npa, npb, kp, sa_bytes, sb_bytes, base, have0, pf, \
+                               nr0, nc0, nLA, nLB);                                                          \
     break;
 #define DET_CR7_ROW(a) DET_CR7_CASE(a, 1) DET_CR7_CASE(a, 2) DET_CR7_CASE(a, 3) DET_CR7_CASE(a, 4) DET_CR7_CASE(a, 5)
-    DET_CR7_ROW(1) DET_CR7_ROW(2) DET_CR7_ROW(3) DET_CR7_ROW(4) DET_CR7_ROW(5)
+        DET_CR7_ROW(1) DET_CR7_ROW(2) DET_CR7_ROW(3) DET_CR7_ROW(4) DET_CR7_ROW(5)
 #undef DET_CR7_ROW
 #undef DET_CR7_CASE
-    default:
-      break;
+        default:
+          break;
+      }
+    }
+    have0 = nb >= 0;
+    base = nb >= 0 ? nb : 0;
+    LA = nLA;
+    LB = nLB;
+    ew = nEW;
   }
 }
 
@@ -1453,9 +1501,11 @@ hipError_t launch_typed(const GemmArgs& a, int force_fallback, hipStream_t strea
     const int on7 = s7a < (size_t(1) << 31) && s7b < (size_t(1) << 31) ? 1 : 0;
     hipLaunchKernelGGL((slice7_prep_kernel<E, A_RC, B_RC>), dim3(static_cast<unsigned>((npa + npb) / 64 * (kp7 / 64))),
                        dim3(256), 0, stream, a, st, npa, npb, kp7, SA7, SB7, npa / 64 * (kp7 / 64));
-    hipLaunchKernelGGL((sliced7_kernel<O>), dim3(static_cast<unsigned>(tiles)), dim3(512), 0, stream, a, st,
-                       static_cast<int>(tiles_c), SA7, SB7, npa, npb, kp7, static_cast<int64_t>(s7a),
-                       static_cast<int64_t>(s7b), on7);
+    // one workgroup per compute unit when that gives each at least four tiles
+    const int64_t g7 = a.num_cu > 0 && 4 * a.num_cu <= tiles ? a.num_cu : tiles;
+    hipLaunchKernelGGL((sliced7_kernel<O>), dim3(static_cast<unsigned>(g7)), dim3(512), 0, stream, a, st,
+                       static_cast<int>(tiles_c), static_cast<int>(tiles), SA7, SB7, npa, npb, kp7,
+                       static_cast<int64_t>(s7a), static_cast<int64_t>(s7b), on7);
     hipLaunchKernelGGL((slice8_prep_kernel<E, A_RC, B_RC>), dim3(static_cast<unsigned>((npa + npb) / 64 * (kp8 / 64))),
                        dim3(256), 0, stream, a, st, npa, npb, kp8, SA8, SB8, npa / 64 * (kp8 / 64));
     hipLaunchKernelGGL((sliced8_kernel<O>), dim3(static_cast<unsigned>(tiles)), dim3(256), 0, stream, a, st,

@@ -232,3 +232,39 @@ def test_cr_seven_bit_slice_counts(dt):
     A, B = stor(ia * 2.0 ** -24, dt), stor(ib * 2.0 ** -24, dt)
     want = oracle.gemm_cr("fwd", dt, A, B, m, k, n)
     assert_bits_equal(_gpu("fwd", dt, A, B), want, f"7-bit slices, long reduction {dt}")
+
+
+def test_cr_many_tiles_mixed():
+    """More than four 64 x 64 tiles per compute unit (the int8 path's workgroups then take several
+    tiles each and stage a tile's first slices during the previous tile's last stage): row blocks
+    of A with one to five slices, an all-zero row block, a row block past five slices and a column
+    block of B with a non-finite value mixed over 33 x 33 tiles with ragged edges and a bias.
+    Every output against the 23-bit path and the superaccumulator, sampled rows against the oracle."""
+    import deterministic_invariant_gemm_det_amd as dg
+    dt = "bf16"
+    m, k, n = 64 * 32 + 37, 300, 64 * 32 + 5
+    v = vals(syn.normal(1620, 0, (m, k), dt="f32"), "f32")
+    ia = np.clip(np.rint(v * 40.0), -127, 127)
+    ia[:, 1] = 3.0
+    for i in range(m // 64 + 1):
+        ia[64 * i:64 * (i + 1), 0] = 65.0 * 2.0 ** (7 * (i % 5))
+    ia[64 * 7:64 * 8, :] = 0.0                  # all zero: the zero path
+    ia[64 * 11:64 * 12, 2] = 2.0 ** 40          # six slices: another path
+    Bv = vals(syn.normal(1620, 1, (k, n), sigma=0.5, dt=dt), dt)
+    Bv[5, 64 * 9 + 3] = np.inf                  # non-finite: the superaccumulator
+    A, B = stor(ia * 2.0 ** -24, dt), stor(Bv, dt)
+    bias = syn.normal(1620, 2, (n,), sigma=0.3, dt=dt)
+    got = _gpu("fwd", dt, A, B, bias)
+    for path in (2, 1):
+        dg.det_gemm_debug_force_cr_fallback(path)
+        assert_bits_equal(got, _gpu("fwd", dt, A, B, bias), f"many tiles, against path {path}")
+        dg.det_gemm_debug_force_cr_fallback(0)
+    rows = np.array([0, 1, 63, 64, 64 * 7 + 5, 64 * 11 + 9, 64 * 16 + 31, 64 * 25 + 2, m - 1])
+    want = oracle.gemm_cr("fwd", dt, A, B, m, k, n, bias=bias, rows=rows)
+    # a NaN's sign and payload are not part of the result (as in test_cr_nonfinite): positions only
+    def nan16(b):
+        return ((b & 0x7f80) == 0x7f80) & ((b & 0x7f) != 0)
+    g = got[rows]
+    assert np.array_equal(nan16(g), nan16(want)) and nan16(want).any()
+    assert_bits_equal(np.where(nan16(g), 0, g).astype(np.uint16), np.where(nan16(want), 0, want).astype(np.uint16),
+                      "many tiles, sampled rows")
