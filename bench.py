@@ -36,6 +36,7 @@ if ROOT not in sys.path:
 METRIC = "deterministic GEMM TFLOP/s (fp64-KBN & bf16-MFMA tiers) + % of peak, 1 GPU"
 PEAK_FP64 = 78.6      # TFLOP/s, MI355X FP64 vector and FP64 matrix
 PEAK_BF16 = 2516.6    # TFLOP/s, MI355X dense bf16 MFMA
+PEAK_INT8 = 5033.2    # TOP/s, MI355X dense int8 MFMA
 TOKENS = 8192
 LAYERS = (("c_fc", 768, 3072), ("c_proj", 3072, 768))
 OPS = ("fwd", "dx", "dw")
@@ -301,15 +302,23 @@ def next_rows(data, dev):
         out[f"dw_f32.c_fc.{tier}"] = {"us": round(us, 2), "tflops": round(tf, 2),
                                       "roofline": {"bound": "mfma", "achieved": round(tf, 2), "peak": peak,
                                                    "unit": "TFLOP/s", "frac": round(tf / peak, 4)}}
-    # the correctly rounded tier on c_fc (useful flops 2MNK; the kernels run one pass per slice pair)
+    # The correctly rounded tier on c_fc: tflops = useful 2MNK rate; the roofline is the int8
+    # matrix work its 7-bit slice path issues (every 64 x 64 tile of these operands takes it).
+    xb = d["x"].view(torch.int16).cpu().numpy().view("uint16")              # [m][k]
+    wb = d["w"].view(torch.int16).cpu().numpy().view("uint16")              # [k][n]
+    gb = d["g"].view(torch.int16).cpu().numpy().view("uint16")              # [m][n]
+    int8_ops = {"fwd": cr_int8_ops(xb, wb.T.copy(), d["k"]),                 # X rows, W columns
+                "dx": cr_int8_ops(gb, wb, d["n"]),                           # dY rows, W rows
+                "dw": cr_int8_ops(xb.T.copy(), gb.T.copy(), TOKENS)}         # X columns, dY columns
     for op, f in (("fwd", lambda: dg.fwd(d["x"], d["w"], None, "cr", out=d["y"])),
                   ("dx", lambda: dg.dx(d["g"], d["w"], "cr", out=d["gx"])),
                   ("dw", lambda: dg.dw(d["x"], d["g"], "cr", out=d["gw"]))):
         us = _time_calls(f, stream, reps=3, warmup=1)
         tf = fl / (us * 1e-6) / 1e12
-        out[f"cr.c_fc.{op}"] = {"us": round(us, 2), "tflops": round(tf, 2),
-                                "roofline": {"bound": "mfma", "achieved": round(tf, 2), "peak": PEAK_FP64,
-                                             "unit": "TFLOP/s", "frac": round(tf / PEAK_FP64, 4)}}
+        tops = int8_ops[op] / (us * 1e-6) / 1e12
+        out[f"cr.c_fc.{op}"] = {"us": round(us, 2), "tflops": round(tf, 2), "int8_ops": int8_ops[op],
+                                "roofline": {"bound": "mfma", "achieved": round(tops, 2), "peak": PEAK_INT8,
+                                             "unit": "TOP/s", "frac": round(tops / PEAK_INT8, 4)}}
     h = 768
     x = data["c_fc"]["x"]                      # 8192 x 768 bf16
     gy = data["c_proj"]["g"]                   # 8192 x 768 bf16, the LayerNorm's incoming gradient
@@ -322,6 +331,35 @@ def next_rows(data, dev):
     us = _time_calls(lambda: dg.layer_norm_backward(gy, x, mean, rstd, gamma, param_dtype=torch.float32), stream)
     out["layernorm_bwd.8192x768"] = hbm(us, 3 * TOKENS * h * 2 + 16 * TOKENS + h * 2 + 2 * h * 4)
     return out
+
+
+def cr_int8_ops(a_rows, b_cols, red):
+    """Integer operations the correctly rounded tier's int8 path issues for bf16 operands given as
+    uint16 bit arrays a_rows[rows][red] and b_cols[cols][red] (each reduction line contiguous):
+    2 * 64 * 64 * kp per slice pair of every 64 x 64 tile that path takes (kp = red rounded up to
+    128; a line needs (top - low) // 7 + 1 slices of 7 bits, a tile the most of its lines, at
+    most five each side)."""
+    import numpy as np
+
+    def slices(bits):
+        b = bits.astype(np.int32)
+        e, f = (b >> 7) & 0xff, b & 0x7f
+        sig = np.where(e > 0, f | 0x80, f)
+        lsb = np.where(e > 0, e - 134, -133)
+        nz = sig > 0
+        hi = np.where(nz, lsb + np.floor(np.log2(np.maximum(sig, 1))).astype(np.int32), -(1 << 20))
+        ctz = np.log2(sig & -sig, where=nz, out=np.zeros(sig.shape)).astype(np.int32)
+        lo = np.where(nz, lsb + ctz, 1 << 20)
+        top, low = hi.max(axis=1), lo.min(axis=1)
+        n = np.where(top > -(1 << 20), (top - low) // 7 + 1, 0)
+        pad = (-len(n)) % 64
+        return np.pad(n, (0, pad)).reshape(-1, 64).max(axis=1)
+
+    la, lb = slices(a_rows), slices(b_cols)
+    ok_a, ok_b = la <= 5, lb <= 5
+    kp = (red + 127) // 128 * 128
+    pairs = float((la * ok_a).sum()) * float((lb * ok_b).sum())
+    return 2.0 * 64 * 64 * kp * pairs
 
 
 def output_hashes(data, steps):
