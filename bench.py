@@ -62,7 +62,7 @@ def parse():
     p.add_argument("--no-next", action="store_true",
                    help="skip the bias-gradient, f32-dW and LayerNorm measurements")
     p.add_argument("--only", default=None,
-                   help="profiling aid: run only the launches of one tier and op (e.g. exact.dw) and print their times")
+                   help="profiling aid: run only the launches of one tier and op (e.g. exact.dw, cr.fwd) and print their times")
     p.add_argument("--copy-mib", type=int, default=0,
                    help="profiling aid: time a plain device copy of this many MiB instead (counter calibration)")
     return p.parse_args()
@@ -90,10 +90,11 @@ def make_inputs(dev):
 
 
 def launches(data, only=None):
-    """The step as a list of (tier, layer, op, callable); `only` = "tier.op" keeps those launches."""
+    """The step as a list of (tier, layer, op, callable); `only` = "tier.op" keeps those launches
+    (tier "cr", the correctly rounded tier, is not part of the step: profiling only)."""
     import deterministic_invariant_gemm_det_amd as dg
     out = []
-    for tier in ("exact", "fast"):
+    for tier in ("exact", "fast") + (("cr",) if only and only.startswith("cr.") else ()):
         for name, _, _ in LAYERS:
             d = data[name]
             out.append((tier, name, "fwd", lambda d=d, t=tier: dg.fwd(d["x"], d["w"], None, t, out=d["y"])))
@@ -313,7 +314,7 @@ def next_rows(data, dev):
     for op, f in (("fwd", lambda: dg.fwd(d["x"], d["w"], None, "cr", out=d["y"])),
                   ("dx", lambda: dg.dx(d["g"], d["w"], "cr", out=d["gx"])),
                   ("dw", lambda: dg.dw(d["x"], d["g"], "cr", out=d["gw"]))):
-        us = _time_calls(f, stream, reps=3, warmup=1)
+        us = _time_calls(f, stream, reps=10, warmup=2)
         tf = fl / (us * 1e-6) / 1e12
         tops = int8_ops[op] / (us * 1e-6) / 1e12
         out[f"cr.c_fc.{op}"] = {"us": round(us, 2), "tflops": round(tf, 2), "int8_ops": int8_ops[op],
