@@ -268,3 +268,26 @@ def test_cr_many_tiles_mixed():
     assert np.array_equal(nan16(g), nan16(want)) and nan16(want).any()
     assert_bits_equal(np.where(nan16(g), 0, g).astype(np.uint16), np.where(nan16(want), 0, want).astype(np.uint16),
                       "many tiles, sampled rows")
+
+
+def test_cr_many_tiles_long_reduction():
+    """The int8 path's persistent form with more than one exact int32 sum per class: 32 x 32 tiles of
+    64 x 64 over a reduction of 16384 + 136 indices (small integers and one large value per row and
+    column, five slices a side). Every output against the 23-bit path, sampled rows against the oracle."""
+    import deterministic_invariant_gemm_det_amd as dg
+    dt = "bf16"
+    m, k, n = 64 * 32, 16384 + 136, 64 * 32
+    ia = np.clip(np.rint(vals(syn.normal(1630, 0, (m, k), dt="f32"), "f32") * 40.0), -127, 127)
+    ib = np.clip(np.rint(vals(syn.normal(1630, 1, (k, n), dt="f32"), "f32") * 40.0), -127, 127)
+    ia[:, 1] = 1.0
+    ib[1, :] = -1.0
+    ia[:, 0] = 127.0 * 2.0 ** 28
+    ib[0, :] = 127.0 * 2.0 ** 28
+    A, B = stor(ia * 2.0 ** -24, dt), stor(ib * 2.0 ** -24, dt)
+    got = _gpu("fwd", dt, A, B)
+    dg.det_gemm_debug_force_cr_fallback(2)
+    assert_bits_equal(got, _gpu("fwd", dt, A, B), "many tiles, long reduction, against path 2")
+    dg.det_gemm_debug_force_cr_fallback(0)
+    rows = np.array([0, 700, m - 1])
+    want = oracle.gemm_cr("fwd", dt, A, B, m, k, n, rows=rows)
+    assert_bits_equal(got[rows], want, "many tiles, long reduction, sampled rows")
