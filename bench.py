@@ -15,7 +15,7 @@ bandwidth and the CPU oracle's rate on a bounded sample are included.
 
 Per launch the mean time gives the reported rate (median and minimum beside
 it); the SHA-256 of every output is recorded, and each tier is also stated as
-a fraction of the peak the library's own microkernels measure on the box. For context only, the vendor
+a fraction of the peak the library's own microkernels measure on the same GPU. For context only, the vendor
 BLAS behind torch.matmul is timed on the same tensors (it carries no
 determinism contract and is not the product path).
 
@@ -365,7 +365,7 @@ def cr_int8_ops(a_rows, b_cols, red):
 
 def output_hashes(data, steps):
     """SHA-256 (first 16 hex digits) of every GEMM output of one more pass of the step, so runs
-    on different boxes and days can be compared bit for bit."""
+    on different machines and days can be compared bit for bit."""
     import hashlib
     import torch
     out = {}
@@ -642,7 +642,7 @@ def main():
         from deterministic_invariant_gemm_det_amd import peak as dpeak
         peaks = {"fp64_mfma_4x4x4": round(dpeak.measure(0, 4000), 2), "fp64_fma_valu": round(dpeak.measure(1, 4000), 2),
                  "bf16_mfma_32x32x16": round(dpeak.measure(2, 2000), 2), "unit": "TFLOP/s",
-                 "note": "peak-rate microkernels (libdetpeak.so) at the box's running clock (no memory traffic)"}
+                 "note": "peak-rate microkernels (libdetpeak.so) at the GPU's running clock (no memory traffic)"}
         result["measured_peak"] = peaks
         result["tiers"]["exact"]["pct_of_measured_peak"] = round(100 * result["tiers"]["exact"]["tflops"] / peaks["fp64_mfma_4x4x4"], 2)
         result["tiers"]["fast"]["pct_of_measured_peak"] = round(100 * result["tiers"]["fast"]["tflops"] / peaks["bf16_mfma_32x32x16"], 2)

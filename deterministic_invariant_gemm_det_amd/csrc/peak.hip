@@ -1,6 +1,6 @@
 // Peak-rate microkernels for measurement: the instruction each tier is built
 // on, issued back to back with no memory traffic, so that a tier's rate can be
-// stated as a fraction of what the box itself sustains at its running clock
+// stated as a fraction of what the GPU itself sustains at its running clock
 // as well as of the datasheet peak.
 //
 //   kind 0: V_MFMA_F64_4X4X4_4B_F64 (the exact tier's fma chains), eight

@@ -49,7 +49,7 @@ def _check_rows(op, dt, tier, X, W, G, b, m, k, n, y, rows, what):
 
 
 def _host_threads():
-    """Oracle threads: the host cores this process may use, at most 16 (the box's share)."""
+    """Oracle threads: the host cores this process may use, at most 16."""
     try:
         n = len(os.sched_getaffinity(0))
     except AttributeError:
