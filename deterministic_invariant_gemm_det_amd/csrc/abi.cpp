@@ -433,7 +433,7 @@ det_status_t det_gemm_debug_force_family(int family) {
 }
 
 det_status_t det_gemm_debug_force_exact_kernel(int variant) {
-  if (variant < -1 || variant > 5) return fail(DET_EINVAL, "det_gemm: exact kernel must be -1 .. 5%s");
+  if (variant < -1 || variant > 7) return fail(DET_EINVAL, "det_gemm: exact kernel must be -1 .. 7%s");
   g_force_exact.store(variant, std::memory_order_relaxed);
   return DET_OK;
 }

@@ -407,6 +407,125 @@ __global__ void __launch_bounds__(THREADS, NBUF == 1 ? 3 : 2) exact_mfma4_kernel
   }
 }
 
+// ---- m16s kernel (default) ---------------------------------------------------
+//
+// The mfma4 kernel's structure (single LDS buffer, three workgroups per CU, 64
+// or 48 rows x 64 columns, a wave owning all rows x 16 columns) with the
+// tile's chains on V_MFMA_F64_16X16X4_F64: one instruction per 16-row block
+// and k-step instead of four, and one B fragment read instead of four (the
+// instruction computes each output as the same ascending fma chain over its
+// four products, so the bits are unchanged). With 48-row blocks the running
+// sums alternate between two register sets tile by tile (two tiles per loop
+// trip), so Neumaier's s <- t costs no copy; with 64 rows that second set would
+// not fit the registers three workgroups per CU leave.
+template <typename E, bool A_RED_CONTIG, bool B_RED_CONTIG, int BMT, typename O = E>
+__global__ void __launch_bounds__(THREADS, 3) exact_m16s_kernel(GemmArgs args) {
+  constexpr int NU = BMT / 16;
+  constexpr bool PP = NU <= 3;   // ping-pong running sums
+  static_assert(BMT % 16 == 0 && BMT <= BM, "row block");
+  __shared__ double As[KT * LS];
+  __shared__ double Bs[KT * LS];
+  const int64_t tiles_n = (args.cols + BN - 1) / BN;
+  const int64_t row0 = (static_cast<int64_t>(blockIdx.x) / tiles_n) * BMT;
+  const int64_t col0 = (static_cast<int64_t>(blockIdx.x) % tiles_n) * BN;
+  const int wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int wn = wave * 16;
+  const int lr = lane & 15;   // row (A) / column (B, results) inside a 16 x 16 block
+  const int lk = lane >> 4;   // k inside a group of four (operands); row group (results)
+  const Stager<E, A_RED_CONTIG, BMT> sa(static_cast<const typename E::T*>(args.A), args.lda, row0, args.rows, args.red,
+                                        args.vec_a, args.off32_a);
+  const Stager<E, B_RED_CONTIG> sb(static_cast<const typename E::T*>(args.B), args.ldb, col0, args.cols, args.red,
+                                   args.vec_b, args.off32_b);
+  typename decltype(sa)::Raw ra;
+  typename decltype(sb)::Raw rb;
+
+  double s0[NU][4], s1[NU][4], c[NU][4];
+#pragma unroll
+  for (int u = 0; u < NU; ++u)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) { s0[u][e] = 0.0; s1[u][e] = 0.0; c[u][e] = 0.0; }
+
+  const int ntiles = tiles_of(args.red);
+  sa.load(0, ra);
+  sb.load(0, rb);
+  sa.store(As, ra);
+  sb.store(Bs, rb);
+  __syncthreads();
+
+  // tile t: its chains, then (sout, c) <- Neumaier(sin, c, partial)
+  auto step = [&](int t, double (&sin)[NU][4], double (&sout)[NU][4]) {
+    const bool more = t + 1 < ntiles;
+    if (more) { sa.load(t + 1, ra); sb.load(t + 1, rb); }
+    const double* __restrict__ as = As + lk * LS + lr;
+    const double* __restrict__ bs = Bs + lk * LS + wn + lr;
+    v4d p[NU];
+    double a[2][NU], b[2];
+#pragma unroll
+    for (int u = 0; u < NU; ++u) a[0][u] = as[16 * u];
+    b[0] = bs[0];
+#pragma unroll
+    for (int g = 0; g < KT / 4; ++g) {
+      const int cur = g & 1;
+      if (g + 1 < KT / 4) {
+        const int kr = (g + 1) * 4 * LS;
+#pragma unroll
+        for (int u = 0; u < NU; ++u) a[cur ^ 1][u] = as[kr + 16 * u];
+        b[cur ^ 1] = bs[kr];
+      }
+#pragma unroll
+      for (int u = 0; u < NU; ++u)   // the chain of each tile starts from +0
+        p[u] = __builtin_amdgcn_mfma_f64_16x16x4f64(a[cur][u], b[cur], g == 0 ? v4d{0.0, 0.0, 0.0, 0.0} : p[u], 0, 0,
+                                                    0);
+    }
+    __syncthreads();   // every wave is done reading the single buffer
+#pragma unroll
+    for (int u = 0; u < NU; ++u)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {   // kbn_add with the new sum in a register of its own
+        const double sv = sin[u][e], pv = p[u][e];
+        const double tv = sv + pv;
+        const double bp = tv - sv;
+        const double ap = tv - bp;
+        c[u][e] = c[u][e] + ((sv - ap) + (pv - bp));
+        sout[u][e] = tv;
+      }
+    if (more) { sa.store(As, ra); sb.store(Bs, rb); }
+    __syncthreads();
+  };
+  int t = 0;
+  if constexpr (PP) {
+    for (; t + 1 < ntiles; t += 2) {
+      step(t, s0, s1);
+      step(t + 1, s1, s0);
+    }
+  }
+  for (; t < ntiles; ++t) {
+    step(t, s0, s1);
+#pragma unroll
+    for (int u = 0; u < NU; ++u)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) s0[u][e] = s1[u][e];
+  }
+
+  typename O::T* __restrict__ Y = static_cast<typename O::T*>(args.out);
+  const typename E::T* __restrict__ bias = static_cast<const typename E::T*>(args.bias);
+  const int64_t col = col0 + wn + lr;
+  if (col >= args.cols) return;
+  const double bj = bias ? E::up(bias[col]) : 0.0;
+#pragma unroll
+  for (int u = 0; u < NU; ++u)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int64_t row = row0 + 16 * u + 4 * e + lk;   // accumulator e of lane l: row 4e + l/16, column l%16
+      if (row < args.rows) {
+        double v = s0[u][e] + c[u][e];
+        if (bias) v = v + bj;
+        Y[row * args.cols + col] = round_from_f64<O>(v);
+      }
+    }
+}
+
 // ---- mfma16 kernel ----------------------------------------------------------
 
 template <typename E, bool A_RED_CONTIG, bool B_RED_CONTIG>
@@ -683,27 +802,33 @@ hipError_t launch_typed(const GemmArgs& a, int variant, hipStream_t stream) {
     (void)hipGetLastError();   // nothing was enqueued: the blocked kernels below, same bits
     variant = use_48_rows(a) ? 4 : use_mfma16(a) ? 1 : 0;
   }
-  // f32 output: the default kernel in its two row-block forms (identical bits)
+  // f32 output: the default kernel in its two row-block forms, or the mfma4
+  // kernel in the same two forms (identical bits)
   if constexpr (!std::is_same<O, E>::value) {
-    if (variant != 4) variant = 0;
+    if (variant != 4 && variant != 6 && variant != 7) variant = 0;
   }
   const int64_t blocks = ((a.cols + BN - 1) / BN) * ((a.rows + BM - 1) / BM);
   if (blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
   const dim3 grid(static_cast<unsigned>(blocks));
-  // (variants 1 .. 3 write the input type only; for f32 output variant is 0 or 4 here)
+  // (variants 1 .. 3 write the input type only; for f32 output variant is 0, 4, 6 or 7 here)
+  const int64_t b48 = ((a.cols + BN - 1) / BN) * ((a.rows + 47) / 48);
+  if (b48 > 0x7fffffff) return hipErrorInvalidConfiguration;
   if (variant == 1)
     hipLaunchKernelGGL((exact_mfma_kernel<E, AC, BC>), grid, dim3(THREADS), 0, stream, a);
   else if (variant == 2)
     hipLaunchKernelGGL((exact_valu_kernel<E, AC, BC>), grid, dim3(THREADS), 0, stream, a);
   else if (variant == 3)
     hipLaunchKernelGGL((exact_mfma4_kernel<E, AC, BC, 2, 64>), grid, dim3(THREADS), 0, stream, a);
-  else if (variant == 4) {
-    const int64_t b48 = ((a.cols + BN - 1) / BN) * ((a.rows + 47) / 48);
-    if (b48 > 0x7fffffff) return hipErrorInvalidConfiguration;
+  else if (variant == 4)
+    hipLaunchKernelGGL((exact_m16s_kernel<E, AC, BC, 48, O>), dim3(static_cast<unsigned>(b48)), dim3(THREADS), 0,
+                       stream, a);
+  else if (variant == 6)
+    hipLaunchKernelGGL((exact_mfma4_kernel<E, AC, BC, 1, 64, O>), grid, dim3(THREADS), 0, stream, a);
+  else if (variant == 7)
     hipLaunchKernelGGL((exact_mfma4_kernel<E, AC, BC, 1, 48, O>), dim3(static_cast<unsigned>(b48)), dim3(THREADS), 0,
                        stream, a);
-  } else
-    hipLaunchKernelGGL((exact_mfma4_kernel<E, AC, BC, 1, 64, O>), grid, dim3(THREADS), 0, stream, a);
+  else
+    hipLaunchKernelGGL((exact_m16s_kernel<E, AC, BC, 64, O>), grid, dim3(THREADS), 0, stream, a);
   return hipGetLastError();
 }
 

@@ -280,13 +280,15 @@ det_status_t det_gemm_debug_force_family(int family);
 
 /*
  * Test hook: force the exact tier's kernel for later calls from any thread
- * (-1 automatic, 0 = 4x4x4 float64 matrix-core kernel with 64-row blocks,
- * 1 = 16x16x4 float64 matrix-core kernel, 2 = float64 vector-ALU kernel,
- * 3 = the 4x4x4 kernel with a double-buffered LDS stage, 4 = the 4x4x4 kernel
- * with 48-row blocks, 5 = the few-rows path: tile partials of every output in
- * parallel, then the ordered combine, through the stream's workspace). All
- * produce the same bits (the oracle's), so this changes speed only. Returns
- * DET_EINVAL for other values.
+ * (-1 automatic, 0 = 16x16x4 float64 matrix-core kernel with 64-row blocks of
+ * 64 x 16 per wave, 1 = 16x16x4 kernel with 32 x 32 per wave and a
+ * double-buffered LDS stage, 2 = float64 vector-ALU kernel, 3 = 4x4x4 float64
+ * matrix-core kernel with a double-buffered LDS stage, 4 = kernel 0 with
+ * 48-row blocks, 5 = the few-rows path: tile partials of every output in
+ * parallel, then the ordered combine, through the stream's workspace, 6 = the
+ * 4x4x4 kernel with 64-row blocks and one LDS stage, 7 = that kernel with
+ * 48-row blocks). All produce the same bits (the oracle's), so this changes
+ * speed only. Returns DET_EINVAL for other values.
  */
 det_status_t det_gemm_debug_force_exact_kernel(int variant);
 

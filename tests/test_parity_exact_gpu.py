@@ -38,7 +38,8 @@ def _auto_variant():
     dg.det_gemm_debug_force_exact_kernel(-1)
 
 
-@pytest.mark.parametrize("variant", [0, 1, 2, 3, 4, 5], ids=["mfma4", "mfma16", "valu", "mfma4db", "mfma4r48", "skinny"])
+@pytest.mark.parametrize("variant", [0, 1, 2, 3, 4, 5, 6, 7],
+                         ids=["m16s", "mfma16", "valu", "mfma4db", "m16s48", "skinny", "mfma4", "mfma4r48"])
 @pytest.mark.parametrize("dt", DTS)
 @pytest.mark.parametrize("op", ["fwd", "dx", "dw"])
 def test_ragged_shapes(op, dt, variant):
@@ -65,8 +66,8 @@ def test_integer_inputs_exact(dt):
             assert_bits_equal(gpu_op(op, dt, A, B), want, f"int {op} {dt} {(m, k, n)}")
 
 
-VARIANTS = [0, 1, 2, 3, 4, 5]
-VARIANT_IDS = ["mfma4", "mfma16", "valu", "mfma4db", "mfma4r48", "skinny"]
+VARIANTS = [0, 1, 2, 3, 4, 5, 6, 7]
+VARIANT_IDS = ["m16s", "mfma16", "valu", "mfma4db", "m16s48", "skinny", "mfma4", "mfma4r48"]
 
 
 @pytest.mark.parametrize("variant", VARIANTS, ids=VARIANT_IDS)
