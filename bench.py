@@ -616,9 +616,9 @@ def main():
     dom_tf = dom_flops / (dom_us * 1e-6) / 1e12
     roofline = {"bound": "mfma", "achieved": round(dom_tf, 2), "peak": PEAK_FP64, "unit": "TFLOP/s",
                 "frac": round(dom_tf / PEAK_FP64, 4), "traffic": stored_traffic(),
-                "kernel": "exact_mfma4_kernel<BF16, dW> (exact.c_fc.dw, exact.c_proj.dw)",
+                "kernel": "exact_m16s_kernel<BF16, 48-row blocks, dW> (exact.c_fc.dw, exact.c_proj.dw)",
                 "avg_launch_us": round(dom_us, 2), "flops_per_launch": dom_flops,
-                "note": "exact tier on FP64 matrix cores (V_MFMA_F64_4X4X4); peak is MI355X FP64 (vector = matrix)"}
+                "note": "exact tier on FP64 matrix cores (V_MFMA_F64_16X16X4); peak is MI355X FP64 (vector = matrix)"}
     fast = tier_stats("fast", PEAK_BF16)
     roofline_fast = {"bound": "mfma", "achieved": fast["tflops"], "peak": PEAK_BF16, "unit": "TFLOP/s",
                      "frac": round(fast["tflops"] / PEAK_BF16, 4), "traffic": None,
