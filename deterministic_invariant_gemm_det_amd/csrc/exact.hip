@@ -770,13 +770,15 @@ bool use_48_rows(const GemmArgs& a) {
   return l48 < l64;
 }
 
-// Small grids: with at most two 64 x 64 blocks per compute unit (and 48-row
-// blocks no better), the mfma16 kernel's double-buffered stage runs them
-// faster than mfma4 (measured: GPT-2 QKV dW 779 -> 726 us, fwd of 512 rows
-// into 3072 columns 80.3 -> 74.8 us; no worse elsewhere). Same bits.
+// Small grids over short reductions: with at most two 64 x 64 blocks per
+// compute unit (and 48-row blocks no better) and at most 4096 reduction
+// indices, the mfma16 kernel's double-buffered stage runs them a little faster
+// than the default (measured: fwd of 512 rows into 3072 columns 74.8 -> 73.3
+// us, dX of 1024 rows 165.8 -> 161.8); over long reductions the default is
+// faster (GPT-2 QKV dW 731 -> 699 us). Same bits.
 bool use_mfma16(const GemmArgs& a) {
   const int64_t units = a.num_cu > 0 ? a.num_cu : 1;
-  return ((a.cols + BN - 1) / BN) * ((a.rows + BM - 1) / BM) <= 2 * units;
+  return ((a.cols + BN - 1) / BN) * ((a.rows + BM - 1) / BM) <= 2 * units && a.red <= 4096;
 }
 
 // The few-rows path keeps every tile partial: 8 * rows * cols * ceil(red / 32)
