@@ -412,14 +412,18 @@ hipError_t launch_fast(Op op, Dt dt, const GemmArgs& a, int family, hipStream_t 
   if (op == OP_FWD && dt != DT_F32 && (automatic || family == 16) && fast16_skinny_ok(a))
     return launch_fast16_skinny(dt, a, stream);
   if (family == 16) family = 0;
-  // Forward of 16-bit inputs with many rows and a long reduction: the weight
-  // copied transposed first ([n][k], contiguous along the reduction), so that
-  // the kernel stages both operands straight into LDS, as for dX. Same values
-  // in the same instruction order, so the same bits. Measured: GPT-2 c_proj
-  // (k = 3072) 53.9 -> 49.8 us and 4096 x 11008 x 4096 915 -> 849 us at
-  // m = 8192; slower for k = 768 (c_fc 51.4 -> 52.7 us) and, the copy being
-  // 2 k n bytes each way, on few rows.
-  if (op == OP_FWD && dt != DT_F32 && family == 0 && fast16_w_ok(a) && a.rows >= 4096 && a.red >= 3072 &&
+  // Forward of 16-bit inputs with many rows and a long reduction or a wide
+  // output: the weight copied transposed first ([n][k], contiguous along the
+  // reduction), so that the kernel stages both operands straight into LDS, as
+  // for dX. Same values in the same instruction order, so the same bits.
+  // Measured: GPT-2 c_proj (k = 3072) 53.9 -> 49.8 us and 4096 x 11008 x 4096
+  // 915 -> 849 us at m = 8192; with k = 768: QKV (n = 2304) 46.8 -> 44.6 us,
+  // c_fc (n = 3072) 50.7 -> 50.1 us and at m = 16384 97.7 -> 90.1 us,
+  // 4096 x 1024 x 4096 56.3 -> 52.1 us; slower into 768 columns
+  // (attention projection 18.0 -> 19.5 us) and, the copy being 2 k n bytes
+  // each way, on few rows.
+  if (op == OP_FWD && dt != DT_F32 && family == 0 && fast16_w_ok(a) && a.rows >= 4096 &&
+      (a.red >= 3072 || a.cols >= 1536) &&
       a.red % 8 == 0 && a.cols % 8 == 0 && a.red <= int64_t(64) * 65535 && a.cols * a.red * 2 < (int64_t(1) << 31)) {
     void* ws = nullptr;
     hipError_t e = stream_workspace(stream, static_cast<size_t>(a.cols) * static_cast<size_t>(a.red) * 2, &ws);

@@ -56,7 +56,8 @@
  *   The caller owns every buffer. The library keeps no reference to any of
  *   them. Some calls need device memory beyond their inputs and outputs (a
  *   workspace); the library keeps one per (device, stream):
- *     - fast tier, bf16/f16 forward with k >= 3072 and m >= 4096: a transposed
+ *     - fast tier, bf16/f16 forward with m >= 4096 and k >= 3072 or
+ *       n >= 1536: a transposed
  *       copy of the weight, 2 * k * n bytes (when it cannot be had, the call
  *       runs without the copy: same bits);
  *     - fast tier, bf16/f16 dW: possibly a transposed copy of its smaller

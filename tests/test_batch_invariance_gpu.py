@@ -46,7 +46,8 @@ def test_m_sweep(dt, tier):
 @pytest.mark.parametrize("dt", ["bf16", "f16"])
 def test_m_sweep_long_reduction_fast(dt):
     """K = 3072, N = 768 (GPT-2 c_proj): from m = 4096 on, the fast forward
-    first copies the weight transposed; rows must not change across that
+    first copies the weight transposed (for K = 768, N = 3072 the same switch
+    sits inside the main sweep's 4095/4096); rows must not change across that
     switch (nor anywhere else in the sweep), with and without the bias."""
     import deterministic_invariant_gemm_det_amd as dg
     k, n = 3072, 768
