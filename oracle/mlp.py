@@ -3,7 +3,7 @@
 End-to-end reproducibility check in the spirit of the Carbon README
 (alia-carbon 0.2.0), "The Proof": train a small model from a seed and hash
 every weight tensor with SHA-256. The model, data and optimiser are not given
-there; this run fixes them (readings listed in the design doc):
+there; this module fixes them as follows:
   forward  h_l = fwd(a_{l-1}, W_l, b_l) with the compensated tiled GEMM;
            a_l = h_l if h_l > 0 else +0.0 for l = 1..3; the last layer is linear;
   loss     mean squared error over the 128 x 64 outputs; its gradient is

@@ -14,7 +14,7 @@
 // tiles, the operands are upcast to float64, and the tile results are
 // accumulated with Kahan-Babushka-Neumaier (KBN) compensation in a fixed order.
 // The page leaves the tile geometry and the within-tile order open; the
-// readings taken here (each one listed in DESIGN.md, "Readings of the pages"):
+// readings taken here:
 //   * the reduction index is cut into tiles of KT = 32 consecutive indices,
 //     anchored at index 0; the last tile may be short;
 //   * inside tile t the partial is p_t = +0.0 followed by p_t = fma(a_k, b_k, p_t)
