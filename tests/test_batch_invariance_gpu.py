@@ -68,6 +68,7 @@ def test_m_sweep_long_reduction_fast(dt):
 # with m for K = 768, N = 3072 (each choice gives the same bits; the rows must not change):
 #   fwd: 128 x 64 tiles when m is a multiple of 128 and 256 x 192 tiles would number fewer
 #        than 256 (m <= 3840), else 256 x 192 tiles -- m = 127/128/129, 3840/3841/3968;
+#        from m = 4096 on, the weight copied transposed first -- m = 4095/4096;
 #   dX (768 columns): 64 x 192 tiles when m is a multiple of 64 and 128 x 192 tiles would
 #        number fewer than 256 (m <= 8064), else 128 x 192 -- m = 63/64/65, 8064/8065/8128;
 #   plus the few-rows limit of the exact tier (m = 32/33).
